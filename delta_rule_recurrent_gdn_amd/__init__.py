@@ -1,0 +1,10 @@
+"""Gated Delta Rule-2 (GDN-2) operator for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+include/gdn2.h (libgdn2.so, built in-tree by ``delta_rule_recurrent_gdn_amd.build``).
+This package only marshals torch tensors and streams into that ABI.
+"""
+
+from .ops import gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked, gdn2_workspace_bytes  # noqa: F401
+
+__all__ = ["gdn2_fwd_chunked", "gdn2_decode_step", "gdn2_bwd_chunked", "gdn2_workspace_bytes"]

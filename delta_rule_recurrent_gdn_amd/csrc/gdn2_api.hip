@@ -1,0 +1,174 @@
+// gdn2_api.hip -- the C ABI declared in include/gdn2.h: argument validation,
+// workspace sizing, dispatch to the kernel launchers. No allocation, no host
+// synchronisation, no state between calls.
+
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "gdn2.h"
+#include "gdn2_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common checks of sizes, dtype and pointer alignment. Returns GDN2_OK or an error.
+int check_common(int B, int T, int H, int Dk, int Dv, int dt) {
+  if (dt != GDN2_F32 && dt != GDN2_BF16) return GDN2_ERR_DTYPE;
+  if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return GDN2_ERR_SHAPE;
+  // token indices are int32 inside the kernels
+  if (T > (1 << 30)) return GDN2_ERR_SHAPE;
+  if (!dim_ok(Dk) || !dim_ok(Dv)) return GDN2_ERR_UNSUPPORTED;
+  return GDN2_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> required, std::initializer_list<const void*> optional) {
+  for (const void* p : required)
+    if (p == nullptr) return GDN2_ERR_NULL;
+  for (const void* p : required)
+    if (!aligned16(p)) return GDN2_ERR_ALIGN;
+  for (const void* p : optional)
+    if (p != nullptr && !aligned16(p)) return GDN2_ERR_ALIGN;
+  return GDN2_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; }
+
+size_t state_bytes(int B, int H, int Dk, int Dv) { return (size_t)B * H * Dk * Dv * sizeof(float); }
+
+size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk) {
+  const size_t nc = (size_t)((T + chunk - 1) / chunk);
+  // gradient of every chunk's exit state, plus room to recompute the chunk
+  // entry states when the caller passes none; each part 256-byte aligned
+  const size_t part = nc * state_bytes(B, H, Dk, Dv);
+  const size_t aligned = (part + 255) & ~(size_t)255;
+  return 2 * aligned;
+}
+
+}  // namespace
+
+namespace gdn2 {
+
+// dst[i] = src ? src[i] : 0 -- a plain kernel rather than a memset/memcpy node so
+// that the call can be captured into a HIP graph and replayed.
+__global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace gdn2
+
+extern "C" {
+
+int gdn2_version(void) { return kVersion; }
+
+const char* gdn2_status_string(int status) {
+  switch (status) {
+    case GDN2_OK: return "GDN2_OK: success";
+    case GDN2_ERR_NULL: return "GDN2_ERR_NULL: a required pointer is NULL";
+    case GDN2_ERR_SHAPE: return "GDN2_ERR_SHAPE: a size is negative or too large";
+    case GDN2_ERR_DTYPE: return "GDN2_ERR_DTYPE: unknown input dtype";
+    case GDN2_ERR_ALIGN: return "GDN2_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case GDN2_ERR_UNSUPPORTED: return "GDN2_ERR_UNSUPPORTED: Dk, Dv or chunk not supported";
+    case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE: workspace missing or too small";
+    case GDN2_ERR_HIP: return "GDN2_ERR_HIP: a HIP call or kernel launch failed";
+  }
+  return "unknown gdn2 status";
+}
+
+size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chunk, int dt) {
+  if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK) return 0;
+  if (op == GDN2_OP_BWD) {
+    if (!chunk_ok(chunk) || T == 0) return 0;
+    return bwd_workspace(B, T, H, Dk, Dv, chunk);
+  }
+  return 0;
+}
+
+int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, const float* S0, float* o, float* S_final, float* chunk_states, int B,
+                     int T, int H, int Dk, int Dv, int chunk, int dt, void* stream) {
+  int st = check_common(B, T, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
+  if (!gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32)) return GDN2_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    st = check_ptrs({}, {S0, S_final});
+    if (st != GDN2_OK) return st;
+    if (S_final == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(S_final, S0, (int64_t)B * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
+  if (st != GDN2_OK) return st;
+  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
+  return hip_status(gdn2::launch_fwd(a, s));
+}
+
+int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, float* S, float* o, int B, int H, int Dk, int Dv, int dt, void* stream) {
+  int st = check_common(B, 1, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if (B == 0 || H == 0) return GDN2_OK;
+  st = check_ptrs({q, k, v, log_alpha, b, w, S, o}, {});
+  if (st != GDN2_OK) return st;
+  gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dt == GDN2_F32};
+  return hip_status(gdn2::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, const float* S0, const void* dO, const float* dS_final,
+                     const float* chunk_states, float* dq, float* dk, float* dv, float* dlog_alpha, float* db,
+                     float* dw, float* dS0, void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                     int Dv, int chunk, int dt, void* stream) {
+  int st = check_common(B, T, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
+  if (!gdn2::bwd_supported(Dk, Dv, chunk, dt == GDN2_F32) || !gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32))
+    return GDN2_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    // no tokens: S_T = S0, so dS0 = dS_final
+    st = check_ptrs({}, {dS_final, dS0});
+    if (st != GDN2_OK) return st;
+    if (dS0 == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(dS0, dS_final, (int64_t)B * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, dO, dq, dk, dv, dlog_alpha, db, dw},
+                  {S0, dS_final, chunk_states, dS0});
+  if (st != GDN2_OK) return st;
+  const size_t need = bwd_workspace(B, T, H, Dk, Dv, chunk);
+  if (workspace == nullptr || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  float* dS_chunks = reinterpret_cast<float*>(ws);
+  float* states = const_cast<float*>(chunk_states);
+  if (states == nullptr) {
+    states = reinterpret_cast<float*>(ws + need / 2);
+    gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, B, T, H, Dk, Dv, chunk,
+                    dt == GDN2_F32};
+    st = hip_status(gdn2::launch_fwd(f, s));
+    if (st != GDN2_OK) return st;
+  }
+  gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
+                  dS0, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
+  return hip_status(gdn2::launch_bwd(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,306 @@
+// gdn2_common.h -- device helpers shared by the GDN-2 kernels (gfx950, wave64).
+//
+// Matrix-core tiles are 16x16 with fp32 accumulators. For every
+// v_mfma_f32_16x16xK instruction used here, lane l of the wave supplies row
+// (l % 16) of the left operand and column (l % 16) of the right operand, with
+// a contiguous group of K/4 contraction indices selected by (l / 16); the
+// accumulator holds column (l % 16), rows 4*(l/16) .. 4*(l/16)+3. The two
+// operands always take their contraction indices from the same lane slot, so
+// the products below only rely on that row/column assignment and on the
+// accumulator layout.
+//
+// Operands staged in LDS are stored "K-contiguous": a left operand X as
+// [M][K] and a right operand as [N][K] (its transpose), both row-major with a
+// padded leading dimension, so every lane reads its contraction group with one
+// vector load. C(16x16) += X(16xK) * Y(16xK)^T is the basic tile product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------------------
+// storage conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf16>(f); }
+__device__ __forceinline__ float bf16_to_f32(__bf16 h) { return static_cast<float>(h); }
+
+// Load 8 consecutive inputs of storage type (fp32 or bf16) as fp32.
+template <bool F32IN>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&out)[8]) {
+  if constexpr (F32IN) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// Load 4 consecutive inputs as fp32.
+template <bool F32IN>
+__device__ __forceinline__ void load4(const void* base, int64_t idx, float (&out)[4]) {
+  if constexpr (F32IN) {
+    float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    out[0] = __uint_as_float(u.x << 16);
+    out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16);
+    out[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+}
+
+template <bool F32IN>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (F32IN) return static_cast<const float*>(base)[idx];
+  else return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core primitives
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// C += X(16xK) Y(16xK)^T with X, Y in LDS, K-contiguous rows; K % 16 == 0.
+// T = _Float16 or __bf16 (16-bit matrix-core operands) or float (fp32 matrix cores).
+template <typename T>
+__device__ __forceinline__ void mma_nt(f32x4& acc, const T* X, int ldx, const T* Y, int ldy, int K) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    int k0 = 0;
+    for (; k0 + 32 <= K; k0 += 32) {
+      const v8 a = *reinterpret_cast<const v8*>(X + r * ldx + k0 + 8 * g);
+      const v8 b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      acc = mfma16x16x32(a, b, acc);
+    }
+    if (k0 < K) {
+      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + k0 + 4 * g);
+      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + k0 + 4 * g);
+      acc = mfma16x16x16(a, b, acc);
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
+  }
+}
+
+// Compile-time-K variant (fully unrolled).
+template <int K, typename T>
+__device__ __forceinline__ void mma_nt_k(f32x4& acc, const T* X, int ldx, const T* Y, int ldy) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    typedef T v4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int k0 = 0; k0 + 32 <= K; k0 += 32) {
+      const v8 a = *reinterpret_cast<const v8*>(X + r * ldx + k0 + 8 * g);
+      const v8 b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      acc = mfma16x16x32(a, b, acc);
+    }
+    if constexpr (K % 32 == 16) {
+      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + (K - 16) + 4 * g);
+      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + (K - 16) + 4 * g);
+      acc = mfma16x16x16(a, b, acc);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
+  }
+}
+
+// Split product for wide-range operands: X = Xh + Xl, Y = Yh + Yl (bf16 pairs);
+// C += Xh Yh^T + Xh Yl^T + Xl Yh^T  (the Xl Yl^T term is below fp32 rounding).
+template <int K>
+__device__ __forceinline__ void mma_nt_split_k(f32x4& acc, const __bf16* Xh, const __bf16* Xl, int ldx,
+                                               const __bf16* Yh, const __bf16* Yl, int ldy) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 + 32 <= K; k0 += 32) {
+    const int ox = r * ldx + k0 + 8 * g, oy = r * ldy + k0 + 8 * g;
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Xh + ox);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(Xl + ox);
+    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Yh + oy);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Yl + oy);
+    acc = mfma16x16x32(al, bh, acc);
+    acc = mfma16x16x32(ah, bl, acc);
+    acc = mfma16x16x32(ah, bh, acc);
+  }
+  if constexpr (K % 32 == 16) {
+    const int ox = r * ldx + (K - 16) + 4 * g, oy = r * ldy + (K - 16) + 4 * g;
+    const bf16x4 ah = *reinterpret_cast<const bf16x4*>(Xh + ox);
+    const bf16x4 al = *reinterpret_cast<const bf16x4*>(Xl + ox);
+    const bf16x4 bh = *reinterpret_cast<const bf16x4*>(Yh + oy);
+    const bf16x4 bl = *reinterpret_cast<const bf16x4*>(Yl + oy);
+    acc = mfma16x16x16(al, bh, acc);
+    acc = mfma16x16x16(ah, bl, acc);
+    acc = mfma16x16x16(ah, bh, acc);
+  }
+}
+
+// C += X Y^T where X and Y are fp32 in LDS, converted on load to the operand
+// type T. Y is read either K-contiguous ([N][K], YT=true) or as [K][N]
+// (YT=false). Used for the small triangular products; K % 16 == 0.
+template <typename T, bool YT>
+__device__ __forceinline__ void mma_f32src(f32x4& acc, const float* X, int ldx, const float* Y, int ldy, int K) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      v4 a, b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + 4 * g + i;
+        a[i] = static_cast<T>(X[r * ldx + k]);
+        b[i] = static_cast<T>(YT ? Y[r * ldy + k] : Y[k * ldy + r]);
+      }
+      acc = mfma16x16x16(a, b, acc);
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      const int k = k0 + g;
+      acc = mfma16x16x4(X[r * ldx + k], YT ? Y[r * ldy + k] : Y[k * ldy + r], acc);
+    }
+  }
+}
+
+// C += X Y^T with X 16-bit in LDS (K-contiguous) and Y fp32 in LDS K-contiguous,
+// converted on load. K % 16 == 0.
+template <typename T>
+__device__ __forceinline__ void mma_nt_yf32(f32x4& acc, const T* X, int ldx, const float* Y, int ldy, int K) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    int k0 = 0;
+    for (; k0 + 32 <= K; k0 += 32) {
+      const v8 a = *reinterpret_cast<const v8*>(X + r * ldx + k0 + 8 * g);
+      const float4 y0 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 8 * g);
+      const float4 y1 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 8 * g + 4);
+      v8 b;
+      b[0] = static_cast<T>(y0.x); b[1] = static_cast<T>(y0.y); b[2] = static_cast<T>(y0.z); b[3] = static_cast<T>(y0.w);
+      b[4] = static_cast<T>(y1.x); b[5] = static_cast<T>(y1.y); b[6] = static_cast<T>(y1.z); b[7] = static_cast<T>(y1.w);
+      acc = mfma16x16x32(a, b, acc);
+    }
+    if (k0 < K) {
+      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + k0 + 4 * g);
+      const float4 y0 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 4 * g);
+      v4 b;
+      b[0] = static_cast<T>(y0.x); b[1] = static_cast<T>(y0.y); b[2] = static_cast<T>(y0.z); b[3] = static_cast<T>(y0.w);
+      acc = mfma16x16x16(a, b, acc);
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
+  }
+}
+
+// Same with X fp32 (converted) and Y 16-bit.
+template <typename T>
+__device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx, const T* Y, int ldy, int K) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    int k0 = 0;
+    for (; k0 + 32 <= K; k0 += 32) {
+      const float4 x0 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 8 * g);
+      const float4 x1 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 8 * g + 4);
+      v8 a;
+      a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
+      a[4] = static_cast<T>(x1.x); a[5] = static_cast<T>(x1.y); a[6] = static_cast<T>(x1.z); a[7] = static_cast<T>(x1.w);
+      const v8 b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      acc = mfma16x16x32(a, b, acc);
+    }
+    if (k0 < K) {
+      const float4 x0 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 4 * g);
+      v4 a;
+      a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
+      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + k0 + 4 * g);
+      acc = mfma16x16x16(a, b, acc);
+    }
+  } else {
+    for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// accumulator tile stores (lane holds rows 4*(l/16)+i, column l%16)
+// ---------------------------------------------------------------------------
+// Row-major store of a tile into an LDS/global matrix [rows][ld] of type T.
+template <typename T>
+__device__ __forceinline__ void store_tile(T* dst, int ld, const f32x4& acc, float scale = 1.f) {
+  const int l = lane_id();
+  const int c = l & 15, r0 = 4 * (l >> 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(r0 + i) * ld + c] = static_cast<T>(scale * acc[i]);
+}
+
+// Transposed store: dst[col][row] so the 4 rows of a lane are contiguous.
+template <typename T>
+__device__ __forceinline__ void store_tile_t(T* dst, int ld, const f32x4& acc, float scale = 1.f) {
+  const int l = lane_id();
+  const int c = l & 15, r0 = 4 * (l >> 4);
+  if constexpr (sizeof(T) == 2) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    v4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<T>(scale * acc[i]);
+    *reinterpret_cast<v4*>(dst + c * ld + r0) = v;
+  } else {
+    *reinterpret_cast<float4*>(dst + c * ld + r0) =
+        make_float4(scale * acc[0], scale * acc[1], scale * acc[2], scale * acc[3]);
+  }
+}
+
+}  // namespace gdn2

@@ -1,0 +1,146 @@
+// gdn2_decode.hip -- one-token decode step of the Gated Delta Rule-2 operator.
+//
+// Constant-memory decoding (arXiv 2605.22791 abstract): per (batch, head) the
+// fp32 state S (Dk x Dv) is read once and written once:
+//   S~ = Diag(alpha) S,  r = S~^T (b*k),  p = S~^T q,  u = w*v - r,
+//   o  = p + (k.q) u,    S <- S~ + k u^T
+// (o = S_new^T q expanded so that a single pass over S~ gives both reads).
+//
+// Roofline: HBM-bound. Per (b, h): 2 * 4 * Dk * Dv state bytes plus the small
+// per-token vectors; about 7 flops per state element on the fp32 vector ALUs.
+//
+// Layout of the work: one workgroup per (b, h). Each thread owns 4 adjacent
+// value columns (one float4) of RPT key rows; consecutive threads cover a row
+// from left to right, so each wave-wide load or store touches one contiguous
+// block of the state. Column partial sums of r and p are reduced across row
+// groups through LDS.
+
+#include "gdn2_common.h"
+#include "gdn2_internal.h"
+
+namespace gdn2 {
+
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int kCols4 = DV / 4;                               // threads per state row
+  static constexpr int kThreads = (kCols4 * DK < 256) ? kCols4 * DK : 256;
+  static constexpr int kRowGroups = kThreads / kCols4;
+  static constexpr int kRowsPerThread = DK / kRowGroups;
+  static_assert(kRowsPerThread >= 1 && kRowGroups * kRowsPerThread == DK, "decode tiling");
+};
+
+template <int DK, int DV, bool F32IN>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_kernel(DecodeArgs a) {
+  using Sh = DecodeShape<DK, DV>;
+  constexpr int NT = Sh::kThreads, RG = Sh::kRowGroups, RPT = Sh::kRowsPerThread, C4 = Sh::kCols4;
+  constexpr int NWAVES = (NT + kWave - 1) / kWave;
+
+  __shared__ float s_alpha[DK], s_e[DK], s_q[DK], s_k[DK];
+  __shared__ float s_red_r[RG][DV + 4], s_red_p[RG][DV + 4];
+  __shared__ float s_wsum[NWAVES];
+
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t vec_k = bh * DK, vec_v = bh * DV;
+  float* S = a.S + bh * (int64_t)DK * DV;
+
+  // per-channel key-side vectors
+  float kq = 0.f;
+  if (tid < DK) {
+    const float qv = load1<F32IN>(a.q, vec_k + tid);
+    const float kv = load1<F32IN>(a.k, vec_k + tid);
+    const float bv = load1<F32IN>(a.b, vec_k + tid);
+    s_alpha[tid] = expf(a.log_alpha[vec_k + tid]);
+    s_e[tid] = bv * kv;
+    s_q[tid] = qv;
+    s_k[tid] = kv;
+    kq = kv * qv;
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
+  if ((tid & (kWave - 1)) == 0) s_wsum[tid / kWave] = kq;
+
+  // stream the state rows owned by this thread
+  const int j4 = tid % C4, rg = tid / C4;
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const float4*>(S + (rg + RG * i) * DV + 4 * j4);
+  __syncthreads();
+
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + RG * i;
+    const float al = s_alpha[c], e = s_e[c], qc = s_q[c];
+    s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
+    r.x += e * s[i].x; r.y += e * s[i].y; r.z += e * s[i].z; r.w += e * s[i].w;
+    p.x += qc * s[i].x; p.y += qc * s[i].y; p.z += qc * s[i].z; p.w += qc * s[i].w;
+  }
+  *reinterpret_cast<float4*>(&s_red_r[rg][4 * j4]) = r;
+  *reinterpret_cast<float4*>(&s_red_p[rg][4 * j4]) = p;
+  __syncthreads();
+
+  r = make_float4(0.f, 0.f, 0.f, 0.f);
+  p = r;
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const float4 x = *reinterpret_cast<const float4*>(&s_red_r[g][4 * j4]);
+    const float4 y = *reinterpret_cast<const float4*>(&s_red_p[g][4 * j4]);
+    r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+    p.x += y.x; p.y += y.y; p.z += y.z; p.w += y.w;
+  }
+  float kqs = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < NWAVES; ++wv) kqs += s_wsum[wv];
+
+  float vv[4], wg[4];
+  load4<F32IN>(a.v, vec_v + 4 * j4, vv);
+  load4<F32IN>(a.w, vec_v + 4 * j4, wg);
+  const float4 u = make_float4(wg[0] * vv[0] - r.x, wg[1] * vv[1] - r.y, wg[2] * vv[2] - r.z, wg[3] * vv[3] - r.w);
+  if (rg == 0) {
+    *reinterpret_cast<float4*>(a.o + vec_v + 4 * j4) =
+        make_float4(p.x + kqs * u.x, p.y + kqs * u.y, p.z + kqs * u.z, p.w + kqs * u.w);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + RG * i;
+    const float kc = s_k[c];
+    const float4 n = make_float4(s[i].x + kc * u.x, s[i].y + kc * u.y, s[i].z + kc * u.z, s[i].w + kc * u.w);
+    *reinterpret_cast<float4*>(S + c * DV + 4 * j4) = n;
+  }
+}
+
+template <int DK, int DV, bool F32IN>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  using Sh = DecodeShape<DK, DV>;
+  hipLaunchKernelGGL((gdn2_decode_kernel<DK, DV, F32IN>), dim3(a.B * a.H), dim3(Sh::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK, bool F32IN>
+static hipError_t launch_decode_dv(const DecodeArgs& a, hipStream_t s) {
+  switch (a.Dv) {
+    case 16: return launch_decode_t<DK, 16, F32IN>(a, s);
+    case 32: return launch_decode_t<DK, 32, F32IN>(a, s);
+    case 64: return launch_decode_t<DK, 64, F32IN>(a, s);
+    case 128: return launch_decode_t<DK, 128, F32IN>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool F32IN>
+static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t s) {
+  switch (a.Dk) {
+    case 16: return launch_decode_dv<16, F32IN>(a, s);
+    case 32: return launch_decode_dv<32, F32IN>(a, s);
+    case 64: return launch_decode_dv<64, F32IN>(a, s);
+    case 128: return launch_decode_dv<128, F32IN>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.f32_inputs ? launch_decode_dk<true>(a, stream) : launch_decode_dk<false>(a, stream);
+}
+
+}  // namespace gdn2

@@ -1,0 +1,69 @@
+// gdn2_internal.h -- argument blocks and launchers shared between the C ABI
+// (gdn2_api.hip) and the kernel translation units. Not a public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const void* b;
+  const void* w;
+  float* S;
+  float* o;
+  int B, H, Dk, Dv;
+  bool f32_inputs;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const void* b;
+  const void* w;
+  const float* S0;       // nullable
+  float* o;
+  float* S_final;        // nullable
+  float* chunk_states;   // nullable
+  int B, T, H, Dk, Dv, chunk;
+  bool f32_inputs;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const void* b;
+  const void* w;
+  const void* dO;
+  const float* dS_final;     // nullable
+  const float* chunk_states; // required here (the C ABI fills it in when the caller passes none)
+  float* dS_chunks;          // workspace [B,H,NC,Dk,Dv]: gradient of each chunk's exit state
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlog_alpha;
+  float* db;
+  float* dw;
+  float* dS0;                // nullable
+  int B, T, H, Dk, Dv, chunk;
+  bool f32_inputs;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Shapes with a compiled kernel (checked by the C ABI before launching).
+bool fwd_supported(int Dk, int Dv, int chunk, bool f32_inputs);
+bool bwd_supported(int Dk, int Dv, int chunk, bool f32_inputs);
+
+}  // namespace gdn2

@@ -1,0 +1,127 @@
+"""Thin torch binding of the GDN-2 C ABI (argument marshalling only).
+
+Each function has the name of the C entry point it calls. torch supplies the
+device memory and the current stream; every step of the computation runs in
+the HIP kernels of libgdn2.so. Layouts and semantics are those of
+include/gdn2.h:
+
+    q, k, b, log_alpha : [B, T, H, Dk]     v, w, dO : [B, T, H, Dv]
+    states             : [B, H, Dk, Dv] fp32
+"""
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.GDN2_F32, torch.bfloat16: _lib.GDN2_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_inputs(names, tensors, dtype, device):
+    for n, t in zip(names, tensors):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.device != device:
+            raise ValueError(f"{n} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if t.dtype != dtype:
+            raise TypeError(f"{n} has dtype {t.dtype}, expected {dtype}")
+
+
+def _f32_state(t, name, device, shape):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.device != device or not t.is_contiguous() or tuple(t.shape) != shape:
+        raise ValueError(f"{name} must be a contiguous fp32 {shape} tensor on {device}")
+    return t
+
+
+def _dtype_code(dtype):
+    if dtype not in _DT:
+        raise TypeError(f"inputs must be float32 or bfloat16, got {dtype}")
+    return _DT[dtype]
+
+
+def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_state=True,
+                     want_chunk_states=False):
+    """Chunked forward. Returns (o, S_final or None, chunk_states or None)."""
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    for n, t, d in (("k", k, Dk), ("b", b, Dk), ("log_alpha", log_alpha, Dk), ("v", v, Dv), ("w", w, Dv)):
+        if tuple(t.shape) != (B, T, H, d):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {(B, T, H, d)}")
+    S0 = _f32_state(S0, "S0", dev, (B, H, Dk, Dv))
+    o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
+    S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
+    NC = (T + chunk - 1) // chunk
+    states = (torch.empty((B, H, NC, Dk, Dv), dtype=torch.float32, device=dev) if want_chunk_states else None)
+    st = lib.gdn2_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
+                              _ptr(S_final), _ptr(states), B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype),
+                              _stream(dev))
+    _lib.check(st, "gdn2_fwd_chunked")
+    return o, S_final, states
+
+
+def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None):
+    """One decode step; S ([B,H,Dk,Dv] fp32) is updated in place. Returns o [B,H,Dv] fp32."""
+    lib = _lib.load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _f32_state(S, "S", dev, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+    st = lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o),
+                              B, H, Dk, Dv, _dtype_code(q.dtype), _stream(dev))
+    _lib.check(st, "gdn2_decode_step")
+    return o
+
+
+def gdn2_workspace_bytes(op, B, T, H, Dk, Dv, chunk, dtype):
+    return _lib.load().gdn2_workspace_bytes(op, B, T, H, Dk, Dv, chunk, _dtype_code(dtype))
+
+
+def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk_states=None, chunk=64,
+                     want_dS0=True, workspace=None):
+    """Chunked backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw (fp32) and dS0 (or None)."""
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w", "dO"), (v, w, dO), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    S0 = _f32_state(S0, "S0", dev, (B, H, Dk, Dv))
+    dS_final = _f32_state(dS_final, "dS_final", dev, (B, H, Dk, Dv))
+    NC = (T + chunk - 1) // chunk
+    chunk_states = _f32_state(chunk_states, "chunk_states", dev, (B, H, NC, Dk, Dv))
+    kshape, vshape = (B, T, H, Dk), (B, T, H, Dv)
+    g = {n: torch.empty(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "db", "dlog_alpha")}
+    g.update({n: torch.empty(vshape, dtype=torch.float32, device=dev) for n in ("dv", "dw")})
+    g["dS0"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.gdn2_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO),
+                              _ptr(dS_final), _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                              _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H, Dk, Dv,
+                              chunk, _dtype_code(q.dtype), _stream(dev))
+    _lib.check(st, "gdn2_bwd_chunked")
+    return g

@@ -1,0 +1,163 @@
+/*
+ * gdn2.h -- C ABI of the Gated Delta Rule-2 (GDN-2) operator on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operator (per batch row b and head h; S_t is a Dk x Dv matrix):
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = S_t^T q_t,          alpha_t = exp(log_alpha_t)
+ *
+ * with b_t in [0,1]^Dk the channel-wise erase gate (key side), w_t in
+ * [0,1]^Dv the channel-wise write gate (value side) and alpha_t the
+ * channel-wise decay on the key axis. Sources: the NVlabs/GatedDeltaNet-2
+ * README ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"),
+ * its gate bullet list and the update-rule paragraph after it (the page text
+ * lacks the equation; the paragraph states that the right factor of the
+ * rank-one erase is key-channel-selective and the write is value-channel-
+ * selective), and the arXiv 2605.22791 abstract (fast-weight update view,
+ * delta rule, reductions to KDA and Gated DeltaNet, chunkwise WY algorithm,
+ * gate-aware backward, constant-memory decoding).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a device pointer owned by the caller. The library
+ *   allocates nothing, keeps no state between calls and is thread-safe.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL is the default stream). No host synchronisation happens inside.
+ * - Tensors are contiguous, row-major, with 16-byte-aligned base pointers.
+ *     q, k, b, log_alpha and their gradients : [B, T, H, Dk]
+ *     v, w, dO, o and their gradients        : [B, T, H, Dv]
+ *     states S0, S_final, dS_final, dS0      : [B, H, Dk, Dv]  fp32
+ *     chunk_states                           : [B, H, NC, Dk, Dv] fp32,
+ *       NC = ceil(T / chunk); entry n is the state entering chunk n
+ *       (entry 0 is S0).
+ *     Decode drops the T axis.
+ * - `dt` is the storage type of q, k, v, b, w and dO (GDN2_F32 or GDN2_BF16).
+ *   log_alpha, every state, o and every gradient are always fp32.
+ * - Gates are post-activation values; gradients are with respect to the
+ *   tensors as passed. Nothing is clamped or range-checked; q is not scaled.
+ * - Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *   B, H >= 1; T >= 0 (T = 0 writes S_final = S0 and nothing else). A ragged
+ *   last chunk is handled exactly.
+ * - Numerics: fp32 inputs are computed with fp32 matrix-core products. bf16
+ *   inputs use fp16 matrix-core operands for the value-side products and a
+ *   two-term bf16 split for the decay-scaled key Gram matrices, always with
+ *   fp32 accumulation and an fp32 state. The in-chunk decay factors are taken
+ *   relative to the middle of the chunk, so within every chunk the cumulative
+ *   log-decay of each channel from the chunk middle to either end must stay
+ *   above -87 (exp of it must be a normal fp32 number) -- at chunk 64 that is
+ *   an average log_alpha above about -2.7 per token; use a smaller chunk for
+ *   stronger decay.
+ * - Results are deterministic (no floating-point atomics): identical inputs
+ *   give bitwise identical outputs.
+ * - A nullable input means zeros; a nullable output means "not written".
+ * - Errors are returned as a negative gdn2_status; nothing is launched when a
+ *   call returns an error detected on the host. GDN2_ERR_HIP reports a failed
+ *   kernel launch (hipGetLastError after the launch).
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN2_OK = 0,
+  GDN2_ERR_NULL = -1,        /* a required pointer is NULL */
+  GDN2_ERR_SHAPE = -2,       /* a size is negative or out of range */
+  GDN2_ERR_DTYPE = -3,       /* unknown dtype enum */
+  GDN2_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  GDN2_ERR_UNSUPPORTED = -5, /* Dk, Dv or chunk not in the supported set */
+  GDN2_ERR_WORKSPACE = -6,   /* workspace missing or smaller than gdn2_workspace_bytes */
+  GDN2_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+} gdn2_status;
+
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+typedef enum { GDN2_OP_FWD = 0, GDN2_OP_DECODE = 1, GDN2_OP_BWD = 2 } gdn2_op;
+
+/*
+ * gdn2_fwd_chunked -- chunkwise WY forward over T tokens.
+ *
+ * Computes o (all T outputs) and optionally S_final = S_T and the chunk entry
+ * states, by the chunkwise WY algorithm with the channel-wise decay absorbed
+ * into asymmetric erase factors (arXiv 2605.22791 abstract; research-wiki
+ * summary, "Key findings"): per chunk, the in-chunk cumulative log-decay g
+ * (gate preprocessing), the strictly lower triangular erase Gram matrix A of
+ * the decayed b*k against the inverse-decayed k, T = (I + A)^-1 by blocked
+ * forward substitution, the WY factors W = T (decayed b*k) and
+ * U = T (w*v) - W S, then o = (decayed q) S + (causal q-k term) U and
+ * S <- Diag(exp(g_last)) S + (k decayed to the chunk end)^T U.
+ *
+ *   q, k, b      [B,T,H,Dk] dt      v, w [B,T,H,Dv] dt     log_alpha [B,T,H,Dk] fp32
+ *   S0           [B,H,Dk,Dv] fp32, nullable (zero initial state)
+ *   o            [B,T,H,Dv] fp32, required when T > 0
+ *   S_final      [B,H,Dk,Dv] fp32, nullable
+ *   chunk_states [B,H,NC,Dk,Dv] fp32, nullable (training mode when given)
+ */
+int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha,
+                     const void* b, const void* w, const float* S0, float* o, float* S_final,
+                     float* chunk_states, int B, int T, int H, int Dk, int Dv, int chunk,
+                     int dt, void* stream);
+
+/*
+ * gdn2_decode_step -- one recurrence step per sequence, state updated in place
+ * (constant-memory decoding, arXiv 2605.22791 abstract).
+ *
+ * Per (b, h): S~ = Diag(alpha) S; r = S~^T (b*k); p = S~^T q; u = w*v - r;
+ * o = p + (k.q) u; S <- S~ + k u^T.  One read and one write of the fp32 state.
+ *
+ *   q, k, b  [B,H,Dk] dt     v, w [B,H,Dv] dt     log_alpha [B,H,Dk] fp32
+ *   S        [B,H,Dk,Dv] fp32, in/out, required
+ *   o        [B,H,Dv] fp32, required
+ */
+int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                     const void* b, const void* w, float* S, float* o, int B, int H, int Dk,
+                     int Dv, int dt, void* stream);
+
+/*
+ * gdn2_bwd_chunked -- gate-aware chunkwise backward (arXiv 2605.22791
+ * abstract; aiexpert.news method paragraph).
+ *
+ * Gradients of L = <dO, o> + <dS_final, S_T> with respect to q, k, v,
+ * log_alpha, b, w and S0. A reverse pass over the chunks carries the state
+ * gradient from the last chunk to the first (and yields dS0); a chunk-parallel
+ * pass forms every per-token gradient from the chunk's entry state and the
+ * gradient of its exit state. The decay gradient is a reverse cumulative sum
+ * inside each chunk plus rowsum(S_exit * dS_exit), which follows from the
+ * operator's invariance under a rescaling of the key axis.
+ *
+ *   inputs as gdn2_fwd_chunked; dO [B,T,H,Dv] dt
+ *   dS_final     [B,H,Dk,Dv] fp32, nullable (zero)
+ *   chunk_states [B,H,NC,Dk,Dv] fp32 from gdn2_fwd_chunked on the same
+ *                inputs, nullable (then recomputed into the workspace)
+ *   dq, dk, db, dlog_alpha [B,T,H,Dk] fp32, dv, dw [B,T,H,Dv] fp32: required when T > 0
+ *   dS0          [B,H,Dk,Dv] fp32, nullable (computed even when S0 is NULL)
+ *   workspace    device scratch of at least gdn2_workspace_bytes(GDN2_OP_BWD, ...)
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ */
+int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha,
+                     const void* b, const void* w, const float* S0, const void* dO,
+                     const float* dS_final, const float* chunk_states, float* dq, float* dk,
+                     float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
+                     void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                     int Dv, int chunk, int dt, void* stream);
+
+/* Workspace bytes an entry point needs for these sizes (0 for forward and
+ * decode). Returns 0 for invalid sizes as well; the call itself reports them. */
+size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chunk, int dt);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn2_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int gdn2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

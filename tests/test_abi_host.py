@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before launching anything (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_recurrent_gdn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdn2_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"gdn2_fwd_chunked", "gdn2_decode_step", "gdn2_bwd_chunked", "gdn2_workspace_bytes",
+            "gdn2_status_string", "gdn2_version"} <= set(names)
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    for code in range(0, -8, -1):
+        s = lib.gdn2_status_string(code).decode()
+        assert s.startswith("GDN2_")
+    assert lib.gdn2_status_string(-99).decode() == "unknown gdn2 status"
+    assert lib.gdn2_version() >= 100
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    B, T, H, D, C = 8, 4096, 16, 128, 64
+    nc = T // C
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == 0
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4
+
+
+A = 4096  # a fake, 16-byte aligned address: never dereferenced because validation fails first
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, Sf=None, cs=None, B=1, T=64, H=2, Dk=16, Dv=16,
+                C=16, dt=0)
+    args.update(kw)
+    return _lib.load().gdn2_fwd_chunked(args["q"], args["k"], args["v"], args["la"], args["b"], args["w"],
+                                        args["S0"], args["o"], args["Sf"], args["cs"], args["B"], args["T"],
+                                        args["H"], args["Dk"], args["Dv"], args["C"], args["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.GDN2_ERR_NULL),
+    (dict(o=None), _lib.GDN2_ERR_NULL),
+    (dict(k=A + 8), _lib.GDN2_ERR_ALIGN),
+    (dict(Sf=A + 4), _lib.GDN2_ERR_ALIGN),
+    (dict(dt=7), _lib.GDN2_ERR_DTYPE),
+    (dict(Dk=48), _lib.GDN2_ERR_UNSUPPORTED),
+    (dict(Dv=256), _lib.GDN2_ERR_UNSUPPORTED),
+    (dict(C=128), _lib.GDN2_ERR_UNSUPPORTED),
+    (dict(T=-1), _lib.GDN2_ERR_SHAPE),
+    (dict(B=-2), _lib.GDN2_ERR_SHAPE),
+    (dict(dt=0, Dk=128, Dv=128, C=64), _lib.GDN2_ERR_UNSUPPORTED),   # fp32 inputs at d=128 need chunk <= 32
+    (dict(B=0), _lib.GDN2_OK),                                       # nothing to do, nothing launched
+    (dict(H=0), _lib.GDN2_OK),
+])
+def test_fwd_argument_errors(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_decode_argument_errors():
+    lib = _lib.load()
+    call = lambda S=A, dt=1, Dk=128, Dv=128, B=4: lib.gdn2_decode_step(A, A, A, A, A, A, S, A, B, 16, Dk, Dv, dt,  # noqa
+                                                                      None)
+    assert call(S=None) == _lib.GDN2_ERR_NULL
+    assert call(S=A + 2) == _lib.GDN2_ERR_ALIGN
+    assert call(dt=5) == _lib.GDN2_ERR_DTYPE
+    assert call(Dk=100) == _lib.GDN2_ERR_UNSUPPORTED
+    assert call(B=0) == _lib.GDN2_OK
+
+
+def test_error_raised_by_binding_names_the_status():
+    e = _lib.GDN2Error(_lib.GDN2_ERR_WORKSPACE, "gdn2_bwd_chunked")
+    assert "GDN2_ERR_WORKSPACE" in str(e) and e.status == _lib.GDN2_ERR_WORKSPACE
+
+
+def test_signature_table_matches_header_arity():
+    text = open(HEADER).read()
+    for name, (_, args) in _lib.SIGNATURES.items():
+        m = re.search(name + r"\s*\(([^;]*)\);", text, re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(params) == len(args), name
+    assert ctypes.sizeof(ctypes.c_size_t) == 8
