@@ -9,6 +9,13 @@
 // the products below only rely on that row/column assignment and on the
 // accumulator layout.
 //
+// Accumulation chains never mix instruction shapes: a contraction remainder of
+// 16 is issued as a 16x16x32 product with the upper half of K zeroed (lane
+// groups 2 and 3 contribute zeros), so every product accumulating into one
+// register tile is the same instruction. (A 16x16x16 product feeding a
+// 16x16x32 product's accumulator input back-to-back gave wrong results on
+// gfx950 with the compiler's instruction spacing.)
+//
 // Operands staged in LDS are stored "K-contiguous": a left operand X as
 // [M][K] and a right operand as [N][K] (its transpose), both row-major with a
 // padded leading dimension, so every lane reads its contraction group with one
@@ -84,6 +91,74 @@ __device__ __forceinline__ float load1(const void* base, int64_t idx) {
   else return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
 }
 
+// Raw register copies of 4 / 8 consecutive inputs in their storage type, so a
+// chunk's inputs can be fetched from HBM one chunk ahead of their use.
+template <bool F32IN> struct Raw4 { uint2 u; };
+template <> struct Raw4<true> { float4 f; };
+template <bool F32IN> struct Raw8 { uint4 u; };
+template <> struct Raw8<true> { float4 f0, f1; };
+
+template <bool F32IN>
+__device__ __forceinline__ void ld_raw(Raw4<F32IN>& r, const void* base, int64_t idx) {
+  if constexpr (F32IN) r.f = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+  else r.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+}
+template <bool F32IN>
+__device__ __forceinline__ void ld_raw(Raw8<F32IN>& r, const void* base, int64_t idx) {
+  if constexpr (F32IN) {
+    r.f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    r.f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+  } else {
+    r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+  }
+}
+template <bool F32IN>
+__device__ __forceinline__ void zero_raw(Raw4<F32IN>& r) {
+  if constexpr (F32IN) r.f = make_float4(0.f, 0.f, 0.f, 0.f);
+  else r.u = make_uint2(0u, 0u);
+}
+template <bool F32IN>
+__device__ __forceinline__ void zero_raw(Raw8<F32IN>& r) {
+  if constexpr (F32IN) r.f0 = r.f1 = make_float4(0.f, 0.f, 0.f, 0.f);
+  else r.u = make_uint4(0u, 0u, 0u, 0u);
+}
+template <bool F32IN>
+__device__ __forceinline__ void cvt(const Raw4<F32IN>& r, float (&o)[4]) {
+  if constexpr (F32IN) {
+    o[0] = r.f.x; o[1] = r.f.y; o[2] = r.f.z; o[3] = r.f.w;
+  } else {
+    o[0] = __uint_as_float(r.u.x << 16); o[1] = __uint_as_float(r.u.x & 0xffff0000u);
+    o[2] = __uint_as_float(r.u.y << 16); o[3] = __uint_as_float(r.u.y & 0xffff0000u);
+  }
+}
+template <bool F32IN>
+__device__ __forceinline__ void cvt(const Raw8<F32IN>& r, float (&o)[8]) {
+  if constexpr (F32IN) {
+    o[0] = r.f0.x; o[1] = r.f0.y; o[2] = r.f0.z; o[3] = r.f0.w;
+    o[4] = r.f1.x; o[5] = r.f1.y; o[6] = r.f1.z; o[7] = r.f1.w;
+  } else {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// Store 4 consecutive values of type T (8 bytes for 16-bit T, 16 bytes for fp32).
+template <typename T>
+__device__ __forceinline__ void st4(T* dst, float a0, float a1, float a2, float a3) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    v4 v;
+    v[0] = static_cast<T>(a0); v[1] = static_cast<T>(a1); v[2] = static_cast<T>(a2); v[3] = static_cast<T>(a3);
+    *reinterpret_cast<v4*>(dst) = v;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(a0, a1, a2, a3);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // matrix-core primitives
 // ---------------------------------------------------------------------------
@@ -122,9 +197,12 @@ __device__ __forceinline__ void mma_nt(f32x4& acc, const T* X, int ldx, const T*
       acc = mfma16x16x32(a, b, acc);
     }
     if (k0 < K) {
-      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + k0 + 4 * g);
-      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + k0 + 4 * g);
-      acc = mfma16x16x16(a, b, acc);
+      v8 a = {}, b = {};
+      if (g < 2) {
+        a = *reinterpret_cast<const v8*>(X + r * ldx + k0 + 8 * g);
+        b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      }
+      acc = mfma16x16x32(a, b, acc);
     }
   } else {
     for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
@@ -146,9 +224,12 @@ __device__ __forceinline__ void mma_nt_k(f32x4& acc, const T* X, int ldx, const 
       acc = mfma16x16x32(a, b, acc);
     }
     if constexpr (K % 32 == 16) {
-      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + (K - 16) + 4 * g);
-      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + (K - 16) + 4 * g);
-      acc = mfma16x16x16(a, b, acc);
+      v8 a = {}, b = {};
+      if (g < 2) {
+        a = *reinterpret_cast<const v8*>(X + r * ldx + (K - 16) + 8 * g);
+        b = *reinterpret_cast<const v8*>(Y + r * ldy + (K - 16) + 8 * g);
+      }
+      acc = mfma16x16x32(a, b, acc);
     }
   } else {
 #pragma unroll
@@ -175,14 +256,17 @@ __device__ __forceinline__ void mma_nt_split_k(f32x4& acc, const __bf16* Xh, con
     acc = mfma16x16x32(ah, bh, acc);
   }
   if constexpr (K % 32 == 16) {
-    const int ox = r * ldx + (K - 16) + 4 * g, oy = r * ldy + (K - 16) + 4 * g;
-    const bf16x4 ah = *reinterpret_cast<const bf16x4*>(Xh + ox);
-    const bf16x4 al = *reinterpret_cast<const bf16x4*>(Xl + ox);
-    const bf16x4 bh = *reinterpret_cast<const bf16x4*>(Yh + oy);
-    const bf16x4 bl = *reinterpret_cast<const bf16x4*>(Yl + oy);
-    acc = mfma16x16x16(al, bh, acc);
-    acc = mfma16x16x16(ah, bl, acc);
-    acc = mfma16x16x16(ah, bh, acc);
+    bf16x8 ah = {}, al = {}, bh = {}, bl = {};
+    if (g < 2) {
+      const int ox = r * ldx + (K - 16) + 8 * g, oy = r * ldy + (K - 16) + 8 * g;
+      ah = *reinterpret_cast<const bf16x8*>(Xh + ox);
+      al = *reinterpret_cast<const bf16x8*>(Xl + ox);
+      bh = *reinterpret_cast<const bf16x8*>(Yh + oy);
+      bl = *reinterpret_cast<const bf16x8*>(Yl + oy);
+    }
+    acc = mfma16x16x32(al, bh, acc);
+    acc = mfma16x16x32(ah, bl, acc);
+    acc = mfma16x16x32(ah, bh, acc);
   }
 }
 
@@ -233,11 +317,15 @@ __device__ __forceinline__ void mma_nt_yf32(f32x4& acc, const T* X, int ldx, con
       acc = mfma16x16x32(a, b, acc);
     }
     if (k0 < K) {
-      const v4 a = *reinterpret_cast<const v4*>(X + r * ldx + k0 + 4 * g);
-      const float4 y0 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 4 * g);
-      v4 b;
-      b[0] = static_cast<T>(y0.x); b[1] = static_cast<T>(y0.y); b[2] = static_cast<T>(y0.z); b[3] = static_cast<T>(y0.w);
-      acc = mfma16x16x16(a, b, acc);
+      v8 a = {}, b = {};
+      if (g < 2) {
+        a = *reinterpret_cast<const v8*>(X + r * ldx + k0 + 8 * g);
+        const float4 y0 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 8 * g);
+        const float4 y1 = *reinterpret_cast<const float4*>(Y + r * ldy + k0 + 8 * g + 4);
+        b[0] = static_cast<T>(y0.x); b[1] = static_cast<T>(y0.y); b[2] = static_cast<T>(y0.z); b[3] = static_cast<T>(y0.w);
+        b[4] = static_cast<T>(y1.x); b[5] = static_cast<T>(y1.y); b[6] = static_cast<T>(y1.z); b[7] = static_cast<T>(y1.w);
+      }
+      acc = mfma16x16x32(a, b, acc);
     }
   } else {
     for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
@@ -263,11 +351,15 @@ __device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx,
       acc = mfma16x16x32(a, b, acc);
     }
     if (k0 < K) {
-      const float4 x0 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 4 * g);
-      v4 a;
-      a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
-      const v4 b = *reinterpret_cast<const v4*>(Y + r * ldy + k0 + 4 * g);
-      acc = mfma16x16x16(a, b, acc);
+      v8 a = {}, b = {};
+      if (g < 2) {
+        const float4 x0 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 8 * g);
+        const float4 x1 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 8 * g + 4);
+        a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
+        a[4] = static_cast<T>(x1.x); a[5] = static_cast<T>(x1.y); a[6] = static_cast<T>(x1.z); a[7] = static_cast<T>(x1.w);
+        b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      }
+      acc = mfma16x16x32(a, b, acc);
     }
   } else {
     for (int k0 = 0; k0 < K; k0 += 4) acc = mfma16x16x4(X[r * ldx + k0 + g], Y[r * ldy + k0 + g], acc);
@@ -301,6 +393,101 @@ __device__ __forceinline__ void store_tile_t(T* dst, int ld, const f32x4& acc, f
     *reinterpret_cast<float4*>(dst + c * ld + r0) =
         make_float4(scale * acc[0], scale * acc[1], scale * acc[2], scale * acc[3]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// (I + A)^-1 of one strictly lower triangular 16x16 block, by one wave.
+//
+// A is nilpotent (A^16 = 0), so (I + A)^-1 = sum_{j=0}^{15} (-A)^j, evaluated
+// by the Horner recursion X <- I - A X (15 steps, starting from X = I). A stays
+// in registers in the left-operand layout; the accumulator layout of a 16x16
+// product is the right-operand layout (lane holds rows 4*(l/16)+i of column
+// l%16), so X never leaves registers. With 16-bit operands X is carried as an
+// fp16 hi/lo pair (two products per step) so that its rounding does not build
+// up over the 15 steps. On return the block at Ab (fp32, leading dimension
+// ld) holds (I + A)^-1, including its zero upper triangle.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void invert_unit_lower16(float* Ab, int ld) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  f32x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (4 * g + i == r) ? 1.f : 0.f;
+  if constexpr (sizeof(T) == 2) {
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    v4 a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = static_cast<T>(Ab[r * ld + 4 * g + i]);
+#pragma unroll 1
+    for (int step = 0; step < 15; ++step) {
+      v4 xh, xl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xh[i] = static_cast<T>(x[i]);
+        xl[i] = static_cast<T>(x[i] - static_cast<float>(xh[i]));
+      }
+      f32x4 d = zero4();
+      d = mfma16x16x16(a, xl, d);
+      d = mfma16x16x16(a, xh, d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = ((4 * g + i == r) ? 1.f : 0.f) - d[i];
+    }
+  } else {
+    // fp32 matrix cores: product j pairs lane group g with contraction index 4g+j,
+    // which is exactly the row this lane holds in x[j]
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = Ab[r * ld + 4 * g + j];
+#pragma unroll 1
+    for (int step = 0; step < 15; ++step) {
+      f32x4 d = zero4();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d = mfma16x16x4(a[j], x[j], d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = ((4 * g + i == r) ? 1.f : 0.f) - d[i];
+    }
+  }
+  // all lanes have read A before any lane overwrites the block (one wave, in order)
+  store_tile(Ab, ld, x);
+}
+
+// Runtime-K split product (K % 16 == 0): C += Xh Yh^T + Xh Yl^T + Xl Yh^T, bf16 pairs.
+__device__ __forceinline__ void mma_nt_split(f32x4& acc, const __bf16* Xh, const __bf16* Xl, int ldx,
+                                             const __bf16* Yh, const __bf16* Yl, int ldy, int K) {
+  const int l = lane_id();
+  const int r = l & 15, g = l >> 4;
+  int k0 = 0;
+  for (; k0 + 32 <= K; k0 += 32) {
+    const int ox = r * ldx + k0 + 8 * g, oy = r * ldy + k0 + 8 * g;
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Xh + ox);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(Xl + ox);
+    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Yh + oy);
+    const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Yl + oy);
+    acc = mfma16x16x32(al, bh, acc);
+    acc = mfma16x16x32(ah, bl, acc);
+    acc = mfma16x16x32(ah, bh, acc);
+  }
+  if (k0 < K) {
+    bf16x8 ah = {}, al = {}, bh = {}, bl = {};
+    if (g < 2) {
+      const int ox = r * ldx + k0 + 8 * g, oy = r * ldy + k0 + 8 * g;
+      ah = *reinterpret_cast<const bf16x8*>(Xh + ox);
+      al = *reinterpret_cast<const bf16x8*>(Xl + ox);
+      bh = *reinterpret_cast<const bf16x8*>(Yh + oy);
+      bl = *reinterpret_cast<const bf16x8*>(Yl + oy);
+    }
+    acc = mfma16x16x32(al, bh, acc);
+    acc = mfma16x16x32(ah, bl, acc);
+    acc = mfma16x16x32(ah, bh, acc);
+  }
+}
+
+// Store a value as a bf16 hi/lo pair (hi = rne(x), lo = rne(x - hi)).
+__device__ __forceinline__ void st_split(__bf16* hi, __bf16* lo, int off, float x) {
+  const __bf16 h = f32_to_bf16(x);
+  hi[off] = h;
+  lo[off] = f32_to_bf16(x - bf16_to_f32(h));
 }
 
 }  // namespace gdn2

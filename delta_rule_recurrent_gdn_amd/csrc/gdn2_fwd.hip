@@ -44,58 +44,44 @@
 // magnitude of v and S); accumulation, the state and g are fp32. fp32 inputs
 // use fp32 matrix-core products throughout.
 
-#include <type_traits>
-
-#include "gdn2_common.h"
+#include "gdn2_chunk.h"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
 
 template <int DK, int C, int BV, bool F32IN>
 struct FwdCfg {
-  using OpT = typename std::conditional<F32IN, float, _Float16>::type;  // value-side operand type
-  using TriT = OpT;                                                     // operand type of the T blocks
-  static constexpr int kThreads = 256;
+  using KS = KSide<DK, C, F32IN>;
+  using OpT = typename KS::OpT;
+  static constexpr int kThreads = 512;
   static constexpr int kWaves = kThreads / kWave;
-  static constexpr int NB = C / 16;                    // 16-token row blocks per chunk
-  static constexpr int SW = DK < 32 ? DK : 32;         // channel slice of the Gram phase
-  static constexpr int NSL = DK / SW;
-  static constexpr int PADOP = F32IN ? 4 : 8;          // 16-byte row padding
-  static constexpr int LDC = C + PADOP;                // rows of C tokens
-  static constexpr int LDK = DK + PADOP;               // rows of DK channels
-  static constexpr int LDSW = SW + (F32IN ? 4 : 8);    // Gram slice rows
-  static constexpr int LDCF = C + 4;                   // fp32 [C][C] (A, then T)
-  static constexpr int LDX = 20;                       // fp32 16x16 scratch tiles
+  static constexpr int NB = KS::NB;
+  static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF, LDX = KS::LDX;
   static constexpr int OPB = sizeof(OpT);
-  static constexpr int GRAMB = F32IN ? 4 : 2;          // bytes per Gram slice element (per part)
-  static constexpr int GRAMPARTS = F32IN ? 3 : 6;      // KhM, QhM, KtM (hi/lo each for bf16 split)
 
   // persistent region
-  static constexpr int oKhT = 0;                                   // OpT [DK][LDC]
-  static constexpr int oQs = oKhT + DK * LDC * OPB;                // OpT [C][LDK]
-  static constexpr int oKbT = oQs + C * LDK * OPB;                 // OpT [DK][LDC]
-  static constexpr int oWVT = oKbT + DK * LDC * OPB;               // OpT [BV][LDC]
-  static constexpr int oST = oWVT + BV * LDC * OPB;                // OpT [BV][LDK]
-  static constexpr int oGC = oST + BV * LDK * OPB;                 // float [DK]
-  static constexpr int oGM = oGC + DK * 4;                         // float [DK]
-  static constexpr int oX = oGM + DK * 4;                          // start of the phase-shared region
+  static constexpr int oKhT = 0;                                   // OpT [DK][LDC]  (b k exp(g))^T
+  static constexpr int oQs = oKhT + DK * LDC * OPB;                // OpT [C][LDK]   q exp(g)
+  static constexpr int oKbT = oQs + C * LDK * OPB;                 // OpT [DK][LDC]  (k exp(g_C - g))^T
+  static constexpr int oWVT = oKbT + DK * LDC * OPB;               // OpT [BV][LDC]  (w v)^T
+  static constexpr int oST = oWVT + BV * LDC * OPB;                // OpT [BV][LDK]  S^T
+  static constexpr int oCH = oST + BV * LDK * OPB;                 // float [4][DK]  per-channel gate constants
+  static constexpr int oTOT = oCH + KS::kChanBytes;                // float cumsum segment totals
+  static constexpr int oX = oTOT + KS::kTotBytes;                  // start of the phase-shared region
   // phase F (gate preprocessing + Gram)
-  static constexpr int oG = oX;                                    // float [C][DK]
-  static constexpr int oSL = oG + C * DK * 4;                      // Gram slices
-  static constexpr int kSliceBytes = C * LDSW * GRAMB;
-  static constexpr int endF = oSL + GRAMPARTS * kSliceBytes;
+  static constexpr int oG = oX;
+  static constexpr int oSL = oG + KS::kGBytes;
+  static constexpr int endF = oSL + KS::kSlicesBytes;
   // phase W (after the Gram products)
-  static constexpr int oAf = oX;                                   // float [C][LDCF]
-  static constexpr int oPm = oAf + C * LDCF * 4;                   // OpT [C][LDC]
-  static constexpr int oWm = oPm + C * LDC * OPB;                  // OpT [C][LDK]  (holds -W)
-  static constexpr int oUT = oWm + C * LDK * OPB;                  // OpT [BV][LDC]
-  static constexpr int oXs = oUT + BV * LDC * OPB;                 // float [4][16][LDX]
-  static constexpr int endW = oXs + 4 * 16 * LDX * 4;
+  static constexpr int oAf = oX;                                   // float [C][LDCF]  A, then T
+  static constexpr int oPm = oAf + KS::kAfBytes;                   // OpT [C][LDC]   P
+  static constexpr int oWm = oPm + C * LDC * OPB;                  // OpT [C][LDK]   -W
+  static constexpr int oUT = oWm + C * LDK * OPB;                  // OpT [BV][LDC]  U^T
+  static constexpr int oXs = oUT + BV * LDC * OPB;                 // float inversion scratch
+  static constexpr int endW = oXs + KS::kXsBytes;
   static constexpr int kLdsBytes = endF > endW ? endF : endW;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
 
-  static constexpr int NGT = NB * (NB + 1);                        // A and P lower tiles
-  static constexpr int GPW = (NGT + kWaves - 1) / kWaves;
   static constexpr int NUT = NB * (BV / 16);                       // U / O tiles
   static constexpr int UPW = (NUT + kWaves - 1) / kWaves;
   static constexpr int NST = (DK / 16) * (BV / 16);                // state tiles
@@ -104,23 +90,13 @@ struct FwdCfg {
   static constexpr int WPW = (NWT + kWaves - 1) / kWaves;
 };
 
-// lower-triangular tile index p -> (R, I) with I <= R, R-major
-__device__ __forceinline__ void tri_index(int p, int& R, int& I) {
-  R = 0;
-  while (p > R) {
-    p -= R + 1;
-    ++R;
-  }
-  I = p;
-}
-
 template <int DK, int C, int BV, bool F32IN>
-__global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512) void gdn2_fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<DK, C, BV, F32IN>;
+  using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
-  using TriT = typename Cfg::TriT;
-  constexpr int NW = Cfg::kWaves, NT = Cfg::kThreads, NB = Cfg::NB, SW = Cfg::SW;
-  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDSW = Cfg::LDSW, LDCF = Cfg::LDCF, LDX = Cfg::LDX;
+  constexpr int NW = Cfg::kWaves, NB = Cfg::NB;
+  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF;
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
@@ -128,8 +104,8 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
   OpT* sKbT = reinterpret_cast<OpT*>(smem + Cfg::oKbT);
   OpT* sWVT = reinterpret_cast<OpT*>(smem + Cfg::oWVT);
   OpT* sST = reinterpret_cast<OpT*>(smem + Cfg::oST);
-  float* sgC = reinterpret_cast<float*>(smem + Cfg::oGC);
-  float* sgm = reinterpret_cast<float*>(smem + Cfg::oGM);
+  float* sCh = reinterpret_cast<float*>(smem + Cfg::oCH);
+  float* sTot = reinterpret_cast<float*>(smem + Cfg::oTOT);
   float* sG = reinterpret_cast<float*>(smem + Cfg::oG);
   char* sSL = smem + Cfg::oSL;
   float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
@@ -156,6 +132,27 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
   const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
   const int64_t stBase = (int64_t)bh * DK * Dv + j0;
 
+  KS ks;
+  ks.init(tid);
+  // v, w: 8 consecutive value columns of one row
+  const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
+  const bool vw_on = vw_r < C;
+  Raw8<F32IN> rv, rw;
+  auto load_chunk = [&](int nn) {
+    const int tn = nn * C, Ln = min(C, T - tn);
+    ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, tn, Ln);
+    if (vw_on) {
+      if (vw_r < Ln) {
+        const int64_t idx = baseV + (int64_t)(tn + vw_r) * rowV + 8 * vw_j8;
+        ld_raw(rv, a.v, idx);
+        ld_raw(rw, a.w, idx);
+      } else {
+        zero_raw(rv);
+        zero_raw(rw);
+      }
+    }
+  };
+
   // ---- initial state: accumulators (fp32) and the operand copy S^T ----
   f32x4 accS[Cfg::SPW];
 #pragma unroll
@@ -172,6 +169,7 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
       store_tile_t(sST + 16 * jb * LDK + 16 * cb, LDK, accS[i]);
     }
   }
+  load_chunk(0);
 
   for (int n = 0; n < NC; ++n) {
     const int t0 = n * C;
@@ -191,184 +189,36 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();  // the previous chunk's readers of the per-chunk buffers are done
 
-    // ---- (1) gate preprocessing: log_alpha -> sG, w*v -> sWVT ----
-    for (int e = tid; e < C * (DK / 4); e += NT) {
-      const int r = e / (DK / 4), c4 = e % (DK / 4);
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < Lr) val = *reinterpret_cast<const float4*>(a.log_alpha + baseK + (int64_t)(t0 + r) * rowK + 4 * c4);
-      *reinterpret_cast<float4*>(sG + r * DK + 4 * c4) = val;
-    }
-    for (int e = tid; e < C * (BV / 8); e += NT) {
-      const int r = e / (BV / 8), j8 = e % (BV / 8);
+    // ---- (1) gate preprocessing; w*v -> sWVT ----
+    if (vw_on) {
       float vv[8], ww[8];
-      if (r < Lr) {
-        load8<F32IN>(a.v, baseV + (int64_t)(t0 + r) * rowV + 8 * j8, vv);
-        load8<F32IN>(a.w, baseV + (int64_t)(t0 + r) * rowV + 8 * j8, ww);
-      } else {
+      cvt(rv, vv);
+      cvt(rw, ww);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vv[i] = ww[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sWVT[(8 * j8 + i) * LDC + r] = static_cast<OpT>(ww[i] * vv[i]);
+      for (int i = 0; i < 8; ++i) sWVT[(8 * vw_j8 + i) * LDC + vw_r] = static_cast<OpT>(ww[i] * vv[i]);
     }
-    __syncthreads();
-    for (int c = tid; c < DK; c += NT) {
-      float run = 0.f;
-#pragma unroll 16
-      for (int r = 0; r < C; ++r) {
-        run += sG[r * DK + c];
-        sG[r * DK + c] = run;
-        if (r == C / 2 - 1) sgm[c] = run;
-      }
-      sgC[c] = run;
-    }
-    __syncthreads();
+    ks.gates(sTot, sG, sCh);
 
-    // ---- (2)+(3a) factors and the Gram products A, P (channel slices) ----
-    f32x4 accG[Cfg::GPW];
+    // ---- (2)+(3a) factors and the Gram products A, P ----
+    f32x4 accG[KS::GPW];
+    ks.factors_gram(sG, sCh, sSL, accG,
+                    [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
+                        const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
+                      (void)e1;
+                      st4(sQs + r * LDK + c0, qv[0] * eg[0], qv[1] * eg[1], qv[2] * eg[2], qv[3] * eg[3]);
 #pragma unroll
-    for (int i = 0; i < Cfg::GPW; ++i) accG[i] = zero4();
+                      for (int i = 0; i < 4; ++i) {
+                        sKhT[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * eg[i]);
+                        sKbT[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * ec[i]);
+                      }
+                    });
+    ks.template gram_store<false>(accG, sAf, sPm);
 
-    for (int sl = 0; sl < Cfg::NSL; ++sl) {
-      for (int e = tid; e < C * (SW / 8); e += NT) {
-        const int r = e / (SW / 8), cl = 8 * (e % (SW / 8));
-        const int c0 = sl * SW + cl;
-        float qv[8], kv[8], bv[8];
-        if (r < Lr) {
-          const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c0;
-          load8<F32IN>(a.q, idx, qv);
-          load8<F32IN>(a.k, idx, kv);
-          load8<F32IN>(a.b, idx, bv);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) qv[i] = kv[i] = bv[i] = 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int c = c0 + i;
-          const float g = sG[r * DK + c], gm = sgm[c], gc = sgC[c];
-          const float eg = __expf(g), emr = __expf(g - gm), emc = __expf(gm - g), ec = __expf(gc - g);
-          const float bk = bv[i] * kv[i];
-          const float khm = bk * emr, qhm = qv[i] * emr, ktm = kv[i] * emc;
-          if constexpr (F32IN) {
-            float* sl0 = reinterpret_cast<float*>(sSL);
-            sl0[0 * (C * LDSW) + r * LDSW + cl + i] = khm;
-            sl0[1 * (C * LDSW) + r * LDSW + cl + i] = qhm;
-            sl0[2 * (C * LDSW) + r * LDSW + cl + i] = ktm;
-          } else {
-            __bf16* sl0 = reinterpret_cast<__bf16*>(sSL);
-            const __bf16 kh_h = f32_to_bf16(khm), qh_h = f32_to_bf16(qhm), kt_h = f32_to_bf16(ktm);
-            const int o = r * LDSW + cl + i;
-            sl0[0 * (C * LDSW) + o] = kh_h;
-            sl0[1 * (C * LDSW) + o] = f32_to_bf16(khm - bf16_to_f32(kh_h));
-            sl0[2 * (C * LDSW) + o] = qh_h;
-            sl0[3 * (C * LDSW) + o] = f32_to_bf16(qhm - bf16_to_f32(qh_h));
-            sl0[4 * (C * LDSW) + o] = kt_h;
-            sl0[5 * (C * LDSW) + o] = f32_to_bf16(ktm - bf16_to_f32(kt_h));
-          }
-          sKhT[c * LDC + r] = static_cast<OpT>(bk * eg);
-          sQs[r * LDK + c] = static_cast<OpT>(qv[i] * eg);
-          sKbT[c * LDC + r] = static_cast<OpT>(kv[i] * ec);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < Cfg::GPW; ++i) {
-        const int t = wid + NW * i;
-        if (t < Cfg::NGT) {
-          const bool isP = t >= Cfg::NGT / 2;
-          int R, I;
-          tri_index(isP ? t - Cfg::NGT / 2 : t, R, I);
-          if constexpr (F32IN) {
-            const float* sl0 = reinterpret_cast<const float*>(sSL);
-            const float* X = sl0 + (isP ? 1 : 0) * (C * LDSW) + 16 * R * LDSW;
-            const float* Y = sl0 + 2 * (C * LDSW) + 16 * I * LDSW;
-            mma_nt_k<SW>(accG[i], X, LDSW, Y, LDSW);
-          } else {
-            const __bf16* sl0 = reinterpret_cast<const __bf16*>(sSL);
-            const __bf16* Xh = sl0 + (isP ? 2 : 0) * (C * LDSW) + 16 * R * LDSW;
-            const __bf16* Y0 = sl0 + 4 * (C * LDSW) + 16 * I * LDSW;
-            mma_nt_split_k<SW>(accG[i], Xh, Xh + C * LDSW, LDSW, Y0, Y0 + C * LDSW, LDSW);
-          }
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---- A -> sAf (strict lower), P -> sPm (lower incl. diagonal) ----
-#pragma unroll
-    for (int i = 0; i < Cfg::GPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NGT) {
-        const bool isP = t >= Cfg::NGT / 2;
-        int R, I;
-        tri_index(isP ? t - Cfg::NGT / 2 : t, R, I);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * R + 4 * lg + e, col = 16 * I + lr;
-          if (isP) sPm[row * LDC + col] = static_cast<OpT>(row >= col ? accG[i][e] : 0.f);
-          else sAf[row * LDCF + col] = row > col ? accG[i][e] : 0.f;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- (3b) T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ----
-    if (wid < NB && l < 16) {
-      float* Ab = sAf + 16 * wid * LDCF + 16 * wid;
-      float tcol[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) tcol[m] = (m == l) ? 1.f : 0.f;
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) s += Ab[r * LDCF + m] * tcol[m];
-        if (r > l) tcol[r] = -s;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ab[r * LDCF + l] = tcol[r];
-    }
-    __syncthreads();
-    // level 1: T_{2j+1,2j} = -T_{2j+1,2j+1} A_{2j+1,2j} T_{2j,2j}
-    if constexpr (NB >= 2) {
-      if (wid < NB / 2) {
-        const int I = 2 * wid + 1, J = 2 * wid;
-        f32x4 x = zero4();
-        mma_f32src<TriT, false>(x, sAf + 16 * I * LDCF + 16 * J, LDCF, sAf + 16 * J * LDCF + 16 * J, LDCF, 16);
-        store_tile(sXs + wid * 16 * LDX, LDX, x);
-      }
-      __syncthreads();
-      if (wid < NB / 2) {
-        const int I = 2 * wid + 1, J = 2 * wid;
-        f32x4 y = zero4();
-        mma_f32src<TriT, false>(y, sAf + 16 * I * LDCF + 16 * I, LDCF, sXs + wid * 16 * LDX, LDX, 16);
-        store_tile(sAf + 16 * I * LDCF + 16 * J, LDCF, y, -1.f);
-      }
-      __syncthreads();
-    }
-    // level 2 (C = 64): T_{[23],[01]} = -T_{[23],[23]} A_{[23],[01]} T_{[01],[01]}
-    if constexpr (NB == 4) {
-      {
-        const int I = 2 + wid / 2, J = wid % 2;
-        f32x4 x = zero4();
-        for (int K = J; K <= 1; ++K)
-          mma_f32src<TriT, false>(x, sAf + 16 * I * LDCF + 16 * K, LDCF, sAf + 16 * K * LDCF + 16 * J, LDCF, 16);
-        store_tile(sXs + wid * 16 * LDX, LDX, x);
-      }
-      __syncthreads();
-      {
-        const int I = 2 + wid / 2, J = wid % 2;
-        f32x4 y = zero4();
-        for (int K = 2; K <= I; ++K)
-          mma_f32src<TriT, false>(y, sAf + 16 * I * LDCF + 16 * K, LDCF, sXs + ((K - 2) * 2 + J) * 16 * LDX, LDX, 16);
-        store_tile(sAf + 16 * I * LDCF + 16 * J, LDCF, y, -1.f);
-      }
-      __syncthreads();
-    }
+    // ---- (3b) T = (I + A)^-1 ----
+    ks.invert(sAf, sXs);
 
     // ---- (4a) W^T = Kh^T T^T -> sWm holds -W ; U tiles start as T (w*v) ----
-#pragma unroll
+#pragma unroll 1
     for (int i = 0; i < Cfg::WPW; ++i) {
       const int t = wid + NW * i;
       if (t < Cfg::NWT) {
@@ -391,6 +241,10 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();
 
+    // every raw input of this chunk is consumed: fetch the next chunk now so the
+    // HBM latency overlaps the rest of this chunk's work
+    if (n + 1 < NC) load_chunk(n + 1);
+
     // ---- (4b) U = T(w*v) - W S ; O = (q*exp(g)) S ----
 #pragma unroll
     for (int i = 0; i < Cfg::UPW; ++i) {
@@ -398,25 +252,27 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
       if (t < Cfg::NUT) {
         const int R = t / (BV / 16), jb = t % (BV / 16);
         mma_nt_k<DK>(accU[i], sWm + 16 * R * LDK, LDK, sST + 16 * jb * LDK, LDK);
-        mma_nt_k<DK>(accO[i], sQs + 16 * R * LDK, LDK, sST + 16 * jb * LDK, LDK);
+        if (a.o) mma_nt_k<DK>(accO[i], sQs + 16 * R * LDK, LDK, sST + 16 * jb * LDK, LDK);
         store_tile_t(sUT + 16 * jb * LDC + 16 * R, LDC, accU[i]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
     // ---- (4c) O += P U -> o ;  S <- Diag(exp(g_C)) S + Kb^T U ----
+    if (a.o) {
 #pragma unroll
-    for (int i = 0; i < Cfg::UPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NUT) {
-        const int R = t / (BV / 16), jb = t % (BV / 16);
-        if (a.o == nullptr) continue;  // state-only pass (chunk states for the backward)
-        mma_nt<OpT>(accO[i], sPm + 16 * R * LDC, LDC, sUT + 16 * jb * LDC, LDC, 16 * (R + 1));
-        float* op = a.o + baseV + 16 * jb + lr;
+      for (int i = 0; i < Cfg::UPW; ++i) {
+        const int t = wid + NW * i;
+        if (t < Cfg::NUT) {
+          const int R = t / (BV / 16), jb = t % (BV / 16);
+          mma_nt<OpT>(accO[i], sPm + 16 * R * LDC, LDC, sUT + 16 * jb * LDC, LDC, 16 * (R + 1));
+          float* op = a.o + baseV + 16 * jb + lr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * lg + e;
-          if (r < Lr) op[(int64_t)(t0 + r) * rowV] = accO[i][e];
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * lg + e;
+            if (r < Lr) op[(int64_t)(t0 + r) * rowV] = accO[i][e];
+          }
         }
       }
     }
@@ -426,10 +282,11 @@ __global__ __launch_bounds__(256) void gdn2_fwd_kernel(FwdArgs a) {
       if (t < Cfg::NST) {
         const int cb = t / (BV / 16), jb = t % (BV / 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) accS[i][e] *= __expf(sgC[16 * cb + 4 * lg + e]);
+        for (int e = 0; e < 4; ++e) accS[i][e] *= __expf(sCh[DK + 16 * cb + 4 * lg + e]);
         mma_nt_k<C>(accS[i], sKbT + 16 * cb * LDC, LDC, sUT + 16 * jb * LDC, LDC);
         store_tile_t(sST + 16 * jb * LDK + 16 * cb, LDK, accS[i]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -458,7 +315,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int nv = a.Dv / BV;
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * nv;
-    hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN>), dim3(grid), dim3(FwdCfg<DK, C, BV, F32IN>::kThreads), 0, stream, a);
     return hipGetLastError();
   }
 }

@@ -103,3 +103,20 @@ def test_signature_table_matches_header_arity():
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), name
     assert ctypes.sizeof(ctypes.c_size_t) == 8
+
+
+def test_bwd_argument_errors():
+    lib = _lib.load()
+
+    def call(ws=A, ws_bytes=1 << 20, dO=A, dq=A, C=16, dt=0):
+        return lib.gdn2_bwd_chunked(A, A, A, A, A, A, None, dO, None, None, dq, A, A, A, A, A, None, ws, ws_bytes,
+                                    1, 64, 2, 16, 16, C, dt, None)
+
+    need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, 1, 64, 2, 16, 16, 16, 0)
+    assert call(ws_bytes=need - 1) == _lib.GDN2_ERR_WORKSPACE
+    assert call(ws=None) == _lib.GDN2_ERR_WORKSPACE
+    assert call(ws=A + 16, ws_bytes=need) == _lib.GDN2_ERR_ALIGN      # workspace must be 256-byte aligned
+    assert call(dO=None) == _lib.GDN2_ERR_NULL
+    assert call(dq=A + 4) == _lib.GDN2_ERR_ALIGN
+    assert call(C=48) == _lib.GDN2_ERR_UNSUPPORTED
+    assert call(dt=3) == _lib.GDN2_ERR_DTYPE
