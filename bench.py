@@ -1,0 +1,276 @@
+"""Benchmark of the GDN-2 operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--curve]
+
+A step is one training pass of the operator over one batch of synthetic input
+with the pages' layer shape: the chunked forward that also saves the chunk
+entry states, then the gate-aware chunked backward (B=8, H=16, T=4096,
+d_k=d_v=128, chunk 64, bf16 q/k/v/b/w/dO, fp32 log_alpha). W untimed steps,
+then K timed steps between two synchronisations. The one-token decode step
+(B=256 sequences, H=16, d=128, fp32 state, 128 consecutive steps) is timed
+separately and reported under "decode". Inputs are resident in HBM before any
+timed region.
+
+Prints one JSON line: value = whole-job tokens/s of the forward+backward step,
+plus "roofline" for the dominant kernel (HIP events on the launch stream),
+"mfma_frac" (FLOP model / bf16 dense peak), "decode" and "cpu_baseline" (the
+float64 oracle on a bounded sample, on this host's cores).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0        # HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16/fp16 matrix cores, TFLOP/s
+
+# FLOP and byte models per token-head at chunk C, d_k = d_v = d (algorithmic,
+# dense-counted; redundant recompute is not counted).
+def fwd_flops(C, d):
+    return 2 * (C * (3 * d + 2 * d) + 3 * d * d) + C * C / 3
+
+
+def bwd_flops(C, d):
+    return 2 * (C * (9 * d + 5 * d) + 7 * d * d) + 13 * C * C / 3
+
+
+def fwd_bytes(C, d, e_in=2, save_states=True):
+    # q, k, v, b, w read once (e_in bytes), log_alpha fp32 read, o fp32 written,
+    # chunk entry states fp32 written once per chunk
+    return 5 * d * e_in + 4 * d + 4 * d + (4 * d * d / C if save_states else 0)
+
+
+def bwd_bytes(C, d, e_in=2):
+    # reads q, k, v, b, w, dO (e_in), log_alpha (fp32), chunk states (fp32 per chunk);
+    # writes dq, dk, db, dlog_alpha, dv, dw (fp32)
+    return 6 * d * e_in + 4 * d + 4 * d * d / C + 6 * d * 4
+
+
+def decode_bytes(B, H, d, e_in=2):
+    # state read + written once (fp32), q, k, v, b, w (e_in), log_alpha fp32, o fp32
+    return B * H * (2 * 4 * d * d + 5 * d * e_in + 4 * d + 4 * d)
+
+
+def _oracle_worker(args):
+    """One (batch row, head) slice of the workload through the float64 oracle (fwd + bwd)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    q, k, v, la, b, w, dO = args
+    with threadpool_limits(limits=1):
+        oracle.forward(q, k, v, la, b, w, None)
+        oracle.backward(q, k, v, la, b, w, None, dO)
+    return q.shape[1]
+
+
+def cpu_baseline(inp, heads):
+    """Time the oracle (fwd + bwd) on batch row 0, `heads` heads, full T, over a process pool."""
+    import multiprocessing as mp
+
+    import torch
+
+    cores = min(len(os.sched_getaffinity(0)), 16, heads)
+    f = lambda t: t[0:1, :, :heads].to(torch.float64).numpy()  # noqa: E731
+    full = [f(inp[n]) for n in ("q", "k", "v", "log_alpha", "b", "w", "dO")]
+    jobs = [tuple(x[:, :, h:h + 1].copy() for x in full) for h in range(heads)]
+    ctx = mp.get_context("fork")
+    t = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_worker, jobs, chunksize=1)
+    dt = time.perf_counter() - t
+    T = full[0].shape[1]
+    H = inp["q"].shape[2]
+    # tokens of the workload carry H heads each: the sample covers heads/H of T tokens
+    tokens = T * heads / H
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"batch row 0, {heads} of {H} heads, T={T}: float64 stepwise forward + reverse-mode "
+                      f"backward, one process per head ({dt:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--curve", action="store_true", help="also time the long-sequence forward, T = 8K..64K")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the operator runs on a single MI355X; "
+              "multi-GPU runs are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from delta_rule_recurrent_gdn_amd import _lib, gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked
+
+    cfg = synth.CONFIGS[4]
+    B, T, H, D, C = cfg["B"], cfg["T"], cfg["H"], cfg["Dk"], cfg["chunk"]
+    inp = synth.config_inputs(4)
+    # the oracle baseline runs first, in forked worker processes, before this
+    # process touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline(inp, heads=16)
+
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev)
+
+    # preallocated outputs and workspace: the timed region only launches kernels
+    NC = (T + C - 1) // C
+    o = torch.empty(B, T, H, D, device=dev)
+    states = torch.empty(B, H, NC, D, D, device=dev)
+    grads = {n: torch.empty(B, T, H, D, device=dev) for n in ("dq", "dk", "dv", "dlog_alpha", "db", "dw")}
+    dS0 = torch.empty(B, H, D, D, device=dev)
+    need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, _lib.GDN2_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    sh = stream.cuda_stream
+
+    def fwd():
+        st = lib.gdn2_fwd_chunked(P(d["q"]), P(d["k"]), P(d["v"]), P(d["log_alpha"]), P(d["b"]), P(d["w"]), None,
+                                  P(o), None, P(states), B, T, H, D, D, C, _lib.GDN2_BF16, sh)
+        _lib.check(st, "gdn2_fwd_chunked")
+
+    def bwd():
+        st = lib.gdn2_bwd_chunked(P(d["q"]), P(d["k"]), P(d["v"]), P(d["log_alpha"]), P(d["b"]), P(d["w"]), None,
+                                  P(d["dO"]), None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
+                                  P(grads["dlog_alpha"]), P(grads["db"]), P(grads["dw"]), P(dS0), P(ws), need,
+                                  B, T, H, D, D, C, _lib.GDN2_BF16, sh)
+        _lib.check(st, "gdn2_bwd_chunked")
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        fwd()
+        ev[2 * i + 1].record(stream)
+        bwd()
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    t_fwd = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps  # ms
+    t_bwd = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    tokens = B * T
+    value = tokens / (ms_step / 1e3)
+
+    th = B * T * H
+    F_f, F_b = fwd_flops(C, D) * th, bwd_flops(C, D) * th
+    by_f, by_b = fwd_bytes(C, D) * th, bwd_bytes(C, D) * th
+    # dominant launch: the one with the larger share of the step; the forward
+    # is a single kernel, the backward call is its two kernels back to back
+    if t_fwd >= t_bwd:
+        dom, t_dom, by_dom, f_dom = "gdn2_fwd_kernel (chunked forward, chunk states saved)", t_fwd, by_f, F_f
+    else:
+        dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_bwd_dstate_kernel + gdn2_bwd_grad_kernel)",
+                                     t_bwd, by_b, F_b)
+    achieved = by_dom / (t_dom / 1e3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes_per_launch": int(by_dom), "avg_launch_ms": round(t_dom, 4)}
+    mfma = (F_f + F_b) / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+
+    out = {
+        "metric": "GDN-2 fwd+bwd tokens/s (H=16,d=128,T=4K) + % MFMA peak; decode % HBM peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded normal / sigmoid / -softplus draws, config 4 recipe)",
+        "config": {"workload": "GDN-2 chunked forward (saving chunk states) + gate-aware backward, "
+                               "B=8 H=16 T=4096 d_k=d_v=128 chunk=64, bf16 q/k/v/b/w/dO, fp32 log_alpha, "
+                               "fp32 outputs and gradients",
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,
+                   "parallelism": "single GPU"},
+        "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+        "mfma_frac": round(mfma, 4),
+        "hbm_frac_step": round((by_f + by_b) / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_decode:
+        c3 = synth.CONFIGS[3]
+        dec = synth.config_inputs(3)
+        dd = {k: v.to(dev) for k, v in dec.items()}
+        S = dd["S0"].clone()
+        od = torch.empty(c3["B"], c3["H"], c3["Dv"], device=dev)
+        steps = c3["steps"]
+        xs = [[dd[n][t] for n in ("q", "k", "v", "log_alpha", "b", "w")] for t in range(steps)]
+
+        def dstep(t):
+            x = xs[t]
+            st = lib.gdn2_decode_step(P(x[0]), P(x[1]), P(x[2]), P(x[3]), P(x[4]), P(x[5]), P(S), P(od),
+                                      c3["B"], c3["H"], c3["Dk"], c3["Dv"], _lib.GDN2_BF16, sh)
+            _lib.check(st, "gdn2_decode_step")
+
+        for t in range(8):
+            dstep(t)
+        S.copy_(dd["S0"])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(steps):
+            dstep(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        byt = decode_bytes(c3["B"], c3["H"], c3["Dk"])
+        gbs = byt / (us / 1e6) / 1e9
+        out["decode"] = {"workload": "one-token decode, B=256 H=16 d=128, fp32 state 256x16x128x128, "
+                                     "bf16 token inputs, 128 consecutive steps",
+                         "us_per_step": round(us, 2), "tokens_per_s": round(c3["B"] / (us / 1e6), 1),
+                         "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_step": int(byt)}
+        del dd, dec, xs, S
+
+    if args.curve:
+        curve = {}
+        for Tc in synth.CONFIGS[2]["T"]:
+            ci = synth.config_inputs(2, T=Tc)
+            cd = {k: v.to(dev) for k, v in ci.items()}
+            oc = torch.empty(1, Tc, 16, D, device=dev)
+            Sf = torch.empty(1, 16, D, D, device=dev)
+
+            def cf():
+                st = lib.gdn2_fwd_chunked(P(cd["q"]), P(cd["k"]), P(cd["v"]), P(cd["log_alpha"]), P(cd["b"]),
+                                          P(cd["w"]), P(cd["S0"]), P(oc), P(Sf), None, 1, Tc, 16, D, D, C,
+                                          _lib.GDN2_BF16, sh)
+                _lib.check(st, "gdn2_fwd_chunked")
+
+            cf()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(3):
+                cf()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            ms = a0.elapsed_time(a1) / 3
+            curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1)}
+            del cd, ci
+        out["fwd_long_sequence_curve"] = curve
+
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

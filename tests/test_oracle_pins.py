@@ -397,3 +397,19 @@ def test_planted_mistakes_are_caught(kind):
     o_c, ST_c = _planted_forward("none", q, k, v, la, b, w, S0)
     assert maxrel(o_c, o_ok) < TOL and maxrel(ST_c, ST_ok) < TOL
     assert math.isfinite(float(np.sum(o)))
+
+
+def test_oracle_matches_its_recorded_small_case():
+    """Regression record written by tests/golden/make_golden.py (which calls only the oracle)."""
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_small_case.json")
+    rec = json.load(open(path))
+    inp = {k: np.array(v) for k, v in rec["inputs"].items()}
+    o, ST = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
+    g = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"], inp["dO"],
+                        inp["dS_final"], checkpoint_every=2)
+    out = {"o": o, "S_T": ST, **g}
+    for k, v in rec["outputs"].items():
+        assert np.max(np.abs(out[k] - np.array(v))) < 1e-12, k
