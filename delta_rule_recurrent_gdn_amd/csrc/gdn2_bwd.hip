@@ -42,11 +42,14 @@ namespace gdn2 {
 // =============================================================================
 // reverse state-gradient chain
 // =============================================================================
+// Reverse chain: 8 waves per workgroup, as in the forward.
+constexpr int kDstThreads = 512;
+
 template <int DK, int C, int BV, bool F32IN>
 struct DstCfg {
-  using KS = KSide<DK, C, F32IN>;
+  static constexpr int kThreads = kDstThreads;
+  using KS = KSide<DK, C, F32IN, kThreads>;
   using OpT = typename KS::OpT;
-  static constexpr int kThreads = 512;
   static constexpr int kWaves = kThreads / kWave;
   static constexpr int NB = KS::NB;
   static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF;
@@ -75,10 +78,12 @@ struct DstCfg {
   static constexpr int UPW = (NUT + kWaves - 1) / kWaves;
   static constexpr int NST = (DK / 16) * (BV / 16);
   static constexpr int SPW = (NST + kWaves - 1) / kWaves;
+  static constexpr int VW_RPP = kThreads / (BV / 8);
+  static constexpr int VW_RPT = (C + VW_RPP - 1) / VW_RPP;
 };
 
 template <int DK, int C, int BV, bool F32IN>
-__global__ __launch_bounds__(512) void gdn2_bwd_dstate_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDstThreads) void gdn2_bwd_dstate_kernel(BwdArgs a) {
   using Cfg = DstCfg<DK, C, BV, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
@@ -120,15 +125,17 @@ __global__ __launch_bounds__(512) void gdn2_bwd_dstate_kernel(BwdArgs a) {
 
   KS ks;
   ks.init(tid);
+  constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
   const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
-  const bool vw_on = vw_r < C;
-  Raw8<F32IN> rdo;
+  Raw8<F32IN> rdo[VW_RPT];
   auto load_chunk = [&](int nn) {
     const int tn = nn * C, Ln = min(C, T - tn);
     ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, tn, Ln);
-    if (vw_on) {
-      if (vw_r < Ln) ld_raw(rdo, a.dO, baseV + (int64_t)(tn + vw_r) * rowV + 8 * vw_j8);
-      else zero_raw(rdo);
+#pragma unroll
+    for (int i = 0; i < VW_RPT; ++i) {
+      const int r = vw_r + i * VW_RPP;
+      if (r < Ln) ld_raw(rdo[i], a.dO, baseV + (int64_t)(tn + r) * rowV + 8 * vw_j8);
+      else zero_raw(rdo[i]);
     }
   };
 
@@ -165,11 +172,15 @@ __global__ __launch_bounds__(512) void gdn2_bwd_dstate_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (vw_on) {
-      float d8[8];
-      cvt(rdo, d8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sDOT[(8 * vw_j8 + i) * LDC + vw_r] = static_cast<OpT>(d8[i]);
+    for (int i = 0; i < VW_RPT; ++i) {
+      const int r = vw_r + i * VW_RPP;
+      if (r < C) {
+        float d8[8];
+        cvt(rdo[i], d8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sDOT[(8 * vw_j8 + e) * LDC + r] = static_cast<OpT>(d8[e]);
+      }
     }
     ks.gates(sTot, sG, sCh);
     f32x4 accG[KS::GPW];
@@ -251,9 +262,33 @@ __global__ __launch_bounds__(512) void gdn2_bwd_dstate_kernel(BwdArgs a) {
 // =============================================================================
 // chunk-parallel gradients
 // =============================================================================
+
+// Four input values kept in registers: fp32 as is, bf16 as two packed pairs
+// (exact: the inputs are bf16 numbers).
+template <bool F32IN>
+struct Vals4 {
+  float v[4];
+  __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0.f; }
+  __device__ __forceinline__ void set(int e, const void* base, int64_t idx) {
+    v[e] = static_cast<const float*>(base)[idx];
+  }
+  __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+};
+template <>
+struct Vals4<false> {
+  uint32_t p[2];
+  __device__ __forceinline__ void zero() { p[0] = p[1] = 0u; }
+  __device__ __forceinline__ void set(int e, const void* base, int64_t idx) {
+    const uint32_t x = static_cast<const uint16_t*>(base)[idx];
+    p[e >> 1] = (e & 1) ? ((p[e >> 1] & 0x0000ffffu) | (x << 16)) : ((p[e >> 1] & 0xffff0000u) | x);
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    return __uint_as_float((e & 1) ? (p[e >> 1] & 0xffff0000u) : (p[e >> 1] << 16));
+  }
+};
 template <int DK, int C, int BVB_, bool F32IN>
 struct GradCfg {
-  using KS = KSide<DK, C, F32IN>;
+  using KS = KSide<DK, C, F32IN, 512, 4>;  // float4 log_alpha rows: the decay-gradient scan reuses them
   using OpT = typename KS::OpT;
   // operand type of the products with the wide-range Gram factors: a bf16 hi/lo
   // pair for bf16 inputs, fp32 for fp32 inputs
@@ -305,21 +340,30 @@ struct GradCfg {
   static constexpr int oWdA = 0;                                   // dA, dA^T, dP, dP^T (hi/lo or fp32)
   static constexpr int oWF = oWdA + 4 * WPARTS * kWM;              // factor^T [DK][LDC] (hi/lo or fp32)
   static constexpr int endB = oWF + WPARTS * DK * LDC * WB;
-  // phase D (decay-gradient scan) starts at 0 as well
-  static constexpr int endD = C * DK * 4;
-  static constexpr int endMain = [] {
+  // phase D (output staging and the decay-gradient scan) starts at 0 as well:
+  // x, and where they fit, dq, dk, db as fp32 [C][DK] (staged for full-row stores)
+  static constexpr int endBase = [] {
     int m = endPF;
     if (endPT > m) m = endPT;
     if (endV > m) m = endV;
     if (endA > m) m = endA;
     if (endB > m) m = endB;
-    if (endD > m) m = endD;
     return m;
   }();
+  // cumsum segment totals: scratch of the gate prep and of the final scan only,
+  // so they sit past the prep buffers and the output staging
+  static constexpr int tot_at(int endD_) { return ((endPF > endD_ ? endPF : endD_) + 15) & ~15; }
+  static constexpr int main_end(int endD_) {
+    return endBase > tot_at(endD_) + KS::kTotBytes ? endBase : tot_at(endD_) + KS::kTotBytes;
+  }
+  static constexpr int kTail = KS::kChanBytes + 2 * DK * 4 + kWaves * DK * 4;
+  static constexpr bool kStage = ((main_end(4 * C * DK * 4) + 15) & ~15) + kTail <= 160 * 1024;
+  static constexpr int endD = (kStage ? 4 : 1) * C * DK * 4;
+  static constexpr int oTOT = tot_at(endD);
+  static constexpr int endMain = main_end(endD);
   // tail (always live)
   static constexpr int oCH = (endMain + 15) & ~15;
-  static constexpr int oTOT = oCH + KS::kChanBytes;
-  static constexpr int oEX = oTOT + KS::kTotBytes;                 // float [2][DK] exit-term pieces
+  static constexpr int oEX = oCH + KS::kChanBytes;                 // float [2][DK] exit-term pieces
   static constexpr int oEXW = oEX + 2 * DK * 4;                    // float [kWaves][DK] per-wave partials
   static constexpr int kLdsBytes = oEXW + kWaves * DK * 4;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
@@ -398,12 +442,16 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 
   // the C x DK tiles this lane owns: rows 16R + 4lg + e, column 16cb + lr.
   // Keep q, k, b and e1 = exp(g - g_m) there for the final chain rule.
-  float pq[KPW][4], pk[KPW][4], pb[KPW][4], pe1[KPW][4];
+  Vals4<F32IN> pq[KPW], pk[KPW], pb[KPW];
+  float pe1[KPW][4];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int t = wid + NW * i;
+    pq[i].zero();
+    pk[i].zero();
+    pb[i].zero();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pq[i][e] = pk[i][e] = pb[i][e] = 0.f, pe1[i][e] = 1.f;
+    for (int e = 0; e < 4; ++e) pe1[i][e] = 1.f;
     if (t < Cfg::NKT) {
       const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
 #pragma unroll
@@ -412,9 +460,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         pe1[i][e] = __expf(sG[r * DK + c] - sCh[c]);
         if (r < Lr) {
           const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
-          pq[i][e] = load1<F32IN>(a.q, idx);
-          pk[i][e] = load1<F32IN>(a.k, idx);
-          pb[i][e] = load1<F32IN>(a.b, idx);
+          pq[i].set(e, a.q, idx);
+          pk[i].set(e, a.k, idx);
+          pb[i].set(e, a.b, idx);
         }
       }
     }
@@ -454,7 +502,41 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int p = 0; p < SPASS; ++p) rs[p] = 0.f;
 
-  for (int jt = 0; jt < Dv / BVB; ++jt) {
+  // value-tile inputs, fetched one tile ahead into registers
+  constexpr int VG = C * (BVB / 4);                                // 4-value groups of dO, v, w per tile
+  constexpr int VLD = (VG + NT - 1) / NT;
+  float4 rS0[SPASS], rDS[SPASS];
+  Raw4<F32IN> rDO[VLD], rV[VLD], rW[VLD];
+  const int nvt = Dv / BVB;
+  auto vload = [&](int jt) {
+    const int j0 = jt * BVB;
+#pragma unroll
+    for (int p = 0; p < SPASS; ++p) {
+      const int c = st_c + p * SROWS;
+      if (c < DK) {
+        rS0[p] = *reinterpret_cast<const float4*>(S0g + (int64_t)c * Dv + j0 + 4 * st_j4);
+        rDS[p] = *reinterpret_cast<const float4*>(dSg + (int64_t)c * Dv + j0 + 4 * st_j4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int e = tid + i * NT;
+      const int r = e / (BVB / 4), j4 = e % (BVB / 4);
+      if (e < VG && r < Lr) {
+        const int64_t idx = baseV + (int64_t)(t0 + r) * rowV + j0 + 4 * j4;
+        ld_raw(rDO[i], a.dO, idx);
+        ld_raw(rV[i], a.v, idx);
+        ld_raw(rW[i], a.w, idx);
+      } else {
+        zero_raw(rDO[i]);
+        zero_raw(rV[i]);
+        zero_raw(rW[i]);
+      }
+    }
+  };
+  vload(0);
+
+  for (int jt = 0; jt < nvt; ++jt) {
     const int j0 = jt * BVB;
     __syncthreads();  // previous users of the phase region are done
     // S0 and dS tiles: both layouts; rowsum(S0 * dS) partials
@@ -462,8 +544,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
     for (int p = 0; p < SPASS; ++p) {
       const int c = st_c + p * SROWS;
       if (c < DK) {
-        const float4 s4 = *reinterpret_cast<const float4*>(S0g + (int64_t)c * Dv + j0 + 4 * st_j4);
-        const float4 d4 = *reinterpret_cast<const float4*>(dSg + (int64_t)c * Dv + j0 + 4 * st_j4);
+        const float4 s4 = rS0[p], d4 = rDS[p];
         st4(sS0 + c * LDB + 4 * st_j4, s4.x, s4.y, s4.z, s4.w);
         st4(sDS + c * LDB + 4 * st_j4, d4.x, d4.y, d4.z, d4.w);
         const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
@@ -476,20 +557,22 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       }
     }
     // dO, w*v: 4 consecutive value columns of one row
-    for (int e = tid; e < C * (BVB / 4); e += NT) {
-      const int r = e / (BVB / 4), j4 = e % (BVB / 4);
-      float d4[4] = {0.f, 0.f, 0.f, 0.f}, v4[4] = {0.f, 0.f, 0.f, 0.f}, w4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (r < Lr) {
-        const int64_t idx = baseV + (int64_t)(t0 + r) * rowV + j0 + 4 * j4;
-        load4<F32IN>(a.dO, idx, d4);
-        load4<F32IN>(a.v, idx, v4);
-        load4<F32IN>(a.w, idx, w4);
-      }
-      st4(sDO + r * LDB + 4 * j4, d4[0], d4[1], d4[2], d4[3]);
-      st4(sWV + r * LDB + 4 * j4, w4[0] * v4[0], w4[1] * v4[1], w4[2] * v4[2], w4[3] * v4[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sDOT[(4 * j4 + i) * LDC + r] = static_cast<OpT>(d4[i]);
+    for (int i = 0; i < VLD; ++i) {
+      const int e = tid + i * NT;
+      if (e < VG) {
+        const int r = e / (BVB / 4), j4 = e % (BVB / 4);
+        float d4[4], v4[4], w4[4];
+        cvt(rDO[i], d4);
+        cvt(rV[i], v4);
+        cvt(rW[i], w4);
+        st4(sDO + r * LDB + 4 * j4, d4[0], d4[1], d4[2], d4[3]);
+        st4(sWV + r * LDB + 4 * j4, w4[0] * v4[0], w4[1] * v4[1], w4[2] * v4[2], w4[3] * v4[3]);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) sDOT[(4 * j4 + q4) * LDC + r] = static_cast<OpT>(d4[q4]);
+      }
     }
+    if (jt + 1 < nvt) vload(jt + 1);
     __syncthreads();
     // X = w*v - Kh S0  -> X^T
 #pragma unroll
@@ -765,9 +848,12 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   }
   __syncthreads();  // phase B buffers are dead
 
-  // ---- outputs dq, dk, db; x = q dq + 2 b db - k dk for the decay gradient ----
+  // ---- outputs dq, dk, db (staged through LDS for full-row stores); x = q dq + 2 b db - k dk ----
   // per-wave colsum partials of Kb * dKb (one wave per row block of each column block)
   for (int e = tid; e < NW * DK; e += NT) sExW[e] = 0.f;
+  float* sOq = sX + C * DK;
+  float* sOk = sX + 2 * C * DK;
+  float* sOb = sX + 3 * C * DK;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
@@ -778,9 +864,12 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * R + 4 * lg + e;
-        const float x = pq[i][e] * gq[i][e] + 2.f * pb[i][e] * gb[i][e] - pk[i][e] * gk[i][e];
-        sX[r * DK + c] = x;
-        if (r < Lr) {
+        sX[r * DK + c] = pq[i][e] * gq[i][e] + 2.f * pb[i][e] * gb[i][e] - pk[i][e] * gk[i][e];
+        if constexpr (Cfg::kStage) {
+          sOq[r * DK + c] = gq[i][e];
+          sOk[r * DK + c] = gk[i][e];
+          sOb[r * DK + c] = gb[i][e];
+        } else if (r < Lr) {  // no room to stage: column-per-lane stores
           const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
           a.dq[idx] = gq[i][e];
           a.dk[idx] = gk[i][e];
@@ -790,33 +879,53 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
+  for (int e = tid; Cfg::kStage && e < C * (DK / 4); e += NT) {
+    const int r = e / (DK / 4), c4 = 4 * (e % (DK / 4));
+    if (r < Lr) {
+      const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c4;
+      *reinterpret_cast<float4*>(a.dq + idx) = *reinterpret_cast<const float4*>(sOq + r * DK + c4);
+      *reinterpret_cast<float4*>(a.dk + idx) = *reinterpret_cast<const float4*>(sOk + r * DK + c4);
+      *reinterpret_cast<float4*>(a.db + idx) = *reinterpret_cast<const float4*>(sOb + r * DK + c4);
+    }
+  }
   // dlog_alpha: reverse cumulative sum over the chunk plus the exit term
   {
     constexpr int RPS = KS::LA_RPS, SEGS = KS::LA_SEGS;
-    const int c = ks.la_c, sg = ks.la_sg;
-    float loc[RPS];
+    const int c = ks.la_c, sg = ks.la_sg;  // 4 channels c..c+3, rows sg*RPS ..
+    float4 loc[RPS];
     if (ks.la_on) {
-      float run = 0.f;
+      float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int i = RPS - 1; i >= 0; --i) {
-        run += sX[(sg * RPS + i) * DK + c];
+        const float4 x = *reinterpret_cast<const float4*>(sX + (sg * RPS + i) * DK + c);
+        run.x += x.x; run.y += x.y; run.z += x.z; run.w += x.w;
         loc[i] = run;
       }
-      sTot[sg * DK + c] = run;
+      *reinterpret_cast<float4*>(sTot + sg * DK + c) = run;
     }
     __syncthreads();
     if (ks.la_on) {
-      float after = 0.f;
+      float after[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < SEGS; ++s2)
-        if (s2 > sg) after += sTot[s2 * DK + c];
-      float exitc = __expf(sCh[DK + c]) * sEx[c];
+      for (int s2 = 0; s2 < SEGS; ++s2) {
+        if (s2 > sg) {
+          const float4 tt = *reinterpret_cast<const float4*>(sTot + s2 * DK + c);
+          after[0] += tt.x; after[1] += tt.y; after[2] += tt.z; after[3] += tt.w;
+        }
+      }
+      float ex[4];
 #pragma unroll
-      for (int R = 0; R < NB; ++R) exitc += sExW[R * DK + c];
+      for (int j = 0; j < 4; ++j) {
+        ex[j] = __expf(sCh[DK + c + j]) * sEx[c + j] + after[j];
+#pragma unroll
+        for (int R = 0; R < NB; ++R) ex[j] += sExW[R * DK + c + j];
+      }
 #pragma unroll
       for (int i = 0; i < RPS; ++i) {
         const int r = sg * RPS + i;
-        if (r < Lr) a.dlog_alpha[baseK + (int64_t)(t0 + r) * rowK + c] = loc[i] + after + exitc;
+        if (r < Lr)
+          *reinterpret_cast<float4*>(a.dlog_alpha + baseK + (int64_t)(t0 + r) * rowK + c) =
+              make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
       }
     }
   }
@@ -838,8 +947,8 @@ static hipError_t launch_dstate_t(const BwdArgs& a, hipStream_t s) {
     return hipErrorInvalidConfiguration;
   } else {
     const int nv = a.Dv / BV, nbh = a.B * a.H;
-    hipLaunchKernelGGL((gdn2_bwd_dstate_kernel<DK, C, BV, F32IN>), dim3(((nbh + 7) / 8) * 8 * nv), dim3(512), 0, s,
-                       a);
+    hipLaunchKernelGGL((gdn2_bwd_dstate_kernel<DK, C, BV, F32IN>), dim3(((nbh + 7) / 8) * 8 * nv),
+                       dim3(kDstThreads), 0, s, a);
     return hipGetLastError();
   }
 }

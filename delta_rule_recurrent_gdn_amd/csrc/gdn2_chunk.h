@@ -38,7 +38,26 @@ __device__ __forceinline__ void tri_index(int p, int& R, int& I) {
   I = p;
 }
 
-template <int DK, int C, bool F32IN, int NT = 512>
+// N (1 or 4) consecutive fp32 values to / from LDS in one access
+template <int N>
+__device__ __forceinline__ void st_lanes(float* dst, const float (&x)[N]) {
+  if constexpr (N == 4) *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+  else *dst = x[0];
+}
+template <int N>
+__device__ __forceinline__ void ld_lanes(float (&x)[N], const float* src) {
+  if constexpr (N == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(src);
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+  } else {
+    x[0] = *src;
+  }
+}
+
+template <int DK, int C, bool F32IN, int NT = 512, int LAW = 1>
 struct KSide {
   using OpT = typename std::conditional<F32IN, float, _Float16>::type;  // value-side operand type
   static constexpr int NW = NT / kWave;
@@ -51,8 +70,14 @@ struct KSide {
   static constexpr int LDSW = SW + (F32IN ? 4 : 8);   // Gram slice rows
   static constexpr int LDCF = C + 4;                  // fp32 [C][C]
   static constexpr int LDX = 20;                      // fp32 16x16 scratch tiles
-  static constexpr int LA_SEGS = (NT / DK) < C ? (NT / DK) : C;
+  // log_alpha: each thread owns LAW adjacent channels (1 or 4) of LA_RPS consecutive rows.
+  // The wide form takes fewer instructions; the narrow one fewer address registers.
+  static_assert(LAW == 1 || LAW == 4, "log_alpha vector width");
+  static constexpr int LA_SEGS = (NT / (DK / LAW)) < C ? (NT / (DK / LAW)) : C;
   static constexpr int LA_RPS = C / LA_SEGS;
+  // q, k, b: groups of 4 channels of one row; rows qk_r + i * QK_RPP, i < QK_RPT
+  static constexpr int QK_RPP = NT / (SW / 4);
+  static constexpr int QK_RPT = (C + QK_RPP - 1) / QK_RPP;
   static constexpr int GRAMB = F32IN ? 4 : 2;
   static constexpr int GRAMPARTS = F32IN ? 3 : 6;     // Kh', Qh', Kt' (hi/lo each for the bf16 split)
   static constexpr int kSliceBytes = C * LDSW * GRAMB;
@@ -69,18 +94,18 @@ struct KSide {
   static_assert(LA_SEGS >= 2 && LA_SEGS * LA_RPS == C, "cumsum tiling");
 
   // ---- raw registers of one chunk ----
-  float la[LA_RPS];
-  Raw4<F32IN> rq[NSL], rk[NSL], rb[NSL];
+  float la[LA_RPS][LAW];
+  Raw4<F32IN> rq[NSL][QK_RPT], rk[NSL][QK_RPT], rb[NSL][QK_RPT];
   int la_c, la_sg, qk_r, qk_c4;
   bool la_on, qk_on;
 
   __device__ __forceinline__ void init(int tid) {
-    la_c = tid % DK;
-    la_sg = tid / DK;
+    la_c = LAW * (tid % (DK / LAW));  // first of the thread's channels
+    la_sg = tid / (DK / LAW);
     la_on = la_sg < LA_SEGS;
     qk_r = tid / (SW / 4);
     qk_c4 = tid % (SW / 4);
-    qk_on = qk_r < C;
+    qk_on = qk_r < C && qk_r < QK_RPP;
   }
 
   // Fetch chunk rows [tn, tn + Ln) of one (batch, head): base* index token 0.
@@ -90,21 +115,34 @@ struct KSide {
 #pragma unroll
       for (int i = 0; i < LA_RPS; ++i) {
         const int r = la_sg * LA_RPS + i;
-        la[i] = r < Ln ? log_alpha[baseK + (int64_t)(tn + r) * rowK + la_c] : 0.f;
+        const float* src = log_alpha + baseK + (int64_t)(tn + r) * rowK + la_c;
+        if constexpr (LAW == 4) {
+          const float4 x = r < Ln ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+          la[i][0] = x.x;
+          la[i][1] = x.y;
+          la[i][2] = x.z;
+          la[i][3] = x.w;
+        } else {
+          la[i][0] = r < Ln ? *src : 0.f;
+        }
       }
     }
     if (qk_on) {
 #pragma unroll
       for (int s = 0; s < NSL; ++s) {
-        if (qk_r < Ln) {
-          const int64_t idx = baseK + (int64_t)(tn + qk_r) * rowK + s * SW + 4 * qk_c4;
-          ld_raw(rq[s], q, idx);
-          ld_raw(rk[s], k, idx);
-          ld_raw(rb[s], b, idx);
-        } else {
-          zero_raw(rq[s]);
-          zero_raw(rk[s]);
-          zero_raw(rb[s]);
+#pragma unroll
+        for (int i = 0; i < QK_RPT; ++i) {
+          const int r = qk_r + i * QK_RPP;
+          if (r < Ln) {
+            const int64_t idx = baseK + (int64_t)(tn + r) * rowK + s * SW + 4 * qk_c4;
+            ld_raw(rq[s][i], q, idx);
+            ld_raw(rk[s][i], k, idx);
+            ld_raw(rb[s][i], b, idx);
+          } else {
+            zero_raw(rq[s][i]);
+            zero_raw(rk[s][i]);
+            zero_raw(rb[s][i]);
+          }
         }
       }
     }
@@ -115,31 +153,52 @@ struct KSide {
   // have synchronised since the last readers of sG/sChan/sTot. Ends synchronised.
   __device__ __forceinline__ void gates(float* sTot, float* sG, float* sChan) {
     if (la_on) {
-      float run = 0.f;
+      float run[LAW];
 #pragma unroll
-      for (int i = 0; i < LA_RPS; ++i) {
-        run += la[i];
-        la[i] = run;
-      }
-      sTot[la_sg * DK + la_c] = run;
+      for (int j = 0; j < LAW; ++j) run[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < LA_RPS; ++i)
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) {
+          run[j] += la[i][j];
+          la[i][j] = run[j];
+        }
+      st_lanes(sTot + la_sg * DK + la_c, run);
     }
     __syncthreads();
     if (la_on) {
-      float off = 0.f, gmid = 0.f, gend = 0.f;
+      float off[LAW], gmid[LAW], gend[LAW];
+#pragma unroll
+      for (int j = 0; j < LAW; ++j) off[j] = gmid[j] = gend[j] = 0.f;
 #pragma unroll
       for (int sgi = 0; sgi < LA_SEGS; ++sgi) {
-        const float tt = sTot[sgi * DK + la_c];
-        if (sgi < la_sg) off += tt;
-        if (sgi < LA_SEGS / 2) gmid += tt;  // the middle row C/2-1 ends segment LA_SEGS/2-1
-        gend += tt;
+        float tt[LAW];
+        ld_lanes(tt, sTot + sgi * DK + la_c);
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) {
+          if (sgi < la_sg) off[j] += tt[j];
+          if (sgi < LA_SEGS / 2) gmid[j] += tt[j];  // the middle row C/2-1 ends segment LA_SEGS/2-1
+          gend[j] += tt[j];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < LA_RPS; ++i) sG[(la_sg * LA_RPS + i) * DK + la_c] = la[i] + off;
+      for (int i = 0; i < LA_RPS; ++i) {
+        float g[LAW];
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) g[j] = la[i][j] + off[j];
+        st_lanes(sG + (la_sg * LA_RPS + i) * DK + la_c, g);
+      }
       if (la_sg == 0) {
-        sChan[la_c] = gmid;
-        sChan[DK + la_c] = gend;
-        sChan[2 * DK + la_c] = __expf(gmid);
-        sChan[3 * DK + la_c] = __expf(gend - gmid);
+        float e1[LAW], e2[LAW];
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) {
+          e1[j] = __expf(gmid[j]);
+          e2[j] = __expf(gend[j] - gmid[j]);
+        }
+        st_lanes(sChan + la_c, gmid);
+        st_lanes(sChan + DK + la_c, gend);
+        st_lanes(sChan + 2 * DK + la_c, e1);
+        st_lanes(sChan + 3 * DK + la_c, e2);
       }
     }
     __syncthreads();
@@ -158,12 +217,14 @@ struct KSide {
     for (int i = 0; i < GPW; ++i) accG[i] = zero4();
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      if (qk_on) {
-        const int r = qk_r, cl = 4 * qk_c4, c0 = sl * SW + cl;
+#pragma unroll
+      for (int ri = 0; ri < QK_RPT; ++ri) {
+        const int r = qk_r + ri * QK_RPP, cl = 4 * qk_c4, c0 = sl * SW + cl;
+        if (!qk_on || r >= C) continue;
         float qv[4], kv[4], bv[4];
-        cvt(rq[sl], qv);
-        cvt(rk[sl], kv);
-        cvt(rb[sl], bv);
+        cvt(rq[sl][ri], qv);
+        cvt(rk[sl][ri], kv);
+        cvt(rb[sl][ri], bv);
         const float4 g4 = *reinterpret_cast<const float4*>(sG + r * DK + c0);
         const float4 gm4 = *reinterpret_cast<const float4*>(sChan + c0);
         const float4 eg4 = *reinterpret_cast<const float4*>(sChan + 2 * DK + c0);

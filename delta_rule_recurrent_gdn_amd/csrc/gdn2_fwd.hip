@@ -49,11 +49,15 @@
 
 namespace gdn2 {
 
+// Workgroup size: 8 waves (two per SIMD) hide each other's LDS and matrix-core
+// latencies; every wave has 256 registers.
+constexpr int kFwdThreads = 512;
+
 template <int DK, int C, int BV, bool F32IN>
 struct FwdCfg {
-  using KS = KSide<DK, C, F32IN>;
+  static constexpr int kThreads = kFwdThreads;
+  using KS = KSide<DK, C, F32IN, kThreads>;
   using OpT = typename KS::OpT;
-  static constexpr int kThreads = 512;
   static constexpr int kWaves = kThreads / kWave;
   static constexpr int NB = KS::NB;
   static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF, LDX = KS::LDX;
@@ -88,10 +92,13 @@ struct FwdCfg {
   static constexpr int SPW = (NST + kWaves - 1) / kWaves;
   static constexpr int NWT = (DK / 16) * NB;                       // W^T tiles
   static constexpr int WPW = (NWT + kWaves - 1) / kWaves;
+  // v, w: 8 consecutive value columns of one row; rows vw_r + i * VW_RPP
+  static constexpr int VW_RPP = kThreads / (BV / 8);
+  static constexpr int VW_RPT = (C + VW_RPP - 1) / VW_RPP;
 };
 
 template <int DK, int C, int BV, bool F32IN>
-__global__ __launch_bounds__(512) void gdn2_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<DK, C, BV, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
@@ -134,21 +141,22 @@ __global__ __launch_bounds__(512) void gdn2_fwd_kernel(FwdArgs a) {
 
   KS ks;
   ks.init(tid);
-  // v, w: 8 consecutive value columns of one row
+  constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
   const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
-  const bool vw_on = vw_r < C;
-  Raw8<F32IN> rv, rw;
+  Raw8<F32IN> rv[VW_RPT], rw[VW_RPT];
   auto load_chunk = [&](int nn) {
     const int tn = nn * C, Ln = min(C, T - tn);
     ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, tn, Ln);
-    if (vw_on) {
-      if (vw_r < Ln) {
-        const int64_t idx = baseV + (int64_t)(tn + vw_r) * rowV + 8 * vw_j8;
-        ld_raw(rv, a.v, idx);
-        ld_raw(rw, a.w, idx);
+#pragma unroll
+    for (int i = 0; i < VW_RPT; ++i) {
+      const int r = vw_r + i * VW_RPP;
+      if (r < Ln) {
+        const int64_t idx = baseV + (int64_t)(tn + r) * rowV + 8 * vw_j8;
+        ld_raw(rv[i], a.v, idx);
+        ld_raw(rw[i], a.w, idx);
       } else {
-        zero_raw(rv);
-        zero_raw(rw);
+        zero_raw(rv[i]);
+        zero_raw(rw[i]);
       }
     }
   };
@@ -190,12 +198,16 @@ __global__ __launch_bounds__(512) void gdn2_fwd_kernel(FwdArgs a) {
     __syncthreads();  // the previous chunk's readers of the per-chunk buffers are done
 
     // ---- (1) gate preprocessing; w*v -> sWVT ----
-    if (vw_on) {
-      float vv[8], ww[8];
-      cvt(rv, vv);
-      cvt(rw, ww);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sWVT[(8 * vw_j8 + i) * LDC + vw_r] = static_cast<OpT>(ww[i] * vv[i]);
+    for (int i = 0; i < VW_RPT; ++i) {
+      const int r = vw_r + i * VW_RPP;
+      if (r < C) {
+        float vv[8], ww[8];
+        cvt(rv[i], vv);
+        cvt(rw[i], ww);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sWVT[(8 * vw_j8 + e) * LDC + r] = static_cast<OpT>(ww[e] * vv[e]);
+      }
     }
     ks.gates(sTot, sG, sCh);
 
@@ -315,7 +327,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int nv = a.Dv / BV;
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * nv;
-    hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN>), dim3(grid), dim3(FwdCfg<DK, C, BV, F32IN>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
     return hipGetLastError();
   }
 }
