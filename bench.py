@@ -133,12 +133,15 @@ def main():
     dS0 = torch.empty(B, H, D, D, device=dev)
     need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, _lib.GDN2_BF16)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need_f = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, _lib.GDN2_BF16)
+    ws_f = torch.empty(max(need_f, 1), dtype=torch.uint8, device=dev)
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     sh = stream.cuda_stream
 
-    def fwd():
+    def fwd(single_pass=False):
+        wsp, wsn = (None, 0) if single_pass else (P(ws_f), need_f)
         st = lib.gdn2_fwd_chunked(P(d["q"]), P(d["k"]), P(d["v"]), P(d["log_alpha"]), P(d["b"]), P(d["w"]), None,
-                                  P(o), None, P(states), B, T, H, D, D, C, _lib.GDN2_BF16, sh)
+                                  P(o), None, P(states), wsp, wsn, B, T, H, D, D, C, _lib.GDN2_BF16, sh)
         _lib.check(st, "gdn2_fwd_chunked")
 
     def bwd():
@@ -168,6 +171,15 @@ def main():
     t_fwd = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps  # ms
     t_bwd = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
     ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    # the single-pass forward (no workspace), timed on its own for comparison
+    fwd(single_pass=True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        fwd(single_pass=True)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    t_fwd_single = s0.elapsed_time(s1) / args.steps
     tokens = B * T
     value = tokens / (ms_step / 1e3)
 
@@ -177,7 +189,8 @@ def main():
     # dominant launch: the one with the larger share of the step; the forward
     # is a single kernel, the backward call is its two kernels back to back
     if t_fwd >= t_bwd:
-        dom, t_dom, by_dom, f_dom = "gdn2_fwd_kernel (chunked forward, chunk states saved)", t_fwd, by_f, F_f
+        dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked launch (gdn2_prep_fwd_kernel + gdn2_chain_fwd_kernel, "
+                                     "chunk states saved)", t_fwd, by_f, F_f)
     else:
         dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_bwd_dstate_kernel + gdn2_bwd_grad_kernel)",
                                      t_bwd, by_b, F_b)
@@ -197,7 +210,7 @@ def main():
                                "fp32 outputs and gradients",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,
                    "parallelism": "single GPU"},
-        "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+        "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4), "fwd_single_pass_ms": round(t_fwd_single, 4),
         "mfma_frac": round(mfma, 4),
         "hbm_frac_step": round((by_f + by_b) / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline,
@@ -246,11 +259,13 @@ def main():
             cd = {k: v.to(dev) for k, v in ci.items()}
             oc = torch.empty(1, Tc, 16, D, device=dev)
             Sf = torch.empty(1, 16, D, D, device=dev)
+            nwc = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, Tc, 16, D, D, C, _lib.GDN2_BF16)
+            wc = torch.empty(max(nwc, 1), dtype=torch.uint8, device=dev)
 
             def cf():
                 st = lib.gdn2_fwd_chunked(P(cd["q"]), P(cd["k"]), P(cd["v"]), P(cd["log_alpha"]), P(cd["b"]),
-                                          P(cd["w"]), P(cd["S0"]), P(oc), P(Sf), None, 1, Tc, 16, D, D, C,
-                                          _lib.GDN2_BF16, sh)
+                                          P(cd["w"]), P(cd["S0"]), P(oc), P(Sf), None, P(wc), nwc, 1, Tc, 16, D,
+                                          D, C, _lib.GDN2_BF16, sh)
                 _lib.check(st, "gdn2_fwd_chunked")
 
             cf()

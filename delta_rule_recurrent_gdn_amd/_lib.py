@@ -32,7 +32,7 @@ _SZ = ctypes.c_size_t
 
 # name -> (restype, argtypes), in the order of include/gdn2.h
 SIGNATURES = {
-    "gdn2_fwd_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "gdn2_fwd_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gdn2_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "gdn2_bwd_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                               _I, _I, _I, _I, _I, _I, _I, _P]),

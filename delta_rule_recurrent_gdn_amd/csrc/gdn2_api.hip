@@ -50,6 +50,14 @@ size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk) {
   return 2 * aligned;
 }
 
+// Two-stage forward workspace: records, then T (w*v) for every chunk; 0 when
+// the chunk-parallel kernel does not cover the sizes.
+size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  if (!gdn2::prep_fwd_supported(Dk, chunk, f32)) return 0;
+  const size_t nchunks = (size_t)B * H * ((T + chunk - 1) / chunk);
+  return nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+}
+
 }  // namespace
 
 namespace gdn2 {
@@ -95,12 +103,17 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
     if (!chunk_ok(chunk) || T == 0) return 0;
     return bwd_workspace(B, T, H, Dk, Dv, chunk);
   }
+  if (op == GDN2_OP_FWD) {
+    if (!chunk_ok(chunk) || T == 0) return 0;
+    return fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+  }
   return 0;
 }
 
 int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                     const void* w, const float* S0, float* o, float* S_final, float* chunk_states, int B,
-                     int T, int H, int Dk, int Dv, int chunk, int dt, void* stream) {
+                     const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
+                     void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
+                     int dt, void* stream) {
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
@@ -116,7 +129,16 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
   st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
   if (st != GDN2_OK) return st;
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
-  return hip_status(gdn2::launch_fwd(a, s));
+  const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+  if (workspace == nullptr || need == 0) return hip_status(gdn2::launch_fwd(a, s));
+  if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+  char* rec = static_cast<char*>(workspace);
+  float* ut = reinterpret_cast<float*>(rec + (size_t)B * H * ((T + chunk - 1) / chunk) *
+                                                 gdn2::fwd_record_bytes(Dk, chunk, dt == GDN2_F32));
+  st = hip_status(gdn2::launch_prep_fwd(a, rec, ut, s));
+  if (st != GDN2_OK) return st;
+  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, s));
 }
 
 int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,

@@ -1,0 +1,111 @@
+// gdn2_frag.h -- matrix-core operand fragments and the per-chunk record layout
+// shared by the chunk-parallel preparation kernels and the sequential chain
+// kernels (gfx950, wave64).
+//
+// Fragment. A "unit" is the left operand of one matrix-core step for a 16-row
+// tile: 16 rows x KU contraction indices, 64 lanes x 16 bytes = 1 KB, lane l at
+// byte 16*l. Lane l holds row (l % 16) and the contraction slots of lane group
+// g = l / 16:
+//   16-bit operands (KU = 32, v_mfma_f32_16x16x32_f16): slot j < 4 is index
+//     4g + j, slot j >= 4 is index 16 + 4g + (j - 4);
+//   fp32 operands (KU = 16, four v_mfma_f32_16x16x4_f32): slot j is 4g + j.
+// An fp32 accumulator tile holds rows 4g + i of column (l % 16), so the right
+// operand of one unit is exactly the accumulators of the 16-row tiles 2u and
+// 2u+1 (16-bit; slots j < 4 from the first, j >= 4 from the second) or of tile
+// u (fp32; step i uses accumulator element i). A product whose right operand
+// is a running state or write matrix therefore never stages it through LDS,
+// and the left operand is read with one 16-byte access per lane.
+//
+// Record. The chunk-parallel kernels store, per (batch*head, chunk), the left
+// operands the chain needs as consecutive units (row tile major, then unit),
+// followed by one unit holding exp(g_C) per key channel.
+#pragma once
+
+#include "gdn2_common.h"
+
+namespace gdn2 {
+
+template <bool F32IN>
+struct Frag {
+  using OpT = typename std::conditional<F32IN, float, _Float16>::type;
+  static constexpr int KU = F32IN ? 16 : 32;      // contraction indices per unit
+  static constexpr int kUnitBytes = 1024;
+  // contraction index of slot j in lane group g
+  __device__ __forceinline__ static int kslot(int g, int j) {
+    if constexpr (F32IN) return 4 * g + j;
+    else return j < 4 ? 4 * g + j : 12 + 4 * g + j;
+  }
+  static constexpr int units(int K) { return (K + KU - 1) / KU; }
+};
+
+// Per-chunk record: matrices in units, then the exp(g_C) unit.
+// Forward (DIR = 0):  Wn = -W [C x DK], Qs = q exp(g) [C x DK],
+//                     KbT = (k exp(g_C - g))^T [DK x C], P [C x C].
+// Backward (DIR = 1): PT = P^T [C x C], Kb [C x DK], QsT [DK x C], WnT = -W^T [DK x C].
+template <int DK, int C, bool F32IN, int DIR>
+struct Record {
+  using F = Frag<F32IN>;
+  static constexpr int UK = F::units(DK), UC = F::units(C);
+  static constexpr int RC = C / 16, RK = DK / 16;  // 16-row tiles
+  // unit offsets of the four matrices
+  static constexpr int u0 = 0;
+  static constexpr int u1 = u0 + (DIR == 0 ? RC * UK : RC * UC);
+  static constexpr int u2 = u1 + (DIR == 0 ? RC * UK : RC * UK);
+  static constexpr int u3 = u2 + (DIR == 0 ? RK * UC : RK * UC);
+  static constexpr int uG = u3 + (DIR == 0 ? RC * UC : RK * UC);
+  static constexpr int kUnits = uG + 1;
+  static constexpr int kBytes = kUnits * F::kUnitBytes;
+  static_assert(DK * 4 <= 1024, "exp(g_C) must fit one unit");
+};
+
+// Write the units of a row-major matrix X [M][K] (operand type, leading
+// dimension ld, in LDS) to dst (global): unit (R, u) at dst + (R * units(K) + u) KB.
+// Units are dealt round-robin to the nw waves starting at wave w0.
+template <bool F32IN>
+__device__ __forceinline__ void write_units(const typename Frag<F32IN>::OpT* X, int ld, int M, int K, char* dst,
+                                            int wid, int nw) {
+  using F = Frag<F32IN>;
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int nu = F::units(K), total = (M / 16) * nu;
+  for (int t = wid; t < total; t += nw) {
+    const int R = t / nu, u = t - R * nu;
+    const int k0 = F::KU * u;
+    const auto* row = X + (16 * R + r) * ld;
+    uint4 out;
+    if constexpr (F32IN) {
+      const float4 v = *reinterpret_cast<const float4*>(row + k0 + 4 * g);
+      out = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(row + k0 + 4 * g);
+      uint2 b = make_uint2(0u, 0u);
+      if (k0 + 16 < K) b = *reinterpret_cast<const uint2*>(row + k0 + 16 + 4 * g);
+      out = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    *reinterpret_cast<uint4*>(dst + (int64_t)t * F::kUnitBytes + 16 * l) = out;
+  }
+}
+
+// Right operand of unit u from accumulator tiles (16-bit: tiles 2u, 2u+1).
+__device__ __forceinline__ f16x8 rhs_from_acc(const f32x4& t0, const f32x4& t1) {
+  f16x8 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[i] = static_cast<_Float16>(t0[i]);
+    b[4 + i] = static_cast<_Float16>(t1[i]);
+  }
+  return b;
+}
+
+// acc += unit(A) * rhs, 16-bit.
+__device__ __forceinline__ void unit_mma(f32x4& acc, const uint4& a, const f16x8& b) {
+  acc = mfma16x16x32(__builtin_bit_cast(f16x8, a), b, acc);
+}
+// acc += unit(A) * rhs, fp32: the right operand is the accumulator tile itself.
+__device__ __forceinline__ void unit_mma(f32x4& acc, const uint4& a, const f32x4& b) {
+  acc = mfma16x16x4(__uint_as_float(a.x), b[0], acc);
+  acc = mfma16x16x4(__uint_as_float(a.y), b[1], acc);
+  acc = mfma16x16x4(__uint_as_float(a.z), b[2], acc);
+  acc = mfma16x16x4(__uint_as_float(a.w), b[3], acc);
+}
+
+}  // namespace gdn2

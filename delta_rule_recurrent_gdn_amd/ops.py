@@ -51,8 +51,14 @@ def _dtype_code(dtype):
 
 
 def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_state=True,
-                     want_chunk_states=False):
-    """Chunked forward. Returns (o, S_final or None, chunk_states or None)."""
+                     want_chunk_states=False, single_pass=False, workspace=None):
+    """Chunked forward. Returns (o, S_final or None, chunk_states or None).
+
+    By default the two-stage path runs (chunk-parallel factors into a workspace,
+    then the sequential state chain); `workspace` may supply that scratch (a
+    uint8 device tensor of at least gdn2_workspace_bytes(GDN2_OP_FWD, ...)
+    bytes), else it is allocated here. single_pass=True runs the one-kernel
+    path, which needs no workspace."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -68,9 +74,16 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
     NC = (T + chunk - 1) // chunk
     states = (torch.empty((B, H, NC, Dk, Dv), dtype=torch.float32, device=dev) if want_chunk_states else None)
+    need = 0 if single_pass else lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, Dk, Dv, chunk,
+                                                           _dtype_code(q.dtype))
+    if need == 0:
+        workspace = None
+    elif workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn2_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
-                              _ptr(S_final), _ptr(states), B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype),
-                              _stream(dev))
+                              _ptr(S_final), _ptr(states), _ptr(workspace), ws_bytes, B, T, H, Dk, Dv, chunk,
+                              _dtype_code(q.dtype), _stream(dev))
     _lib.check(st, "gdn2_fwd_chunked")
     return o, S_final, states
 

@@ -97,11 +97,22 @@ typedef enum { GDN2_OP_FWD = 0, GDN2_OP_DECODE = 1, GDN2_OP_BWD = 2 } gdn2_op;
  *   o            [B,T,H,Dv] fp32, required when T > 0
  *   S_final      [B,H,Dk,Dv] fp32, nullable
  *   chunk_states [B,H,NC,Dk,Dv] fp32, nullable (training mode when given)
+ *   workspace    nullable. NULL selects the single-pass kernel: one workgroup
+ *                per (batch, head, value tile) walks the chunks and recomputes
+ *                each chunk's state-independent part in turn. Otherwise it must
+ *                hold at least gdn2_workspace_bytes(GDN2_OP_FWD, ...) bytes,
+ *                256-byte aligned, and the two-stage path runs: a
+ *                chunk-parallel kernel writes every chunk's state-independent
+ *                factors (W, T (w*v), decayed q and k, the causal q-k term,
+ *                exp(g_last)) to the workspace, then a light sequential kernel
+ *                carries the state through the chunks. Same arithmetic, same
+ *                results up to rounding order. When gdn2_workspace_bytes returns
+ *                0 for the sizes, the workspace is ignored.
  */
 int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha,
                      const void* b, const void* w, const float* S0, float* o, float* S_final,
-                     float* chunk_states, int B, int T, int H, int Dk, int Dv, int chunk,
-                     int dt, void* stream);
+                     float* chunk_states, void* workspace, size_t workspace_bytes, int B, int T,
+                     int H, int Dk, int Dv, int chunk, int dt, void* stream);
 
 /*
  * gdn2_decode_step -- one recurrence step per sequence, state updated in place
@@ -146,8 +157,10 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
                      void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
                      int Dv, int chunk, int dt, void* stream);
 
-/* Workspace bytes an entry point needs for these sizes (0 for forward and
- * decode). Returns 0 for invalid sizes as well; the call itself reports them. */
+/* Workspace bytes an entry point needs for these sizes: the backward's
+ * requirement, the forward's two-stage path (0 when that path does not cover
+ * the sizes), 0 for decode. Returns 0 for invalid sizes as well; the call
+ * itself reports them. */
 size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chunk, int dt);
 
 /* Static, NUL-terminated description of a status code. */

@@ -42,7 +42,10 @@ def test_workspace_bytes():
     B, T, H, D, C = 8, 4096, 16, 128, 64
     nc = T // C
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == 0
+    # two-stage forward: per chunk a record of 57 units of 1 KB (W, decayed q: 16 each; decayed k^T: 16;
+    # causal term: 8; exp(g_last): 1) plus T (w v) in fp32
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 4)
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == 0   # fp32 at d=128, chunk 64: no
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4
@@ -52,12 +55,13 @@ A = 4096  # a fake, 16-byte aligned address: never dereferenced because validati
 
 
 def fwd(**kw):
-    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, Sf=None, cs=None, B=1, T=64, H=2, Dk=16, Dv=16,
-                C=16, dt=0)
+    args = dict(q=A, k=A, v=A, la=A, b=A, w=A, S0=None, o=A, Sf=None, cs=None, ws=None, ws_bytes=0, B=1, T=64,
+                H=2, Dk=16, Dv=16, C=16, dt=0)
     args.update(kw)
     return _lib.load().gdn2_fwd_chunked(args["q"], args["k"], args["v"], args["la"], args["b"], args["w"],
-                                        args["S0"], args["o"], args["Sf"], args["cs"], args["B"], args["T"],
-                                        args["H"], args["Dk"], args["Dv"], args["C"], args["dt"], None)
+                                        args["S0"], args["o"], args["Sf"], args["cs"], args["ws"], args["ws_bytes"],
+                                        args["B"], args["T"], args["H"], args["Dk"], args["Dv"], args["C"],
+                                        args["dt"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,6 +76,8 @@ def fwd(**kw):
     (dict(T=-1), _lib.GDN2_ERR_SHAPE),
     (dict(B=-2), _lib.GDN2_ERR_SHAPE),
     (dict(dt=0, Dk=128, Dv=128, C=64), _lib.GDN2_ERR_UNSUPPORTED),   # fp32 inputs at d=128 need chunk <= 32
+    (dict(ws=A, ws_bytes=1), _lib.GDN2_ERR_WORKSPACE),              # two-stage path: workspace too small
+    (dict(ws=A + 16, ws_bytes=1 << 30), _lib.GDN2_ERR_ALIGN),       # workspace must be 256-byte aligned
     (dict(B=0), _lib.GDN2_OK),                                       # nothing to do, nothing launched
     (dict(H=0), _lib.GDN2_OK),
 ])
@@ -98,7 +104,7 @@ def test_error_raised_by_binding_names_the_status():
 def test_signature_table_matches_header_arity():
     text = open(HEADER).read()
     for name, (_, args) in _lib.SIGNATURES.items():
-        m = re.search(name + r"\s*\(([^;]*)\);", text, re.S)
+        m = re.search(r"^\s*(?:int|size_t|const char\*)\s+" + name + r"\s*\(([^;]*)\);", text, re.S | re.M)
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(params) == len(args), name

@@ -14,18 +14,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(inp, chunk, states=False):
+def _run(inp, chunk, states=False, single=False):
     d = to_dev(inp)
     o, S, cs = gdn2_fwd_chunked(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d.get("S0"), chunk=chunk,
-                                want_chunk_states=states)
+                                want_chunk_states=states, single_pass=single)
     torch.cuda.synchronize()
     return o, S, cs
 
 
-def test_config0_tiny_fp32_exact():
+# both forward paths: the two-stage one (workspace) and the single-pass kernel
+PATHS = pytest.mark.parametrize("single", [False, True], ids=["two_stage", "single_pass"])
+
+
+@PATHS
+def test_config0_tiny_fp32_exact(single):
     """B=1, H=2, T=64, d=16, chunk 16, fp32, seed 0: every output against the stepwise oracle."""
     inp = synth.config_inputs(0)
-    o, S, _ = _run(inp, 16)
+    o, S, _ = _run(inp, 16, single=single)
     o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], None)
     print("config0 err o %.3e S %.3e" % (rel_err(f64(o), o_ref), rel_err(f64(S), S_ref)))
     assert rel_err(f64(o), o_ref) <= TOL_F32
@@ -36,9 +41,10 @@ SWEEP = [(dk, dv, c) for (dk, dv) in ((16, 16), (32, 64), (64, 32), (128, 128), 
          for c in (16, 32, 64)]
 
 
+@PATHS
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("Dk,Dv,C", SWEEP)
-def test_sweep_small(dtype, Dk, Dv, C):
+def test_sweep_small(dtype, Dk, Dv, C, single):
     """Several tiles, a ragged tail, nonzero S0, chunk states, B*H not a multiple of 8."""
     B, H = 1, 3
     T = 2 * C + 5
@@ -46,10 +52,10 @@ def test_sweep_small(dtype, Dk, Dv, C):
     tdt = synth.torch_dtype(dtype)
     if dtype == "fp32" and Dk == 128 and C == 64:
         with pytest.raises(_lib.GDN2Error) as ei:
-            _run(inp, C)
+            _run(inp, C, single=single)
         assert ei.value.status == _lib.GDN2_ERR_UNSUPPORTED
         return
-    o, S, cs = _run(inp, C, states=True)
+    o, S, cs = _run(inp, C, states=True, single=single)
     o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
     tol = tol_for(tdt)
     assert rel_err(f64(o), o_ref) <= tol, rel_err(f64(o), o_ref)
@@ -65,10 +71,11 @@ def test_sweep_small(dtype, Dk, Dv, C):
         assert rel_err(cs[:, :, n], ref) <= tol
 
 
-def test_config1_sampled_pairs():
+@PATHS
+def test_config1_sampled_pairs(single):
     """B=8, H=16, T=4096, d=128, chunk 64, bf16: all outputs of sampled (b, h) pairs."""
     inp = synth.config_inputs(1)
-    o, S, _ = _run(inp, 64)
+    o, S, _ = _run(inp, 64, single=single)
     pairs = [(0, 0), (3, 7), (7, 15), (5, 2)]
     o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
     eo, es = rel_err(gpu_pairs(o, pairs), o_ref), rel_err(gpu_state_pairs(S, pairs), S_ref)
@@ -79,10 +86,11 @@ def test_config1_sampled_pairs():
 
 
 @pytest.mark.parametrize("T", [8192, 65536])
-def test_config2_long_sequence_sampled(T):
+@PATHS
+def test_config2_long_sequence_sampled(T, single):
     """B=1, H=16, T up to 64K, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1)."""
     inp = synth.config_inputs(2, T=T)
-    o, S, _ = _run(inp, 64)
+    o, S, _ = _run(inp, 64, single=single)
     pairs = [(0, 0), (0, 9)] if T <= 8192 else [(0, 5)]
     o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
     eo, es = rel_err(gpu_pairs(o, pairs), o_ref), rel_err(gpu_state_pairs(S, pairs), S_ref)
@@ -90,41 +98,45 @@ def test_config2_long_sequence_sampled(T):
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
-def test_bitwise_deterministic():
+@PATHS
+def test_bitwise_deterministic(single):
     inp = synth.make_inputs(4, 1000, 16, 128, 128, "bf16", seed=11, s0_std=0.02)
-    o1, S1, _ = _run(inp, 64)
-    o2, S2, _ = _run(inp, 64)
+    o1, S1, _ = _run(inp, 64, single=single)
+    o2, S2, _ = _run(inp, 64, single=single)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-def test_split_sequence_composes_on_gpu():
+@PATHS
+def test_split_sequence_composes_on_gpu(single):
     """fwd(x1 || x2) = fwd(x2; S0 = S_final(x1)) at full head size."""
     inp = synth.make_inputs(2, 640, 16, 128, 128, "bf16", seed=12, s0_std=0.02)
-    o, S, _ = _run(inp, 64)
+    o, S, _ = _run(inp, 64, single=single)
     a = {k_: (v_[:, :320].contiguous() if k_ != "S0" else v_) for k_, v_ in inp.items()}
-    o1, S1, _ = _run(a, 64)
+    o1, S1, _ = _run(a, 64, single=single)
     b = {k_: (v_[:, 320:].contiguous() if k_ != "S0" else v_) for k_, v_ in inp.items()}
     b["S0"] = S1.cpu()
-    o2, S2, _ = _run(b, 64)
+    o2, S2, _ = _run(b, 64, single=single)
     oc = torch.cat([o1, o2], dim=1)
     assert rel_err(f64(oc), f64(o)) < 1e-3 and rel_err(f64(S2), f64(S)) < 1e-3
 
 
-def test_chunk_size_invariance():
+@PATHS
+def test_chunk_size_invariance(single):
     inp = synth.make_inputs(1, 300, 4, 64, 64, "bf16", seed=13, s0_std=0.1)
     ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
     for C in (16, 32, 64):
-        o, _, _ = _run(inp, C)
+        o, _, _ = _run(inp, C, single=single)
         assert rel_err(f64(o), ref) <= TOL_BF16
 
 
-def test_reduces_to_kda_on_gpu():
+@PATHS
+def test_reduces_to_kda_on_gpu(single):
     """b = w = beta * 1 on the GPU equals the oracle's KDA case (pinned separately on the CPU)."""
     inp = synth.make_inputs(2, 200, 3, 32, 32, "fp32", seed=14, s0_std=0.1)
     beta = torch.sigmoid(torch.randn(2, 200, 3, 1, generator=torch.Generator().manual_seed(3)))
     inp["b"] = beta.expand(2, 200, 3, 32).contiguous()
     inp["w"] = beta.expand(2, 200, 3, 32).contiguous()
-    o, S, _ = _run(inp, 32)
+    o, S, _ = _run(inp, 32, single=single)
     o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
     assert rel_err(f64(o), o_ref) <= TOL_F32 and rel_err(f64(S), S_ref) <= TOL_F32
 
@@ -141,17 +153,32 @@ def test_empty_sequence_copies_state():
     assert torch.count_nonzero(S) == 0
 
 
-def test_single_token_and_odd_batch():
+@PATHS
+def test_single_token_and_odd_batch(single):
     for T in (1, 17):
         inp = synth.make_inputs(3, T, 5, 128, 64, "bf16", seed=15 + T, s0_std=0.2)
-        o, S, _ = _run(inp, 64)
+        o, S, _ = _run(inp, 64, single=single)
         o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
         assert rel_err(f64(o), o_ref) <= TOL_BF16 and rel_err(f64(S), S_ref) <= TOL_BF16
 
 
-def test_nan_propagates():
+@PATHS
+def test_nan_propagates(single):
     inp = synth.make_inputs(1, 64, 2, 16, 16, "fp32", seed=16)
     inp["v"][0, 10, 1, 3] = float("nan")
-    o, S, _ = _run(inp, 16)
+    o, S, _ = _run(inp, 16, single=single)
     assert torch.isnan(o[0, 10:, 1]).any() and torch.isnan(S[0, 1]).any()
     assert not torch.isnan(o[0, :, 0]).any()
+
+
+@pytest.mark.parametrize("Dk,Dv,C,dtype", [(128, 128, 64, "bf16"), (64, 32, 32, "fp32"), (16, 128, 16, "bf16")])
+def test_two_stage_matches_single_pass(Dk, Dv, C, dtype):
+    """The two paths perform the same products with the same operand roundings; only the fp32 accumulation
+    order differs. With 16-bit operands that can move an operand's rounding by one fp16 ulp (2^-11 relative),
+    which the state carries to later chunks, so the bar there is a few ulp; with fp32 operands it is 1e-5."""
+    inp = synth.make_inputs(2, 3 * C + 7, 5, Dk, Dv, dtype, seed=17 + C, s0_std=0.1)
+    a = _run(inp, C, states=True, single=False)
+    b = _run(inp, C, states=True, single=True)
+    bar = 1e-5 if dtype == "fp32" else 4e-3
+    for x, y in zip(a, b):
+        assert rel_err(f64(x), f64(y)) < bar
