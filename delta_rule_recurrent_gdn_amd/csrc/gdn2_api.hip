@@ -117,7 +117,9 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
-  if (!gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32)) return GDN2_ERR_UNSUPPORTED;
+  // the two-stage path runs when a workspace is given and covers the sizes
+  const bool two_stage = workspace != nullptr && gdn2::prep_fwd_supported(Dk, chunk, dt == GDN2_F32);
+  if (!two_stage && !gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32)) return GDN2_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {
@@ -129,8 +131,8 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
   st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
   if (st != GDN2_OK) return st;
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
+  if (!two_stage) return hip_status(gdn2::launch_fwd(a, s));
   const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
-  if (workspace == nullptr || need == 0) return hip_status(gdn2::launch_fwd(a, s));
   if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
   char* rec = static_cast<char*>(workspace);

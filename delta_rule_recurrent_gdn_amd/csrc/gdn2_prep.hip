@@ -24,6 +24,13 @@
 // of their decay-scaled factors (referenced to the chunk middle so that the
 // exp(+-g) factors stay in range), all other operands fp16 for bf16 inputs;
 // fp32 matrix cores for fp32 inputs.
+//
+// Layout for occupancy (two workgroups per CU at d_k = 128, chunk 64, bf16):
+// each thread owns one row and 4 channels of every channel slice, so the
+// in-chunk cumsum of log_alpha runs in registers (wave shuffles, then one
+// cross-wave total); decayed q and the causal term (computed transposed, as
+// P^T tiles, whose accumulators are P's record units) go straight to the
+// workspace; the transposed decayed k and b*k share one LDS buffer in turn.
 
 #include "gdn2_chunk.h"
 #include "gdn2_frag.h"
@@ -33,68 +40,70 @@ namespace gdn2 {
 
 template <int DK, int C, bool F32IN>
 struct PrepCfg {
-  static constexpr int kThreads = 512;
-  using KS = KSide<DK, C, F32IN, kThreads>;
+  static constexpr int NT = 512, NW = NT / kWave;
+  using KS = KSide<DK, C, F32IN, NT>;  // slice geometry and the blocked inversion
   using OpT = typename KS::OpT;
   using Rec = Record<DK, C, F32IN, 0>;
-  static constexpr int kWaves = kThreads / kWave;
-  static constexpr int NB = KS::NB;
-  static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF;
+  using F = Frag<F32IN>;
+  static constexpr int NB = KS::NB, SW = KS::SW, NSL = KS::NSL;
+  static constexpr int LDC = KS::LDC, LDCF = KS::LDCF, LDSW = KS::LDSW;
   static constexpr int OPB = sizeof(OpT);
-  static constexpr int DVM = 128;                                  // largest value width
-  // persistent region
-  static constexpr int oKhT = 0;                                   // OpT [DK][LDC]  (b k exp(g))^T
-  static constexpr int oQs = oKhT + DK * LDC * OPB;                // OpT [C][LDK]   q exp(g)
-  static constexpr int oKbT = oQs + C * LDK * OPB;                 // OpT [DK][LDC]  (k exp(g_C - g))^T
-  static constexpr int oCH = oKbT + DK * LDC * OPB;                // float [4][DK]
-  static constexpr int oTOT = oCH + KS::kChanBytes;
-  static constexpr int oX = oTOT + KS::kTotBytes;
-  // phase F
-  static constexpr int oG = oX;
-  static constexpr int oSL = oG + KS::kGBytes;
-  static constexpr int endF = oSL + KS::kSlicesBytes;
-  // phase W
-  static constexpr int oAf = oX;                                   // float [C][LDCF]  A, then T
-  static constexpr int oPm = oAf + KS::kAfBytes;                   // OpT [C][LDC]     P
-  static constexpr int oWVT = oPm + C * LDC * OPB;                 // OpT [DVM][LDC]   (w v)^T
-  static constexpr int oXs = oWVT + DVM * LDC * OPB;
-  static constexpr int endW = oXs + KS::kXsBytes;
-  static constexpr int kLdsBytes = endF > endW ? endF : endW;
+  static constexpr int DVM = 128;                // largest value width
+  // thread -> (row, 4 channels of every slice): TPR threads per row
+  static constexpr int TPR = SW / 4;
+  static constexpr int RPW = kWave / TPR;        // rows per wave
+  static constexpr int NGT = KS::NGT, GPW = KS::GPW;
+  // LDS
+  static constexpr int oCH = 0;                                    // float [4][DK] g_m, g_C, exp(g_m), exp(g_C-g_m)
+  static constexpr int oTOT = oCH + 4 * DK * 4;                    // float [NW][DK] per-wave cumsum totals
+  static constexpr int oR = oTOT + NW * DK * 4;
+  static constexpr int oSL = oR;                                   // Gram factor slices (factor phase)
+  static constexpr int oAf = oR;                                   // float [C][LDCF] A, then T (after the Gram)
+  static constexpr int oXs = oAf + KS::kAfBytes;
+  static constexpr int endR = (KS::kSlicesBytes > KS::kAfBytes + KS::kXsBytes ? KS::kSlicesBytes
+                                                                              : KS::kAfBytes + KS::kXsBytes);
+  static constexpr int oT1 = oR + ((endR + 15) & ~15);            // OpT [DK][LDC]: Kb^T, later Kh^T
+  static constexpr int oWVT = oT1 + DK * LDC * OPB;                // OpT [DVM][LDC] (w v)^T
+  static constexpr int kLdsBytes = oWVT + DVM * LDC * OPB;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
-  // v, w: 8 consecutive value columns of one row, up to DVM columns
-  static constexpr int VW_PT = (C * DVM / 8 + kThreads - 1) / kThreads;
+  static constexpr int VW_PT = (C * DVM / 8 + NT - 1) / NT;
 };
 
+// Byte offset, inside a record matrix with `nu` units per row tile, of the
+// 4 consecutive contraction indices k0..k0+3 (k0 % 4 == 0) of row r.
+template <bool F32IN>
+__device__ __forceinline__ int unit_off4(int r, int k0, int nu) {
+  using F = Frag<F32IN>;
+  const int u = k0 / F::KU, kl = k0 - u * F::KU;
+  const int g = (kl & 15) >> 2, half = F32IN ? 0 : (kl >> 4);
+  return ((r >> 4) * nu + u) * F::kUnitBytes + 16 * ((r & 15) + 16 * g) + 8 * half;
+}
+
 template <int DK, int C, bool F32IN>
-__global__ __launch_bounds__(512) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec_base, float* ut_base) {
+__global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec_base, float* ut_base) {
   using Cfg = PrepCfg<DK, C, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   using Rec = typename Cfg::Rec;
   using F = Frag<F32IN>;
-  constexpr int NW = Cfg::kWaves, NB = Cfg::NB, NT = Cfg::kThreads;
-  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, SW = Cfg::SW, NSL = Cfg::NSL, TPR = Cfg::TPR;
+  constexpr int LDC = Cfg::LDC, LDCF = Cfg::LDCF, LDSW = Cfg::LDSW;
+  constexpr int NGT = Cfg::NGT, GPW = Cfg::GPW;
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
-  OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
-  OpT* sQs = reinterpret_cast<OpT*>(smem + Cfg::oQs);
-  OpT* sKbT = reinterpret_cast<OpT*>(smem + Cfg::oKbT);
   float* sCh = reinterpret_cast<float*>(smem + Cfg::oCH);
   float* sTot = reinterpret_cast<float*>(smem + Cfg::oTOT);
-  float* sG = reinterpret_cast<float*>(smem + Cfg::oG);
   char* sSL = smem + Cfg::oSL;
   float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
-  OpT* sPm = reinterpret_cast<OpT*>(smem + Cfg::oPm);
-  OpT* sWVT = reinterpret_cast<OpT*>(smem + Cfg::oWVT);
   float* sXs = reinterpret_cast<float*>(smem + Cfg::oXs);
+  OpT* sT1 = reinterpret_cast<OpT*>(smem + Cfg::oT1);
+  OpT* sWVT = reinterpret_cast<OpT*>(smem + Cfg::oWVT);
 
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
-  const int lg = l >> 4;
 
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int NC = (T + C - 1) / C;
-  // block -> (batch*head, chunk), chunk fastest
-  const int bh = blockIdx.x / NC, n = blockIdx.x - bh * NC;
+  const int bh = blockIdx.x / NC, n = blockIdx.x - bh * NC;  // chunk fastest
   const int bi = bh / H, h = bh - bi * H;
   const int t0 = n * C, Lr = min(C, T - t0);
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
@@ -103,58 +112,243 @@ __global__ __launch_bounds__(512) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec
   char* rec = rec_base + ((int64_t)bh * NC + n) * Rec::kBytes;
   float* ut = ut_base + ((int64_t)bh * NC + n) * C * Dv;
 
-  KS ks;
-  ks.init(tid);
-  ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, t0, Lr);
-  const int vpr = Dv / 8;  // threads per row of v, w
-  Raw8<F32IN> rv[Cfg::VW_PT], rw[Cfg::VW_PT];
+  // ---- loads: row r, channels sl*SW + 4*c4 .. +3 of every slice sl ----
+  const int r = tid / TPR, c4 = tid - r * TPR;
+  const bool live = r < C;  // a row of the chunk (rows >= Lr are zero padding)
+  Raw4<F32IN> rq[NSL], rk[NSL], rb[NSL];
+  float g[NSL][4];
 #pragma unroll
-  for (int i = 0; i < Cfg::VW_PT; ++i) {
-    const int e = tid + NT * i, r = e / vpr, j8 = e - r * vpr;
-    if (r < Lr) {
-      const int64_t idx = baseV + (int64_t)(t0 + r) * rowV + 8 * j8;
-      ld_raw(rv[i], a.v, idx);
-      ld_raw(rw[i], a.w, idx);
+  for (int sl = 0; sl < NSL; ++sl) {
+    const int c0 = sl * SW + 4 * c4;
+    if (live && r < Lr) {
+      const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c0;
+      ld_raw(rq[sl], a.q, idx);
+      ld_raw(rk[sl], a.k, idx);
+      ld_raw(rb[sl], a.b, idx);
+      const float4 x = *reinterpret_cast<const float4*>(a.log_alpha + idx);
+      g[sl][0] = x.x; g[sl][1] = x.y; g[sl][2] = x.z; g[sl][3] = x.w;
     } else {
-      zero_raw(rv[i]);
-      zero_raw(rw[i]);
+      zero_raw(rq[sl]);
+      zero_raw(rk[sl]);
+      zero_raw(rb[sl]);
+      g[sl][0] = g[sl][1] = g[sl][2] = g[sl][3] = 0.f;
+    }
+  }
+  // (w v)^T for the whole value width, into its own LDS region
+  {
+    const int vpr = Dv / 8;
+#pragma unroll
+    for (int i = 0; i < Cfg::VW_PT; ++i) {
+      const int e = tid + NT * i, rr = e / vpr, j8 = e - rr * vpr;
+      if (rr < C) {
+        float vv[8], ww[8];
+        if (rr < Lr) {
+          const int64_t idx = baseV + (int64_t)(t0 + rr) * rowV + 8 * j8;
+          load8<F32IN>(a.v, idx, vv);
+          load8<F32IN>(a.w, idx, ww);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) vv[q] = ww[q] = 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sWVT[(8 * j8 + q) * LDC + rr] = static_cast<OpT>(ww[q] * vv[q]);
+      }
     }
   }
 
-  // ---- gates, factors, Gram products ----
-  ks.gates(sTot, sG, sCh);
-  f32x4 accG[KS::GPW];
-  ks.factors_gram(sG, sCh, sSL, accG,
-                  [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
-                      const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
-                    (void)e1;
-                    st4(sQs + r * LDK + c0, qv[0] * eg[0], qv[1] * eg[1], qv[2] * eg[2], qv[3] * eg[3]);
+  // ---- gates: inclusive cumsum over the rows of the chunk ----
+  // within the wave (rows r = lane / TPR of this wave), then across waves
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                      sKhT[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * eg[i]);
-                      sKbT[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * ec[i]);
-                    }
-                  });
-  ks.template gram_store<false>(accG, sAf, sPm);
-  // (w v)^T: the Gram slices are dead now
+  for (int off = TPR; off < kWave; off *= 2) {
 #pragma unroll
-  for (int i = 0; i < Cfg::VW_PT; ++i) {
-    const int e = tid + NT * i, r = e / vpr, j8 = e - r * vpr;
-    if (r < C) {
-      float vv[8], ww[8];
-      cvt(rv[i], vv);
-      cvt(rw[i], ww);
+    for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sWVT[(8 * j8 + q) * LDC + r] = static_cast<OpT>(ww[q] * vv[q]);
+      for (int j = 0; j < 4; ++j) {
+        const float y = __shfl_up(g[sl][j], off, kWave);
+        if (l >= off) g[sl][j] += y;
+      }
+  }
+  if (l >= kWave - TPR) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+      *reinterpret_cast<float4*>(sTot + wid * DK + sl * SW + 4 * c4) = make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int w2 = 0; w2 < wid; ++w2) {
+      const float4 t4 = *reinterpret_cast<const float4*>(sTot + w2 * DK + sl * SW + 4 * c4);
+      off.x += t4.x; off.y += t4.y; off.z += t4.z; off.w += t4.w;
+    }
+    g[sl][0] += off.x; g[sl][1] += off.y; g[sl][2] += off.z; g[sl][3] += off.w;
+    const int c0 = sl * SW + 4 * c4;
+    if (r == C / 2 - 1) *reinterpret_cast<float4*>(sCh + c0) = make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+    if (r == C - 1) *reinterpret_cast<float4*>(sCh + DK + c0) = make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+  }
+  __syncthreads();
+  for (int c = tid; c < DK; c += NT) {
+    sCh[2 * DK + c] = __expf(sCh[c]);
+    sCh[3 * DK + c] = __expf(sCh[DK + c] - sCh[c]);
+  }
+  __syncthreads();
+
+  // ---- factors and the Gram products, one channel slice at a time ----
+  // A tiles (R, I) from Kh' Kt'^T; the causal term as P^T tiles (I, R) from
+  // Kt' Qh'^T, whose accumulators are P's record units directly
+  f32x4 accG[GPW];
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) accG[i] = zero4();
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    const int cl = 4 * c4, c0 = sl * SW + cl;
+    if (live) {
+      float qv[4], kv[4], bv[4];
+      cvt(rq[sl], qv);
+      cvt(rk[sl], kv);
+      cvt(rb[sl], bv);
+      const float4 gm4 = *reinterpret_cast<const float4*>(sCh + c0);
+      const float4 eg4 = *reinterpret_cast<const float4*>(sCh + 2 * DK + c0);
+      const float4 ec4 = *reinterpret_cast<const float4*>(sCh + 3 * DK + c0);
+      const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+      const float egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w}, egcm[4] = {ec4.x, ec4.y, ec4.z, ec4.w};
+      float khm[4], qhm[4], ktm[4], qs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e1 = __expf(g[sl][i] - gm[i]);     // exp(g - g_m)
+        const float e2 = __builtin_amdgcn_rcpf(e1);     // exp(g_m - g)
+        khm[i] = bv[i] * kv[i] * e1;
+        qhm[i] = qv[i] * e1;
+        ktm[i] = kv[i] * e2;
+        qs[i] = qv[i] * e1 * egm[i];                    // q exp(g)
+        sT1[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * egcm[i] * e2);  // (k exp(g_C - g))^T
+      }
+      // decayed q straight into its record units
+      {
+        char* dst = rec + Rec::u1 * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
+        if constexpr (F32IN) {
+          *reinterpret_cast<float4*>(dst) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+        } else {
+          f16x4 hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(qs[i]);
+          *reinterpret_cast<f16x4*>(dst) = hv;
+          if (DK < 32) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);  // unit wider than Dk
+        }
+      }
+      if constexpr (F32IN) {
+        float* s0 = reinterpret_cast<float*>(sSL) + r * LDSW + cl;
+        st4(s0 + 0 * (C * LDSW), khm[0], khm[1], khm[2], khm[3]);
+        st4(s0 + 1 * (C * LDSW), qhm[0], qhm[1], qhm[2], qhm[3]);
+        st4(s0 + 2 * (C * LDSW), ktm[0], ktm[1], ktm[2], ktm[3]);
+      } else {
+        __bf16* s0 = reinterpret_cast<__bf16*>(sSL) + r * LDSW + cl;
+        const float* src[3] = {khm, qhm, ktm};
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          float hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = bf16_to_f32(f32_to_bf16(src[p][i]));
+            lo[i] = src[p][i] - hi[i];
+          }
+          st4(s0 + (2 * p) * (C * LDSW), hi[0], hi[1], hi[2], hi[3]);
+          st4(s0 + (2 * p + 1) * (C * LDSW), lo[0], lo[1], lo[2], lo[3]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int t = wid + NW * i;
+      if (t < NGT) {
+        const bool isP = t >= NGT / 2;
+        int R, I;
+        tri_index(isP ? t - NGT / 2 : t, R, I);
+        if constexpr (F32IN) {
+          const float* sl0 = reinterpret_cast<const float*>(sSL);
+          const float* Kh = sl0;
+          const float* Qh = sl0 + C * LDSW;
+          const float* Kt = sl0 + 2 * (C * LDSW);
+          if (isP) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
+          else mma_nt_k<SW>(accG[i], Kh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
+        } else {
+          const __bf16* sl0 = reinterpret_cast<const __bf16*>(sSL);
+          const __bf16* Kh = sl0;
+          const __bf16* Qh = sl0 + 2 * (C * LDSW);
+          const __bf16* Kt = sl0 + 4 * (C * LDSW);
+          if (isP)
+            mma_nt_split_k<SW>(accG[i], Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW,
+                               Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW);
+          else
+            mma_nt_split_k<SW>(accG[i], Kh + 16 * R * LDSW, Kh + C * LDSW + 16 * R * LDSW, LDSW,
+                               Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+
+  // ---- Kb^T units; A -> LDS (strict lower); P units from the P^T accumulators ----
+  write_units<F32IN>(sT1, LDC, DK, C, rec + Rec::u2 * F::kUnitBytes, wid, NW);
+  {
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int t = wid + NW * i;
+      if (t < NGT) {
+        const bool isP = t >= NGT / 2;
+        int R, I;
+        tri_index(isP ? t - NGT / 2 : t, R, I);
+        if (!isP) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * R + 4 * lg + e, col = 16 * I + lr;
+            sAf[row * LDCF + col] = row > col ? accG[i][e] : 0.f;
+          }
+        } else {
+          // accumulator: rows j = 16I + 4lg + e, column i = 16R + lr; keep j <= i
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = (I < R || 4 * lg + e <= lr) ? accG[i][e] : 0.f;
+          char* dst = rec + Rec::u3 * F::kUnitBytes + unit_off4<F32IN>(16 * R + lr, 16 * I + 4 * lg, Rec::UC);
+          if constexpr (F32IN) {
+            *reinterpret_cast<float4*>(dst) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+          } else {
+            f16x4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(pv[e]);
+            *reinterpret_cast<f16x4*>(dst) = hv;
+            // the other half of a diagonal unit lies above the diagonal (or past the chunk)
+            if (I == R && (R & 1) == 0) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+          }
+        }
+      }
     }
   }
+
+  // ---- T = (I + A)^-1 ----
+  KS ks;
   ks.invert(sAf, sXs);  // begins and ends with a barrier
 
-  // ---- record: -W (from W^T tiles), Qs, Kb^T, P, gamma ----
+  // ---- Kh^T = (b k exp(g))^T over the dead Kb^T staging ----
+  if (live) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int c0 = sl * SW + 4 * c4;
+      float kv[4], bv[4];
+      cvt(rk[sl], kv);
+      cvt(rb[sl], bv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * __expf(g[sl][i]));
+    }
+  }
+  __syncthreads();
+
+  // ---- -W units from W^T tiles (channel blocks 2u, 2u+1, or u for fp32) ----
   {
-    // unit (R, u) of -W pairs the W^T tiles of channel blocks 2u, 2u+1 (16-bit)
-    // or is the tile of channel block u (fp32)
-    constexpr int CPU = F32IN ? 1 : 2;  // channel tiles per unit
+    constexpr int CPU = F32IN ? 1 : 2;
     constexpr int NWU = (C / 16) * Rec::UK;
     for (int t = wid; t < NWU; t += NW) {
       const int R = t / Rec::UK, u = t - R * Rec::UK;
@@ -163,7 +357,7 @@ __global__ __launch_bounds__(512) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec
       for (int p = 0; p < CPU; ++p) {
         w2[p] = zero4();
         const int cb = CPU * u + p;
-        if (cb < DK / 16) mma_nt_yf32<OpT>(w2[p], sKhT + 16 * cb * LDC, LDC, sAf + 16 * R * LDCF, LDCF, 16 * (R + 1));
+        if (cb < DK / 16) mma_nt_yf32<OpT>(w2[p], sT1 + 16 * cb * LDC, LDC, sAf + 16 * R * LDCF, LDCF, 16 * (R + 1));
       }
       uint4 out;
       if constexpr (F32IN) {
@@ -180,9 +374,8 @@ __global__ __launch_bounds__(512) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec
       }
       *reinterpret_cast<uint4*>(rec + (int64_t)(Rec::u0 + t) * F::kUnitBytes + 16 * l) = out;
     }
-    write_units<F32IN>(sQs, LDK, C, DK, rec + Rec::u1 * F::kUnitBytes, wid, NW);
-    write_units<F32IN>(sKbT, LDC, DK, C, rec + Rec::u2 * F::kUnitBytes, wid, NW);
-    write_units<F32IN>(sPm, LDC, C, C, rec + Rec::u3 * F::kUnitBytes, wid, NW);
+  }
+  {
     float* gam = reinterpret_cast<float*>(rec + Rec::uG * F::kUnitBytes);
     for (int c = tid; c < DK; c += NT) gam[c] = __expf(sCh[DK + c]);
   }
@@ -197,7 +390,6 @@ __global__ __launch_bounds__(512) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec
       *reinterpret_cast<float4*>(ut + (int64_t)t * 256 + 4 * l) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
-  (void)lg;
 }
 
 template <int DK, int C, bool F32IN>

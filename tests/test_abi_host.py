@@ -45,7 +45,8 @@ def test_workspace_bytes():
     # two-stage forward: per chunk a record of 57 units of 1 KB (W, decayed q: 16 each; decayed k^T: 16;
     # causal term: 8; exp(g_last): 1) plus T (w v) in fp32
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 4)
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == 0   # fp32 at d=128, chunk 64: no
+    # fp32: units of 16 contraction indices, so twice the units (113), and T (w v) the same size
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == B * H * nc * (113 * 1024 + C * D * 4)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4

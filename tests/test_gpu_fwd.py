@@ -50,7 +50,8 @@ def test_sweep_small(dtype, Dk, Dv, C, single):
     T = 2 * C + 5
     inp = synth.make_inputs(B, T, H, Dk, Dv, dtype, seed=Dk * 7 + Dv * 3 + C, s0_std=0.3)
     tdt = synth.torch_dtype(dtype)
-    if dtype == "fp32" and Dk == 128 and C == 64:
+    if dtype == "fp32" and Dk == 128 and C == 64 and single:
+        # the single-pass kernel's LDS cannot hold fp32 operands at this size; the two-stage path can
         with pytest.raises(_lib.GDN2Error) as ei:
             _run(inp, C, single=single)
         assert ei.value.status == _lib.GDN2_ERR_UNSUPPORTED
