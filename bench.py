@@ -186,14 +186,14 @@ def main():
     th = B * T * H
     F_f, F_b = fwd_flops(C, D) * th, bwd_flops(C, D) * th
     by_f, by_b = fwd_bytes(C, D) * th, bwd_bytes(C, D) * th
-    # dominant launch: the one with the larger share of the step; the forward
-    # is a single kernel, the backward call is its two kernels back to back
+    # dominant launch: the entry-point call with the larger share of the step
+    # (each call is its kernels back to back on one stream)
     if t_fwd >= t_bwd:
-        dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked launch (gdn2_prep_fwd_kernel + gdn2_chain_fwd_kernel, "
+        dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked launch (gdn2_prep_kernel forward records + gdn2_chain_fwd_kernel, "
                                      "chunk states saved)", t_fwd, by_f, F_f)
     else:
-        dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_bwd_dstate_kernel + gdn2_bwd_grad_kernel)",
-                                     t_bwd, by_b, F_b)
+        dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_prep_kernel backward records + "
+                                     "gdn2_chain_bwd_kernel + gdn2_bwd_grad_kernel)", t_bwd, by_b, F_b)
     achieved = by_dom / (t_dom / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,

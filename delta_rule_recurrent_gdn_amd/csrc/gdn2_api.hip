@@ -41,13 +41,37 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; 
 
 size_t state_bytes(int B, int H, int Dk, int Dv) { return (size_t)B * H * Dk * Dv * sizeof(float); }
 
-size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk) {
+size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32);
+
+// Backward plan: the two-stage reverse pass (chunk-parallel records, then the
+// register-resident reverse chain) where the kernels cover the sizes, else the
+// single-kernel reverse pass.
+struct BwdPlan {
+  bool two_stage;
+  size_t part;     // one [B,H,NC,Dk,Dv] fp32 array, 256-byte aligned
+  size_t records;  // records region (two-stage only): forward records for a
+                   // state recompute, then the backward records
+  size_t need;
+};
+
+BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  BwdPlan p{};
   const size_t nc = (size_t)((T + chunk - 1) / chunk);
-  // gradient of every chunk's exit state, plus room to recompute the chunk
-  // entry states when the caller passes none; each part 256-byte aligned
-  const size_t part = nc * state_bytes(B, H, Dk, Dv);
-  const size_t aligned = (part + 255) & ~(size_t)255;
-  return 2 * aligned;
+  p.part = (nc * state_bytes(B, H, Dk, Dv) + 255) & ~(size_t)255;
+  p.two_stage = gdn2::grad_supported(Dk, chunk, f32) && gdn2::prep_fwd_supported(Dk, chunk, f32);
+  if (p.two_stage) {
+    const size_t rb = (size_t)B * H * nc * gdn2::record_bytes(Dk, chunk, f32, 1);
+    const size_t fw = fwd_workspace(B, T, H, Dk, Dv, chunk, f32);
+    p.records = rb > fw ? rb : fw;
+  }
+  // gradient of every chunk's exit state, room to recompute the chunk entry
+  // states when the caller passes none, and the records
+  p.need = 2 * p.part + p.records;
+  return p;
+}
+
+size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  return bwd_plan(B, T, H, Dk, Dv, chunk, f32).need;
 }
 
 // Two-stage forward workspace: records, then T (w*v) for every chunk; 0 when
@@ -101,7 +125,7 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
   if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK) return 0;
   if (op == GDN2_OP_BWD) {
     if (!chunk_ok(chunk) || T == 0) return 0;
-    return bwd_workspace(B, T, H, Dk, Dv, chunk);
+    return bwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
   }
   if (op == GDN2_OP_FWD) {
     if (!chunk_ok(chunk) || T == 0) return 0;
@@ -162,8 +186,10 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
-  if (!gdn2::bwd_supported(Dk, Dv, chunk, dt == GDN2_F32) || !gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32))
-    return GDN2_ERR_UNSUPPORTED;
+  const bool f32 = dt == GDN2_F32;
+  const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
+  const bool single_fwd = gdn2::fwd_supported(Dk, Dv, chunk, f32);
+  if (!plan.two_stage && !(gdn2::bwd_supported(Dk, Dv, chunk, f32) && single_fwd)) return GDN2_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {
@@ -176,23 +202,37 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   st = check_ptrs({q, k, v, log_alpha, b, w, dO, dq, dk, dv, dlog_alpha, db, dw},
                   {S0, dS_final, chunk_states, dS0});
   if (st != GDN2_OK) return st;
-  const size_t need = bwd_workspace(B, T, H, Dk, Dv, chunk);
-  if (workspace == nullptr || workspace_bytes < need) return GDN2_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < plan.need) return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
 
   char* ws = static_cast<char*>(workspace);
   float* dS_chunks = reinterpret_cast<float*>(ws);
+  char* rec = ws + 2 * plan.part;
   float* states = const_cast<float*>(chunk_states);
+  gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, B, T, H, Dk, Dv, chunk, f32};
   if (states == nullptr) {
-    states = reinterpret_cast<float*>(ws + need / 2);
-    gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, states, B, T, H, Dk, Dv, chunk,
-                    dt == GDN2_F32};
-    st = hip_status(gdn2::launch_fwd(f, s));
+    states = reinterpret_cast<float*>(ws + plan.part);
+    f.chunk_states = states;
+    if (!plan.two_stage) {
+      st = hip_status(gdn2::launch_fwd(f, s));
+    } else {
+      // the two-stage forward (the default forward path, so the states match a
+      // saved forward's bit for bit) in the records region; the backward
+      // records overwrite it afterwards
+      float* ut = reinterpret_cast<float*>(rec + (size_t)B * H * ((T + chunk - 1) / chunk) *
+                                                     gdn2::fwd_record_bytes(Dk, chunk, f32));
+      st = hip_status(gdn2::launch_prep_fwd(f, rec, ut, s));
+      if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, s));
+    }
     if (st != GDN2_OK) return st;
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
-                  dS0, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
-  return hip_status(gdn2::launch_bwd(a, s));
+                  dS0, B, T, H, Dk, Dv, chunk, f32};
+  if (!plan.two_stage) return hip_status(gdn2::launch_bwd(a, s));
+  st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
+  return st;
 }
 
 }  // extern "C"

@@ -1013,11 +1013,56 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   return a.f32_inputs ? launch_bwd_f<true>(a, stream) : launch_bwd_f<false>(a, stream);
 }
 
+template <int DK, bool F32IN>
+static hipError_t launch_grad_dk(const BwdArgs& a, hipStream_t s) {
+  switch (a.chunk) {
+    case 16: return launch_grad<DK, 16, F32IN>(a, s);
+    case 32: return launch_grad<DK, 32, F32IN>(a, s);
+    case 64: return launch_grad<DK, 64, F32IN>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool F32IN>
+static hipError_t launch_grad_f(const BwdArgs& a, hipStream_t s) {
+  switch (a.Dk) {
+    case 16: return launch_grad_dk<16, F32IN>(a, s);
+    case 32: return launch_grad_dk<32, F32IN>(a, s);
+    case 64: return launch_grad_dk<64, F32IN>(a, s);
+    case 128: return launch_grad_dk<128, F32IN>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream) {
+  return a.f32_inputs ? launch_grad_f<true>(a, stream) : launch_grad_f<false>(a, stream);
+}
+
 template <int DK, int C, bool F32IN>
 static bool bwd_fits() {
   return GradCfg<DK, C, 16, F32IN>::kFits && (F32IN || GradCfg<DK, C, 32, F32IN>::kFits) &&
          DstCfg<DK, C, 16, F32IN>::kFits && DstCfg<DK, C, 32, F32IN>::kFits &&
          (F32IN || DstCfg<DK, C, 64, F32IN>::kFits);
+}
+
+template <int DK, bool F32IN>
+static bool grad_fits_c(int chunk) {
+  switch (chunk) {
+    case 16: return GradCfg<DK, 16, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 16, 32, F32IN>::kFits);
+    case 32: return GradCfg<DK, 32, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 32, 32, F32IN>::kFits);
+    case 64: return GradCfg<DK, 64, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 64, 32, F32IN>::kFits);
+  }
+  return false;
+}
+
+bool grad_supported(int Dk, int chunk, bool f32) {
+  switch (Dk) {
+    case 16: return f32 ? grad_fits_c<16, true>(chunk) : grad_fits_c<16, false>(chunk);
+    case 32: return f32 ? grad_fits_c<32, true>(chunk) : grad_fits_c<32, false>(chunk);
+    case 64: return f32 ? grad_fits_c<64, true>(chunk) : grad_fits_c<64, false>(chunk);
+    case 128: return f32 ? grad_fits_c<128, true>(chunk) : grad_fits_c<128, false>(chunk);
+  }
+  return false;
 }
 
 template <int DK, bool F32IN>

@@ -230,9 +230,9 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
       }
     }
 
-    // ---- o ----
+    // ---- o (not written when the caller only wants states) ----
 #pragma unroll
-    for (int R = 0; R < RC; ++R)
+    for (int R = 0; R < RC && a.o; ++R)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * R + 4 * lg + i;
@@ -257,6 +257,238 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           a.S_final[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = accS[R][c][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse chain of the backward: the gradient of every chunk's exit state.
+//
+// For L = <dO, o> + <dS_final, S_T>, the chunk relations above give, walking
+// the chunks from last to first with dS the gradient of the chunk's exit state
+// (the chunkwise form of the gate-aware backward, aiexpert.news method
+// paragraph; arXiv 2605.22791 abstract):
+//   dU = P^T dO + Kb dS,
+//   dS <- Diag(gamma) dS + Qs^T dO - W^T dU      (gradient of the entry state).
+// The backward record holds P^T, Kb, Qs^T, -W^T and gamma as left-operand
+// units; dS and dU stay in accumulators as in the forward chain, and dO is
+// gathered straight into right-operand fragments, one chunk ahead.
+// dS_chunks[n] receives the exit-state gradient of chunk n; dS0 the final one.
+// ---------------------------------------------------------------------------
+template <int DK, int C, bool F32IN, int NCT, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, const char* rec_base) {
+  using Rec = Record<DK, C, F32IN, 1>;
+  using F = Frag<F32IN>;
+  constexpr int RC = C / 16, RK = DK / 16, UK = Rec::UK, UC = Rec::UC;
+  constexpr int KU = F::KU;
+  constexpr int NBUF = 2 * Rec::kBytes <= 160 * 1024 ? 2 : 1;
+  constexpr int kCols = 16 * NCT * NWV;
+
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * Rec::kBytes];
+
+  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
+  const int lr = l & 15, lg = l >> 4;
+  const int Dv = a.Dv, T = a.T, H = a.H;
+  const int ncg = Dv / kCols;
+  const int nbh = a.B * H;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int bh = (slot / ncg) * 8 + xcd, cg = slot % ncg;
+  if (bh >= nbh) return;
+  const int bi = bh / H, h = bh - bi * H;
+  const int NC = (T + C - 1) / C;
+  const int j0 = cg * kCols + wid * 16 * NCT;
+  const int64_t rowV = (int64_t)H * Dv;
+  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
+  const int64_t stBase = (int64_t)bh * DK * Dv + j0;
+  const char* recs = rec_base + (int64_t)bh * NC * Rec::kBytes;
+
+  f32x4 accD[RK][NCT];
+#pragma unroll
+  for (int R = 0; R < RK; ++R)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      accD[R][c] = zero4();
+      if (a.dS_final) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          accD[R][c][i] = a.dS_final[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
+      }
+    }
+
+  // dO of chunk nn as right-operand fragments (contraction over the chunk's tokens)
+  constexpr int NDU = F32IN ? RC : UC;    // fragments per column tile
+  constexpr int NDE = F32IN ? 4 : 8;      // elements per fragment
+  using RawT = typename std::conditional<F32IN, float, uint16_t>::type;
+  RawT rdo[NDU][NCT][NDE];
+  auto load_do = [&](int nn) {
+    const int tn = nn * C, Ln = min(C, T - tn);
+#pragma unroll
+    for (int u = 0; u < NDU; ++u)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int j = 0; j < NDE; ++j) {
+          const int t = F32IN ? 16 * u + 4 * lg + j : KU * u + F::kslot(lg, j);
+          RawT x = 0;
+          if (t < Ln) {
+            const int64_t idx = baseV + (int64_t)(tn + t) * rowV + 16 * c + lr;
+            if constexpr (F32IN) x = static_cast<const float*>(a.dO)[idx];
+            else x = static_cast<const uint16_t*>(a.dO)[idx];
+          }
+          rdo[u][c][j] = x;
+        }
+  };
+
+  dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * Rec::kBytes : 0),
+            Rec::kUnits, wid, NWV);
+  load_do(NC - 1);
+
+  for (int n = NC - 1; n >= 0; --n) {
+    char* buf = smem + (NBUF == 2 ? (n & 1) * Rec::kBytes : 0);
+    wait_vm_all();
+    __syncthreads();  // record n is in LDS; every wave is done with chunk n+1
+    if (NBUF == 2 && n > 0)
+      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * Rec::kBytes, Rec::kUnits, wid, NWV);
+
+    {
+      float* ws = a.dS_chunks + ((int64_t)bh * NC + n) * DK * Dv + j0;
+#pragma unroll
+      for (int R = 0; R < RK; ++R)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ws[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = accD[R][c][i];
+    }
+
+    // this chunk's dO fragments; the previous chunk's start loading
+    using DoF = typename std::conditional<F32IN, f32x4, f16x8>::type;
+    DoF dof[NDU][NCT];
+#pragma unroll
+    for (int u = 0; u < NDU; ++u)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int j = 0; j < NDE; ++j) {
+          if constexpr (F32IN) dof[u][c][j] = rdo[u][c][j];
+          else dof[u][c][j] = static_cast<_Float16>(bf16_bits_to_f32(rdo[u][c][j]));
+        }
+    if (n > 0) load_do(n - 1);
+
+    const uint4* uPT = reinterpret_cast<const uint4*>(buf + Rec::u0 * 1024) + l;
+    const uint4* uKb = reinterpret_cast<const uint4*>(buf + Rec::u1 * 1024) + l;
+    const uint4* uQT = reinterpret_cast<const uint4*>(buf + Rec::u2 * 1024) + l;
+    const uint4* uWT = reinterpret_cast<const uint4*>(buf + Rec::u3 * 1024) + l;
+    const float* gam = reinterpret_cast<const float*>(buf + Rec::uG * 1024);
+
+    // ---- dU = P^T dO + Kb dS  (P^T row tile R is zero below contraction 16R) ----
+    f32x4 accU[RC][NCT];
+#pragma unroll
+    for (int R = 0; R < RC; ++R)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) accU[R][c] = zero4();
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int R = 0; R < RC; ++R) {
+#pragma unroll
+        for (int u = 0; u < UC; ++u) {
+          if (KU * u + KU - 1 >= 16 * R) {
+            const uint4 ap = uPT[(R * UC + u) * 64];
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], ap, dof[u][c]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const uint4 ak = uKb[(R * UK + u) * 64];
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], ak, accD[u][c]);
+        }
+      }
+    } else {
+      f16x8 sb[UK][NCT];
+#pragma unroll
+      for (int u = 0; u < UK; ++u)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) sb[u][c] = rhs_from_acc(accD[2 * u][c], 2 * u + 1 < RK ? accD[2 * u + 1][c] : zero4());
+#pragma unroll
+      for (int R = 0; R < RC; ++R) {
+#pragma unroll
+        for (int u = 0; u < UC; ++u) {
+          if (KU * u + KU - 1 >= 16 * R) {
+            const uint4 ap = uPT[(R * UC + u) * 64];
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], ap, dof[u][c]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const uint4 ak = uKb[(R * UK + u) * 64];
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], ak, sb[u][c]);
+        }
+      }
+    }
+
+    // ---- dS <- Diag(gamma) dS + Qs^T dO - W^T dU ----
+    float gm[RK][4];
+#pragma unroll
+    for (int R = 0; R < RK; ++R) {
+      const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * R + 4 * lg);
+      gm[R][0] = g4.x; gm[R][1] = g4.y; gm[R][2] = g4.z; gm[R][3] = g4.w;
+    }
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int R = 0; R < RK; ++R)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accD[R][c][i] *= gm[R][i];
+#pragma unroll
+          for (int u = 0; u < UC; ++u) {
+            unit_mma(accD[R][c], uQT[(R * UC + u) * 64], dof[u][c]);
+            unit_mma(accD[R][c], uWT[(R * UC + u) * 64], accU[u][c]);
+          }
+        }
+    } else {
+      f16x8 ub[UC][NCT];
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) ub[u][c] = rhs_from_acc(accU[2 * u][c], 2 * u + 1 < RC ? accU[2 * u + 1][c] : zero4());
+#pragma unroll
+      for (int R = 0; R < RK; ++R) {
+        uint4 aq[UC], aw[UC];
+#pragma unroll
+        for (int u = 0; u < UC; ++u) {
+          aq[u] = uQT[(R * UC + u) * 64];
+          aw[u] = uWT[(R * UC + u) * 64];
+        }
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accD[R][c][i] *= gm[R][i];
+#pragma unroll
+          for (int u = 0; u < UC; ++u) {
+            unit_mma(accD[R][c], aq[u], dof[u][c]);
+            unit_mma(accD[R][c], aw[u], ub[u][c]);
+          }
+        }
+      }
+    }
+
+    if (NBUF == 1 && n > 0) {
+      __syncthreads();  // every wave is done reading the single buffer
+      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
+    }
+  }
+
+  if (a.dS0) {
+#pragma unroll
+    for (int R = 0; R < RK; ++R)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.dS0[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = accD[R][c][i];
   }
 }
 
@@ -313,6 +545,55 @@ static hipError_t launch_chain_f(const FwdArgs& a, const char* rec, const float*
 
 hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
   return a.f32_inputs ? launch_chain_f<true>(a, rec, ut, s) : launch_chain_f<false>(a, rec, ut, s);
+}
+
+template <int DK, int C, bool F32IN, int NCT, int NWV>
+static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStream_t s) {
+  using Rec = Record<DK, C, F32IN, 1>;
+  if constexpr (Rec::kBytes > 160 * 1024) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    const int ncg = a.Dv / (16 * NCT * NWV);
+    const int nbh = a.B * a.H;
+    const int grid = ((nbh + 7) / 8) * 8 * ncg;
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, NCT, NWV>), dim3(grid), dim3(NWV * 64), 0, s, a, rec);
+    return hipGetLastError();
+  }
+}
+
+template <int DK, int C, bool F32IN>
+static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, hipStream_t s) {
+  const int nbh = a.B * a.H;
+  if (a.Dv == 16) return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
+  const int tiles = a.Dv / 32;
+  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 2>(a, rec, s);
+  if (nbh * tiles >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 1>(a, rec, s);
+  return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
+}
+
+template <int DK, bool F32IN>
+static hipError_t launch_chain_bwd_k(const BwdArgs& a, const char* rec, hipStream_t s) {
+  switch (a.chunk) {
+    case 16: return launch_chain_bwd_c<DK, 16, F32IN>(a, rec, s);
+    case 32: return launch_chain_bwd_c<DK, 32, F32IN>(a, rec, s);
+    case 64: return launch_chain_bwd_c<DK, 64, F32IN>(a, rec, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool F32IN>
+static hipError_t launch_chain_bwd_f(const BwdArgs& a, const char* rec, hipStream_t s) {
+  switch (a.Dk) {
+    case 16: return launch_chain_bwd_k<16, F32IN>(a, rec, s);
+    case 32: return launch_chain_bwd_k<32, F32IN>(a, rec, s);
+    case 64: return launch_chain_bwd_k<64, F32IN>(a, rec, s);
+    case 128: return launch_chain_bwd_k<128, F32IN>(a, rec, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chain_bwd(const BwdArgs& a, const char* rec, hipStream_t s) {
+  return a.f32_inputs ? launch_chain_bwd_f<true>(a, rec, s) : launch_chain_bwd_f<false>(a, rec, s);
 }
 
 }  // namespace gdn2

@@ -68,6 +68,17 @@ hipError_t launch_prep_fwd(const FwdArgs& a, char* rec, float* ut, hipStream_t s
 hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, hipStream_t stream);
 bool prep_fwd_supported(int Dk, int chunk, bool f32_inputs);
 size_t fwd_record_bytes(int Dk, int chunk, bool f32_inputs);
+// dir 0: forward record, 1: backward record (gdn2_frag.h)
+size_t record_bytes(int Dk, int chunk, bool f32_inputs, int dir);
+
+// Two-stage reverse pass of the backward: chunk-parallel backward records
+// (B*H*NC of record_bytes(.., 1)), then the reverse state-gradient chain,
+// which writes a.dS_chunks and a.dS0; launch_bwd_grad then forms the
+// per-token gradients.
+hipError_t launch_prep_bwd(const FwdArgs& a, char* rec, hipStream_t stream);
+hipError_t launch_chain_bwd(const BwdArgs& a, const char* rec, hipStream_t stream);
+hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream);
+bool grad_supported(int Dk, int chunk, bool f32_inputs);
 
 // Shapes with a compiled kernel (checked by the C ABI before launching).
 bool fwd_supported(int Dk, int Dv, int chunk, bool f32_inputs);

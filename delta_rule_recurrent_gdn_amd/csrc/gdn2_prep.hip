@@ -38,17 +38,18 @@
 
 namespace gdn2 {
 
-template <int DK, int C, bool F32IN>
+// DIR 0: forward record (+ T (w v)); DIR 1: backward record (no value side).
+template <int DK, int C, bool F32IN, int DIR>
 struct PrepCfg {
   static constexpr int NT = 512, NW = NT / kWave;
   using KS = KSide<DK, C, F32IN, NT>;  // slice geometry and the blocked inversion
   using OpT = typename KS::OpT;
-  using Rec = Record<DK, C, F32IN, 0>;
+  using Rec = Record<DK, C, F32IN, DIR>;
   using F = Frag<F32IN>;
   static constexpr int NB = KS::NB, SW = KS::SW, NSL = KS::NSL;
   static constexpr int LDC = KS::LDC, LDCF = KS::LDCF, LDSW = KS::LDSW;
   static constexpr int OPB = sizeof(OpT);
-  static constexpr int DVM = 128;                // largest value width
+  static constexpr int DVM = DIR == 0 ? 128 : 0;  // largest value width staged
   // thread -> (row, 4 channels of every slice): TPR threads per row
   static constexpr int TPR = SW / 4;
   static constexpr int RPW = kWave / TPR;        // rows per wave
@@ -79,9 +80,9 @@ __device__ __forceinline__ int unit_off4(int r, int k0, int nu) {
   return ((r >> 4) * nu + u) * F::kUnitBytes + 16 * ((r & 15) + 16 * g) + 8 * half;
 }
 
-template <int DK, int C, bool F32IN>
-__global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* rec_base, float* ut_base) {
-  using Cfg = PrepCfg<DK, C, F32IN>;
+template <int DK, int C, bool F32IN, int DIR>
+__global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base) {
+  using Cfg = PrepCfg<DK, C, F32IN, DIR>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   using Rec = typename Cfg::Rec;
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
     }
   }
   // (w v)^T for the whole value width, into its own LDS region
-  {
+  if constexpr (DIR == 0) {
     const int vpr = Dv / 8;
 #pragma unroll
     for (int i = 0; i < Cfg::VW_PT; ++i) {
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
       const float4 ec4 = *reinterpret_cast<const float4*>(sCh + 3 * DK + c0);
       const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
       const float egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w}, egcm[4] = {ec4.x, ec4.y, ec4.z, ec4.w};
-      float khm[4], qhm[4], ktm[4], qs[4];
+      float khm[4], qhm[4], ktm[4], qs[4], kb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e1 = __expf(g[sl][i] - gm[i]);     // exp(g - g_m)
@@ -221,17 +222,23 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
         qhm[i] = qv[i] * e1;
         ktm[i] = kv[i] * e2;
         qs[i] = qv[i] * e1 * egm[i];                    // q exp(g)
-        sT1[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * egcm[i] * e2);  // (k exp(g_C - g))^T
+        kb[i] = kv[i] * egcm[i] * e2;                   // k exp(g_C - g)
       }
-      // decayed q straight into its record units
+      // the token-major factor (forward: decayed q; backward: k decayed to the
+      // chunk end) straight into its record units; the channel-major one
+      // (forward: k decayed to the chunk end; backward: decayed q) staged transposed
       {
+        const float* tm = DIR == 0 ? qs : kb;
+        const float* cm = DIR == 0 ? kb : qs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(cm[i]);
         char* dst = rec + Rec::u1 * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
         if constexpr (F32IN) {
-          *reinterpret_cast<float4*>(dst) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+          *reinterpret_cast<float4*>(dst) = make_float4(tm[0], tm[1], tm[2], tm[3]);
         } else {
           f16x4 hv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(qs[i]);
+          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(tm[i]);
           *reinterpret_cast<f16x4*>(dst) = hv;
           if (DK < 32) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);  // unit wider than Dk
         }
@@ -270,16 +277,20 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
           const float* Kh = sl0;
           const float* Qh = sl0 + C * LDSW;
           const float* Kt = sl0 + 2 * (C * LDSW);
-          if (isP) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
+          if (isP && DIR == 0) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
+          else if (isP) mma_nt_k<SW>(accG[i], Qh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
           else mma_nt_k<SW>(accG[i], Kh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
         } else {
           const __bf16* sl0 = reinterpret_cast<const __bf16*>(sSL);
           const __bf16* Kh = sl0;
           const __bf16* Qh = sl0 + 2 * (C * LDSW);
           const __bf16* Kt = sl0 + 4 * (C * LDSW);
-          if (isP)
+          if (isP && DIR == 0)
             mma_nt_split_k<SW>(accG[i], Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW,
                                Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW);
+          else if (isP)
+            mma_nt_split_k<SW>(accG[i], Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW,
+                               Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
           else
             mma_nt_split_k<SW>(accG[i], Kh + 16 * R * LDSW, Kh + C * LDSW + 16 * R * LDSW, LDSW,
                                Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
@@ -290,7 +301,8 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
     __syncthreads();
   }
 
-  // ---- Kb^T units; A -> LDS (strict lower); P units from the P^T accumulators ----
+  // ---- channel-major factor units; A -> LDS (strict lower); the causal term's
+  //      units: forward P from P^T accumulators, backward P^T from P accumulators ----
   write_units<F32IN>(sT1, LDC, DK, C, rec + Rec::u2 * F::kUnitBytes, wid, NW);
   {
     const int lr = l & 15, lg = l >> 4;
@@ -308,11 +320,18 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
             sAf[row * LDCF + col] = row > col ? accG[i][e] : 0.f;
           }
         } else {
-          // accumulator: rows j = 16I + 4lg + e, column i = 16R + lr; keep j <= i
+          // forward accumulator: rows j = 16I + 4lg + e, column i = 16R + lr (keep j <= i),
+          // unit row i; backward: rows i = 16R + 4lg + e, column j = 16I + lr (keep
+          // j <= i), unit row j of P^T -- the same mask and offsets with (R, I) swapped
           float pv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = (I < R || 4 * lg + e <= lr) ? accG[i][e] : 0.f;
-          char* dst = rec + Rec::u3 * F::kUnitBytes + unit_off4<F32IN>(16 * R + lr, 16 * I + 4 * lg, Rec::UC);
+          for (int e = 0; e < 4; ++e) {
+            const bool keep = DIR == 0 ? (I < R || 4 * lg + e <= lr) : (I < R || lr <= 4 * lg + e);
+            pv[e] = keep ? accG[i][e] : 0.f;
+          }
+          const int urow = DIR == 0 ? 16 * R + lr : 16 * I + lr;
+          const int ukk = DIR == 0 ? 16 * I + 4 * lg : 16 * R + 4 * lg;
+          char* dst = rec + (DIR == 0 ? Rec::u3 : Rec::u0) * F::kUnitBytes + unit_off4<F32IN>(urow, ukk, Rec::UC);
           if constexpr (F32IN) {
             *reinterpret_cast<float4*>(dst) = make_float4(pv[0], pv[1], pv[2], pv[3]);
           } else {
@@ -320,8 +339,13 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
 #pragma unroll
             for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(pv[e]);
             *reinterpret_cast<f16x4*>(dst) = hv;
-            // the other half of a diagonal unit lies above the diagonal (or past the chunk)
-            if (I == R && (R & 1) == 0) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+            // the other half of a diagonal unit lies on the zero side of the diagonal
+            // (forward: the next block; backward: the previous one) or past the chunk
+            if (I == R) {
+              if (DIR == 0 && (R & 1) == 0) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+              if (DIR == 1 && (R & 1) == 1) *reinterpret_cast<uint2*>(dst - 8) = make_uint2(0u, 0u);
+              if (DIR == 1 && (R & 1) == 0 && R + 1 == NB) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+            }
           }
         }
       }
@@ -346,8 +370,8 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
   }
   __syncthreads();
 
-  // ---- -W units from W^T tiles (channel blocks 2u, 2u+1, or u for fp32) ----
-  {
+  // ---- forward: -W units from W^T tiles (channel blocks 2u, 2u+1, or u for fp32) ----
+  if constexpr (DIR == 0) {
     constexpr int CPU = F32IN ? 1 : 2;
     constexpr int NWU = (C / 16) * Rec::UK;
     for (int t = wid; t < NWU; t += NW) {
@@ -375,13 +399,34 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
       *reinterpret_cast<uint4*>(rec + (int64_t)(Rec::u0 + t) * F::kUnitBytes + 16 * l) = out;
     }
   }
+  // ---- backward: -W^T units from W tiles (rows t, column d): the accumulator
+  //      lane (d, g) holds tokens 4g+e, which are -W^T's unit slots ----
+  if constexpr (DIR == 1) {
+    const int lr = l & 15, lg = l >> 4;
+    constexpr int NWT = (C / 16) * (DK / 16);
+    for (int t = wid; t < NWT; t += NW) {
+      const int R = t / (DK / 16), cb = t - R * (DK / 16);
+      f32x4 acc = zero4();
+      mma_nt_xf32<OpT>(acc, sAf + 16 * R * LDCF, LDCF, sT1 + 16 * cb * LDC, LDC, 16 * (R + 1));
+      char* dst = rec + Rec::u3 * F::kUnitBytes + unit_off4<F32IN>(16 * cb + lr, 16 * R + 4 * lg, Rec::UC);
+      if constexpr (F32IN) {
+        *reinterpret_cast<float4*>(dst) = make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+      } else {
+        f16x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-acc[e]);
+        *reinterpret_cast<f16x4*>(dst) = hv;
+        if (C < 32) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);  // unit wider than the chunk
+      }
+    }
+  }
   {
     float* gam = reinterpret_cast<float*>(rec + Rec::uG * F::kUnitBytes);
     for (int c = tid; c < DK; c += NT) gam[c] = __expf(sCh[DK + c]);
   }
 
   // ---- Ut = T (w v): accumulator tiles straight to the workspace ----
-  {
+  if constexpr (DIR == 0) {
     const int nvt = Dv / 16, ntile = (C / 16) * nvt;
     for (int t = wid; t < ntile; t += NW) {
       const int R = t / nvt, jb = t - R * nvt;
@@ -392,49 +437,53 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_fwd_kernel(FwdArgs a, char* 
   }
 }
 
-template <int DK, int C, bool F32IN>
-static hipError_t launch_prep_fwd_t(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
-  if constexpr (!PrepCfg<DK, C, F32IN>::kFits) {
+template <int DK, int C, bool F32IN, int DIR>
+static hipError_t launch_prep_t(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+  if constexpr (!PrepCfg<DK, C, F32IN, DIR>::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
     const int NC = (a.T + C - 1) / C;
     const int64_t grid = (int64_t)a.B * a.H * NC;
-    hipLaunchKernelGGL((gdn2_prep_fwd_kernel<DK, C, F32IN>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut);
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, C, F32IN, DIR>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut);
     return hipGetLastError();
   }
 }
 
-template <int DK, bool F32IN>
-static hipError_t launch_prep_fwd_c(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+template <int DK, bool F32IN, int DIR>
+static hipError_t launch_prep_c(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_prep_fwd_t<DK, 16, F32IN>(a, rec, ut, s);
-    case 32: return launch_prep_fwd_t<DK, 32, F32IN>(a, rec, ut, s);
-    case 64: return launch_prep_fwd_t<DK, 64, F32IN>(a, rec, ut, s);
+    case 16: return launch_prep_t<DK, 16, F32IN, DIR>(a, rec, ut, s);
+    case 32: return launch_prep_t<DK, 32, F32IN, DIR>(a, rec, ut, s);
+    case 64: return launch_prep_t<DK, 64, F32IN, DIR>(a, rec, ut, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool F32IN>
-static hipError_t launch_prep_fwd_f(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+template <bool F32IN, int DIR>
+static hipError_t launch_prep_f(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
   switch (a.Dk) {
-    case 16: return launch_prep_fwd_c<16, F32IN>(a, rec, ut, s);
-    case 32: return launch_prep_fwd_c<32, F32IN>(a, rec, ut, s);
-    case 64: return launch_prep_fwd_c<64, F32IN>(a, rec, ut, s);
-    case 128: return launch_prep_fwd_c<128, F32IN>(a, rec, ut, s);
+    case 16: return launch_prep_c<16, F32IN, DIR>(a, rec, ut, s);
+    case 32: return launch_prep_c<32, F32IN, DIR>(a, rec, ut, s);
+    case 64: return launch_prep_c<64, F32IN, DIR>(a, rec, ut, s);
+    case 128: return launch_prep_c<128, F32IN, DIR>(a, rec, ut, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prep_fwd(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
-  return a.f32_inputs ? launch_prep_fwd_f<true>(a, rec, ut, s) : launch_prep_fwd_f<false>(a, rec, ut, s);
+  return a.f32_inputs ? launch_prep_f<true, 0>(a, rec, ut, s) : launch_prep_f<false, 0>(a, rec, ut, s);
+}
+
+hipError_t launch_prep_bwd(const FwdArgs& a, char* rec, hipStream_t s) {
+  return a.f32_inputs ? launch_prep_f<true, 1>(a, rec, nullptr, s) : launch_prep_f<false, 1>(a, rec, nullptr, s);
 }
 
 template <int DK, bool F32IN>
 static bool prep_fits_c(int chunk) {
   switch (chunk) {
-    case 16: return PrepCfg<DK, 16, F32IN>::kFits;
-    case 32: return PrepCfg<DK, 32, F32IN>::kFits;
-    case 64: return PrepCfg<DK, 64, F32IN>::kFits;
+    case 16: return PrepCfg<DK, 16, F32IN, 0>::kFits && PrepCfg<DK, 16, F32IN, 1>::kFits;
+    case 32: return PrepCfg<DK, 32, F32IN, 0>::kFits && PrepCfg<DK, 32, F32IN, 1>::kFits;
+    case 64: return PrepCfg<DK, 64, F32IN, 0>::kFits && PrepCfg<DK, 64, F32IN, 1>::kFits;
   }
   return false;
 }
@@ -449,10 +498,12 @@ bool prep_fwd_supported(int Dk, int chunk, bool f32) {
   return false;
 }
 
-size_t fwd_record_bytes(int Dk, int chunk, bool f32) {
-#define GDN2_REC(DK, CC)                                                              \
-  if (Dk == DK && chunk == CC)                                                        \
-    return f32 ? (size_t)Record<DK, CC, true, 0>::kBytes : (size_t)Record<DK, CC, false, 0>::kBytes;
+size_t record_bytes(int Dk, int chunk, bool f32, int dir) {
+#define GDN2_REC(DK, CC)                                                                            \
+  if (Dk == DK && chunk == CC) {                                                                    \
+    if (dir == 0) return f32 ? (size_t)Record<DK, CC, true, 0>::kBytes : (size_t)Record<DK, CC, false, 0>::kBytes; \
+    return f32 ? (size_t)Record<DK, CC, true, 1>::kBytes : (size_t)Record<DK, CC, false, 1>::kBytes;  \
+  }
   GDN2_REC(16, 16) GDN2_REC(16, 32) GDN2_REC(16, 64)
   GDN2_REC(32, 16) GDN2_REC(32, 32) GDN2_REC(32, 64)
   GDN2_REC(64, 16) GDN2_REC(64, 32) GDN2_REC(64, 64)
@@ -460,5 +511,7 @@ size_t fwd_record_bytes(int Dk, int chunk, bool f32) {
 #undef GDN2_REC
   return 0;
 }
+
+size_t fwd_record_bytes(int Dk, int chunk, bool f32) { return record_bytes(Dk, chunk, f32, 0); }
 
 }  // namespace gdn2

@@ -41,7 +41,11 @@ def test_workspace_bytes():
     lib = _lib.load()
     B, T, H, D, C = 8, 4096, 16, 128, 64
     nc = T // C
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4
+    # backward: exit-state gradients and room for recomputed entry states (one [B,H,NC,D,D] fp32 array
+    # each), then a records region that holds the forward records (for a state recompute) and later the
+    # backward ones: 57 units of 1 KB per chunk plus T (w v)
+    rec = lambda n: B * H * n * (57 * 1024 + C * D * 4)  # noqa: E731
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4 + rec(nc)
     # two-stage forward: per chunk a record of 57 units of 1 KB (W, decayed q: 16 each; decayed k^T: 16;
     # causal term: 8; exp(g_last): 1) plus T (w v) in fp32
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 4)
@@ -49,7 +53,7 @@ def test_workspace_bytes():
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == B * H * nc * (113 * 1024 + C * D * 4)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4 + rec(2)
 
 
 A = 4096  # a fake, 16-byte aligned address: never dereferenced because validation fails first
