@@ -231,6 +231,7 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   if (!plan.two_stage) return hip_status(gdn2::launch_bwd(a, s));
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
+  a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;
 }

@@ -35,6 +35,7 @@
 // two-term bf16 split for the products with the wide-range factors Kh', Qh', Kt'.
 
 #include "gdn2_chunk.h"
+#include "gdn2_frag.h"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
@@ -376,7 +377,9 @@ struct GradCfg {
   static constexpr int VPW = (NVT + kWaves - 1) / kWaves;
 };
 
-template <int DK, int C, int BVB_, bool F32IN>
+// REC: T and P^T come from the backward records (a.records) and the chunk's
+// Gram products and inversion are skipped; otherwise they are recomputed here.
+template <int DK, int C, int BVB_, bool F32IN, bool REC>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   using Cfg = GradCfg<DK, C, BVB_, F32IN>;
   using KS = typename Cfg::KS;
@@ -437,7 +440,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // ---- key-side preparation ----
   KS ks;
   ks.init(tid);
-  ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, t0, Lr);
+  if constexpr (REC) ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
+  else ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
 
   // the C x DK tiles this lane owns: rows 16R + 4lg + e, column 16cb + lr.
@@ -468,23 +472,57 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
     }
   }
 
-  f32x4 accG[KS::GPW];
-  ks.factors_gram(sG, sCh, sSL, accG,
-                  [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
-                      const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
-                    (void)qv;
-                    (void)e1;
-                    st4(sKh + r * LDK + c0, bv[0] * kv[0] * eg[0], bv[1] * kv[1] * eg[1], bv[2] * kv[2] * eg[2],
-                        bv[3] * kv[3] * eg[3]);
-                    st4(sKb + r * LDK + c0, kv[0] * ec[0], kv[1] * ec[1], kv[2] * ec[2], kv[3] * ec[3]);
-                  });
-  ks.template gram_store<true>(accG, sAf, sPT);
-  ks.invert(sAf, sXs);
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, i = e % C;
-    const OpT v = static_cast<OpT>(sAf[r * LDCF + i]);
-    sTm[r * LDC + i] = v;
-    sTT[i * LDC + r] = v;
+  if constexpr (REC) {
+    // Kh = b k exp(g) and Kb = k exp(g_C - g) at the lane's positions
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int t = wid + NW * i;
+      if (t < Cfg::NKT) {
+        const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * lg + e;
+          const float eg = pe1[i][e] * sCh[2 * DK + c];
+          const float ec = sCh[3 * DK + c] * __builtin_amdgcn_rcpf(pe1[i][e]);
+          sKh[r * LDK + c] = static_cast<OpT>(pb[i][e] * pk[i][e] * eg);
+          sKb[r * LDK + c] = static_cast<OpT>(pk[i][e] * ec);
+        }
+      }
+    }
+    // T (and T^T) and P^T from the record's units; P^T units that lie wholly
+    // below the diagonal are not stored (zero)
+    using Rec = Record<DK, C, F32IN, 1>;
+    using F = Frag<F32IN>;
+    const char* rec = a.records + ((int64_t)bh * NC + n) * Rec::kBytes;
+    constexpr int NU = Rec::RC * Rec::UC;
+    for (int t = wid; t < 2 * NU; t += NW) {
+      const bool isT = t < NU;
+      const int tt = isT ? t : t - NU, R = tt / Rec::UC, u = tt - R * Rec::UC;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (isT || F::KU * u + F::KU - 1 >= 16 * R)
+        v = *reinterpret_cast<const uint4*>(rec + (int64_t)((isT ? Rec::u4 : Rec::u0) + tt) * F::kUnitBytes + 16 * l);
+      if (isT) unpack_unit<F32IN>(v, R, u, C, sTm, LDC, sTT, LDC);
+      else unpack_unit<F32IN>(v, R, u, C, sPT, LDC, static_cast<OpT*>(nullptr), 0);
+    }
+  } else {
+    f32x4 accG[KS::GPW];
+    ks.factors_gram(sG, sCh, sSL, accG,
+                    [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
+                        const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
+                      (void)qv;
+                      (void)e1;
+                      st4(sKh + r * LDK + c0, bv[0] * kv[0] * eg[0], bv[1] * kv[1] * eg[1], bv[2] * kv[2] * eg[2],
+                          bv[3] * kv[3] * eg[3]);
+                      st4(sKb + r * LDK + c0, kv[0] * ec[0], kv[1] * ec[1], kv[2] * ec[2], kv[3] * ec[3]);
+                    });
+    ks.template gram_store<true>(accG, sAf, sPT);
+    ks.invert(sAf, sXs);
+    for (int e = tid; e < C * C; e += NT) {
+      const int r = e / C, i = e % C;
+      const OpT v = static_cast<OpT>(sAf[r * LDCF + i]);
+      sTm[r * LDC + i] = v;
+      sTT[i * LDC + r] = v;
+    }
   }
 
   // ---- value-tile loop: U, dU, d(w*v) and the key-side partial products ----
@@ -959,7 +997,10 @@ static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
     return hipErrorInvalidConfiguration;
   } else {
     const int NC = (a.T + C - 1) / C;
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, BVB, F32IN>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+    if (a.records)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, BVB, F32IN, true>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, BVB, F32IN, false>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -108,6 +108,26 @@ struct KSide {
     qk_on = qk_r < C && qk_r < QK_RPP;
   }
 
+  // Fetch only the log_alpha rows of the chunk (for gates()).
+  __device__ __forceinline__ void load_la(const float* log_alpha, int64_t baseK, int64_t rowK, int tn, int Ln) {
+    if (la_on) {
+#pragma unroll
+      for (int i = 0; i < LA_RPS; ++i) {
+        const int r = la_sg * LA_RPS + i;
+        const float* src = log_alpha + baseK + (int64_t)(tn + r) * rowK + la_c;
+        if constexpr (LAW == 4) {
+          const float4 x = r < Ln ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+          la[i][0] = x.x;
+          la[i][1] = x.y;
+          la[i][2] = x.z;
+          la[i][3] = x.w;
+        } else {
+          la[i][0] = r < Ln ? *src : 0.f;
+        }
+      }
+    }
+  }
+
   // Fetch chunk rows [tn, tn + Ln) of one (batch, head): base* index token 0.
   __device__ __forceinline__ void load(const void* q, const void* k, const void* b, const float* log_alpha,
                                       int64_t baseK, int64_t rowK, int tn, int Ln) {

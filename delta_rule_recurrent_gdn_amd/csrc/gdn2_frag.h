@@ -41,18 +41,20 @@ struct Frag {
 // Per-chunk record: matrices in units, then the exp(g_C) unit.
 // Forward (DIR = 0):  Wn = -W [C x DK], Qs = q exp(g) [C x DK],
 //                     KbT = (k exp(g_C - g))^T [DK x C], P [C x C].
-// Backward (DIR = 1): PT = P^T [C x C], Kb [C x DK], QsT [DK x C], WnT = -W^T [DK x C].
+// Backward (DIR = 1): PT = P^T [C x C], Kb [C x DK], QsT [DK x C], WnT = -W^T [DK x C],
+//                     T = (I + A)^-1 [C x C] (for the per-chunk gradient kernel).
 template <int DK, int C, bool F32IN, int DIR>
 struct Record {
   using F = Frag<F32IN>;
   static constexpr int UK = F::units(DK), UC = F::units(C);
   static constexpr int RC = C / 16, RK = DK / 16;  // 16-row tiles
-  // unit offsets of the four matrices
+  // unit offsets of the matrices
   static constexpr int u0 = 0;
   static constexpr int u1 = u0 + (DIR == 0 ? RC * UK : RC * UC);
   static constexpr int u2 = u1 + (DIR == 0 ? RC * UK : RC * UK);
   static constexpr int u3 = u2 + (DIR == 0 ? RK * UC : RK * UC);
-  static constexpr int uG = u3 + (DIR == 0 ? RC * UC : RK * UC);
+  static constexpr int u4 = u3 + (DIR == 0 ? RC * UC : RK * UC);
+  static constexpr int uG = u4 + (DIR == 0 ? 0 : RC * UC);
   static constexpr int kUnits = uG + 1;
   static constexpr int kBytes = kUnits * F::kUnitBytes;
   static_assert(DK * 4 <= 1024, "exp(g_C) must fit one unit");
@@ -82,6 +84,62 @@ __device__ __forceinline__ void write_units(const typename Frag<F32IN>::OpT* X, 
       out = make_uint4(a.x, a.y, b.x, b.y);
     }
     *reinterpret_cast<uint4*>(dst + (int64_t)t * F::kUnitBytes + 16 * l) = out;
+  }
+}
+
+// Same for an fp32 matrix in LDS, rounded to the operand type on the way.
+template <bool F32IN>
+__device__ __forceinline__ void write_units_f32(const float* X, int ld, int M, int K, char* dst, int wid, int nw) {
+  using F = Frag<F32IN>;
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int nu = F::units(K), total = (M / 16) * nu;
+  for (int t = wid; t < total; t += nw) {
+    const int R = t / nu, u = t - R * nu;
+    const int k0 = F::KU * u;
+    const float* row = X + (16 * R + r) * ld;
+    uint4 out;
+    if constexpr (F32IN) {
+      const float4 v = *reinterpret_cast<const float4*>(row + k0 + 4 * g);
+      out = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
+    } else {
+      f16x8 h;
+      const float4 a = *reinterpret_cast<const float4*>(row + k0 + 4 * g);
+      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k0 + 16 < K) b = *reinterpret_cast<const float4*>(row + k0 + 16 + 4 * g);
+      h[0] = static_cast<_Float16>(a.x); h[1] = static_cast<_Float16>(a.y);
+      h[2] = static_cast<_Float16>(a.z); h[3] = static_cast<_Float16>(a.w);
+      h[4] = static_cast<_Float16>(b.x); h[5] = static_cast<_Float16>(b.y);
+      h[6] = static_cast<_Float16>(b.z); h[7] = static_cast<_Float16>(b.w);
+      out = __builtin_bit_cast(uint4, h);
+    }
+    *reinterpret_cast<uint4*>(dst + (int64_t)t * F::kUnitBytes + 16 * l) = out;
+  }
+}
+
+// Unpack unit (R, u) of a record matrix [M][K] into row-major LDS copies:
+// X[row][k] (ldx) and, when XT is not null, XT[k][row] (ldt); indices past K skipped.
+template <bool F32IN, typename OpT>
+__device__ __forceinline__ void unpack_unit(const uint4& v, int R, int u, int K, OpT* X, int ldx, OpT* XT, int ldt) {
+  using F = Frag<F32IN>;
+  const int l = lane_id(), r = 16 * R + (l & 15), g = l >> 4;
+  if constexpr (F32IN) {
+    const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = F::KU * u + F::kslot(g, j);
+      X[r * ldx + k] = x[j];
+      if (XT) XT[k * ldt + r] = x[j];
+    }
+  } else {
+    const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = F::KU * u + F::kslot(g, j);
+      if (k < K) {
+        X[r * ldx + k] = h[j];
+        if (XT) XT[k * ldt + r] = h[j];
+      }
+    }
   }
 }
 

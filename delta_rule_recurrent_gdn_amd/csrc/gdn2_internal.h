@@ -56,6 +56,7 @@ struct BwdArgs {
   float* dS0;                // nullable
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
+  const char* records = nullptr;  // backward records (T, P^T) for launch_bwd_grad
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -356,6 +356,9 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
   KS ks;
   ks.invert(sAf, sXs);  // begins and ends with a barrier
 
+  // ---- backward: T units for the per-chunk gradient kernel ----
+  if constexpr (DIR == 1) write_units_f32<F32IN>(sAf, LDCF, C, C, rec + Rec::u4 * F::kUnitBytes, wid, NW);
+
   // ---- Kh^T = (b k exp(g))^T over the dead Kb^T staging ----
   if (live) {
 #pragma unroll
