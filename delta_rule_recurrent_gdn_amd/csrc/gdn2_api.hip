@@ -188,8 +188,7 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   const bool f32 = dt == GDN2_F32;
   const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
-  const bool single_fwd = gdn2::fwd_supported(Dk, Dv, chunk, f32);
-  if (!plan.two_stage && !(gdn2::bwd_supported(Dk, Dv, chunk, f32) && single_fwd)) return GDN2_ERR_UNSUPPORTED;
+  if (!plan.two_stage) return GDN2_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {
@@ -213,9 +212,7 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   if (states == nullptr) {
     states = reinterpret_cast<float*>(ws + plan.part);
     f.chunk_states = states;
-    if (!plan.two_stage) {
-      st = hip_status(gdn2::launch_fwd(f, s));
-    } else {
+    {
       // the two-stage forward (the default forward path, so the states match a
       // saved forward's bit for bit) in the records region; the backward
       // records overwrite it afterwards
@@ -228,7 +225,6 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
                   dS0, B, T, H, Dk, Dv, chunk, f32};
-  if (!plan.two_stage) return hip_status(gdn2::launch_bwd(a, s));
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
   a.records = rec;

@@ -41,253 +41,33 @@
 namespace gdn2 {
 
 // =============================================================================
-// reverse state-gradient chain
-// =============================================================================
-// Reverse chain: 8 waves per workgroup, as in the forward.
-constexpr int kDstThreads = 512;
-
-template <int DK, int C, int BV, bool F32IN>
-struct DstCfg {
-  static constexpr int kThreads = kDstThreads;
-  using KS = KSide<DK, C, F32IN, kThreads>;
-  using OpT = typename KS::OpT;
-  static constexpr int kWaves = kThreads / kWave;
-  static constexpr int NB = KS::NB;
-  static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF;
-  static constexpr int OPB = sizeof(OpT);
-  static constexpr int oKhT = 0;                                   // OpT [DK][LDC]  (b k exp(g))^T
-  static constexpr int oQhT = oKhT + DK * LDC * OPB;               // OpT [DK][LDC]  (q exp(g))^T
-  static constexpr int oKb = oQhT + DK * LDC * OPB;                // OpT [C][LDK]   k exp(g_C - g)
-  static constexpr int oDOT = oKb + C * LDK * OPB;                 // OpT [BV][LDC]  dO^T
-  static constexpr int oDST = oDOT + BV * LDC * OPB;               // OpT [BV][LDK]  dS^T
-  static constexpr int oCH = oDST + BV * LDK * OPB;
-  static constexpr int oTOT = oCH + KS::kChanBytes;
-  static constexpr int oX = oTOT + KS::kTotBytes;
-  static constexpr int oG = oX;
-  static constexpr int oSL = oG + KS::kGBytes;
-  static constexpr int endF = oSL + KS::kSlicesBytes;
-  static constexpr int oAf = oX;                                   // float [C][LDCF] T
-  static constexpr int oPT = oAf + KS::kAfBytes;                   // OpT [C][LDC]   P^T
-  static constexpr int oTT = oPT + C * LDC * OPB;                  // OpT [C][LDC]   T^T
-  static constexpr int oDUT = oTT + C * LDC * OPB;                 // OpT [BV][LDC]  dU^T
-  static constexpr int oZT = oDUT + BV * LDC * OPB;                // OpT [BV][LDC]  -(T^T dU)^T
-  static constexpr int oXs = oZT + BV * LDC * OPB;
-  static constexpr int endW = oXs + KS::kXsBytes;
-  static constexpr int kLdsBytes = endF > endW ? endF : endW;
-  static constexpr bool kFits = kLdsBytes <= 160 * 1024;
-  static constexpr int NUT = NB * (BV / 16);
-  static constexpr int UPW = (NUT + kWaves - 1) / kWaves;
-  static constexpr int NST = (DK / 16) * (BV / 16);
-  static constexpr int SPW = (NST + kWaves - 1) / kWaves;
-  static constexpr int VW_RPP = kThreads / (BV / 8);
-  static constexpr int VW_RPT = (C + VW_RPP - 1) / VW_RPP;
-};
-
-template <int DK, int C, int BV, bool F32IN>
-__global__ __launch_bounds__(kDstThreads) void gdn2_bwd_dstate_kernel(BwdArgs a) {
-  using Cfg = DstCfg<DK, C, BV, F32IN>;
-  using KS = typename Cfg::KS;
-  using OpT = typename Cfg::OpT;
-  constexpr int NW = Cfg::kWaves, NB = Cfg::NB, NT = Cfg::kThreads;
-  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF;
-
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
-  OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
-  OpT* sQhT = reinterpret_cast<OpT*>(smem + Cfg::oQhT);
-  OpT* sKb = reinterpret_cast<OpT*>(smem + Cfg::oKb);
-  OpT* sDOT = reinterpret_cast<OpT*>(smem + Cfg::oDOT);
-  OpT* sDST = reinterpret_cast<OpT*>(smem + Cfg::oDST);
-  float* sCh = reinterpret_cast<float*>(smem + Cfg::oCH);
-  float* sTot = reinterpret_cast<float*>(smem + Cfg::oTOT);
-  float* sG = reinterpret_cast<float*>(smem + Cfg::oG);
-  char* sSL = smem + Cfg::oSL;
-  float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
-  OpT* sPT = reinterpret_cast<OpT*>(smem + Cfg::oPT);
-  OpT* sTT = reinterpret_cast<OpT*>(smem + Cfg::oTT);
-  OpT* sDUT = reinterpret_cast<OpT*>(smem + Cfg::oDUT);
-  OpT* sZT = reinterpret_cast<OpT*>(smem + Cfg::oZT);
-  float* sXs = reinterpret_cast<float*>(smem + Cfg::oXs);
-
-  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
-  const int lr = l & 15, lg = l >> 4;
-  const int nv = a.Dv / BV;
-  const int nbh = a.B * a.H;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int bh = (slot / nv) * 8 + xcd, vt = slot % nv;
-  if (bh >= nbh) return;
-  const int bi = bh / a.H, h = bh - bi * a.H;
-  const int j0 = vt * BV;
-  const int Dv = a.Dv, T = a.T, H = a.H;
-  const int NC = (T + C - 1) / C;
-  const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
-  const int64_t baseK = ((int64_t)bi * T * H + h) * DK;
-  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
-  const int64_t stBase = (int64_t)bh * DK * Dv + j0;
-
-  KS ks;
-  ks.init(tid);
-  constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
-  const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
-  Raw8<F32IN> rdo[VW_RPT];
-  auto load_chunk = [&](int nn) {
-    const int tn = nn * C, Ln = min(C, T - tn);
-    ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, tn, Ln);
-#pragma unroll
-    for (int i = 0; i < VW_RPT; ++i) {
-      const int r = vw_r + i * VW_RPP;
-      if (r < Ln) ld_raw(rdo[i], a.dO, baseV + (int64_t)(tn + r) * rowV + 8 * vw_j8);
-      else zero_raw(rdo[i]);
-    }
-  };
-
-  // dS starts as dS_final (or zero)
-  f32x4 accD[Cfg::SPW];
-#pragma unroll
-  for (int i = 0; i < Cfg::SPW; ++i) {
-    const int t = wid + NW * i;
-    accD[i] = zero4();
-    if (t < Cfg::NST) {
-      const int cb = t / (BV / 16), jb = t % (BV / 16);
-      if (a.dS_final) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          accD[i][e] = a.dS_final[stBase + (int64_t)(16 * cb + 4 * lg + e) * Dv + 16 * jb + lr];
-      }
-      store_tile_t(sDST + 16 * jb * LDK + 16 * cb, LDK, accD[i]);
-    }
-  }
-  load_chunk(NC - 1);
-
-  for (int n = NC - 1; n >= 0; --n) {
-    // the carried gradient is that of chunk n's exit state
-    {
-      float* ws = a.dS_chunks + ((int64_t)bh * NC + n) * DK * Dv + j0;
-#pragma unroll
-      for (int i = 0; i < Cfg::SPW; ++i) {
-        const int t = wid + NW * i;
-        if (t < Cfg::NST) {
-          const int cb = t / (BV / 16), jb = t % (BV / 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ws[(int64_t)(16 * cb + 4 * lg + e) * Dv + 16 * jb + lr] = accD[i][e];
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < VW_RPT; ++i) {
-      const int r = vw_r + i * VW_RPP;
-      if (r < C) {
-        float d8[8];
-        cvt(rdo[i], d8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sDOT[(8 * vw_j8 + e) * LDC + r] = static_cast<OpT>(d8[e]);
-      }
-    }
-    ks.gates(sTot, sG, sCh);
-    f32x4 accG[KS::GPW];
-    ks.factors_gram(sG, sCh, sSL, accG,
-                    [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
-                        const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
-                      (void)e1;
-                      st4(sKb + r * LDK + c0, kv[0] * ec[0], kv[1] * ec[1], kv[2] * ec[2], kv[3] * ec[3]);
-#pragma unroll
-                      for (int i = 0; i < 4; ++i) {
-                        sKhT[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * eg[i]);
-                        sQhT[(c0 + i) * LDC + r] = static_cast<OpT>(qv[i] * eg[i]);
-                      }
-                    });
-    ks.template gram_store<true>(accG, sAf, sPT);
-    ks.invert(sAf, sXs);
-    for (int e = tid; e < C * C; e += NT) {
-      const int r = e / C, i = e % C;
-      sTT[i * LDC + r] = static_cast<OpT>(sAf[r * LDCF + i]);
-    }
-    if (n > 0) load_chunk(n - 1);
-    __syncthreads();
-
-    // dU = P^T dO + Kb dS
-#pragma unroll
-    for (int i = 0; i < Cfg::UPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NUT) {
-        const int R = t / (BV / 16), jb = t % (BV / 16);
-        f32x4 acc = zero4();
-        mma_nt<OpT>(acc, sPT + 16 * R * LDC + 16 * R, LDC, sDOT + 16 * jb * LDC + 16 * R, LDC, C - 16 * R);
-        mma_nt_k<DK>(acc, sKb + 16 * R * LDK, LDK, sDST + 16 * jb * LDK, LDK);
-        store_tile_t(sDUT + 16 * jb * LDC + 16 * R, LDC, acc);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    // Z = T^T dU, stored negated
-#pragma unroll
-    for (int i = 0; i < Cfg::UPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NUT) {
-        const int I = t / (BV / 16), jb = t % (BV / 16);
-        f32x4 acc = zero4();
-        mma_nt<OpT>(acc, sTT + 16 * I * LDC + 16 * I, LDC, sDUT + 16 * jb * LDC + 16 * I, LDC, C - 16 * I);
-        store_tile_t(sZT + 16 * jb * LDC + 16 * I, LDC, acc, -1.f);
-      }
-    }
-    __syncthreads();
-    // dS <- Diag(exp(g_C)) dS + Qs^T dO - Kh^T Z
-#pragma unroll
-    for (int i = 0; i < Cfg::SPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NST) {
-        const int cb = t / (BV / 16), jb = t % (BV / 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) accD[i][e] *= __expf(sCh[DK + 16 * cb + 4 * lg + e]);
-        mma_nt_k<C>(accD[i], sQhT + 16 * cb * LDC, LDC, sDOT + 16 * jb * LDC, LDC);
-        mma_nt_k<C>(accD[i], sKhT + 16 * cb * LDC, LDC, sZT + 16 * jb * LDC, LDC);
-        store_tile_t(sDST + 16 * jb * LDK + 16 * cb, LDK, accD[i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  if (a.dS0) {
-#pragma unroll
-    for (int i = 0; i < Cfg::SPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NST) {
-        const int cb = t / (BV / 16), jb = t % (BV / 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a.dS0[stBase + (int64_t)(16 * cb + 4 * lg + e) * Dv + 16 * jb + lr] = accD[i][e];
-      }
-    }
-  }
-}
-
-// =============================================================================
 // chunk-parallel gradients
 // =============================================================================
 
-// Four input values kept in registers: fp32 as is, bf16 as two packed pairs
+// Four input values kept in registers: fp32 as is, bf16 as their bits
 // (exact: the inputs are bf16 numbers).
 template <bool F32IN>
 struct Vals4 {
   float v[4];
   __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0.f; }
-  __device__ __forceinline__ void set(int e, const void* base, int64_t idx) {
-    v[e] = static_cast<const float*>(base)[idx];
+  // raw load of element idx (or of the always-valid safe when !ok); mask() zeroes it later
+  __device__ __forceinline__ void set(int e, const void* base, int64_t idx, int64_t safe, bool ok) {
+    v[e] = static_cast<const float*>(base)[ok ? idx : safe];
   }
+  __device__ __forceinline__ void mask(int e, bool ok) { v[e] = ok ? v[e] : 0.f; }
   __device__ __forceinline__ float operator[](int e) const { return v[e]; }
 };
 template <>
 struct Vals4<false> {
-  uint32_t p[2];
-  __device__ __forceinline__ void zero() { p[0] = p[1] = 0u; }
-  __device__ __forceinline__ void set(int e, const void* base, int64_t idx) {
-    const uint32_t x = static_cast<const uint16_t*>(base)[idx];
-    p[e >> 1] = (e & 1) ? ((p[e >> 1] & 0x0000ffffu) | (x << 16)) : ((p[e >> 1] & 0xffff0000u) | x);
+  uint32_t v[4];  // bf16 bits, one per register (no packing, so the loads need not wait for each other)
+  __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = 0u; }
+  __device__ __forceinline__ void set(int e, const void* base, int64_t idx, int64_t safe, bool ok) {
+    v[e] = static_cast<const uint16_t*>(base)[ok ? idx : safe];
   }
-  __device__ __forceinline__ float operator[](int e) const {
-    return __uint_as_float((e & 1) ? (p[e >> 1] & 0xffff0000u) : (p[e >> 1] << 16));
-  }
+  __device__ __forceinline__ void mask(int e, bool ok) { v[e] = ok ? v[e] : 0u; }
+  __device__ __forceinline__ float operator[](int e) const { return __uint_as_float(v[e] << 16); }
 };
-template <int DK, int C, int BVB_, bool F32IN>
+template <int DK, int C, bool F32IN>
 struct GradCfg {
   using KS = KSide<DK, C, F32IN, 512, 4>;  // float4 log_alpha rows: the decay-gradient scan reuses them
   using OpT = typename KS::OpT;
@@ -298,9 +78,9 @@ struct GradCfg {
   static constexpr int kThreads = 512;
   static constexpr int kWaves = kThreads / kWave;
   static constexpr int NB = KS::NB;
-  static constexpr int BVB = BVB_;                                 // value tile of the inner loop
   static constexpr int LDC = KS::LDC, LDK = KS::LDK, LDCF = KS::LDCF;
-  static constexpr int LDB = BVB + KS::PADOP;                      // rows of BVB values
+  static constexpr int DVM = 128;                                  // widest value axis
+  static constexpr int LDV = DVM + KS::PADOP;                      // rows over the value axis
   static constexpr int OPB = sizeof(OpT);
   static constexpr int WB = sizeof(WideT);
   // persistent (until the post-processing)
@@ -310,26 +90,18 @@ struct GradCfg {
   static constexpr int oTT = oTm + C * LDC * OPB;                  // OpT [C][LDC]  T^T
   static constexpr int oPT = oTT + C * LDC * OPB;                  // OpT [C][LDC]  P^T
   static constexpr int oR = oPT + C * LDC * OPB;                   // phase region
-  // phase F / T (prep)
+  // phase G (gate cumsum)
   static constexpr int oG = oR;
-  static constexpr int oSL = oG + KS::kGBytes;
-  static constexpr int endPF = oSL + KS::kSlicesBytes;
-  static constexpr int oAf = oR;
-  static constexpr int oXs = oAf + KS::kAfBytes;
-  static constexpr int endPT = oXs + KS::kXsBytes;
-  // phase V (value-tile loop)
-  static constexpr int oS0T = oR;                                  // OpT [BVB][LDK]
-  static constexpr int oS0 = oS0T + BVB * LDK * OPB;               // OpT [DK][LDB]
-  static constexpr int oDST = oS0 + DK * LDB * OPB;                // OpT [BVB][LDK]
-  static constexpr int oDS = oDST + BVB * LDK * OPB;               // OpT [DK][LDB]
-  static constexpr int oDO = oDS + DK * LDB * OPB;                 // OpT [C][LDB]
-  static constexpr int oDOT = oDO + C * LDB * OPB;                 // OpT [BVB][LDC]
-  static constexpr int oWV = oDOT + BVB * LDC * OPB;               // OpT [C][LDB]
-  static constexpr int oXT = oWV + C * LDB * OPB;                  // OpT [BVB][LDC]
-  static constexpr int oU = oXT + BVB * LDC * OPB;                 // OpT [C][LDB]
-  static constexpr int oDU = oU + C * LDB * OPB;                   // OpT [C][LDB]
-  static constexpr int oDUT = oDU + C * LDB * OPB;                 // OpT [BVB][LDC]
-  static constexpr int endV = oDUT + BVB * LDC * OPB;
+  static constexpr int endPG = oG + KS::kGBytes;
+  // phase V (U, dU and, for 16-bit operands, dO and w v over the whole value
+  // axis: the row operands of the key-side contractions; fp32 operands read
+  // dO and w v from global memory instead, to fit LDS)
+  static constexpr bool kStageDO = !F32IN;
+  static constexpr int oU = oR;                                    // OpT [C][LDV]
+  static constexpr int oDU = oU + C * LDV * OPB;                   // OpT [C][LDV]
+  static constexpr int oDO = oDU + C * LDV * OPB;                  // OpT [C][LDV]
+  static constexpr int oWV = oDO + (kStageDO ? C * LDV * OPB : 0); // OpT [C][LDV]
+  static constexpr int endV = oWV + (kStageDO ? C * LDV * OPB : 0);
   // phase A (dT, dK, dA)
   static constexpr int oDW = oR;                                   // OpT [C][LDK]
   static constexpr int oDWT = oDW + C * LDK * OPB;                 // OpT [DK][LDC]
@@ -344,16 +116,15 @@ struct GradCfg {
   // phase D (output staging and the decay-gradient scan) starts at 0 as well:
   // x, and where they fit, dq, dk, db as fp32 [C][DK] (staged for full-row stores)
   static constexpr int endBase = [] {
-    int m = endPF;
-    if (endPT > m) m = endPT;
+    int m = endPG;
     if (endV > m) m = endV;
     if (endA > m) m = endA;
     if (endB > m) m = endB;
     return m;
   }();
-  // cumsum segment totals: scratch of the gate prep and of the final scan only,
-  // so they sit past the prep buffers and the output staging
-  static constexpr int tot_at(int endD_) { return ((endPF > endD_ ? endPF : endD_) + 15) & ~15; }
+  // cumsum segment totals: scratch of the gate cumsum and of the final scan
+  // only, so they sit past the gate buffer and the output staging
+  static constexpr int tot_at(int endD_) { return ((endPG > endD_ ? endPG : endD_) + 15) & ~15; }
   static constexpr int main_end(int endD_) {
     return endBase > tot_at(endD_) + KS::kTotBytes ? endBase : tot_at(endD_) + KS::kTotBytes;
   }
@@ -373,22 +144,20 @@ struct GradCfg {
   static constexpr int KPW = (NKT + kWaves - 1) / kWaves;
   static constexpr int NCT = NB * NB;                              // C x C tiles
   static constexpr int CPW = (NCT + kWaves - 1) / kWaves;
-  static constexpr int NVT = NB * (BVB / 16);                      // C x BVB tiles
-  static constexpr int VPW = (NVT + kWaves - 1) / kWaves;
 };
 
-// REC: T and P^T come from the backward records (a.records) and the chunk's
-// Gram products and inversion are skipped; otherwise they are recomputed here.
-template <int DK, int C, int BVB_, bool F32IN, bool REC>
+// One workgroup per (batch, head, chunk). T and P^T come from the backward
+// records (a.records), the exit-state gradient from the reverse chain.
+template <int DK, int C, bool F32IN>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
-  using Cfg = GradCfg<DK, C, BVB_, F32IN>;
+  using Cfg = GradCfg<DK, C, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   using WideT = typename Cfg::WideT;
-  constexpr int NW = Cfg::kWaves, NB = Cfg::NB, NT = Cfg::kThreads, BVB = Cfg::BVB;
-  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF, LDB = Cfg::LDB;
-  constexpr int KPW = Cfg::KPW, CPW = Cfg::CPW, VPW = Cfg::VPW;
-  constexpr int KB16 = DK / 16, VB16 = BVB / 16;
+  constexpr int NW = Cfg::kWaves, NB = Cfg::NB, NT = Cfg::kThreads;
+  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDV = Cfg::LDV;
+  constexpr int KPW = Cfg::KPW, CPW = Cfg::CPW;
+  constexpr int KB16 = DK / 16;
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   OpT* sKh = reinterpret_cast<OpT*>(smem + Cfg::oKh);
@@ -397,20 +166,10 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   OpT* sTT = reinterpret_cast<OpT*>(smem + Cfg::oTT);
   OpT* sPT = reinterpret_cast<OpT*>(smem + Cfg::oPT);
   float* sG = reinterpret_cast<float*>(smem + Cfg::oG);
-  char* sSL = smem + Cfg::oSL;
-  float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
-  float* sXs = reinterpret_cast<float*>(smem + Cfg::oXs);
-  OpT* sS0T = reinterpret_cast<OpT*>(smem + Cfg::oS0T);
-  OpT* sS0 = reinterpret_cast<OpT*>(smem + Cfg::oS0);
-  OpT* sDST = reinterpret_cast<OpT*>(smem + Cfg::oDST);
-  OpT* sDS = reinterpret_cast<OpT*>(smem + Cfg::oDS);
-  OpT* sDO = reinterpret_cast<OpT*>(smem + Cfg::oDO);
-  OpT* sDOT = reinterpret_cast<OpT*>(smem + Cfg::oDOT);
-  OpT* sWV = reinterpret_cast<OpT*>(smem + Cfg::oWV);
-  OpT* sXT = reinterpret_cast<OpT*>(smem + Cfg::oXT);
   OpT* sU = reinterpret_cast<OpT*>(smem + Cfg::oU);
   OpT* sDU = reinterpret_cast<OpT*>(smem + Cfg::oDU);
-  OpT* sDUT = reinterpret_cast<OpT*>(smem + Cfg::oDUT);
+  OpT* sDO = reinterpret_cast<OpT*>(smem + Cfg::oDO);
+  OpT* sWV = reinterpret_cast<OpT*>(smem + Cfg::oWV);
   OpT* sDW = reinterpret_cast<OpT*>(smem + Cfg::oDW);
   OpT* sDWT = reinterpret_cast<OpT*>(smem + Cfg::oDWT);
   OpT* sDTm = reinterpret_cast<OpT*>(smem + Cfg::oDTm);
@@ -440,259 +199,346 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // ---- key-side preparation ----
   KS ks;
   ks.init(tid);
-  if constexpr (REC) ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
-  else ks.load(a.q, a.k, a.b, a.log_alpha, baseK, rowK, t0, Lr);
+  ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
 
   // the C x DK tiles this lane owns: rows 16R + 4lg + e, column 16cb + lr.
-  // Keep q, k, b and e1 = exp(g - g_m) there for the final chain rule.
-  Vals4<F32IN> pq[KPW], pk[KPW], pb[KPW];
+  // e1 = exp(g - g_m) there for the final chain rule (q, k and b are fetched
+  // later, when the key phase starts, so that they are not live meanwhile).
   float pe1[KPW][4];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int t = wid + NW * i;
-    pq[i].zero();
-    pk[i].zero();
-    pb[i].zero();
+    const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pe1[i][e] = 1.f;
-    if (t < Cfg::NKT) {
-      const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * R + 4 * lg + e;
+      pe1[i][e] = t < Cfg::NKT ? __expf(sG[r * DK + c] - sCh[c]) : 1.f;
+    }
+  }
+  // T (and T^T) and P^T from the record's units; P^T units that lie wholly
+  // below the diagonal are not stored (zero)
+  using Rec = Record<DK, C, F32IN, 1>;
+  using F = Frag<F32IN>;
+  const char* rec = a.records + ((int64_t)bh * NC + n) * Rec::kBytes;
+  // units: T, P^T (chunk x chunk), then Kh, Kb (chunk x Dk); every load of
+  // the wave first, then the unpacking
+  constexpr int NU = Rec::RC * Rec::UC, NK = Rec::RC * Rec::UK, NUT = 2 * NU + 2 * NK;
+  constexpr int UPW = (NUT + NW - 1) / NW;
+  // (The unit index arithmetic is written out here: the same arithmetic in a
+  // lambda with reference out-parameters, inside these unrolled loops,
+  // compiled to code that unpacked wrong units for some sizes on gfx950.)
+  uint4 uv[UPW];
+  int uw[UPW], uR[UPW], uu[UPW];
+#pragma unroll
+  for (int p = 0; p < UPW; ++p) {
+    const int t = wid + NW * p;
+    const int which = t < NU ? 0 : t < 2 * NU ? 1 : t < 2 * NU + NK ? 2 : 3;
+    const int tt = which == 0 ? t : which == 1 ? t - NU : which == 2 ? t - 2 * NU : t - 2 * NU - NK;
+    const int nu = which < 2 ? Rec::UC : Rec::UK;
+    const int ub = which == 0 ? Rec::u4 : which == 1 ? Rec::u0 : which == 2 ? Rec::u5 : Rec::u1;
+    uw[p] = t < NUT ? which : -1;
+    uR[p] = tt / nu;
+    uu[p] = tt - uR[p] * nu;
+    const int64_t off = t < NUT ? (int64_t)(ub + tt) * F::kUnitBytes : 0;  // past the units: any valid unit
+    uv[p] = *reinterpret_cast<const uint4*>(rec + off + 16 * l);
+  }
+#pragma unroll
+  for (int p = 0; p < UPW; ++p) {
+    const int which = uw[p], R = uR[p], u = uu[p];
+    // P^T units wholly below the diagonal are not stored: zero
+    const bool zero = which == 1 && F::KU * u + F::KU - 1 < 16 * R;
+    const uint4 v = zero ? make_uint4(0u, 0u, 0u, 0u) : uv[p];
+    if (which == 0) unpack_unit<F32IN>(v, R, u, C, sTm, LDC, sTT, LDC);
+    else if (which == 1) unpack_unit<F32IN>(v, R, u, C, sPT, LDC, static_cast<OpT*>(nullptr), 0);
+    else if (which >= 2) unpack_unit<F32IN>(v, R, u, DK, which == 2 ? sKh : sKb, LDK, static_cast<OpT*>(nullptr), 0);
+  }
+
+  // ---- column phase: each wave owns 16 value columns of the chunk ----
+  // X = w v - Kh S0, U = T X, dU = P^T dO + Kb dS and d(w v) = T^T dU with
+  // their right operands in registers: S0, dS and dO gathered straight into
+  // operand slots, X and dU as the accumulators of the previous product
+  // (lane layout of gdn2_frag.h); the left operands are row-major LDS rows
+  // read in the same slot order. dw, dv leave from here; U and dU go to LDS
+  // for the contractions over the value axis.
+  using Fr = Frag<F32IN>;
+  constexpr int KU = Fr::KU, UKd = Fr::units(DK), UCc = Fr::units(C), RC = C / 16;
+  __syncthreads();  // Kh, Kb, T, T^T, P^T are in LDS; the gate buffer is dead
+  auto lds_unit = [&](const OpT* X, int ld, int row0, int k0, int K) -> uint4 {
+    const OpT* p = X + (row0 + lr) * ld + k0 + 4 * lg;
+    if constexpr (F32IN) {
+      return *reinterpret_cast<const uint4*>(p);
+    } else {
+      const uint2 lo = *reinterpret_cast<const uint2*>(p);
+      uint2 hi = make_uint2(0u, 0u);
+      if (k0 + 16 < K) hi = *reinterpret_cast<const uint2*>(p + 16);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  if (16 * wid < Dv) {
+    const int jc = 16 * wid + lr;
+    using RhsT = typename std::conditional<F32IN, f32x4, f16x8>::type;
+    constexpr int NE = F32IN ? 4 : 8;
+    // every gather first, in flight together; conversions after the fence
+    using InT = typename std::conditional<F32IN, float, __bf16>::type;
+    float s0r[UKd][NE], dsr[UKd][NE];
+    InT dor[UCc][NE], vr[RC][4], wr[RC][4];
+#pragma unroll
+    for (int u = 0; u < UKd; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int d = KU * u + Fr::kslot(lg, j);
+        s0r[u][j] = ld_sel(S0g, (int64_t)d * Dv + jc, jc, d < DK);
+        dsr[u][j] = ld_sel(dSg, (int64_t)d * Dv + jc, jc, d < DK);
+      }
+#pragma unroll
+    for (int u = 0; u < UCc; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int t = KU * u + Fr::kslot(lg, j);
+        dor[u][j] = ld_sel(static_cast<const InT*>(a.dO), baseV + (int64_t)(t0 + t) * rowV + jc,
+                           baseV + (int64_t)t0 * rowV + jc, t < Lr);
+      }
+#pragma unroll
+    for (int R = 0; R < RC; ++R)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * R + 4 * lg + e;
-        pe1[i][e] = __expf(sG[r * DK + c] - sCh[c]);
-        if (r < Lr) {
-          const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
-          pq[i].set(e, a.q, idx);
-          pk[i].set(e, a.k, idx);
-          pb[i].set(e, a.b, idx);
+        const int t = 16 * R + 4 * lg + e;
+        const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc, safe = baseV + (int64_t)t0 * rowV + jc;
+        vr[R][e] = ld_sel(static_cast<const InT*>(a.v), idx, safe, t < Lr);
+        wr[R][e] = ld_sel(static_cast<const InT*>(a.w), idx, safe, t < Lr);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    RhsT s0f[UKd], dsf[UKd], dof[UCc];
+    float vv[RC][4], ww[RC][4];
+#pragma unroll
+    for (int u = 0; u < UKd; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        s0f[u][j] = static_cast<OpT>(s0r[u][j]);
+        dsf[u][j] = static_cast<OpT>(dsr[u][j]);
+      }
+#pragma unroll
+    for (int u = 0; u < UCc; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) dof[u][j] = static_cast<OpT>(static_cast<float>(dor[u][j]));
+#pragma unroll
+    for (int R = 0; R < RC; ++R)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vv[R][e] = static_cast<float>(vr[R][e]);
+        ww[R][e] = static_cast<float>(wr[R][e]);
+      }
+    // X = w v - Kh S0
+    f32x4 X[RC];
+#pragma unroll
+    for (int R = 0; R < RC; ++R) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int u = 0; u < UKd; ++u) unit_mma(acc, lds_unit(sKh, LDK, 16 * R, KU * u, DK), s0f[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[R][e] = vv[R][e] * ww[R][e] - acc[e];
+    }
+    // right operands over the chunk's tokens from accumulator tiles
+    auto rhs_c = [&](const f32x4 (&Y)[RC], int u) -> RhsT {
+      if constexpr (F32IN) return Y[u];
+      else return rhs_from_acc(Y[2 * u], 2 * u + 1 < RC ? Y[2 * u + 1] : zero4());
+    };
+    // U = T X (T lower triangular: contraction units past the row block are zero)
+    f32x4 Uc[RC], dU[RC];
+#pragma unroll
+    for (int R = 0; R < RC; ++R) {
+      Uc[R] = zero4();
+#pragma unroll
+      for (int u = 0; u < UCc; ++u)
+        if (KU * u <= 16 * R + 15) unit_mma(Uc[R], lds_unit(sTm, LDC, 16 * R, KU * u, C), rhs_c(X, u));
+    }
+    // dU = P^T dO + Kb dS (P^T upper triangular)
+#pragma unroll
+    for (int R = 0; R < RC; ++R) {
+      dU[R] = zero4();
+#pragma unroll
+      for (int u = 0; u < UCc; ++u)
+        if (KU * u + KU - 1 >= 16 * R) unit_mma(dU[R], lds_unit(sPT, LDC, 16 * R, KU * u, C), dof[u]);
+#pragma unroll
+      for (int u = 0; u < UKd; ++u) unit_mma(dU[R], lds_unit(sKb, LDK, 16 * R, KU * u, DK), dsf[u]);
+    }
+    // d(w v) = T^T dU -> dw, dv
+#pragma unroll
+    for (int R = 0; R < RC; ++R) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int u = 0; u < UCc; ++u)
+        if (KU * u + KU - 1 >= 16 * R) unit_mma(acc, lds_unit(sTT, LDC, 16 * R, KU * u, C), rhs_c(dU, u));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * R + 4 * lg + e;
+        if (t < Lr) {
+          const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc;
+          a.dw[idx] = acc[e] * vv[R][e];
+          a.dv[idx] = acc[e] * ww[R][e];
         }
       }
     }
-  }
-
-  if constexpr (REC) {
-    // Kh = b k exp(g) and Kb = k exp(g_C - g) at the lane's positions
+    // U, dU, dO and w v row-major over the value axis
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NKT) {
-        const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
+    for (int R = 0; R < RC; ++R)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * lg + e;
-          const float eg = pe1[i][e] * sCh[2 * DK + c];
-          const float ec = sCh[3 * DK + c] * __builtin_amdgcn_rcpf(pe1[i][e]);
-          sKh[r * LDK + c] = static_cast<OpT>(pb[i][e] * pk[i][e] * eg);
-          sKb[r * LDK + c] = static_cast<OpT>(pk[i][e] * ec);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * R + 4 * lg + e;
+        sU[t * LDV + jc] = static_cast<OpT>(Uc[R][e]);
+        sDU[t * LDV + jc] = static_cast<OpT>(dU[R][e]);
+        if constexpr (Cfg::kStageDO) sWV[t * LDV + jc] = static_cast<OpT>(vv[R][e] * ww[R][e]);
       }
-    }
-    // T (and T^T) and P^T from the record's units; P^T units that lie wholly
-    // below the diagonal are not stored (zero)
-    using Rec = Record<DK, C, F32IN, 1>;
-    using F = Frag<F32IN>;
-    const char* rec = a.records + ((int64_t)bh * NC + n) * Rec::kBytes;
-    constexpr int NU = Rec::RC * Rec::UC;
-    for (int t = wid; t < 2 * NU; t += NW) {
-      const bool isT = t < NU;
-      const int tt = isT ? t : t - NU, R = tt / Rec::UC, u = tt - R * Rec::UC;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (isT || F::KU * u + F::KU - 1 >= 16 * R)
-        v = *reinterpret_cast<const uint4*>(rec + (int64_t)((isT ? Rec::u4 : Rec::u0) + tt) * F::kUnitBytes + 16 * l);
-      if (isT) unpack_unit<F32IN>(v, R, u, C, sTm, LDC, sTT, LDC);
-      else unpack_unit<F32IN>(v, R, u, C, sPT, LDC, static_cast<OpT*>(nullptr), 0);
-    }
-  } else {
-    f32x4 accG[KS::GPW];
-    ks.factors_gram(sG, sCh, sSL, accG,
-                    [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
-                        const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
-                      (void)qv;
-                      (void)e1;
-                      st4(sKh + r * LDK + c0, bv[0] * kv[0] * eg[0], bv[1] * kv[1] * eg[1], bv[2] * kv[2] * eg[2],
-                          bv[3] * kv[3] * eg[3]);
-                      st4(sKb + r * LDK + c0, kv[0] * ec[0], kv[1] * ec[1], kv[2] * ec[2], kv[3] * ec[3]);
-                    });
-    ks.template gram_store<true>(accG, sAf, sPT);
-    ks.invert(sAf, sXs);
-    for (int e = tid; e < C * C; e += NT) {
-      const int r = e / C, i = e % C;
-      const OpT v = static_cast<OpT>(sAf[r * LDCF + i]);
-      sTm[r * LDC + i] = v;
-      sTT[i * LDC + r] = v;
+    if constexpr (Cfg::kStageDO) {
+#pragma unroll
+      for (int u = 0; u < UCc; ++u)
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+          const int t = KU * u + Fr::kslot(lg, j);
+          if (t < C) sDO[t * LDV + jc] = dof[u][j];
+        }
     }
   }
+  __syncthreads();
 
-  // ---- value-tile loop: U, dU, d(w*v) and the key-side partial products ----
+  // ---- key phase: contractions over the value axis ----
+  //   dQs = dO S0^T, dKb = U dS^T, dU S0^T (C x DK);  dO U^T, dU (w v)^T (C x C)
+  // Both operands are read row-major (S0 and dS from global memory; dO, U, dU
+  // and w v from LDS), so the natural contraction order is used: 16-bit lane
+  // group g takes 8 consecutive values at 8g (16x16x32), fp32 takes 4 at 4g
+  // (four 16x16x4 products).
   f32x4 aQh[KPW], aKb[KPW], aW[KPW], aP[CPW], aT[CPW];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) aQh[i] = aKb[i] = aW[i] = zero4();
 #pragma unroll
   for (int i = 0; i < CPW; ++i) aP[i] = aT[i] = zero4();
-  // state-tile thread map: channel st_c + p*SROWS, 4 columns at 4*st_j4
-  constexpr int ST4 = BVB / 4;
-  constexpr int SROWS = NT / ST4;                                  // channels per pass
-  constexpr int SPASS = (DK + SROWS - 1) / SROWS;
-  const int st_c = tid / ST4, st_j4 = tid % ST4;
-  float rs[SPASS];                                                 // rowsum(S0 * dS) of those channels
+  // q, k, b at the lane's C x DK positions (for the chain rule after the key
+  // phase): raw loads now, zeroed past the sequence once the key phase is done
+  Vals4<F32IN> pq[KPW], pk[KPW], pb[KPW];
 #pragma unroll
-  for (int p = 0; p < SPASS; ++p) rs[p] = 0.f;
-
-  // value-tile inputs, fetched one tile ahead into registers
-  constexpr int VG = C * (BVB / 4);                                // 4-value groups of dO, v, w per tile
-  constexpr int VLD = (VG + NT - 1) / NT;
-  float4 rS0[SPASS], rDS[SPASS];
-  Raw4<F32IN> rDO[VLD], rV[VLD], rW[VLD];
-  const int nvt = Dv / BVB;
-  auto vload = [&](int jt) {
-    const int j0 = jt * BVB;
+  for (int i = 0; i < KPW; ++i) {
+    const int t = wid + NW * i;
+    const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
 #pragma unroll
-    for (int p = 0; p < SPASS; ++p) {
-      const int c = st_c + p * SROWS;
-      if (c < DK) {
-        rS0[p] = *reinterpret_cast<const float4*>(S0g + (int64_t)c * Dv + j0 + 4 * st_j4);
-        rDS[p] = *reinterpret_cast<const float4*>(dSg + (int64_t)c * Dv + j0 + 4 * st_j4);
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * R + 4 * lg + e;
+      const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
+      const int64_t safe = baseK + (int64_t)t0 * rowK + (c < DK ? c : 0);  // row 0 of the chunk always exists
+      const bool ok = t < Cfg::NKT && r < Lr;
+      pq[i].set(e, a.q, idx, safe, ok);
+      pk[i].set(e, a.k, idx, safe, ok);
+      pb[i].set(e, a.b, idx, safe, ok);
+    }
+  }
+  // right operands: rows of S0 and dS of this wave's key-channel block, all
+  // steps fetched at once; rowsum(S0 * dS) of those channels on the way
+  constexpr int KV = F32IN ? 16 : 32;          // value columns per key-phase step
+  constexpr int NV = F32IN ? 4 : 8;            // per lane group
+  constexpr int NSTEP = Cfg::DVM / KV;
+  using RhsT2 = typename std::conditional<F32IN, f32x4, f16x8>::type;
+  const int cb0 = wid % KB16;                  // = t % KB16 for every tile t of this wave
+  const bool rs_owner = wid < KB16;            // the wave whose first tile is in row block 0
+  RhsT2 bS[NSTEP], bD[NSTEP];
+  float rsum = 0.f;
+  {
+    const int d = 16 * cb0 + lr;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const int c0 = KV * st + NV * lg;
+      float xs[NV], xd[NV];
+      const bool on = c0 < Dv;
+      const int cs = on ? c0 : 0;  // unconditional loads, zeroed below
+      const float* ps = S0g + (int64_t)d * Dv + cs;
+      const float* pd = dSg + (int64_t)d * Dv + cs;
+#pragma unroll
+      for (int j4 = 0; j4 < NV; j4 += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(ps + j4);
+        const float4 b4 = *reinterpret_cast<const float4*>(pd + j4);
+        xs[j4] = a4.x; xs[j4 + 1] = a4.y; xs[j4 + 2] = a4.z; xs[j4 + 3] = a4.w;
+        xd[j4] = b4.x; xd[j4 + 1] = b4.y; xd[j4 + 2] = b4.z; xd[j4 + 3] = b4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        xs[j] = on ? xs[j] : 0.f;
+        xd[j] = on ? xd[j] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        bS[st][j] = static_cast<OpT>(xs[j]);
+        bD[st][j] = static_cast<OpT>(xd[j]);
+        rsum += xs[j] * xd[j];
       }
     }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int e = tid + i * NT;
-      const int r = e / (BVB / 4), j4 = e % (BVB / 4);
-      if (e < VG && r < Lr) {
-        const int64_t idx = baseV + (int64_t)(t0 + r) * rowV + j0 + 4 * j4;
-        ld_raw(rDO[i], a.dO, idx);
-        ld_raw(rV[i], a.v, idx);
-        ld_raw(rW[i], a.w, idx);
-      } else {
-        zero_raw(rDO[i]);
-        zero_raw(rV[i]);
-        zero_raw(rW[i]);
-      }
+  }
+  auto lds_rows = [&](const OpT* X, int row, int c0) -> RhsT2 {
+    const RhsT2 r = *reinterpret_cast<const RhsT2*>(X + row * LDV + (c0 < Dv ? c0 : 0));
+    return c0 < Dv ? r : RhsT2{};
+  };
+  // dO and w v rows (LDS when staged, else global memory; rows past the sequence are zero)
+  auto do_rows = [&](int row, int c0) -> RhsT2 {
+    if constexpr (Cfg::kStageDO) {
+      return lds_rows(sDO, row, c0);
+    } else {
+      const bool on = row < Lr && c0 < Dv;
+      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.dO) + baseV +
+                                                        (int64_t)(t0 + (on ? row : 0)) * rowV + (on ? c0 : 0));
+      return on ? RhsT2{x.x, x.y, x.z, x.w} : RhsT2{};
     }
   };
-  vload(0);
-
-  for (int jt = 0; jt < nvt; ++jt) {
-    const int j0 = jt * BVB;
-    __syncthreads();  // previous users of the phase region are done
-    // S0 and dS tiles: both layouts; rowsum(S0 * dS) partials
-#pragma unroll
-    for (int p = 0; p < SPASS; ++p) {
-      const int c = st_c + p * SROWS;
-      if (c < DK) {
-        const float4 s4 = rS0[p], d4 = rDS[p];
-        st4(sS0 + c * LDB + 4 * st_j4, s4.x, s4.y, s4.z, s4.w);
-        st4(sDS + c * LDB + 4 * st_j4, d4.x, d4.y, d4.z, d4.w);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sS0T[(4 * st_j4 + i) * LDK + c] = static_cast<OpT>(sv[i]);
-          sDST[(4 * st_j4 + i) * LDK + c] = static_cast<OpT>(dv4[i]);
-        }
-        rs[p] += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
-      }
+  auto wv_rows = [&](int row, int c0) -> RhsT2 {
+    if constexpr (Cfg::kStageDO) {
+      return lds_rows(sWV, row, c0);
+    } else {
+      const bool on = row < Lr && c0 < Dv;
+      const int64_t idx = baseV + (int64_t)(t0 + (on ? row : 0)) * rowV + (on ? c0 : 0);
+      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + idx);
+      const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + idx);
+      return on ? RhsT2{x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w} : RhsT2{};
     }
-    // dO, w*v: 4 consecutive value columns of one row
+  };
+  auto kmma = [&](f32x4& acc, const RhsT2& x, const RhsT2& y) {
+    if constexpr (F32IN) acc = unit_mma_ff(acc, x, y);
+    else acc = mfma16x16x32(x, y, acc);
+  };
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int e = tid + i * NT;
-      if (e < VG) {
-        const int r = e / (BVB / 4), j4 = e % (BVB / 4);
-        float d4[4], v4[4], w4[4];
-        cvt(rDO[i], d4);
-        cvt(rV[i], v4);
-        cvt(rW[i], w4);
-        st4(sDO + r * LDB + 4 * j4, d4[0], d4[1], d4[2], d4[3]);
-        st4(sWV + r * LDB + 4 * j4, w4[0] * v4[0], w4[1] * v4[1], w4[2] * v4[2], w4[3] * v4[3]);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) sDOT[(4 * j4 + q4) * LDC + r] = static_cast<OpT>(d4[q4]);
-      }
-    }
-    if (jt + 1 < nvt) vload(jt + 1);
-    __syncthreads();
-    // X = w*v - Kh S0  -> X^T
-#pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NVT) {
-        const int R = t / VB16, jb = t % VB16;
-        f32x4 acc = zero4();
-        mma_nt_k<DK>(acc, sKh + 16 * R * LDK, LDK, sS0T + 16 * jb * LDK, LDK);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[e] = static_cast<float>(sWV[(16 * R + 4 * lg + e) * LDB + 16 * jb + lr]) - acc[e];
-        store_tile_t(sXT + 16 * jb * LDC + 16 * R, LDC, acc);
-      }
-    }
-    __syncthreads();
-    // U = T X ; dU = P^T dO + Kb dS
-#pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NVT) {
-        const int R = t / VB16, jb = t % VB16;
-        f32x4 u = zero4(), du = zero4();
-        mma_nt<OpT>(u, sTm + 16 * R * LDC, LDC, sXT + 16 * jb * LDC, LDC, 16 * (R + 1));
-        store_tile(sU + 16 * R * LDB + 16 * jb, LDB, u);
-        mma_nt<OpT>(du, sPT + 16 * R * LDC + 16 * R, LDC, sDOT + 16 * jb * LDC + 16 * R, LDC, C - 16 * R);
-        mma_nt_k<DK>(du, sKb + 16 * R * LDK, LDK, sDST + 16 * jb * LDK, LDK);
-        store_tile(sDU + 16 * R * LDB + 16 * jb, LDB, du);
-        store_tile_t(sDUT + 16 * jb * LDC + 16 * R, LDC, du);
-      }
-    }
-    __syncthreads();
-    // d(w*v) = T^T dU  -> dw, dv
-#pragma unroll
-    for (int i = 0; i < VPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NVT) {
-        const int R = t / VB16, jb = t % VB16;
-        f32x4 acc = zero4();
-        mma_nt<OpT>(acc, sTT + 16 * R * LDC + 16 * R, LDC, sDUT + 16 * jb * LDC + 16 * R, LDC, C - 16 * R);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * R + 4 * lg + e;
-          if (r < Lr) {
-            const int64_t idx = baseV + (int64_t)(t0 + r) * rowV + j0 + 16 * jb + lr;
-            const float vv = load1<F32IN>(a.v, idx), wv = load1<F32IN>(a.w, idx);
-            a.dw[idx] = acc[e] * vv;
-            a.dv[idx] = acc[e] * wv;
-          }
-        }
-      }
-    }
-    // key-side partials: dO S0^T, U dS^T, dU S0^T (C x DK);  dO U^T, dU (w*v)^T (C x C)
+  for (int st = 0; st < NSTEP; ++st) {
+    const int c0 = KV * st + NV * lg;
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int t = wid + NW * i;
       if (t < Cfg::NKT) {
-        const int R = t / KB16, cb = t % KB16;
-        mma_nt_k<BVB>(aQh[i], sDO + 16 * R * LDB, LDB, sS0 + 16 * cb * LDB, LDB);
-        mma_nt_k<BVB>(aKb[i], sU + 16 * R * LDB, LDB, sDS + 16 * cb * LDB, LDB);
-        mma_nt_k<BVB>(aW[i], sDU + 16 * R * LDB, LDB, sS0 + 16 * cb * LDB, LDB);
+        const int row = 16 * (t / KB16) + lr;
+        const RhsT2 xo = do_rows(row, c0), xu = lds_rows(sU, row, c0), xdu = lds_rows(sDU, row, c0);
+        kmma(aQh[i], xo, bS[st]);
+        kmma(aW[i], xdu, bS[st]);
+        kmma(aKb[i], xu, bD[st]);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int t = wid + NW * i;
       if (t < Cfg::NCT) {
-        const int R = t / NB, I = t % NB;
-        mma_nt_k<BVB>(aP[i], sDO + 16 * R * LDB, LDB, sU + 16 * I * LDB, LDB);
-        mma_nt_k<BVB>(aT[i], sDU + 16 * R * LDB, LDB, sWV + 16 * I * LDB, LDB);
+        const int row = 16 * (t / NB) + lr, col = 16 * (t % NB) + lr;
+        kmma(aP[i], do_rows(row, c0), lds_rows(sU, col, c0));
+        kmma(aT[i], lds_rows(sDU, row, c0), wv_rows(col, c0));
       }
     }
   }
 #pragma unroll
-  for (int p = 0; p < SPASS; ++p) {
-    float part = rs[p];
+  for (int i = 0; i < KPW; ++i) {
+    const int t = wid + NW * i;
 #pragma unroll
-    for (int off = 1; off < ST4; off <<= 1) part += __shfl_xor(part, off);
-    const int c = st_c + p * SROWS;
-    if (st_j4 == 0 && c < DK) sEx[c] = part;
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = t < Cfg::NKT && 16 * (t / KB16) + 4 * lg + e < Lr;
+      pq[i].mask(e, ok);
+      pk[i].mask(e, ok);
+      pb[i].mask(e, ok);
+    }
   }
+  rsum += __shfl_xor(rsum, 16);
+  rsum += __shfl_xor(rsum, 32);
+  if (rs_owner && lg == 0) sEx[16 * cb0 + lr] = rsum;
   __syncthreads();
 
   // ---- phase A: dT, dKh, dA ----
@@ -972,94 +818,24 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 // =============================================================================
 // dispatch
 // =============================================================================
-static int pick_bv_bwd(int B, int H, int Dv, bool f32) {
-  const int maxbv = f32 ? 32 : 64;
-  int bv = Dv < maxbv ? Dv : maxbv;
-  while (bv > 16 && (long)B * H * (Dv / bv) < 256) bv /= 2;
-  return bv;
-}
-
-template <int DK, int C, int BV, bool F32IN>
-static hipError_t launch_dstate_t(const BwdArgs& a, hipStream_t s) {
-  if constexpr (!DstCfg<DK, C, BV, F32IN>::kFits) {
-    return hipErrorInvalidConfiguration;
-  } else {
-    const int nv = a.Dv / BV, nbh = a.B * a.H;
-    hipLaunchKernelGGL((gdn2_bwd_dstate_kernel<DK, C, BV, F32IN>), dim3(((nbh + 7) / 8) * 8 * nv),
-                       dim3(kDstThreads), 0, s, a);
-    return hipGetLastError();
-  }
-}
-
-template <int DK, int C, int BVB, bool F32IN>
+template <int DK, int C, bool F32IN>
 static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
-  if constexpr (!GradCfg<DK, C, BVB, F32IN>::kFits) {
+  if constexpr (!GradCfg<DK, C, F32IN>::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
+    if (a.records == nullptr) return hipErrorInvalidValue;
     const int NC = (a.T + C - 1) / C;
-    if (a.records)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, BVB, F32IN, true>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, BVB, F32IN, false>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
     return hipGetLastError();
   }
-}
-
-// value tile of the gradient kernel's inner loop: 32 (16 for fp32 inputs), never wider than Dv
-template <int DK, int C, bool F32IN>
-static hipError_t launch_grad(const BwdArgs& a, hipStream_t s) {
-  if (F32IN || a.Dv == 16) return launch_grad_t<DK, C, 16, F32IN>(a, s);
-  if constexpr (F32IN) return hipErrorInvalidValue;
-  else return launch_grad_t<DK, C, 32, F32IN>(a, s);
-}
-
-template <int DK, int C, bool F32IN>
-static hipError_t launch_bwd_c(const BwdArgs& a, hipStream_t s) {
-  hipError_t e;
-  switch (pick_bv_bwd(a.B, a.H, a.Dv, F32IN)) {
-    case 16: e = launch_dstate_t<DK, C, 16, F32IN>(a, s); break;
-    case 32: e = launch_dstate_t<DK, C, 32, F32IN>(a, s); break;
-    case 64:
-      if constexpr (F32IN) e = hipErrorInvalidValue;
-      else e = launch_dstate_t<DK, C, 64, F32IN>(a, s);
-      break;
-    default: e = hipErrorInvalidValue;
-  }
-  if (e != hipSuccess) return e;
-  return launch_grad<DK, C, F32IN>(a, s);
-}
-
-template <int DK, bool F32IN>
-static hipError_t launch_bwd_dk(const BwdArgs& a, hipStream_t s) {
-  switch (a.chunk) {
-    case 16: return launch_bwd_c<DK, 16, F32IN>(a, s);
-    case 32: return launch_bwd_c<DK, 32, F32IN>(a, s);
-    case 64: return launch_bwd_c<DK, 64, F32IN>(a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <bool F32IN>
-static hipError_t launch_bwd_f(const BwdArgs& a, hipStream_t s) {
-  switch (a.Dk) {
-    case 16: return launch_bwd_dk<16, F32IN>(a, s);
-    case 32: return launch_bwd_dk<32, F32IN>(a, s);
-    case 64: return launch_bwd_dk<64, F32IN>(a, s);
-    case 128: return launch_bwd_dk<128, F32IN>(a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  return a.f32_inputs ? launch_bwd_f<true>(a, stream) : launch_bwd_f<false>(a, stream);
 }
 
 template <int DK, bool F32IN>
 static hipError_t launch_grad_dk(const BwdArgs& a, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_grad<DK, 16, F32IN>(a, s);
-    case 32: return launch_grad<DK, 32, F32IN>(a, s);
-    case 64: return launch_grad<DK, 64, F32IN>(a, s);
+    case 16: return launch_grad_t<DK, 16, F32IN>(a, s);
+    case 32: return launch_grad_t<DK, 32, F32IN>(a, s);
+    case 64: return launch_grad_t<DK, 64, F32IN>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1079,19 +855,12 @@ hipError_t launch_bwd_grad(const BwdArgs& a, hipStream_t stream) {
   return a.f32_inputs ? launch_grad_f<true>(a, stream) : launch_grad_f<false>(a, stream);
 }
 
-template <int DK, int C, bool F32IN>
-static bool bwd_fits() {
-  return GradCfg<DK, C, 16, F32IN>::kFits && (F32IN || GradCfg<DK, C, 32, F32IN>::kFits) &&
-         DstCfg<DK, C, 16, F32IN>::kFits && DstCfg<DK, C, 32, F32IN>::kFits &&
-         (F32IN || DstCfg<DK, C, 64, F32IN>::kFits);
-}
-
 template <int DK, bool F32IN>
 static bool grad_fits_c(int chunk) {
   switch (chunk) {
-    case 16: return GradCfg<DK, 16, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 16, 32, F32IN>::kFits);
-    case 32: return GradCfg<DK, 32, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 32, 32, F32IN>::kFits);
-    case 64: return GradCfg<DK, 64, 16, F32IN>::kFits && (F32IN || GradCfg<DK, 64, 32, F32IN>::kFits);
+    case 16: return GradCfg<DK, 16, F32IN>::kFits;
+    case 32: return GradCfg<DK, 32, F32IN>::kFits;
+    case 64: return GradCfg<DK, 64, F32IN>::kFits;
   }
   return false;
 }
@@ -1102,27 +871,6 @@ bool grad_supported(int Dk, int chunk, bool f32) {
     case 32: return f32 ? grad_fits_c<32, true>(chunk) : grad_fits_c<32, false>(chunk);
     case 64: return f32 ? grad_fits_c<64, true>(chunk) : grad_fits_c<64, false>(chunk);
     case 128: return f32 ? grad_fits_c<128, true>(chunk) : grad_fits_c<128, false>(chunk);
-  }
-  return false;
-}
-
-template <int DK, bool F32IN>
-static bool bwd_fits_c(int chunk) {
-  switch (chunk) {
-    case 16: return bwd_fits<DK, 16, F32IN>();
-    case 32: return bwd_fits<DK, 32, F32IN>();
-    case 64: return bwd_fits<DK, 64, F32IN>();
-  }
-  return false;
-}
-
-bool bwd_supported(int Dk, int Dv, int chunk, bool f32_inputs) {
-  (void)Dv;
-  switch (Dk) {
-    case 16: return f32_inputs ? bwd_fits_c<16, true>(chunk) : bwd_fits_c<16, false>(chunk);
-    case 32: return f32_inputs ? bwd_fits_c<32, true>(chunk) : bwd_fits_c<32, false>(chunk);
-    case 64: return f32_inputs ? bwd_fits_c<64, true>(chunk) : bwd_fits_c<64, false>(chunk);
-    case 128: return f32_inputs ? bwd_fits_c<128, true>(chunk) : bwd_fits_c<128, false>(chunk);
   }
   return false;
 }

@@ -328,13 +328,9 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
 #pragma unroll
         for (int j = 0; j < NDE; ++j) {
           const int t = F32IN ? 16 * u + 4 * lg + j : KU * u + F::kslot(lg, j);
-          RawT x = 0;
-          if (t < Ln) {
-            const int64_t idx = baseV + (int64_t)(tn + t) * rowV + 16 * c + lr;
-            if constexpr (F32IN) x = static_cast<const float*>(a.dO)[idx];
-            else x = static_cast<const uint16_t*>(a.dO)[idx];
-          }
-          rdo[u][c][j] = x;
+          const int64_t idx = baseV + (int64_t)(tn + t) * rowV + 16 * c + lr;
+          const int64_t safe = baseV + (int64_t)tn * rowV + 16 * c + lr;  // the chunk's first row
+          rdo[u][c][j] = ld_sel(static_cast<const RawT*>(a.dO), idx, safe, t < Ln);
         }
   };
 

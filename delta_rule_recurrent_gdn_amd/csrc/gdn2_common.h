@@ -85,10 +85,27 @@ __device__ __forceinline__ void load4(const void* base, int64_t idx, float (&out
   }
 }
 
+// Guarded element load without a branch: reads element idx when ok, else the
+// always-valid element safe, and returns zero when not ok. A run of these stays
+// in flight together (a load inside an if-block makes the compiler wait for it
+// at the end of the block).
+template <typename T>
+__device__ __forceinline__ T ld_sel(const T* p, int64_t idx, int64_t safe, bool ok) {
+  const T v = p[ok ? idx : safe];
+  return ok ? v : T(0);
+}
+
 template <bool F32IN>
 __device__ __forceinline__ float load1(const void* base, int64_t idx) {
   if constexpr (F32IN) return static_cast<const float*>(base)[idx];
   else return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+
+// load1 with ld_sel's guard: zero when !ok, reading the always-valid element safe.
+template <bool F32IN>
+__device__ __forceinline__ float load1_sel(const void* base, int64_t idx, int64_t safe, bool ok) {
+  if constexpr (F32IN) return ld_sel(static_cast<const float*>(base), idx, safe, ok);
+  else return bf16_bits_to_f32(ld_sel(static_cast<const uint16_t*>(base), idx, safe, ok));
 }
 
 // Raw register copies of 4 / 8 consecutive inputs in their storage type, so a

@@ -42,7 +42,8 @@ struct Frag {
 // Forward (DIR = 0):  Wn = -W [C x DK], Qs = q exp(g) [C x DK],
 //                     KbT = (k exp(g_C - g))^T [DK x C], P [C x C].
 // Backward (DIR = 1): PT = P^T [C x C], Kb [C x DK], QsT [DK x C], WnT = -W^T [DK x C],
-//                     T = (I + A)^-1 [C x C] (for the per-chunk gradient kernel).
+//                     T = (I + A)^-1 [C x C] and Kh = b k exp(g) [C x DK] (for the
+//                     per-chunk gradient kernel).
 template <int DK, int C, bool F32IN, int DIR>
 struct Record {
   using F = Frag<F32IN>;
@@ -54,7 +55,8 @@ struct Record {
   static constexpr int u2 = u1 + (DIR == 0 ? RC * UK : RC * UK);
   static constexpr int u3 = u2 + (DIR == 0 ? RK * UC : RK * UC);
   static constexpr int u4 = u3 + (DIR == 0 ? RC * UC : RK * UC);
-  static constexpr int uG = u4 + (DIR == 0 ? 0 : RC * UC);
+  static constexpr int u5 = u4 + (DIR == 0 ? 0 : RC * UC);
+  static constexpr int uG = u5 + (DIR == 0 ? 0 : RC * UK);
   static constexpr int kUnits = uG + 1;
   static constexpr int kBytes = kUnits * F::kUnitBytes;
   static_assert(DK * 4 <= 1024, "exp(g_C) must fit one unit");
@@ -164,6 +166,16 @@ __device__ __forceinline__ void unit_mma(f32x4& acc, const uint4& a, const f32x4
   acc = mfma16x16x4(__uint_as_float(a.y), b[1], acc);
   acc = mfma16x16x4(__uint_as_float(a.z), b[2], acc);
   acc = mfma16x16x4(__uint_as_float(a.w), b[3], acc);
+}
+
+// acc + x y^T over four contraction indices per lane group, fp32 operands
+// (both taken in the same lane-slot order).
+__device__ __forceinline__ f32x4 unit_mma_ff(f32x4 acc, const f32x4& x, const f32x4& y) {
+  acc = mfma16x16x4(x[0], y[0], acc);
+  acc = mfma16x16x4(x[1], y[1], acc);
+  acc = mfma16x16x4(x[2], y[2], acc);
+  acc = mfma16x16x4(x[3], y[3], acc);
+  return acc;
 }
 
 }  // namespace gdn2

@@ -61,7 +61,6 @@ struct BwdArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Two-stage forward: chunk-parallel records, then the sequential chain.
 // rec: B*H*NC records of fwd_record_bytes(); ut: B*H*NC*C*Dv floats.
@@ -83,6 +82,5 @@ bool grad_supported(int Dk, int chunk, bool f32_inputs);
 
 // Shapes with a compiled kernel (checked by the C ABI before launching).
 bool fwd_supported(int Dk, int Dv, int chunk, bool f32_inputs);
-bool bwd_supported(int Dk, int Dv, int chunk, bool f32_inputs);
 
 }  // namespace gdn2

@@ -232,15 +232,27 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
         const float* cm = DIR == 0 ? kb : qs;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(cm[i]);
-        char* dst = rec + Rec::u1 * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
-        if constexpr (F32IN) {
-          *reinterpret_cast<float4*>(dst) = make_float4(tm[0], tm[1], tm[2], tm[3]);
-        } else {
-          f16x4 hv;
+        auto put = [&](int ubase, const float (&x)[4]) {
+          char* dst = rec + ubase * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
+          if constexpr (F32IN) {
+            *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+          } else {
+            f16x4 hv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(tm[i]);
-          *reinterpret_cast<f16x4*>(dst) = hv;
-          if (DK < 32) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);  // unit wider than Dk
+            for (int i = 0; i < 4; ++i) hv[i] = static_cast<_Float16>(x[i]);
+            *reinterpret_cast<f16x4*>(dst) = hv;
+            if (DK < 32) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);  // unit wider than Dk
+          }
+        };
+        float tmv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmv[i] = tm[i];
+        put(Rec::u1, tmv);
+        if constexpr (DIR == 1) {  // b k exp(g) for the gradient kernel
+          float kh[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kh[i] = khm[i] * egm[i];
+          put(Rec::u5, kh);
         }
       }
       if constexpr (F32IN) {
