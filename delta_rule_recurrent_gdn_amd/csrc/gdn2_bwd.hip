@@ -413,24 +413,6 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   for (int i = 0; i < KPW; ++i) aQh[i] = aKb[i] = aW[i] = zero4();
 #pragma unroll
   for (int i = 0; i < CPW; ++i) aP[i] = aT[i] = zero4();
-  // q, k, b at the lane's C x DK positions (for the chain rule after the key
-  // phase): raw loads now, zeroed past the sequence once the key phase is done
-  Vals4<F32IN> pq[KPW], pk[KPW], pb[KPW];
-#pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    const int t = wid + NW * i;
-    const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * R + 4 * lg + e;
-      const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
-      const int64_t safe = baseK + (int64_t)t0 * rowK + (c < DK ? c : 0);  // row 0 of the chunk always exists
-      const bool ok = t < Cfg::NKT && r < Lr;
-      pq[i].set(e, a.q, idx, safe, ok);
-      pk[i].set(e, a.k, idx, safe, ok);
-      pb[i].set(e, a.b, idx, safe, ok);
-    }
-  }
   // right operands: rows of S0 and dS of this wave's key-channel block, all
   // steps fetched at once; rowsum(S0 * dS) of those channels on the way
   constexpr int KV = F32IN ? 16 : 32;          // value columns per key-phase step
@@ -469,6 +451,25 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         bD[st][j] = static_cast<OpT>(xd[j]);
         rsum += xs[j] * xd[j];
       }
+    }
+  }
+  // q, k, b at the lane's C x DK positions (for the chain rule after the key
+  // phase): raw loads issued after the key-phase operands, so those arrive
+  // first; zeroed past the sequence once the key phase is done
+  Vals4<F32IN> pq[KPW], pk[KPW], pb[KPW];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int t = wid + NW * i;
+    const int R = t / KB16, cb = t % KB16, c = 16 * cb + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * R + 4 * lg + e;
+      const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
+      const int64_t safe = baseK + (int64_t)t0 * rowK + (c < DK ? c : 0);  // row 0 of the chunk always exists
+      const bool ok = t < Cfg::NKT && r < Lr;
+      pq[i].set(e, a.q, idx, safe, ok);
+      pk[i].set(e, a.k, idx, safe, ok);
+      pb[i].set(e, a.b, idx, safe, ok);
     }
   }
   auto lds_rows = [&](const OpT* X, int row, int c0) -> RhsT2 {

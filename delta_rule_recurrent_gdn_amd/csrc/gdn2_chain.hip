@@ -280,10 +280,11 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
   using F = Frag<F32IN>;
   constexpr int RC = C / 16, RK = DK / 16, UK = Rec::UK, UC = Rec::UC;
   constexpr int KU = F::KU;
-  constexpr int NBUF = 2 * Rec::kBytes <= 160 * 1024 ? 2 : 1;
+  constexpr int kBuf = Rec::kChainBytes;  // the chain's prefix of each record
+  constexpr int NBUF = 2 * kBuf <= 160 * 1024 ? 2 : 1;
   constexpr int kCols = 16 * NCT * NWV;
 
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * Rec::kBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kBuf];
 
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
@@ -334,16 +335,16 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
         }
   };
 
-  dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * Rec::kBytes : 0),
-            Rec::kUnits, wid, NWV);
+  dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * kBuf : 0),
+            Rec::kChainUnits, wid, NWV);
   load_do(NC - 1);
 
   for (int n = NC - 1; n >= 0; --n) {
-    char* buf = smem + (NBUF == 2 ? (n & 1) * Rec::kBytes : 0);
+    char* buf = smem + (NBUF == 2 ? (n & 1) * kBuf : 0);
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n+1
     if (NBUF == 2 && n > 0)
-      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * Rec::kBytes, Rec::kUnits, wid, NWV);
+      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * kBuf, Rec::kChainUnits, wid, NWV);
 
     {
       float* ws = a.dS_chunks + ((int64_t)bh * NC + n) * DK * Dv + j0;
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
 
     if (NBUF == 1 && n > 0) {
       __syncthreads();  // every wave is done reading the single buffer
-      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
+      dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem, Rec::kChainUnits, wid, NWV);
     }
   }
 
@@ -546,7 +547,7 @@ hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, 
 template <int DK, int C, bool F32IN, int NCT, int NWV>
 static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStream_t s) {
   using Rec = Record<DK, C, F32IN, 1>;
-  if constexpr (Rec::kBytes > 160 * 1024) {
+  if constexpr (Rec::kChainBytes > 160 * 1024) {
     return hipErrorInvalidConfiguration;
   } else {
     const int ncg = a.Dv / (16 * NCT * NWV);

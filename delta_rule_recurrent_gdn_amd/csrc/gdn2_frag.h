@@ -18,7 +18,8 @@
 //
 // Record. The chunk-parallel kernels store, per (batch*head, chunk), the left
 // operands the chain needs as consecutive units (row tile major, then unit),
-// followed by one unit holding exp(g_C) per key channel.
+// followed by one unit holding exp(g_C) per key channel (and, in the backward
+// record, the operands of the per-chunk gradient kernel).
 #pragma once
 
 #include "gdn2_common.h"
@@ -38,12 +39,13 @@ struct Frag {
   static constexpr int units(int K) { return (K + KU - 1) / KU; }
 };
 
-// Per-chunk record: matrices in units, then the exp(g_C) unit.
+// Per-chunk record: matrices in units and the exp(g_C) unit.
 // Forward (DIR = 0):  Wn = -W [C x DK], Qs = q exp(g) [C x DK],
-//                     KbT = (k exp(g_C - g))^T [DK x C], P [C x C].
+//                     KbT = (k exp(g_C - g))^T [DK x C], P [C x C], then exp(g_C).
 // Backward (DIR = 1): PT = P^T [C x C], Kb [C x DK], QsT [DK x C], WnT = -W^T [DK x C],
-//                     T = (I + A)^-1 [C x C] and Kh = b k exp(g) [C x DK] (for the
-//                     per-chunk gradient kernel).
+//                     exp(g_C), then T = (I + A)^-1 [C x C] and Kh = b k exp(g) [C x DK].
+// The sequential chains read only the leading kChainUnits units (T and Kh are
+// for the per-chunk gradient kernel), so they copy a contiguous prefix.
 template <int DK, int C, bool F32IN, int DIR>
 struct Record {
   using F = Frag<F32IN>;
@@ -52,13 +54,15 @@ struct Record {
   // unit offsets of the matrices
   static constexpr int u0 = 0;
   static constexpr int u1 = u0 + (DIR == 0 ? RC * UK : RC * UC);
-  static constexpr int u2 = u1 + (DIR == 0 ? RC * UK : RC * UK);
-  static constexpr int u3 = u2 + (DIR == 0 ? RK * UC : RK * UC);
-  static constexpr int u4 = u3 + (DIR == 0 ? RC * UC : RK * UC);
-  static constexpr int u5 = u4 + (DIR == 0 ? 0 : RC * UC);
-  static constexpr int uG = u5 + (DIR == 0 ? 0 : RC * UK);
-  static constexpr int kUnits = uG + 1;
+  static constexpr int u2 = u1 + RC * UK;
+  static constexpr int u3 = u2 + RK * UC;
+  static constexpr int uG = u3 + (DIR == 0 ? RC * UC : RK * UC);
+  static constexpr int kChainUnits = uG + 1;
+  static constexpr int u4 = kChainUnits;           // DIR 1 only
+  static constexpr int u5 = u4 + RC * UC;          // DIR 1 only
+  static constexpr int kUnits = DIR == 0 ? kChainUnits : u5 + RC * UK;
   static constexpr int kBytes = kUnits * F::kUnitBytes;
+  static constexpr int kChainBytes = kChainUnits * F::kUnitBytes;
   static_assert(DK * 4 <= 1024, "exp(g_C) must fit one unit");
 };
 
