@@ -57,6 +57,36 @@ def decode_bytes(B, H, d, e_in=2):
     return B * H * (2 * 4 * d * d + 5 * d * e_in + 4 * d + 4 * d)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gdn2_fwd_bwd_B8H16T4096_hbm_traffic.md")
+
+
+def kernel_sources_sha256():
+    """sha256 over the HIP sources (name and bytes of every .hip / .h file, sorted by name)."""
+    import hashlib
+
+    d = os.path.join(ROOT, "delta_rule_recurrent_gdn_amd", "csrc")
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".h")):
+            with open(os.path.join(d, n), "rb") as f:
+                h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary (scaled by the
+    copy calibration there), or None when the kernel sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line and " " not in
+                      line.split(": ", 1)[0])
+    except OSError:
+        return None
+    if kv.get("sources_sha256", "").strip() != kernel_sources_sha256() or key not in kv:
+        return None
+    return int(kv[key].strip())
+
+
 def _oracle_worker(args):
     """One (batch row, head) slice of the workload through the float64 oracle (fwd + bwd)."""
     from threadpoolctl import threadpool_limits
@@ -102,6 +132,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--curve", action="store_true", help="also time the long-sequence forward, T = 8K..64K")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the operator runs on a single MI355X; "
@@ -109,6 +142,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 28  # fp32 elements: 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "copies": 3}), flush=True)
+        return
 
     import synth
     from delta_rule_recurrent_gdn_amd import _lib, gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked
@@ -189,14 +233,16 @@ def main():
     # dominant launch: the entry-point call with the larger share of the step
     # (each call is its kernels back to back on one stream)
     if t_fwd >= t_bwd:
+        tkey = "fwd_launch_traffic_bytes"
         dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked launch (gdn2_prep_kernel forward records + gdn2_chain_fwd_kernel, "
                                      "chunk states saved)", t_fwd, by_f, F_f)
     else:
+        tkey = "bwd_launch_traffic_bytes"
         dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_prep_kernel backward records + "
                                      "gdn2_chain_bwd_kernel + gdn2_bwd_grad_kernel)", t_bwd, by_b, F_b)
     achieved = by_dom / (t_dom / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(tkey), "kernel": dom,
                 "algorithmic_bytes_per_launch": int(by_dom), "avg_launch_ms": round(t_dom, 4)}
     mfma = (F_f + F_b) / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
 
