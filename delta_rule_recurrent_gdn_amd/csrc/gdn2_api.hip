@@ -74,12 +74,28 @@ size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   return bwd_plan(B, T, H, Dk, Dv, chunk, f32).need;
 }
 
-// Two-stage forward workspace: records, then T (w*v) for every chunk; 0 when
-// the chunk-parallel kernel does not cover the sizes.
+// Two-stage forward workspace: records, then T (w*v) for every chunk, then
+// (256-byte aligned) the segment maps and entry states of the two-level chain
+// when it is used for the sizes; 0 when the chunk-parallel kernel does not
+// cover the sizes.
+size_t fwd_seg_offset(int B, int T, int H, int Dv, int Dk, int chunk, bool f32) {
+  const size_t nchunks = (size_t)B * H * ((T + chunk - 1) / chunk);
+  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+  return (base + 255) & ~(size_t)255;
+}
+
 size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   if (!gdn2::prep_fwd_supported(Dk, chunk, f32)) return 0;
   const size_t nchunks = (size_t)B * H * ((T + chunk - 1) / chunk);
-  return nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+  const size_t sb = gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk);
+  return sb ? fwd_seg_offset(B, T, H, Dv, Dk, chunk, f32) + sb : base;
+}
+
+// the two-level chain's buffers inside a forward workspace (or records region), or null
+char* fwd_seg_ptr(char* ws, int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  if (gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk) == 0) return nullptr;
+  return ws + fwd_seg_offset(B, T, H, Dv, Dk, chunk, f32);
 }
 
 }  // namespace
@@ -164,7 +180,8 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
                                                  gdn2::fwd_record_bytes(Dk, chunk, dt == GDN2_F32));
   st = hip_status(gdn2::launch_prep_fwd(a, rec, ut, s));
   if (st != GDN2_OK) return st;
-  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, s));
+  return hip_status(
+      gdn2::launch_chain_fwd(a, rec, ut, fwd_seg_ptr(rec, B, T, H, Dk, Dv, chunk, dt == GDN2_F32), s));
 }
 
 int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
@@ -219,7 +236,8 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
       float* ut = reinterpret_cast<float*>(rec + (size_t)B * H * ((T + chunk - 1) / chunk) *
                                                      gdn2::fwd_record_bytes(Dk, chunk, f32));
       st = hip_status(gdn2::launch_prep_fwd(f, rec, ut, s));
-      if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, s));
+      if (st == GDN2_OK)
+        st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, fwd_seg_ptr(rec, B, T, H, Dk, Dv, chunk, f32), s));
     }
     if (st != GDN2_OK) return st;
   }

@@ -14,6 +14,17 @@
 // waves; the only shared data are the record's left operands, copied once per
 // chunk from the workspace into LDS by direct-to-LDS loads, double-buffered so
 // that chunk n+1 is in flight while chunk n is computed.
+//
+// Segmented (two-level) form, for few (batch, head) pairs and long sequences:
+// the chunk map is affine in the entry state, S_out = M S_in + N with
+// M = prod (Diag(gamma) - Kb^T W) and N the exit state from a zero entry. A
+// head's chunks are cut into segments of L chunks; (1) every segment runs the
+// chain from a zero state on its value columns (-> N) and on DK identity
+// columns with no input (-> M), all segments in parallel; (2) a short
+// sequential pass composes S_in(s+1) = M_s S_in(s) + N_s in fp32; (3) every
+// segment runs again from its true entry state and writes o, the chunk entry
+// states and the final state. Same arithmetic per chunk; the sequential depth
+// drops from NC chunks to about 2L + NC/L.
 
 #include "gdn2_frag.h"
 #include "gdn2_internal.h"
@@ -46,9 +57,9 @@ __device__ __forceinline__ void dma_units(const char* src, char* dst, int units,
 // vmcnt = 0, expcnt and lgkmcnt unconstrained)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DK, int C, bool F32IN, int NCT, int NWV>
+template <int DK, int C, bool F32IN, int NCT, int NWV, bool SEG>
 __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, const char* rec_base,
-                                                                 const float* ut_base) {
+                                                                 const float* ut_base, SegArgs sg) {
   using Cfg = ChainCfg<DK, C, F32IN, NCT, NWV>;
   using Rec = typename Cfg::Rec;
   using F = Frag<F32IN>;
@@ -60,16 +71,34 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
 
-  // block -> (batch*head, column group); the column groups of one head share an XCD
   const int Dv = a.Dv, T = a.T, H = a.H;
-  const int ncg = Dv / Cfg::kCols;
   const int nbh = a.B * H;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int bh = (slot / ncg) * 8 + xcd, cg = slot % ncg;
-  if (bh >= nbh) return;
-  const int bi = bh / H, h = bh - bi * H;
   const int NC = (T + C - 1) / C;
+  int bh, cg, seg = 0, n_begin = 0, n_end = NC;
+  if constexpr (SEG) {
+    // block -> (batch*head, segment, column group); the columns are the value
+    // columns, followed in the map pass by DK identity columns
+    const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
+    const int ncg = ((sg.mode == kSegMap ? Dv + DK : Dv) + Cfg::kCols - 1) / Cfg::kCols;
+    const int item = blockIdx.x / ncg;
+    cg = blockIdx.x - item * ncg;
+    bh = item / nsb;
+    seg = item - bh * nsb;
+    n_begin = seg * sg.seg_len;
+    n_end = min(NC, n_begin + sg.seg_len);
+  } else {
+    // block -> (batch*head, column group); the column groups of one head share an XCD
+    const int ncg = Dv / Cfg::kCols;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bh = (slot / ncg) * 8 + xcd;
+    cg = slot % ncg;
+    if (bh >= nbh) return;
+  }
+  const int bi = bh / H, h = bh - bi * H;
   const int j0 = cg * Cfg::kCols + wid * 16 * NCT;  // first column of this wave
+  // segmented: waves past the columns only copy records; identity columns (j0 >= Dv, map pass) have no input
+  const bool active = !SEG || j0 < (sg.mode == kSegMap ? Dv + DK : Dv);
+  const bool ident = SEG && j0 >= Dv;
   const int64_t rowV = (int64_t)H * Dv;
   const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
   const int64_t stBase = (int64_t)bh * DK * Dv + j0;
@@ -78,15 +107,30 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   const int nvt = Dv / 16, jb0 = j0 / 16;
 
   // state tiles: rows 16*RKt + 4*lg + i, column j0 + 16*c + lr
+  // entry: S0 (or zero); segmented map pass: zero, identity on the identity
+  // columns; segmented run: S0 for the first segment, else the composed entry
+  const float* Sent = a.S0;
+  int64_t sOff = stBase;
+  if constexpr (SEG) {
+    if (sg.mode == kSegMap) {
+      Sent = nullptr;
+    } else if (seg > 0) {
+      Sent = sg.S_in;
+      sOff = ((int64_t)bh * sg.nseg + seg) * DK * Dv + j0;
+    }
+  }
   f32x4 accS[RK][NCT];
 #pragma unroll
   for (int R = 0; R < RK; ++R)
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       accS[R][c] = zero4();
-      if (a.S0) {
+      if (ident) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accS[R][c][i] = a.S0[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
+        for (int i = 0; i < 4; ++i) accS[R][c][i] = (16 * R + 4 * lg + i == j0 - Dv + 16 * c + lr) ? 1.f : 0.f;
+      } else if (Sent && active) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accS[R][c][i] = Sent[sOff + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
       }
     }
 
@@ -101,19 +145,23 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
       }
   };
 
+  // the value columns' outputs: every pass but the segmented map pass
+  const bool outs = !SEG || (sg.mode == kSegRun && active);
+  const bool has_ut = active && !ident;
   f32x4 utn[RC][NCT];
-  dma_units(recs, smem, Rec::kUnits, wid, NWV);
-  load_ut(0, utn);
+  dma_units(recs + (int64_t)n_begin * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
+  if (has_ut) load_ut(n_begin, utn);
 
-  for (int n = 0; n < NC; ++n) {
+  for (int n = n_begin; n < n_end; ++n) {
     const int t0 = n * C, Lr = min(C, T - t0);
-    char* buf = smem + (Cfg::NBUF == 2 ? (n & 1) * Rec::kBytes : 0);
+    char* buf = smem + (Cfg::NBUF == 2 ? ((n - n_begin) & 1) * Rec::kBytes : 0);
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n-1
-    if (Cfg::NBUF == 2 && n + 1 < NC)
-      dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem + ((n + 1) & 1) * Rec::kBytes, Rec::kUnits, wid, NWV);
+    if (Cfg::NBUF == 2 && n + 1 < n_end)
+      dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem + ((n + 1 - n_begin) & 1) * Rec::kBytes, Rec::kUnits,
+                wid, NWV);
 
-    if (a.chunk_states) {
+    if (a.chunk_states && outs) {
       float* cs = a.chunk_states + ((int64_t)bh * NC + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)
@@ -128,10 +176,11 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
     for (int R = 0; R < RC; ++R)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        accU[R][c] = utn[R][c];
+        accU[R][c] = has_ut ? utn[R][c] : zero4();
         accO[R][c] = zero4();
       }
-    if (n + 1 < NC) load_ut(n + 1, utn);
+    if (has_ut && n + 1 < n_end) load_ut(n + 1, utn);
+    if (active) {
 
     const uint4* uW = reinterpret_cast<const uint4*>(buf + Rec::u0 * 1024) + l;
     const uint4* uQ = reinterpret_cast<const uint4*>(buf + Rec::u1 * 1024) + l;
@@ -232,7 +281,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
 
     // ---- o (not written when the caller only wants states) ----
 #pragma unroll
-    for (int R = 0; R < RC && a.o; ++R)
+    for (int R = 0; R < RC && a.o && outs; ++R)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * R + 4 * lg + i;
@@ -242,13 +291,30 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
           for (int c = 0; c < NCT; ++c) op[16 * c] = accO[R][c][i];
         }
       }
+    }  // active
 
-    if (Cfg::NBUF == 1 && n + 1 < NC) {
+    if (Cfg::NBUF == 1 && n + 1 < n_end) {
       __syncthreads();  // every wave is done reading the single buffer
       dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
     }
   }
 
+  if constexpr (SEG) {
+    if (sg.mode == kSegMap && active) {
+      // exit of a zero-entry segment: N (value columns) or M (identity columns)
+      const int64_t sb = (int64_t)bh * sg.nseg + seg;
+      float* dst = ident ? sg.M + sb * DK * DK + (j0 - Dv) : sg.N + sb * DK * Dv + j0;
+      const int ld = ident ? DK : Dv;
+#pragma unroll
+      for (int R = 0; R < RK; ++R)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * R + 4 * lg + i) * ld + 16 * c + lr] = accS[R][c][i];
+      return;
+    }
+    if (seg != sg.nseg - 1 || !active) return;
+  }
   if (a.S_final) {
 #pragma unroll
     for (int R = 0; R < RK; ++R)
@@ -502,15 +568,116 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
     const int ncg = a.Dv / Cfg::kCols;
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * ncg;
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, NCT, NWV>), dim3(grid), dim3(Cfg::kThreads), 0, s, a,
-                       rec, ut);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, NCT, NWV, false>), dim3(grid), dim3(Cfg::kThreads), 0, s,
+                       a, rec, ut, SegArgs{});
+    return hipGetLastError();
+  }
+}
+
+// Composition of the segment maps: S_in(s+1) = M_s S_in(s) + N_s, S_in(0) = S0
+// (or zero), in fp32. One workgroup per (batch*head, 32 value columns); S_in(s)
+// is kept in LDS, M_s is read from global memory one row per thread group.
+template <int DK>
+__global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, SegArgs sg, int nbh, int Dv) {
+  __shared__ float sS[DK][33];
+  const int ncg = Dv / 32;
+  const int bh = blockIdx.x / ncg, j0 = (blockIdx.x - bh * ncg) * 32;
+  const int tid = threadIdx.x, j = tid & 31, rg = tid >> 5;  // 8 row groups
+  constexpr int RPT = DK / 8;                                 // rows per thread
+  for (int e = tid; e < DK * 32; e += 256) {
+    const int d = e >> 5, c = e & 31;
+    sS[d][c] = S0 ? S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
+  }
+  __syncthreads();
+  for (int s = 0; s + 1 < sg.nseg; ++s) {
+    const int64_t sb = (int64_t)bh * sg.nseg + s;
+    const float* M = sg.M + sb * DK * DK;
+    const float* N = sg.N + sb * DK * Dv + j0;
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = N[(int64_t)(rg + 8 * i) * Dv + j];
+    for (int k = 0; k < DK; k += 4) {
+      const float s0 = sS[k][j], s1 = sS[k + 1][j], s2 = sS[k + 2][j], s3 = sS[k + 3][j];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float4 m = *reinterpret_cast<const float4*>(M + (int64_t)(rg + 8 * i) * DK + k);
+        acc[i] += m.x * s0 + m.y * s1 + m.z * s2 + m.w * s3;
+      }
+    }
+    __syncthreads();  // every thread is done reading S_in(s)
+    float* out = sg.S_in + (sb + 1) * DK * Dv + j0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      sS[rg + 8 * i][j] = acc[i];
+      out[(int64_t)(rg + 8 * i) * Dv + j] = acc[i];
+    }
+    __syncthreads();
+  }
+}
+
+// Segment count of the two-level forward: used when the plain chain has too
+// few independent column tiles to fill the GPU (and the sizes suit the
+// compose kernel: Dv >= 32).
+int fwd_segments(int B, int H, int T, int Dk, int Dv, int chunk) {
+  if (Dv < 32) return 1;
+  const int NC = (T + chunk - 1) / chunk;
+  const long nbh = (long)B * H;
+  if (nbh * (Dv / 32) >= 512) return 1;     // enough 32-column wave tiles already
+  long g = 256 / (nbh * ((Dv + 127) / 128)); // about one run-pass workgroup per CU
+  if (g > NC / 8) g = NC / 8;                // at least 8 chunks per segment
+  if (g > 64) g = 64;
+  if (g < 4) return 1;
+  const int L = (NC + (int)g - 1) / (int)g;
+  return (NC + L - 1) / L;                   // segments actually formed
+}
+
+size_t fwd_seg_bytes(int B, int H, int T, int Dk, int Dv, int chunk) {
+  const int G = fwd_segments(B, H, T, Dk, Dv, chunk);
+  if (G <= 1) return 0;
+  const size_t nb = (size_t)B * H * G;
+  return nb * ((size_t)Dk * Dk + 2 * (size_t)Dk * Dv) * sizeof(float);
+}
+
+template <int DK, int C, bool F32IN>
+static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const float* ut, char* seg, int G,
+                                   hipStream_t s) {
+  using Cfg = ChainCfg<DK, C, F32IN, 1, 8>;  // 8 waves of 16 columns
+  if constexpr (!Cfg::kFits) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    const int NC = (a.T + C - 1) / C, nbh = a.B * a.H;
+    SegArgs sg;
+    sg.nseg = G;
+    sg.seg_len = (NC + G - 1) / G;
+    sg.M = reinterpret_cast<float*>(seg);
+    sg.N = sg.M + (size_t)nbh * G * DK * DK;
+    sg.S_in = sg.N + (size_t)nbh * G * DK * a.Dv;
+    // (1) maps of segments 0 .. G-2
+    sg.mode = kSegMap;
+    const int ncg_map = (a.Dv + DK + Cfg::kCols - 1) / Cfg::kCols, ncg_run = (a.Dv + Cfg::kCols - 1) / Cfg::kCols;
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3(nbh * (G - 1) * ncg_map), dim3(512), 0,
+                       s, a, rec, ut, sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // (2) entry states of segments 1 .. G-1
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, sg, nbh, a.Dv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // (3) every segment from its true entry state
+    sg.mode = kSegRun;
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3(nbh * G * ncg_run), dim3(512), 0, s, a,
+                       rec, ut, sg);
     return hipGetLastError();
   }
 }
 
 template <int DK, int C, bool F32IN>
-static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
+static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
   const int nbh = a.B * a.H;
+  {
+    const int G = seg ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
+    if (G > 1) return launch_chain_seg<DK, C, F32IN>(a, rec, ut, seg, G, s);
+  }
   if (a.Dv == 16) return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);
   // 32 columns per wave; as many waves per workgroup as keep >= 256 workgroups
   const int tiles = a.Dv / 32;  // wave tiles per head
@@ -520,28 +687,28 @@ static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float*
 }
 
 template <int DK, bool F32IN>
-static hipError_t launch_chain_k(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
+static hipError_t launch_chain_k(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_chain_c<DK, 16, F32IN>(a, rec, ut, s);
-    case 32: return launch_chain_c<DK, 32, F32IN>(a, rec, ut, s);
-    case 64: return launch_chain_c<DK, 64, F32IN>(a, rec, ut, s);
+    case 16: return launch_chain_c<DK, 16, F32IN>(a, rec, ut, seg, s);
+    case 32: return launch_chain_c<DK, 32, F32IN>(a, rec, ut, seg, s);
+    case 64: return launch_chain_c<DK, 64, F32IN>(a, rec, ut, seg, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool F32IN>
-static hipError_t launch_chain_f(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
+static hipError_t launch_chain_f(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
   switch (a.Dk) {
-    case 16: return launch_chain_k<16, F32IN>(a, rec, ut, s);
-    case 32: return launch_chain_k<32, F32IN>(a, rec, ut, s);
-    case 64: return launch_chain_k<64, F32IN>(a, rec, ut, s);
-    case 128: return launch_chain_k<128, F32IN>(a, rec, ut, s);
+    case 16: return launch_chain_k<16, F32IN>(a, rec, ut, seg, s);
+    case 32: return launch_chain_k<32, F32IN>(a, rec, ut, seg, s);
+    case 64: return launch_chain_k<64, F32IN>(a, rec, ut, seg, s);
+    case 128: return launch_chain_k<128, F32IN>(a, rec, ut, seg, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
-  return a.f32_inputs ? launch_chain_f<true>(a, rec, ut, s) : launch_chain_f<false>(a, rec, ut, s);
+hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
+  return a.f32_inputs ? launch_chain_f<true>(a, rec, ut, seg, s) : launch_chain_f<false>(a, rec, ut, seg, s);
 }
 
 template <int DK, int C, bool F32IN, int NCT, int NWV>

@@ -36,6 +36,18 @@ struct FwdArgs {
   bool f32_inputs;
 };
 
+// Segmented (two-level) forward chain: the pass and its buffers.
+constexpr int kSegMap = 1;  // zero-entry segments -> M (identity columns) and N (value columns)
+constexpr int kSegRun = 2;  // segments from their true entry states -> o, chunk states, S_final
+struct SegArgs {
+  int nseg = 0;             // segments per (batch, head)
+  int seg_len = 0;          // chunks per segment (the last one may be shorter)
+  int mode = 0;
+  float* M = nullptr;       // [B*H][nseg][Dk][Dk]
+  float* N = nullptr;       // [B*H][nseg][Dk][Dv]
+  float* S_in = nullptr;    // [B*H][nseg][Dk][Dv]: entry state of segment s (s >= 1)
+};
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -65,7 +77,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Two-stage forward: chunk-parallel records, then the sequential chain.
 // rec: B*H*NC records of fwd_record_bytes(); ut: B*H*NC*C*Dv floats.
 hipError_t launch_prep_fwd(const FwdArgs& a, char* rec, float* ut, hipStream_t stream);
-hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, hipStream_t stream);
+// seg: nullable buffer of fwd_seg_bytes() bytes; used (two-level chain) when
+// fwd_segments() > 1 for the sizes.
+hipError_t launch_chain_fwd(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t stream);
+int fwd_segments(int B, int H, int T, int Dk, int Dv, int chunk);
+size_t fwd_seg_bytes(int B, int H, int T, int Dk, int Dv, int chunk);
 bool prep_fwd_supported(int Dk, int chunk, bool f32_inputs);
 size_t fwd_record_bytes(int Dk, int chunk, bool f32_inputs);
 // dir 0: forward record, 1: backward record (gdn2_frag.h)

@@ -183,3 +183,54 @@ def test_two_stage_matches_single_pass(Dk, Dv, C, dtype):
     bar = 1e-5 if dtype == "fp32" else 4e-3
     for x, y in zip(a, b):
         assert rel_err(f64(x), f64(y)) < bar
+
+
+# Shapes where the two-stage forward takes the two-level (segmented) chain: few (batch, head) pairs and
+# at least 32 chunks. The segment maps, their fp32 composition and the re-run from the composed entry
+# states must reproduce the stepwise recurrence like the plain chain does.
+SEGMENTED = [
+    # B, H, T, Dk, Dv, C, dtype
+    (1, 2, 33 * 16 + 5, 32, 32, 16, "fp32"),     # 34 chunks, ragged tail, 4 segments
+    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # config-shaped heads, 5 segments
+    (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16: 16 identity columns after 64 value columns
+    (1, 2, 48 * 32 + 31, 128, 32, 32, "bf16"),   # map pass of 160 columns: two column groups
+    (1, 1, 36 * 32, 64, 128, 32, "fp32"),
+]
+
+
+@pytest.mark.parametrize("B,H,T,Dk,Dv,C,dtype", SEGMENTED)
+def test_two_level_chain_matches_oracle(B, H, T, Dk, Dv, C, dtype):
+    lib = _lib.load()
+    code = _lib.GDN2_F32 if dtype == "fp32" else _lib.GDN2_BF16
+    nc = (T + C - 1) // C
+    plain = B * H * nc * (lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, C, 1, Dk, Dv, C, code))
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, Dk, Dv, C, code) > plain  # segment buffers present
+    inp = synth.make_inputs(B, T, H, Dk, Dv, dtype, seed=40 + Dk + Dv + C, s0_std=0.3)
+    o, S, cs = _run(inp, C, states=True)
+    o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
+    tol = tol_for(synth.torch_dtype(dtype))
+    eo, es = rel_err(f64(o), o_ref), rel_err(f64(S), S_ref)
+    print(f"two-level {B}x{H} T={T} Dk={Dk} Dv={Dv} C={C} {dtype}: err o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+    # chunk entry states at a few chunks across segment boundaries
+    cs64 = f64(cs)
+    for n in (1, nc // 3, nc // 2 + 1, nc - 1):
+        sl = {k_: v_[:, :n * C] for k_, v_ in inp.items() if k_ != "S0"}
+        _, ref = oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["b"], sl["w"], inp["S0"])
+        assert rel_err(cs64[:, :, n], ref) <= tol, n
+    # and it agrees with the single-pass kernel (plain chunk order). With 16-bit operands the bar is wider
+    # than for the plain two-stage chain (4e-3, accumulation order only): the two-level chain also rounds
+    # the segment maps' own products (M's identity columns and N feed back as fp16 operands) before the
+    # fp32 composition, so the paths carry separate roundings, each a few 1e-3 of RMS from the oracle.
+    if not (dtype == "fp32" and Dk == 128 and C == 64):
+        b = _run(inp, C, states=True, single=True)
+        bar = 1e-5 if dtype == "fp32" else 1e-2
+        for x, y in zip((o, S, cs), b):
+            assert rel_err(f64(x), f64(y)) < bar
+
+
+def test_two_level_chain_is_deterministic():
+    inp = synth.make_inputs(1, 2000, 4, 128, 128, "bf16", seed=47, s0_std=0.05)
+    o1, S1, c1 = _run(inp, 64, states=True)
+    o2, S2, c2 = _run(inp, 64, states=True)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
