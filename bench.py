@@ -1,6 +1,6 @@
 """Benchmark of the GDN-2 operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--curve]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve]
 
 A step is one training pass of the operator over one batch of synthetic input
 with the pages' layer shape: the chunked forward that also saves the chunk
@@ -8,8 +8,9 @@ entry states, then the gate-aware chunked backward (B=8, H=16, T=4096,
 d_k=d_v=128, chunk 64, bf16 q/k/v/b/w/dO, fp32 log_alpha). W untimed steps,
 then K timed steps between two synchronisations. The one-token decode step
 (B=256 sequences, H=16, d=128, fp32 state, 128 consecutive steps) is timed
-separately and reported under "decode". Inputs are resident in HBM before any
-timed region.
+separately and reported under "decode", and the long-sequence forward (B=1,
+H=16, d=128, T = 8K..64K: few heads, so the two-level chain) under
+"fwd_long_sequence_curve". Inputs are resident in HBM before any timed region.
 
 Prints one JSON line: value = whole-job tokens/s of the forward+backward step,
 plus "roofline" for the dominant kernel (HIP events on the launch stream),
@@ -87,6 +88,16 @@ def measured_traffic(key):
     return int(kv[key].strip())
 
 
+def _segments_from_workspace(lib, _lib, T, D, C, H=16):
+    """Segments of the two-level forward chain at B=1 (1 = the plain chain), read off the workspace size:
+    past the 256-byte aligned records and T (w v), each segment of each head holds M [D x D] and N, S_in
+    [D x D] in fp32."""
+    nc = (T + C - 1) // C
+    base = H * nc * (lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, C, 1, D, D, C, _lib.GDN2_BF16))
+    extra = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, T, H, D, D, C, _lib.GDN2_BF16) - (base + 255) // 256 * 256
+    return max(1, extra // (H * 3 * D * D * 4)) if extra > 0 else 1
+
+
 def _oracle_worker(args):
     """One (batch row, head) slice of the workload through the float64 oracle (fwd + bwd)."""
     from threadpoolctl import threadpool_limits
@@ -131,7 +142,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--curve", action="store_true", help="also time the long-sequence forward, T = 8K..64K")
+    ap.add_argument("--no-curve", action="store_true", help="skip the long-sequence forward curve (T = 8K..64K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -298,7 +309,9 @@ def main():
                          "algorithmic_bytes_per_step": int(byt)}
         del dd, dec, xs, S
 
-    if args.curve:
+    if not args.no_curve:
+        # config 2: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk states) at each T.
+        # Few heads and long sequences: the two-stage forward takes the two-level chain here.
         curve = {}
         for Tc in synth.CONFIGS[2]["T"]:
             ci = synth.config_inputs(2, T=Tc)
@@ -323,7 +336,11 @@ def main():
             a1.record(stream)
             torch.cuda.synchronize()
             ms = a0.elapsed_time(a1) / 3
-            curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1)}
+            byt = fwd_bytes(C, D, save_states=False) * Tc * 16
+            gbs = byt / (ms / 1e3) / 1e9
+            curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1),
+                              "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "segments": _segments_from_workspace(lib, _lib, Tc, D, C)}
             del cd, ci
         out["fwd_long_sequence_curve"] = curve
 

@@ -575,43 +575,87 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
 }
 
 // Composition of the segment maps: S_in(s+1) = M_s S_in(s) + N_s, S_in(0) = S0
-// (or zero), in fp32. One workgroup per (batch*head, 32 value columns); S_in(s)
-// is kept in LDS, M_s is read from global memory one row per thread group.
+// (or zero), in fp32. One workgroup (4 waves) per (batch*head, 32 value
+// columns). S_in(s) lives in LDS; each step copies M_s into LDS with coalesced
+// loads (the next one already in registers) and forms the product on fp32
+// matrix cores, N_s as the initial accumulator: wave w owns row tiles 2w and
+// 2w+1 (times DK / 128) of both 16-column tiles.
 template <int DK>
 __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, SegArgs sg, int nbh, int Dv) {
-  __shared__ float sS[DK][33];
+  constexpr int LDM = DK + 4, LDS_ = 32 + 4;
+  constexpr int NM4 = DK * DK / 4;              // float4 of one M
+  constexpr int MV = (NM4 + 255) / 256;         // per thread
+  constexpr int RT = DK / 16;                   // row tiles
+  constexpr int RPW = (RT + 3) / 4;             // row tiles per wave
+  __shared__ __attribute__((aligned(16))) float sM[DK * LDM];
+  __shared__ __attribute__((aligned(16))) float sS[DK * LDS_];
   const int ncg = Dv / 32;
   const int bh = blockIdx.x / ncg, j0 = (blockIdx.x - bh * ncg) * 32;
-  const int tid = threadIdx.x, j = tid & 31, rg = tid >> 5;  // 8 row groups
-  constexpr int RPT = DK / 8;                                 // rows per thread
+  const int tid = threadIdx.x, wid = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   for (int e = tid; e < DK * 32; e += 256) {
     const int d = e >> 5, c = e & 31;
-    sS[d][c] = S0 ? S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
+    sS[d * LDS_ + c] = S0 ? S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
   }
-  __syncthreads();
+  float4 mr[MV];
+  auto load_m = [&](int s) {
+    const float4* M = reinterpret_cast<const float4*>(sg.M + ((int64_t)bh * sg.nseg + s) * DK * DK);
+#pragma unroll
+    for (int i = 0; i < MV; ++i)
+      if (tid + 256 * i < NM4) mr[i] = M[tid + 256 * i];
+  };
+  if (sg.nseg > 1) load_m(0);
   for (int s = 0; s + 1 < sg.nseg; ++s) {
     const int64_t sb = (int64_t)bh * sg.nseg + s;
-    const float* M = sg.M + sb * DK * DK;
+#pragma unroll
+    for (int i = 0; i < MV; ++i) {
+      const int e = tid + 256 * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
+      if (e < NM4) *reinterpret_cast<float4*>(sM + row * LDM + c4) = mr[i];
+    }
+    __syncthreads();  // M_s and S_in(s) are in LDS
+    if (s + 2 < sg.nseg) load_m(s + 1);
     const float* N = sg.N + sb * DK * Dv + j0;
-    float acc[RPT];
+    f32x4 acc[RPW][2];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) acc[i] = N[(int64_t)(rg + 8 * i) * Dv + j];
-    for (int k = 0; k < DK; k += 4) {
-      const float s0 = sS[k][j], s1 = sS[k + 1][j], s2 = sS[k + 2][j], s3 = sS[k + 3][j];
+    for (int t = 0; t < RPW; ++t) {
+      const int R = wid + 4 * t;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float4 m = *reinterpret_cast<const float4*>(M + (int64_t)(rg + 8 * i) * DK + k);
-        acc[i] += m.x * s0 + m.y * s1 + m.z * s2 + m.w * s3;
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[t][c][i] = R < RT ? N[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < RPW; ++t) {
+      const int R = wid + 4 * t;
+      if (R < RT) {
+        for (int k0 = 0; k0 < DK; k0 += 16) {
+          const float4 a4 = *reinterpret_cast<const float4*>(sM + (16 * R + lr) * LDM + k0 + 4 * lg);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float* srow = sS + (k0 + 4 * lg + m) * LDS_;
+            acc[t][0] = mfma16x16x4(av[m], srow[lr], acc[t][0]);
+            acc[t][1] = mfma16x16x4(av[m], srow[16 + lr], acc[t][1]);
+          }
+        }
       }
     }
-    __syncthreads();  // every thread is done reading S_in(s)
+    __syncthreads();  // every wave is done reading M_s and S_in(s)
     float* out = sg.S_in + (sb + 1) * DK * Dv + j0;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      sS[rg + 8 * i][j] = acc[i];
-      out[(int64_t)(rg + 8 * i) * Dv + j] = acc[i];
+    for (int t = 0; t < RPW; ++t) {
+      const int R = wid + 4 * t;
+      if (R < RT) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 16 * R + 4 * lg + i, col = 16 * c + lr;
+            sS[d * LDS_ + col] = acc[t][c][i];
+            out[(int64_t)d * Dv + col] = acc[t][c][i];
+          }
+      }
     }
-    __syncthreads();
   }
 }
 
