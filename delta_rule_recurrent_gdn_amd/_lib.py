@@ -26,16 +26,24 @@ GDN2_OP_FWD = 0
 GDN2_OP_DECODE = 1
 GDN2_OP_BWD = 2
 
+GDN2_FLAG_RAW_GATES = 1
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
+_U = ctypes.c_uint
 
 # name -> (restype, argtypes), in the order of include/gdn2.h
 SIGNATURES = {
     "gdn2_fwd_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "gdn2_fwd_chunked_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _I, _U,
+                                 _P]),
     "gdn2_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "gdn2_decode_step_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_bwd_chunked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                               _I, _I, _I, _I, _I, _I, _I, _P]),
+    "gdn2_bwd_chunked_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                 _I, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gdn2_status_string": (ctypes.c_char_p, [_I]),
     "gdn2_version": (_I, []),

@@ -11,7 +11,8 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: the _ex entry points (flags)
+constexpr unsigned kKnownFlags = GDN2_FLAG_RAW_GATES;
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
@@ -150,12 +151,13 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
   return 0;
 }
 
-int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                     const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
-                     void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
-                     int dt, void* stream) {
+int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                        const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
+                        void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
+                        int dt, unsigned flags, void* stream) {
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
+  if ((flags & ~kKnownFlags) != 0) return GDN2_ERR_UNSUPPORTED;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   // the two-stage path runs when a workspace is given and covers the sizes
   const bool two_stage = workspace != nullptr && gdn2::prep_fwd_supported(Dk, chunk, dt == GDN2_F32);
@@ -171,6 +173,7 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
   st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
   if (st != GDN2_OK) return st;
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
+  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
   if (!two_stage) return hip_status(gdn2::launch_fwd(a, s));
   const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
   if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
@@ -184,24 +187,42 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
       gdn2::launch_chain_fwd(a, rec, ut, fwd_seg_ptr(rec, B, T, H, Dk, Dv, chunk, dt == GDN2_F32), s));
 }
 
-int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                     const void* w, float* S, float* o, int B, int H, int Dk, int Dv, int dt, void* stream) {
+int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
+                     void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
+                     int dt, void* stream) {
+  return gdn2_fwd_chunked_ex(q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, workspace, workspace_bytes, B,
+                             T, H, Dk, Dv, chunk, dt, 0u, stream);
+}
+
+int gdn2_decode_step_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                        const void* w, float* S, float* o, int B, int H, int Dk, int Dv, int dt, unsigned flags,
+                        void* stream) {
   int st = check_common(B, 1, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
+  if ((flags & ~kKnownFlags) != 0) return GDN2_ERR_UNSUPPORTED;
   if (B == 0 || H == 0) return GDN2_OK;
   st = check_ptrs({q, k, v, log_alpha, b, w, S, o}, {});
   if (st != GDN2_OK) return st;
   gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dt == GDN2_F32};
+  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
   return hip_status(gdn2::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
-int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                     const void* w, const float* S0, const void* dO, const float* dS_final,
-                     const float* chunk_states, float* dq, float* dk, float* dv, float* dlog_alpha, float* db,
-                     float* dw, float* dS0, void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
-                     int Dv, int chunk, int dt, void* stream) {
+int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, float* S, float* o, int B, int H, int Dk, int Dv, int dt, void* stream) {
+  return gdn2_decode_step_ex(q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dt, 0u, stream);
+}
+
+int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                        const void* w, const float* S0, const void* dO, const float* dS_final,
+                        const float* chunk_states, float* dq, float* dk, float* dv, float* dlog_alpha, float* db,
+                        float* dw, float* dS0, void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                        int Dv, int chunk, int dt, unsigned flags, void* stream) {
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
+  if ((flags & ~kKnownFlags) != 0) return GDN2_ERR_UNSUPPORTED;
+  const bool raw = (flags & GDN2_FLAG_RAW_GATES) != 0;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   const bool f32 = dt == GDN2_F32;
   const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
@@ -226,6 +247,7 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   char* rec = ws + 2 * plan.part;
   float* states = const_cast<float*>(chunk_states);
   gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, B, T, H, Dk, Dv, chunk, f32};
+  f.raw_gates = raw;
   if (states == nullptr) {
     states = reinterpret_cast<float*>(ws + plan.part);
     f.chunk_states = states;
@@ -243,11 +265,21 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
                   dS0, B, T, H, Dk, Dv, chunk, f32};
+  a.raw_gates = raw;
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;
+}
+
+int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                     const void* w, const float* S0, const void* dO, const float* dS_final,
+                     const float* chunk_states, float* dq, float* dk, float* dv, float* dlog_alpha, float* db,
+                     float* dw, float* dS0, void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                     int Dv, int chunk, int dt, void* stream) {
+  return gdn2_bwd_chunked_ex(q, k, v, log_alpha, b, w, S0, dO, dS_final, chunk_states, dq, dk, dv, dlog_alpha, db,
+                             dw, dS0, workspace, workspace_bytes, B, T, H, Dk, Dv, chunk, dt, 0u, stream);
 }
 
 }  // extern "C"

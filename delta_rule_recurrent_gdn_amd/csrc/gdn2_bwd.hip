@@ -199,6 +199,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // ---- key-side preparation ----
   KS ks;
   ks.init(tid);
+  ks.raw = a.raw_gates;
   ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
 
@@ -329,6 +330,12 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         vv[R][e] = static_cast<float>(vr[R][e]);
         ww[R][e] = static_cast<float>(wr[R][e]);
       }
+    if (a.raw_gates) {  // w = sigmoid(w_raw) on the sequence's rows (v is zero past it)
+#pragma unroll
+      for (int R = 0; R < RC; ++R)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ww[R][e] = 16 * R + 4 * lg + e < Lr ? sigmoid_f(ww[R][e]) : 0.f;
+    }
     // X = w v - Kh S0
     f32x4 X[RC];
 #pragma unroll
@@ -375,7 +382,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         const int t = 16 * R + 4 * lg + e;
         if (t < Lr) {
           const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc;
-          a.dw[idx] = acc[e] * vv[R][e];
+          // pre-activation w: d/dw_raw = d/dw * w (1 - w)
+          a.dw[idx] = acc[e] * vv[R][e] * (a.raw_gates ? ww[R][e] * (1.f - ww[R][e]) : 1.f);
           a.dv[idx] = acc[e] * ww[R][e];
         }
       }
@@ -494,7 +502,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool on = row < Lr && c0 < Dv;
       const int64_t idx = baseV + (int64_t)(t0 + (on ? row : 0)) * rowV + (on ? c0 : 0);
       const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + idx);
-      const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + idx);
+      float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + idx);
+      if (a.raw_gates) y = make_float4(sigmoid_f(y.x), sigmoid_f(y.y), sigmoid_f(y.z), sigmoid_f(y.w));
       return on ? RhsT2{x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w} : RhsT2{};
     }
   };
@@ -526,6 +535,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       }
     }
   }
+  // b as fp32 values from here on (sigmoid of the input for pre-activation gates), zero past the sequence
+  float pb_[KPW][4];
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int t = wid + NW * i;
@@ -534,7 +545,18 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool ok = t < Cfg::NKT && 16 * (t / KB16) + 4 * lg + e < Lr;
       pq[i].mask(e, ok);
       pk[i].mask(e, ok);
-      pb[i].mask(e, ok);
+      pb_[i][e] = ok ? pb[i][e] : 0.f;
+    }
+  }
+  if (a.raw_gates) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int t = wid + NW * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = t < Cfg::NKT && 16 * (t / KB16) + 4 * lg + e < Lr;
+        pb_[i][e] = ok ? sigmoid_f(pb_[i][e]) : 0.f;
+      }
     }
   }
   rsum += __shfl_xor(rsum, 16);
@@ -597,7 +619,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float eg = pe1[i][e] * sCh[2 * DK + c];
         gb[i][e] += acc[e] * pk[i][e] * eg;
-        gk[i][e] += acc[e] * pb[i][e] * eg;
+        gk[i][e] += acc[e] * pb_[i][e] * eg;
       }
     }
   }
@@ -672,7 +694,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
           const int r = 16 * R + 4 * lg + e;
           const float e1 = pe1[i][e];
           const float x = which == 0 ? pk[i][e] * __builtin_amdgcn_rcpf(e1)
-                        : which == 1 ? pb[i][e] * pk[i][e] * e1 : pq[i][e] * e1;
+                        : which == 1 ? pb_[i][e] * pk[i][e] * e1 : pq[i][e] * e1;
           if constexpr (F32IN) sWF[c * LDC + r] = x;
           else st_split(sWF, sWF + KWF, c * LDC + r, x);
         }
@@ -698,7 +720,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float e1 = pe1[i][e];
         gb[i][e] += x1[e] * pk[i][e] * e1;
-        gk[i][e] += x1[e] * pb[i][e] * e1;
+        gk[i][e] += x1[e] * pb_[i][e] * e1;
         gq[i][e] += x2[e] * e1;
       }
     }
@@ -749,7 +771,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * R + 4 * lg + e;
-        sX[r * DK + c] = pq[i][e] * gq[i][e] + 2.f * pb[i][e] * gb[i][e] - pk[i][e] * gk[i][e];
+        sX[r * DK + c] = pq[i][e] * gq[i][e] + 2.f * pb_[i][e] * gb[i][e] - pk[i][e] * gk[i][e];
+        // pre-activation b: d/db_raw = d/db * b (1 - b)
+        if (a.raw_gates) gb[i][e] *= pb_[i][e] * (1.f - pb_[i][e]);
         if constexpr (Cfg::kStage) {
           sOq[r * DK + c] = gq[i][e];
           sOk[r * DK + c] = gk[i][e];
@@ -808,9 +832,17 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < RPS; ++i) {
         const int r = sg * RPS + i;
-        if (r < Lr)
-          *reinterpret_cast<float4*>(a.dlog_alpha + baseK + (int64_t)(t0 + r) * rowK + c) =
-              make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
+        if (r < Lr) {
+          const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
+          float4 d = make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
+          if (a.raw_gates) {
+            // log_alpha = -softplus(a_raw): d/da_raw = d/dlog_alpha * (-sigmoid(a_raw))
+            const float4 ar = *reinterpret_cast<const float4*>(a.log_alpha + idx);
+            d = make_float4(-d.x * sigmoid_f(ar.x), -d.y * sigmoid_f(ar.y), -d.z * sigmoid_f(ar.z),
+                            -d.w * sigmoid_f(ar.w));
+          }
+          *reinterpret_cast<float4*>(a.dlog_alpha + idx) = d;
+        }
       }
     }
   }

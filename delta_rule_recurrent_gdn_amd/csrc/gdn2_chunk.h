@@ -98,6 +98,7 @@ struct KSide {
   Raw4<F32IN> rq[NSL][QK_RPT], rk[NSL][QK_RPT], rb[NSL][QK_RPT];
   int la_c, la_sg, qk_r, qk_c4;
   bool la_on, qk_on;
+  bool raw = false;  // pre-activation gates: log_alpha = -softplus(input), b = sigmoid(input)
 
   __device__ __forceinline__ void init(int tid) {
     la_c = LAW * (tid % (DK / LAW));  // first of the thread's channels
@@ -125,6 +126,13 @@ struct KSide {
           la[i][0] = r < Ln ? *src : 0.f;
         }
       }
+      if (raw) {
+#pragma unroll
+        for (int i = 0; i < LA_RPS; ++i)
+#pragma unroll
+          for (int j = 0; j < LAW; ++j)
+            if (la_sg * LA_RPS + i < Ln) la[i][j] = neg_softplus_f(la[i][j]);  // padding rows stay 0
+      }
     }
   }
 
@@ -145,6 +153,13 @@ struct KSide {
         } else {
           la[i][0] = r < Ln ? *src : 0.f;
         }
+      }
+      if (raw) {
+#pragma unroll
+        for (int i = 0; i < LA_RPS; ++i)
+#pragma unroll
+          for (int j = 0; j < LAW; ++j)
+            if (la_sg * LA_RPS + i < Ln) la[i][j] = neg_softplus_f(la[i][j]);  // padding rows stay 0
       }
     }
     if (qk_on) {
@@ -245,6 +260,10 @@ struct KSide {
         cvt(rq[sl][ri], qv);
         cvt(rk[sl][ri], kv);
         cvt(rb[sl][ri], bv);
+        if (raw) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[i] = sigmoid_f(bv[i]);  // k is zero on padding rows
+        }
         const float4 g4 = *reinterpret_cast<const float4*>(sG + r * DK + c0);
         const float4 gm4 = *reinterpret_cast<const float4*>(sChan + c0);
         const float4 eg4 = *reinterpret_cast<const float4*>(sChan + 2 * DK + c0);

@@ -47,6 +47,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
+// Gate front end (pre-activation inputs): b = sigmoid(b_raw), w = sigmoid(w_raw),
+// log_alpha = -softplus(a_raw) = -log(1 + exp(a_raw)), in fp32.
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float neg_softplus_f(float x) {
+  // -(max(x, 0) + log(1 + exp(-|x|))): no overflow for large |x|
+  return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+}
+
 // Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
 __device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf16>(f); }
 __device__ __forceinline__ float bf16_to_f32(__bf16 h) { return static_cast<float>(h); }

@@ -49,8 +49,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   if (tid < DK) {
     const float qv = load1<F32IN>(a.q, vec_k + tid);
     const float kv = load1<F32IN>(a.k, vec_k + tid);
-    const float bv = load1<F32IN>(a.b, vec_k + tid);
-    s_alpha[tid] = expf(a.log_alpha[vec_k + tid]);
+    float bv = load1<F32IN>(a.b, vec_k + tid);
+    const float la = a.log_alpha[vec_k + tid];
+    // pre-activation gates: b = sigmoid(b_raw), alpha = exp(-softplus(a_raw)) = sigmoid(-a_raw)
+    if (a.raw_gates) bv = sigmoid_f(bv);
+    s_alpha[tid] = a.raw_gates ? sigmoid_f(-la) : expf(la);
     s_e[tid] = bv * kv;
     s_q[tid] = qv;
     s_k[tid] = kv;
@@ -96,6 +99,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   float vv[4], wg[4];
   load4<F32IN>(a.v, vec_v + 4 * j4, vv);
   load4<F32IN>(a.w, vec_v + 4 * j4, wg);
+  if (a.raw_gates) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wg[e] = sigmoid_f(wg[e]);
+  }
   const float4 u = make_float4(wg[0] * vv[0] - r.x, wg[1] * vv[1] - r.y, wg[2] * vv[2] - r.z, wg[3] * vv[3] - r.w);
   if (rg == 0) {
     *reinterpret_cast<float4*>(a.o + vec_v + 4 * j4) =

@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
 
   KS ks;
   ks.init(tid);
+  ks.raw = a.raw_gates;
   constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
   const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
   Raw8<F32IN> rv[VW_RPT], rw[VW_RPT];
@@ -205,6 +206,10 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
         float vv[8], ww[8];
         cvt(rv[i], vv);
         cvt(rw[i], ww);
+        if (a.raw_gates) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ww[e] = sigmoid_f(ww[e]);  // v is zero on padding rows
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) sWVT[(8 * vw_j8 + e) * LDC + r] = static_cast<OpT>(ww[e] * vv[e]);
       }

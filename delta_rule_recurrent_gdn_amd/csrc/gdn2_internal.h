@@ -19,6 +19,7 @@ struct DecodeArgs {
   float* o;
   int B, H, Dk, Dv;
   bool f32_inputs;
+  bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
 };
 
 struct FwdArgs {
@@ -34,6 +35,7 @@ struct FwdArgs {
   float* chunk_states;   // nullable
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
+  bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
 };
 
 // Segmented (two-level) forward chain: the pass and its buffers.
@@ -68,7 +70,9 @@ struct BwdArgs {
   float* dS0;                // nullable
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
-  const char* records = nullptr;  // backward records (T, P^T) for launch_bwd_grad
+  const char* records = nullptr;  // backward records (T, P^T, Kh, Kb) for launch_bwd_grad
+  bool raw_gates = false;  // b, w, log_alpha hold pre-activations; db, dw, dlog_alpha are taken
+                           // with respect to those
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -128,6 +128,10 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       ld_raw(rb[sl], a.b, idx);
       const float4 x = *reinterpret_cast<const float4*>(a.log_alpha + idx);
       g[sl][0] = x.x; g[sl][1] = x.y; g[sl][2] = x.z; g[sl][3] = x.w;
+      if (a.raw_gates) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[sl][j] = neg_softplus_f(g[sl][j]);
+      }
     } else {
       zero_raw(rq[sl]);
       zero_raw(rk[sl]);
@@ -147,6 +151,10 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
           const int64_t idx = baseV + (int64_t)(t0 + rr) * rowV + 8 * j8;
           load8<F32IN>(a.v, idx, vv);
           load8<F32IN>(a.w, idx, ww);
+          if (a.raw_gates) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ww[q] = sigmoid_f(ww[q]);
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < 8; ++q) vv[q] = ww[q] = 0.f;
@@ -208,6 +216,10 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       cvt(rq[sl], qv);
       cvt(rk[sl], kv);
       cvt(rb[sl], bv);
+      if (a.raw_gates) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = sigmoid_f(bv[i]);  // k is zero on padding rows
+      }
       const float4 gm4 = *reinterpret_cast<const float4*>(sCh + c0);
       const float4 eg4 = *reinterpret_cast<const float4*>(sCh + 2 * DK + c0);
       const float4 ec4 = *reinterpret_cast<const float4*>(sCh + 3 * DK + c0);
@@ -379,6 +391,10 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       float kv[4], bv[4];
       cvt(rk[sl], kv);
       cvt(rb[sl], bv);
+      if (a.raw_gates) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = sigmoid_f(bv[i]);  // k is zero on padding rows
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * __expf(g[sl][i]));
     }

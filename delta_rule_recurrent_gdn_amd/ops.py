@@ -51,14 +51,15 @@ def _dtype_code(dtype):
 
 
 def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_state=True,
-                     want_chunk_states=False, single_pass=False, workspace=None):
+                     want_chunk_states=False, single_pass=False, workspace=None, raw_gates=False):
     """Chunked forward. Returns (o, S_final or None, chunk_states or None).
 
     By default the two-stage path runs (chunk-parallel factors into a workspace,
     then the sequential state chain); `workspace` may supply that scratch (a
     uint8 device tensor of at least gdn2_workspace_bytes(GDN2_OP_FWD, ...)
     bytes), else it is allocated here. single_pass=True runs the one-kernel
-    path, which needs no workspace."""
+    path, which needs no workspace. raw_gates=True passes b, w, log_alpha as
+    pre-activations (gdn2_fwd_chunked_ex with GDN2_FLAG_RAW_GATES)."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -81,15 +82,20 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     elif workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.gdn2_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
-                              _ptr(S_final), _ptr(states), _ptr(workspace), ws_bytes, B, T, H, Dk, Dv, chunk,
-                              _dtype_code(q.dtype), _stream(dev))
-    _lib.check(st, "gdn2_fwd_chunked")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(S_final),
+            _ptr(states), _ptr(workspace), ws_bytes, B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
+    if raw_gates:
+        st = lib.gdn2_fwd_chunked_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+        _lib.check(st, "gdn2_fwd_chunked_ex")
+    else:
+        st = lib.gdn2_fwd_chunked(*args, _stream(dev))
+        _lib.check(st, "gdn2_fwd_chunked")
     return o, S_final, states
 
 
-def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None):
-    """One decode step; S ([B,H,Dk,Dv] fp32) is updated in place. Returns o [B,H,Dv] fp32."""
+def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None, raw_gates=False):
+    """One decode step; S ([B,H,Dk,Dv] fp32) is updated in place. Returns o [B,H,Dv] fp32.
+    raw_gates=True passes b, w, log_alpha as pre-activations (gdn2_decode_step_ex)."""
     lib = _lib.load()
     B, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -100,9 +106,14 @@ def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None):
     _f32_state(S, "S", dev, (B, H, Dk, Dv))
     if o is None:
         o = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
-    st = lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o),
-                              B, H, Dk, Dv, _dtype_code(q.dtype), _stream(dev))
-    _lib.check(st, "gdn2_decode_step")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o), B, H, Dk, Dv,
+            _dtype_code(q.dtype))
+    if raw_gates:
+        st = lib.gdn2_decode_step_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+        _lib.check(st, "gdn2_decode_step_ex")
+    else:
+        st = lib.gdn2_decode_step(*args, _stream(dev))
+        _lib.check(st, "gdn2_decode_step")
     return o
 
 
@@ -111,8 +122,10 @@ def gdn2_workspace_bytes(op, B, T, H, Dk, Dv, chunk, dtype):
 
 
 def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk_states=None, chunk=64,
-                     want_dS0=True, workspace=None):
-    """Chunked backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw (fp32) and dS0 (or None)."""
+                     want_dS0=True, workspace=None, raw_gates=False):
+    """Chunked backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw (fp32) and dS0 (or None).
+    raw_gates=True: b, w, log_alpha are pre-activations and db, dw, dlog_alpha the gradients with
+    respect to them (gdn2_bwd_chunked_ex with GDN2_FLAG_RAW_GATES)."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -131,10 +144,14 @@ def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk
     need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib.gdn2_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO),
-                              _ptr(dS_final), _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
-                              _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
-                              _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H, Dk, Dv,
-                              chunk, _dtype_code(q.dtype), _stream(dev))
-    _lib.check(st, "gdn2_bwd_chunked")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_final),
+            _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]),
+            _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H,
+            Dk, Dv, chunk, _dtype_code(q.dtype))
+    if raw_gates:
+        st = lib.gdn2_bwd_chunked_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+        _lib.check(st, "gdn2_bwd_chunked_ex")
+    else:
+        st = lib.gdn2_bwd_chunked(*args, _stream(dev))
+        _lib.check(st, "gdn2_bwd_chunked")
     return g

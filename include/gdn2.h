@@ -79,6 +79,20 @@ typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 
 typedef enum { GDN2_OP_FWD = 0, GDN2_OP_DECODE = 1, GDN2_OP_BWD = 2 } gdn2_op;
 
+/* Flags of the _ex entry points (bitwise OR; any other bit gives GDN2_ERR_UNSUPPORTED).
+ *
+ * GDN2_FLAG_RAW_GATES -- fused gate front end. b, w and log_alpha carry the
+ *   gates' pre-activations b_raw, w_raw, a_raw (same dtypes and layouts), and
+ *   the kernels form b = sigmoid(b_raw), w = sigmoid(w_raw) and
+ *   log_alpha = -softplus(a_raw) = -log(1 + exp(a_raw)) in fp32 as they load
+ *   them, so no separate elementwise pass over HBM is needed. The pages leave
+ *   the gate parametrisation open; this is the sigmoid erase/write gates and
+ *   softplus log-decay of the workloads (b and w in [0, 1], alpha in (0, 1)).
+ *   In gdn2_bwd_chunked_ex, db, dw and dlog_alpha are then the gradients with
+ *   respect to b_raw, w_raw and a_raw: db * b (1 - b), dw * w (1 - w) and
+ *   -dlog_alpha * sigmoid(a_raw). */
+#define GDN2_FLAG_RAW_GATES 1u
+
 /*
  * gdn2_fwd_chunked -- chunkwise WY forward over T tokens.
  *
@@ -114,6 +128,12 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
                      float* chunk_states, void* workspace, size_t workspace_bytes, int B, int T,
                      int H, int Dk, int Dv, int chunk, int dt, void* stream);
 
+/* gdn2_fwd_chunked with flags (GDN2_FLAG_*); flags = 0 is gdn2_fwd_chunked. */
+int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const void* b, const void* w, const float* S0, float* o, float* S_final,
+                        float* chunk_states, void* workspace, size_t workspace_bytes, int B, int T,
+                        int H, int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream);
+
 /*
  * gdn2_decode_step -- one recurrence step per sequence, state updated in place
  * (constant-memory decoding, arXiv 2605.22791 abstract).
@@ -128,6 +148,11 @@ int gdn2_fwd_chunked(const void* q, const void* k, const void* v, const float* l
 int gdn2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                      const void* b, const void* w, float* S, float* o, int B, int H, int Dk,
                      int Dv, int dt, void* stream);
+
+/* gdn2_decode_step with flags (GDN2_FLAG_*); flags = 0 is gdn2_decode_step. */
+int gdn2_decode_step_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const void* b, const void* w, float* S, float* o, int B, int H, int Dk,
+                        int Dv, int dt, unsigned flags, void* stream);
 
 /*
  * gdn2_bwd_chunked -- gate-aware chunkwise backward (arXiv 2605.22791
@@ -156,6 +181,16 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
                      float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
                      void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
                      int Dv, int chunk, int dt, void* stream);
+
+/* gdn2_bwd_chunked with flags (GDN2_FLAG_*); flags = 0 is gdn2_bwd_chunked. With
+ * GDN2_FLAG_RAW_GATES, chunk_states must come from gdn2_fwd_chunked_ex with the
+ * same flag (or be NULL). */
+int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const void* b, const void* w, const float* S0, const void* dO,
+                        const float* dS_final, const float* chunk_states, float* dq, float* dk,
+                        float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
+                        void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                        int Dv, int chunk, int dt, unsigned flags, void* stream);
 
 /* Workspace bytes an entry point needs for these sizes: the backward's
  * requirement, the forward's two-stage path (0 when that path does not cover

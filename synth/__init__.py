@@ -69,19 +69,22 @@ def _cast(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to(_TORCH_DTYPES[dtype])
 
 
-def make_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, s0_std=None, grad=False):
+def make_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, s0_std=None, grad=False, raw_gates=False):
     """Draw one batch of sequence inputs. Returns a dict of CPU torch tensors.
 
     Keys: q, k, v, b, w (storage dtype), log_alpha (fp32), S0 (fp32 or None),
-    dO (storage dtype, only when ``grad``).
+    dO (storage dtype, only when ``grad``). With ``raw_gates`` the same draws
+    are returned before their activations: b, w are the normal draws (storage
+    dtype) and log_alpha the N(-2, 1) draw (fp32).
     """
     rng = np.random.default_rng(seed)
     q = _l2n(_normal(rng, (B, T, H, Dk)))
     k = _l2n(_normal(rng, (B, T, H, Dk)))
     v = _normal(rng, (B, T, H, Dv))
-    b = _sigmoid(_normal(rng, (B, T, H, Dk)))
-    w = _sigmoid(_normal(rng, (B, T, H, Dv)))
-    la = _neg_softplus(_normal(rng, (B, T, H, Dk), mean=-2.0))
+    act = (lambda f, x: x) if raw_gates else (lambda f, x: f(x))  # noqa: E731
+    b = act(_sigmoid, _normal(rng, (B, T, H, Dk)))
+    w = act(_sigmoid, _normal(rng, (B, T, H, Dv)))
+    la = act(_neg_softplus, _normal(rng, (B, T, H, Dk), mean=-2.0))
     out = dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), b=_cast(b, dtype),
                w=_cast(w, dtype), log_alpha=torch.from_numpy(la))
     out["S0"] = (torch.from_numpy(np.float32(s0_std) * _normal(rng, (B, H, Dk, Dv)))
@@ -91,19 +94,21 @@ def make_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, s0_std=None, grad=False):
     return out
 
 
-def make_decode_inputs(B, H, Dk, Dv, steps, dtype="bf16", seed=3, s0_std=0.02):
+def make_decode_inputs(B, H, Dk, Dv, steps, dtype="bf16", seed=3, s0_std=0.02, raw_gates=False):
     """Inputs for ``steps`` consecutive one-token decode steps.
 
     Each per-token input is one draw of shape [steps, B, H, D] (same
-    distributions as ``make_inputs``); the state is [B, H, Dk, Dv] fp32.
+    distributions as ``make_inputs``, ``raw_gates`` as there); the state is
+    [B, H, Dk, Dv] fp32.
     """
     rng = np.random.default_rng(seed)
     q = _l2n(_normal(rng, (steps, B, H, Dk)))
     k = _l2n(_normal(rng, (steps, B, H, Dk)))
     v = _normal(rng, (steps, B, H, Dv))
-    b = _sigmoid(_normal(rng, (steps, B, H, Dk)))
-    w = _sigmoid(_normal(rng, (steps, B, H, Dv)))
-    la = _neg_softplus(_normal(rng, (steps, B, H, Dk), mean=-2.0))
+    act = (lambda f, x: x) if raw_gates else (lambda f, x: f(x))  # noqa: E731
+    b = act(_sigmoid, _normal(rng, (steps, B, H, Dk)))
+    w = act(_sigmoid, _normal(rng, (steps, B, H, Dv)))
+    la = act(_neg_softplus, _normal(rng, (steps, B, H, Dk), mean=-2.0))
     S0 = np.float32(s0_std) * _normal(rng, (B, H, Dk, Dv))
     return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), b=_cast(b, dtype),
                 w=_cast(w, dtype), log_alpha=torch.from_numpy(la), S0=torch.from_numpy(S0))

@@ -413,3 +413,70 @@ def test_oracle_matches_its_recorded_small_case():
     out = {"o": o, "S_T": ST, **g}
     for k, v in rec["outputs"].items():
         assert np.max(np.abs(out[k] - np.array(v))) < 1e-12, k
+
+
+# ----------------------------------------------------------------------------
+# fused gate front end (pre-activation gates)
+# ----------------------------------------------------------------------------
+
+def test_gate_front_end_closed_forms():
+    """sigmoid(0) = 1/2 and -softplus(0) = -ln 2 exactly; sigmoid(x) + sigmoid(-x) = 1;
+    softplus(a) - softplus(-a) = a; the tails: -softplus(a) -> -a for large a, -> -exp(a) for very negative a."""
+    b, w, la = oracle.gates_from_raw(np.zeros(3), np.zeros(2), np.zeros(4))
+    assert np.all(b == 0.5) and np.all(w == 0.5) and np.allclose(la, -math.log(2.0), rtol=0, atol=1e-16)
+    x = np.linspace(-30.0, 30.0, 61)
+    b1, _, la1 = oracle.gates_from_raw(x, x, x)
+    b2, _, la2 = oracle.gates_from_raw(-x, -x, -x)
+    assert np.max(np.abs(b1 + b2 - 1.0)) < 1e-15
+    assert np.max(np.abs((-la1) - (-la2) - x)) < 1e-12
+    _, _, big = oracle.gates_from_raw(np.zeros(1), np.zeros(1), np.array([60.0]))
+    _, _, small = oracle.gates_from_raw(np.zeros(1), np.zeros(1), np.array([-60.0]))
+    assert abs(big[0] + 60.0) < 1e-15 and abs(small[0] + math.exp(-60.0)) < 1e-40
+    # values in the gates' ranges: b, w in (0, 1), alpha = exp(log_alpha) in (0, 1)
+    assert np.all((b1 > 0) & (b1 < 1)) and np.all(la1 < 0)
+
+
+@pytest.mark.parametrize("seed", [23])
+def test_raw_gate_backward_matches_central_finite_differences(seed):
+    """All seven gradients of L = <dO, o> + <dS_final, S_T> with respect to the pre-activation inputs,
+    against central differences of forward_raw."""
+    rng = np.random.default_rng(seed)
+    B, T, H, Dk, Dv = 1, 5, 1, 3, 2
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk)) * 0.6
+    v = rng.standard_normal((B, T, H, Dv))
+    a_raw = rng.standard_normal((B, T, H, Dk)) - 1.0
+    b_raw = rng.standard_normal((B, T, H, Dk))
+    w_raw = rng.standard_normal((B, T, H, Dv))
+    S0 = rng.standard_normal((B, H, Dk, Dv)) * 0.5
+    dO = rng.standard_normal(v.shape)
+    dS = rng.standard_normal(S0.shape)
+    g = oracle.backward_raw(q, k, v, a_raw, b_raw, w_raw, S0, dO, dS, checkpoint_every=2)
+    inp = [q, k, v, a_raw, b_raw, w_raw, S0]
+    names = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+    def loss(xs):
+        o, ST = oracle.forward_raw(*xs)
+        return float(np.sum(o * dO) + np.sum(ST * dS))
+
+    h = 1e-6
+    for i, name in enumerate(names):
+        x = inp[i]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a.copy() for a in inp]
+            xm = [a.copy() for a in inp]
+            xp[i][idx] += h
+            xm[i][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        err = np.max(np.abs(g[name] - fd)) / max(1e-12, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
+
+
+def test_raw_gate_decode_is_one_forward_step():
+    q, k, v, la, b, w, S0 = rnd_inputs(24, T=1)
+    rng = np.random.default_rng(5)
+    a_raw, b_raw, w_raw = rng.standard_normal(la.shape), rng.standard_normal(b.shape), rng.standard_normal(w.shape)
+    o, S1 = oracle.forward_raw(q, k, v, a_raw, b_raw, w_raw, S0)
+    od, Sd = oracle.decode_step_raw(q[:, 0], k[:, 0], v[:, 0], a_raw[:, 0], b_raw[:, 0], w_raw[:, 0], S0)
+    assert maxrel(od, o[:, 0]) < TOL and maxrel(Sd, S1) < TOL
