@@ -1,6 +1,6 @@
 """Benchmark of the GDN-2 operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve] [--no-front-end]
 
 A step is one training pass of the operator over one batch of synthetic input
 with the pages' layer shape: the chunked forward that also saves the chunk
@@ -10,7 +10,9 @@ then K timed steps between two synchronisations. The one-token decode step
 (B=256 sequences, H=16, d=128, fp32 state, 128 consecutive steps) is timed
 separately and reported under "decode", and the long-sequence forward (B=1,
 H=16, d=128, T = 8K..64K: few heads, so the two-level chain) under
-"fwd_long_sequence_curve". Inputs are resident in HBM before any timed region.
+"fwd_long_sequence_curve", and the same training step with pre-activation
+gates (fused gate front end against torch elementwise passes) under
+"front_end". Inputs are resident in HBM before any timed region.
 
 Prints one JSON line: value = whole-job tokens/s of the forward+backward step,
 plus "roofline" for the dominant kernel (HIP events on the launch stream),
@@ -142,6 +144,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-front-end", action="store_true", help="skip the fused gate front end comparison")
     ap.add_argument("--no-curve", action="store_true", help="skip the long-sequence forward curve (T = 8K..64K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
@@ -273,6 +276,62 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
+
+    if not args.no_front_end:
+        # row f1, the fused gate front end: the same training step with the gates passed as pre-activations
+        # (b, w = sigmoid(.), log_alpha = -softplus(.) inside the kernels; gradients with respect to the
+        # pre-activations), against the same step with the activations and their chain rule done as torch
+        # elementwise passes around the plain entry points
+        raw = synth.make_inputs(B, T, H, D, D, "bf16", seed=4, grad=True, raw_gates=True)
+        rd = {k: (v.to(dev) if v is not None else None) for k, v in raw.items()}
+        del raw
+        FLAG = _lib.GDN2_FLAG_RAW_GATES
+
+        def raw_step():
+            st = lib.gdn2_fwd_chunked_ex(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(rd["log_alpha"]), P(rd["b"]),
+                                         P(rd["w"]), None, P(o), None, P(states), P(ws_f), need_f, B, T, H, D, D, C,
+                                         _lib.GDN2_BF16, FLAG, sh)
+            _lib.check(st, "gdn2_fwd_chunked_ex")
+            st = lib.gdn2_bwd_chunked_ex(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(rd["log_alpha"]), P(rd["b"]),
+                                         P(rd["w"]), None, P(rd["dO"]), None, P(states), P(grads["dq"]),
+                                         P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"]), P(grads["db"]),
+                                         P(grads["dw"]), P(dS0), P(ws), need, B, T, H, D, D, C, _lib.GDN2_BF16,
+                                         FLAG, sh)
+            _lib.check(st, "gdn2_bwd_chunked_ex")
+
+        def unfused_step():
+            bb = torch.sigmoid(rd["b"])
+            ww = torch.sigmoid(rd["w"])
+            la = -torch.nn.functional.softplus(rd["log_alpha"])
+            st = lib.gdn2_fwd_chunked(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(la), P(bb), P(ww), None, P(o), None,
+                                      P(states), P(ws_f), need_f, B, T, H, D, D, C, _lib.GDN2_BF16, sh)
+            _lib.check(st, "gdn2_fwd_chunked")
+            st = lib.gdn2_bwd_chunked(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(la), P(bb), P(ww), None, P(rd["dO"]),
+                                      None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
+                                      P(grads["dlog_alpha"]), P(grads["db"]), P(grads["dw"]), P(dS0), P(ws), need,
+                                      B, T, H, D, D, C, _lib.GDN2_BF16, sh)
+            _lib.check(st, "gdn2_bwd_chunked")
+            grads["db"].mul_(bb * (1 - bb))
+            grads["dw"].mul_(ww * (1 - ww))
+            grads["dlog_alpha"].mul_(-torch.sigmoid(rd["log_alpha"]))
+
+        fe = {}
+        for name, fn in (("fused_ms_per_step", raw_step), ("unfused_ms_per_step", unfused_step)):
+            fn()
+            torch.cuda.synchronize()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            for _ in range(5):
+                fn()
+            f1.record(stream)
+            torch.cuda.synchronize()
+            fe[name] = round(f0.elapsed_time(f1) / 5, 4)
+        fe["fused_tokens_per_s"] = round(tokens / (fe["fused_ms_per_step"] / 1e3), 1)
+        fe["workload"] = ("config-4 training step (forward saving chunk states + backward) with pre-activation "
+                          "gates b, w (bf16) and a (fp32); unfused = torch sigmoid / softplus passes before and "
+                          "chain-rule passes after the plain entry points")
+        out["front_end"] = fe
+        del rd
 
     if not args.no_decode:
         c3 = synth.CONFIGS[3]

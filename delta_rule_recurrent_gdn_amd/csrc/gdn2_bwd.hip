@@ -148,7 +148,7 @@ struct GradCfg {
 
 // One workgroup per (batch, head, chunk). T and P^T come from the backward
 // records (a.records), the exit-state gradient from the reverse chain.
-template <int DK, int C, bool F32IN>
+template <int DK, int C, bool F32IN, bool RAW>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   using Cfg = GradCfg<DK, C, F32IN>;
   using KS = typename Cfg::KS;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // ---- key-side preparation ----
   KS ks;
   ks.init(tid);
-  ks.raw = a.raw_gates;
+  ks.raw = RAW;
   ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
 
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         vv[R][e] = static_cast<float>(vr[R][e]);
         ww[R][e] = static_cast<float>(wr[R][e]);
       }
-    if (a.raw_gates) {  // w = sigmoid(w_raw) on the sequence's rows (v is zero past it)
+    if constexpr (RAW) {  // w = sigmoid(w_raw) on the sequence's rows (v is zero past it)
 #pragma unroll
       for (int R = 0; R < RC; ++R)
 #pragma unroll
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         if (t < Lr) {
           const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc;
           // pre-activation w: d/dw_raw = d/dw * w (1 - w)
-          a.dw[idx] = acc[e] * vv[R][e] * (a.raw_gates ? ww[R][e] * (1.f - ww[R][e]) : 1.f);
+          a.dw[idx] = acc[e] * vv[R][e] * (RAW ? ww[R][e] * (1.f - ww[R][e]) : 1.f);
           a.dv[idx] = acc[e] * ww[R][e];
         }
       }
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const int64_t idx = baseV + (int64_t)(t0 + (on ? row : 0)) * rowV + (on ? c0 : 0);
       const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + idx);
       float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + idx);
-      if (a.raw_gates) y = make_float4(sigmoid_f(y.x), sigmoid_f(y.y), sigmoid_f(y.z), sigmoid_f(y.w));
+      if constexpr (RAW) y = make_float4(sigmoid_f(y.x), sigmoid_f(y.y), sigmoid_f(y.z), sigmoid_f(y.w));
       return on ? RhsT2{x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w} : RhsT2{};
     }
   };
@@ -535,8 +535,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       }
     }
   }
-  // b as fp32 values from here on (sigmoid of the input for pre-activation gates), zero past the sequence
-  float pb_[KPW][4];
+  // b past the sequence is zero; pre-activation gates keep sigmoid(b_raw) as fp32 values in pbr
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
     const int t = wid + NW * i;
@@ -545,20 +544,25 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool ok = t < Cfg::NKT && 16 * (t / KB16) + 4 * lg + e < Lr;
       pq[i].mask(e, ok);
       pk[i].mask(e, ok);
-      pb_[i][e] = ok ? pb[i][e] : 0.f;
+      pb[i].mask(e, ok);
     }
   }
-  if (a.raw_gates) {
+  float pbr[RAW ? KPW : 1][4];
+  if constexpr (RAW) {
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int t = wid + NW * i;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool ok = t < Cfg::NKT && 16 * (t / KB16) + 4 * lg + e < Lr;
-        pb_[i][e] = ok ? sigmoid_f(pb_[i][e]) : 0.f;
+        pbr[i][e] = ok ? sigmoid_f(pb[i][e]) : 0.f;
       }
     }
   }
+  auto bval = [&](int i, int e) -> float {
+    if constexpr (RAW) return pbr[i][e];
+    else return pb[i][e];
+  };
   rsum += __shfl_xor(rsum, 16);
   rsum += __shfl_xor(rsum, 32);
   if (rs_owner && lg == 0) sEx[16 * cb0 + lr] = rsum;
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float eg = pe1[i][e] * sCh[2 * DK + c];
         gb[i][e] += acc[e] * pk[i][e] * eg;
-        gk[i][e] += acc[e] * pb_[i][e] * eg;
+        gk[i][e] += acc[e] * bval(i, e) * eg;
       }
     }
   }
@@ -694,7 +698,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
           const int r = 16 * R + 4 * lg + e;
           const float e1 = pe1[i][e];
           const float x = which == 0 ? pk[i][e] * __builtin_amdgcn_rcpf(e1)
-                        : which == 1 ? pb_[i][e] * pk[i][e] * e1 : pq[i][e] * e1;
+                        : which == 1 ? bval(i, e) * pk[i][e] * e1 : pq[i][e] * e1;
           if constexpr (F32IN) sWF[c * LDC + r] = x;
           else st_split(sWF, sWF + KWF, c * LDC + r, x);
         }
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float e1 = pe1[i][e];
         gb[i][e] += x1[e] * pk[i][e] * e1;
-        gk[i][e] += x1[e] * pb_[i][e] * e1;
+        gk[i][e] += x1[e] * bval(i, e) * e1;
         gq[i][e] += x2[e] * e1;
       }
     }
@@ -756,6 +760,17 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   __syncthreads();  // phase B buffers are dead
 
   // ---- outputs dq, dk, db (staged through LDS for full-row stores); x = q dq + 2 b db - k dk ----
+  // pre-activation decay: sigmoid(a_raw) scales the decay gradient at its stores (the thread's rows of
+  // the final scan); fetched here so that the loads are in flight during the output staging
+  float4 araw[KS::LA_RPS];
+  if (RAW && ks.la_on) {
+#pragma unroll
+    for (int i = 0; i < KS::LA_RPS; ++i) {
+      const int r = ks.la_sg * KS::LA_RPS + i;
+      araw[i] = *reinterpret_cast<const float4*>(a.log_alpha + baseK + (int64_t)(t0 + (r < Lr ? r : 0)) * rowK +
+                                                 ks.la_c);
+    }
+  }
   // per-wave colsum partials of Kb * dKb (one wave per row block of each column block)
   for (int e = tid; e < NW * DK; e += NT) sExW[e] = 0.f;
   float* sOq = sX + C * DK;
@@ -771,9 +786,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * R + 4 * lg + e;
-        sX[r * DK + c] = pq[i][e] * gq[i][e] + 2.f * pb_[i][e] * gb[i][e] - pk[i][e] * gk[i][e];
+        sX[r * DK + c] = pq[i][e] * gq[i][e] + 2.f * bval(i, e) * gb[i][e] - pk[i][e] * gk[i][e];
         // pre-activation b: d/db_raw = d/db * b (1 - b)
-        if (a.raw_gates) gb[i][e] *= pb_[i][e] * (1.f - pb_[i][e]);
+        if constexpr (RAW) gb[i][e] *= bval(i, e) * (1.f - bval(i, e));
         if constexpr (Cfg::kStage) {
           sOq[r * DK + c] = gq[i][e];
           sOk[r * DK + c] = gk[i][e];
@@ -835,9 +850,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         if (r < Lr) {
           const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
           float4 d = make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
-          if (a.raw_gates) {
+          if constexpr (RAW) {
             // log_alpha = -softplus(a_raw): d/da_raw = d/dlog_alpha * (-sigmoid(a_raw))
-            const float4 ar = *reinterpret_cast<const float4*>(a.log_alpha + idx);
+            const float4 ar = araw[i];
             d = make_float4(-d.x * sigmoid_f(ar.x), -d.y * sigmoid_f(ar.y), -d.z * sigmoid_f(ar.z),
                             -d.w * sigmoid_f(ar.w));
           }
@@ -858,7 +873,10 @@ static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
   } else {
     if (a.records == nullptr) return hipErrorInvalidValue;
     const int NC = (a.T + C - 1) / C;
-    hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+    if (a.raw_gates)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -49,10 +49,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) {
 
 // Gate front end (pre-activation inputs): b = sigmoid(b_raw), w = sigmoid(w_raw),
 // log_alpha = -softplus(a_raw) = -log(1 + exp(a_raw)), in fp32.
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+// Hardware exp2 / log2 / reciprocal forms (about 1 ulp each). -softplus is
+// taken as -(max(x, 0) + log(1 + exp(-|x|))), which never overflows; its
+// absolute error stays below 1e-7, also where the result is tiny.
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float neg_softplus_f(float x) {
-  // -(max(x, 0) + log(1 + exp(-|x|))): no overflow for large |x|
-  return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+  return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))));
 }
 
 // Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).

@@ -128,10 +128,6 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       ld_raw(rb[sl], a.b, idx);
       const float4 x = *reinterpret_cast<const float4*>(a.log_alpha + idx);
       g[sl][0] = x.x; g[sl][1] = x.y; g[sl][2] = x.z; g[sl][3] = x.w;
-      if (a.raw_gates) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) g[sl][j] = neg_softplus_f(g[sl][j]);
-      }
     } else {
       zero_raw(rq[sl]);
       zero_raw(rk[sl]);
@@ -163,6 +159,15 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
         for (int q = 0; q < 8; ++q) sWVT[(8 * j8 + q) * LDC + rr] = static_cast<OpT>(ww[q] * vv[q]);
       }
     }
+  }
+
+  // pre-activation decay: log_alpha = -softplus(input) on the sequence's rows
+  // (after every load is issued, so the loads stay in flight together)
+  if (a.raw_gates && live && r < Lr) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[sl][j] = neg_softplus_f(g[sl][j]);
   }
 
   // ---- gates: inclusive cumsum over the rows of the chunk ----
