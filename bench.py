@@ -1,6 +1,7 @@
 """Benchmark of the GDN-2 operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve] [--no-front-end]
+                    [--no-varlen]
 
 A step is one training pass of the operator over one batch of synthetic input
 with the pages' layer shape: the chunked forward that also saves the chunk
@@ -12,7 +13,8 @@ separately and reported under "decode", and the long-sequence forward (B=1,
 H=16, d=128, T = 8K..64K: few heads, so the two-level chain) under
 "fwd_long_sequence_curve", and the same training step with pre-activation
 gates (fused gate front end against torch elementwise passes) under
-"front_end". Inputs are resident in HBM before any timed region.
+"front_end", and the same tokens as a packed batch of variable-length
+sequences under "varlen". Inputs are resident in HBM before any timed region.
 
 Prints one JSON line: value = whole-job tokens/s of the forward+backward step,
 plus "roofline" for the dominant kernel (HIP events on the launch stream),
@@ -145,6 +147,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-front-end", action="store_true", help="skip the fused gate front end comparison")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length step")
     ap.add_argument("--no-curve", action="store_true", help="skip the long-sequence forward curve (T = 8K..64K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
@@ -332,6 +335,55 @@ def main():
                           "chain-rule passes after the plain entry points")
         out["front_end"] = fe
         del rd
+
+    if not args.no_varlen:
+        # row f3, packed variable-length batches: the same 8 x 4096 = 32768 tokens of H = 16 heads (d = 128,
+        # chunk 64, bf16) cut into documents of seeded lengths (uniform 256 .. 8192, the last one takes the
+        # remainder), packed along T; one training step = gdn2_fwd_varlen (saving chunk states) +
+        # gdn2_bwd_varlen
+        import numpy as np
+
+        rng = np.random.default_rng(5)
+        lens = []
+        while sum(lens) < B * T:
+            lens.append(int(min(rng.integers(256, 8193), B * T - sum(lens))))
+        N = len(lens)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev)
+        pk = {n: d[n].reshape(1, B * T, H, -1) for n in ("q", "k", "v", "log_alpha", "b", "w", "dO")}
+        mcx = lib.gdn2_varlen_max_chunks(N, B * T, C)
+        vstates = torch.empty(H, mcx, D, D, device=dev)
+        vws_f = torch.empty(lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, N, B * T, H, D, D, C, _lib.GDN2_BF16),
+                            dtype=torch.uint8, device=dev)
+        vws_b = torch.empty(lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, N, B * T, H, D, D, C, _lib.GDN2_BF16),
+                            dtype=torch.uint8, device=dev)
+        vo = torch.empty(1, B * T, H, D, device=dev)
+
+        def varlen_step():
+            st = lib.gdn2_fwd_varlen(P(pk["q"]), P(pk["k"]), P(pk["v"]), P(pk["log_alpha"]), P(pk["b"]),
+                                     P(pk["w"]), P(cu), N, None, P(vo), None, P(vstates), P(vws_f), vws_f.numel(),
+                                     B * T, H, D, D, C, _lib.GDN2_BF16, 0, sh)
+            _lib.check(st, "gdn2_fwd_varlen")
+            st = lib.gdn2_bwd_varlen(P(pk["q"]), P(pk["k"]), P(pk["v"]), P(pk["log_alpha"]), P(pk["b"]),
+                                     P(pk["w"]), P(cu), N, None, P(pk["dO"]), None, P(vstates), P(grads["dq"]),
+                                     P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"]), P(grads["db"]),
+                                     P(grads["dw"]), None, P(vws_b), vws_b.numel(), B * T, H, D, D, C,
+                                     _lib.GDN2_BF16, 0, sh)
+            _lib.check(st, "gdn2_bwd_varlen")
+
+        varlen_step()
+        torch.cuda.synchronize()
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for _ in range(5):
+            varlen_step()
+        v1.record(stream)
+        torch.cuda.synchronize()
+        vms = v0.elapsed_time(v1) / 5
+        out["varlen"] = {"workload": f"packed batch of {N} sequences (lengths uniform 256..8192, seed 5) totalling "
+                                     f"{B * T} tokens, H=16 d=128 chunk 64 bf16: forward saving chunk states + "
+                                     f"backward",
+                         "sequences": N, "ms_per_step": round(vms, 4), "tokens_per_s": round(B * T / (vms / 1e3), 1)}
+        del vstates, vws_f, vws_b, vo
 
     if not args.no_decode:
         c3 = synth.CONFIGS[3]

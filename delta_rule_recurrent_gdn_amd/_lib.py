@@ -44,6 +44,13 @@ SIGNATURES = {
                               _I, _I, _I, _I, _I, _I, _I, _P]),
     "gdn2_bwd_chunked_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                  _I, _I, _I, _I, _I, _I, _I, _U, _P]),
+    "gdn2_varlen_max_chunks": (_I, [_I, _I, _I]),
+    "gdn2_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "gdn2_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _U,
+                             _P]),
+    "gdn2_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                             _I, _I, _I, _I, _I, _I, _U, _P]),
+    "gdn2_decode_step_slots": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gdn2_status_string": (ctypes.c_char_p, [_I]),
     "gdn2_version": (_I, []),

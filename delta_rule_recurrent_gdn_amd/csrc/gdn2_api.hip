@@ -99,6 +99,33 @@ char* fwd_seg_ptr(char* ws, int B, int T, int H, int Dk, int Dv, int chunk, bool
   return ws + fwd_seg_offset(B, T, H, Dv, Dk, chunk, f32);
 }
 
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Packed variable-length batches: [tables][...] workspaces. Forward: records
+// and T (w v) over [H][max_chunks]; backward: state gradients and recomputed
+// entry states ([H][max_chunks][Dk][Dv] each), then a records region for the
+// forward records (state recompute) and the backward ones.
+struct VarlenPlan {
+  size_t tables, part, records, need;
+};
+
+VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  VarlenPlan p{};
+  const size_t mc = (size_t)gdn2::varlen_max_chunks(N, T, chunk);
+  p.tables = al256(gdn2::varlen_table_bytes(N, T, chunk));
+  const size_t fwd_rec = (size_t)H * mc * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * 4);
+  if (op == GDN2_OP_FWD) {
+    p.records = al256(fwd_rec);
+    p.need = p.tables + p.records;
+  } else {
+    p.part = al256((size_t)H * mc * Dk * Dv * 4);
+    const size_t bwd_rec = (size_t)H * mc * gdn2::record_bytes(Dk, chunk, f32, 1);
+    p.records = al256(bwd_rec > fwd_rec ? bwd_rec : fwd_rec);
+    p.need = p.tables + 2 * p.part + p.records;
+  }
+  return p;
+}
+
 }  // namespace
 
 namespace gdn2 {
@@ -280,6 +307,139 @@ int gdn2_bwd_chunked(const void* q, const void* k, const void* v, const float* l
                      int Dv, int chunk, int dt, void* stream) {
   return gdn2_bwd_chunked_ex(q, k, v, log_alpha, b, w, S0, dO, dS_final, chunk_states, dq, dk, dv, dlog_alpha, db,
                              dw, dS0, workspace, workspace_bytes, B, T, H, Dk, Dv, chunk, dt, 0u, stream);
+}
+
+// ---- packed variable-length batches ----
+
+int gdn2_varlen_max_chunks(int N, int T, int chunk) {
+  if (N < 0 || T < 0 || !chunk_ok(chunk)) return -1;
+  return gdn2::varlen_max_chunks(N, T, chunk);
+}
+
+size_t gdn2_varlen_workspace_bytes(int op, int N, int T, int H, int Dk, int Dv, int chunk, int dt) {
+  if (check_common(1, T, H, Dk, Dv, dt) != GDN2_OK || N < 0 || !chunk_ok(chunk)) return 0;
+  if (op != GDN2_OP_FWD && op != GDN2_OP_BWD) return 0;
+  const bool f32 = dt == GDN2_F32;
+  if (!gdn2::prep_fwd_supported(Dk, chunk, f32) || (op == GDN2_OP_BWD && !gdn2::grad_supported(Dk, chunk, f32)))
+    return 0;
+  return varlen_plan(op, N, T, H, Dk, Dv, chunk, f32).need;
+}
+
+static int varlen_common(const int64_t* cu_seqlens, int N, int T, int H, int Dk, int Dv, int chunk, int dt,
+                         unsigned flags, int op) {
+  int st = check_common(1, T, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if (N < 0 || T > (1 << 30) - N * 64) return GDN2_ERR_SHAPE;
+  if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
+  const bool f32 = dt == GDN2_F32;
+  if (!gdn2::prep_fwd_supported(Dk, chunk, f32) || (op == GDN2_OP_BWD && !gdn2::grad_supported(Dk, chunk, f32)))
+    return GDN2_ERR_UNSUPPORTED;
+  if (N > 0 && cu_seqlens == nullptr) return GDN2_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0) return GDN2_ERR_ALIGN;
+  return GDN2_OK;
+}
+
+int gdn2_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                    const void* w, const long long* cu_seqlens_, int N, const float* S0, float* o, float* S_final,
+                    float* chunk_states, void* workspace, size_t workspace_bytes, int T, int H, int Dk, int Dv,
+                    int chunk, int dt, unsigned flags, void* stream) {
+  const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_FWD);
+  if (st != GDN2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    st = check_ptrs({}, {S0, S_final});
+    if (st != GDN2_OK) return st;
+    if (S_final == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(S_final, S0, (int64_t)N * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
+  if (st != GDN2_OK) return st;
+  const bool f32 = dt == GDN2_F32;
+  const VarlenPlan p = varlen_plan(GDN2_OP_FWD, N, T, H, Dk, Dv, chunk, f32);
+  if (workspace == nullptr || workspace_bytes < p.need) return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, 1, T, H, Dk, Dv, chunk, f32};
+  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, a.vl, s));
+  if (st != GDN2_OK) return st;
+  char* rec = ws + p.tables;
+  float* ut = reinterpret_cast<float*>(rec + (size_t)H * a.vl.max_chunks * gdn2::fwd_record_bytes(Dk, chunk, f32));
+  st = hip_status(gdn2::launch_prep_fwd(a, rec, ut, s));
+  if (st != GDN2_OK) return st;
+  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, nullptr, s));
+}
+
+int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                    const void* w, const long long* cu_seqlens_, int N, const float* S0, const void* dO,
+                    const float* dS_final, const float* chunk_states, float* dq, float* dk, float* dv,
+                    float* dlog_alpha, float* db, float* dw, float* dS0, void* workspace, size_t workspace_bytes,
+                    int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
+  const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
+  if (st != GDN2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    st = check_ptrs({}, {dS_final, dS0});
+    if (st != GDN2_OK) return st;
+    if (dS0 == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(dS0, dS_final, (int64_t)N * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, dO, dq, dk, dv, dlog_alpha, db, dw}, {S0, dS_final, chunk_states, dS0});
+  if (st != GDN2_OK) return st;
+  const bool f32 = dt == GDN2_F32;
+  const VarlenPlan p = varlen_plan(GDN2_OP_BWD, N, T, H, Dk, Dv, chunk, f32);
+  if (workspace == nullptr || workspace_bytes < p.need) return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  const bool raw = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, 1, T, H, Dk, Dv, chunk, f32};
+  f.raw_gates = raw;
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, f.vl, s));
+  if (st != GDN2_OK) return st;
+  float* dS_chunks = reinterpret_cast<float*>(ws + p.tables);
+  char* rec = ws + p.tables + 2 * p.part;
+  float* states = const_cast<float*>(chunk_states);
+  if (states == nullptr) {
+    // the entry states from the two-stage forward, in the records region first
+    states = reinterpret_cast<float*>(ws + p.tables + p.part);
+    f.chunk_states = states;
+    float* ut = reinterpret_cast<float*>(rec + (size_t)H * f.vl.max_chunks * gdn2::fwd_record_bytes(Dk, chunk, f32));
+    st = hip_status(gdn2::launch_prep_fwd(f, rec, ut, s));
+    if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, nullptr, s));
+    if (st != GDN2_OK) return st;
+  }
+  gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
+                  dS0, 1, T, H, Dk, Dv, chunk, f32};
+  a.raw_gates = raw;
+  a.vl = f.vl;
+  st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
+  a.records = rec;
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
+  return st;
+}
+
+int gdn2_decode_step_slots(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                           const void* w, float* S_pool, const int* slots, int num_slots, float* o, int B, int H,
+                           int Dk, int Dv, int dt, unsigned flags, void* stream) {
+  int st = check_common(B, 1, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if (num_slots < 0) return GDN2_ERR_SHAPE;
+  if ((flags & ~kKnownFlags) != 0) return GDN2_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return GDN2_OK;
+  st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S_pool});
+  if (st != GDN2_OK) return st;
+  if (slots == nullptr || (num_slots > 0 && S_pool == nullptr)) return GDN2_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(slots) & 3u) != 0) return GDN2_ERR_ALIGN;
+  gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, S_pool, o, B, H, Dk, Dv, dt == GDN2_F32};
+  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  a.slots = slots;
+  a.num_slots = num_slots;
+  return hip_status(gdn2::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

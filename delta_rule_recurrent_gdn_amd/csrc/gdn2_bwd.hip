@@ -186,13 +186,13 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   const int lr = l & 15, lg = l >> 4;
   const int T = a.T, H = a.H, Dv = a.Dv;
   const int NC = (T + C - 1) / C;
-  const int bh = blockIdx.x / NC, n = blockIdx.x % NC;
-  const int bi = bh / H, h = bh - bi * H;
-  const int t0 = n * C, Lr = min(C, T - t0);
+  // (batch*head, chunk), chunk fastest; packed sequences: (head, global chunk)
+  const ChunkLoc cl = chunk_loc(a.vl, T, H, DK, Dv, C, NC, blockIdx.x);
+  if (cl.Lr <= 0) return;  // past the last chunk of a packed batch
+  const int t0 = cl.t0, Lr = cl.Lr;
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
-  const int64_t baseK = ((int64_t)bi * T * H + h) * DK;
-  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv;
-  const int64_t stOff = ((int64_t)bh * NC + n) * DK * Dv;
+  const int64_t baseK = cl.baseK, baseV = cl.baseV;
+  const int64_t stOff = cl.item * DK * Dv;
   const float* S0g = a.chunk_states + stOff;
   const float* dSg = a.dS_chunks + stOff;
 
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // below the diagonal are not stored (zero)
   using Rec = Record<DK, C, F32IN, 1>;
   using F = Frag<F32IN>;
-  const char* rec = a.records + ((int64_t)bh * NC + n) * Rec::kBytes;
+  const char* rec = a.records + cl.item * Rec::kBytes;
   // units: T, P^T (chunk x chunk), then Kh, Kb (chunk x Dk); every load of
   // the wave first, then the unpacking
   constexpr int NU = Rec::RC * Rec::UC, NK = Rec::RC * Rec::UK, NUT = 2 * NU + 2 * NK;
@@ -872,11 +872,11 @@ static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
     return hipErrorInvalidConfiguration;
   } else {
     if (a.records == nullptr) return hipErrorInvalidValue;
-    const int NC = (a.T + C - 1) / C;
+    const unsigned grid = (unsigned)chunk_items(a.vl, a.B, a.T, a.H, C);
     if (a.raw_gates)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true>), dim3(grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false>), dim3(a.B * a.H * NC), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   const int lr = l & 15, lg = l >> 4;
 
   const int Dv = a.Dv, T = a.T, H = a.H;
-  const int nbh = a.B * H;
+  const int nbh = seq_items(a.vl, a.B, H);
   const int NC = (T + C - 1) / C;
   int bh, cg, seg = 0, n_begin = 0, n_end = NC;
   if constexpr (SEG) {
@@ -94,16 +94,18 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
     cg = slot % ncg;
     if (bh >= nbh) return;
   }
-  const int bi = bh / H, h = bh - bi * H;
+  // the (batch row or packed sequence, head) walked here: its chunks, tokens and states
+  const SeqLoc sl = seq_loc(a.vl, T, H, DK, Dv, C, bh);
+  if (!SEG) n_end = sl.nchunks;
   const int j0 = cg * Cfg::kCols + wid * 16 * NCT;  // first column of this wave
   // segmented: waves past the columns only copy records; identity columns (j0 >= Dv, map pass) have no input
   const bool active = !SEG || j0 < (sg.mode == kSegMap ? Dv + DK : Dv);
   const bool ident = SEG && j0 >= Dv;
   const int64_t rowV = (int64_t)H * Dv;
-  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
-  const int64_t stBase = (int64_t)bh * DK * Dv + j0;
-  const char* recs = rec_base + (int64_t)bh * NC * Rec::kBytes;
-  const float* uts = ut_base + (int64_t)bh * NC * C * Dv;
+  const int64_t baseV = sl.baseV + j0;
+  const int64_t stBase = sl.state * DK * Dv + j0;
+  const char* recs = rec_base + sl.item0 * Rec::kBytes;
+  const float* uts = ut_base + sl.item0 * C * Dv;
   const int nvt = Dv / 16, jb0 = j0 / 16;
 
   // state tiles: rows 16*RKt + 4*lg + i, column j0 + 16*c + lr
@@ -149,11 +151,13 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   const bool outs = !SEG || (sg.mode == kSegRun && active);
   const bool has_ut = active && !ident;
   f32x4 utn[RC][NCT];
-  dma_units(recs + (int64_t)n_begin * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
-  if (has_ut) load_ut(n_begin, utn);
+  if (n_begin < n_end) {  // an empty packed sequence has no chunk: S_final = S0
+    dma_units(recs + (int64_t)n_begin * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
+    if (has_ut) load_ut(n_begin, utn);
+  }
 
   for (int n = n_begin; n < n_end; ++n) {
-    const int t0 = n * C, Lr = min(C, T - t0);
+    const int t0 = sl.tok0 + n * C, Lr = min(C, sl.len - n * C);
     char* buf = smem + (Cfg::NBUF == 2 ? ((n - n_begin) & 1) * Rec::kBytes : 0);
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n-1
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
                 wid, NWV);
 
     if (a.chunk_states && outs) {
-      float* cs = a.chunk_states + ((int64_t)bh * NC + n) * DK * Dv + j0;
+      float* cs = a.chunk_states + (sl.item0 + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)
 #pragma unroll
@@ -356,17 +360,18 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
   const int lr = l & 15, lg = l >> 4;
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int ncg = Dv / kCols;
-  const int nbh = a.B * H;
+  const int nbh = seq_items(a.vl, a.B, H);
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int bh = (slot / ncg) * 8 + xcd, cg = slot % ncg;
   if (bh >= nbh) return;
-  const int bi = bh / H, h = bh - bi * H;
-  const int NC = (T + C - 1) / C;
+  // the (batch row or packed sequence, head) walked here: its chunks, tokens and states
+  const SeqLoc sl = seq_loc(a.vl, T, H, DK, Dv, C, bh);
+  const int NC = sl.nchunks;
   const int j0 = cg * kCols + wid * 16 * NCT;
   const int64_t rowV = (int64_t)H * Dv;
-  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
-  const int64_t stBase = (int64_t)bh * DK * Dv + j0;
-  const char* recs = rec_base + (int64_t)bh * NC * Rec::kBytes;
+  const int64_t baseV = sl.baseV + j0;
+  const int64_t stBase = sl.state * DK * Dv + j0;
+  const char* recs = rec_base + sl.item0 * Rec::kBytes;
 
   f32x4 accD[RK][NCT];
 #pragma unroll
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
   using RawT = typename std::conditional<F32IN, float, uint16_t>::type;
   RawT rdo[NDU][NCT][NDE];
   auto load_do = [&](int nn) {
-    const int tn = nn * C, Ln = min(C, T - tn);
+    const int tn = sl.tok0 + nn * C, Ln = min(C, sl.len - nn * C);
 #pragma unroll
     for (int u = 0; u < NDU; ++u)
 #pragma unroll
@@ -401,9 +406,11 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
         }
   };
 
-  dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * kBuf : 0),
-            Rec::kChainUnits, wid, NWV);
-  load_do(NC - 1);
+  if (NC > 0) {  // an empty packed sequence has no chunk: dS0 = dS_final
+    dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * kBuf : 0),
+              Rec::kChainUnits, wid, NWV);
+    load_do(NC - 1);
+  }
 
   for (int n = NC - 1; n >= 0; --n) {
     char* buf = smem + (NBUF == 2 ? (n & 1) * kBuf : 0);
@@ -413,7 +420,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
       dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * kBuf, Rec::kChainUnits, wid, NWV);
 
     {
-      float* ws = a.dS_chunks + ((int64_t)bh * NC + n) * DK * Dv + j0;
+      float* ws = a.dS_chunks + (sl.item0 + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)
 #pragma unroll
@@ -566,7 +573,7 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
     return hipErrorInvalidConfiguration;
   } else {
     const int ncg = a.Dv / Cfg::kCols;
-    const int nbh = a.B * a.H;
+    const int nbh = seq_items(a.vl, a.B, a.H);
     const int grid = ((nbh + 7) / 8) * 8 * ncg;
     hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, NCT, NWV, false>), dim3(grid), dim3(Cfg::kThreads), 0, s,
                        a, rec, ut, SegArgs{});
@@ -717,9 +724,9 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
 
 template <int DK, int C, bool F32IN>
 static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
-  const int nbh = a.B * a.H;
+  const int nbh = seq_items(a.vl, a.B, a.H);
   {
-    const int G = seg ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
+    const int G = seg && a.vl.cu == nullptr ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
     if (G > 1) return launch_chain_seg<DK, C, F32IN>(a, rec, ut, seg, G, s);
   }
   if (a.Dv == 16) return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);
@@ -762,7 +769,7 @@ static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStrea
     return hipErrorInvalidConfiguration;
   } else {
     const int ncg = a.Dv / (16 * NCT * NWV);
-    const int nbh = a.B * a.H;
+    const int nbh = seq_items(a.vl, a.B, a.H);
     const int grid = ((nbh + 7) / 8) * 8 * ncg;
     hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, NCT, NWV>), dim3(grid), dim3(NWV * 64), 0, s, a, rec);
     return hipGetLastError();
@@ -771,7 +778,7 @@ static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStrea
 
 template <int DK, int C, bool F32IN>
 static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, hipStream_t s) {
-  const int nbh = a.B * a.H;
+  const int nbh = seq_items(a.vl, a.B, a.H);
   if (a.Dv == 16) return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
   const int tiles = a.Dv / 32;
   if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 2>(a, rec, s);

@@ -42,7 +42,18 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int64_t vec_k = bh * DK, vec_v = bh * DV;
-  float* S = a.S + bh * (int64_t)DK * DV;
+  // state: [B, H] in place, or entry b's slot of a state pool [num_slots, H]
+  int64_t sidx = bh;
+  if (a.slots) {
+    const int bi = (int)(bh / a.H), h = (int)(bh - (int64_t)bi * a.H);
+    const int slot = a.slots[bi];
+    if (slot < 0 || slot >= a.num_slots) {  // no state for this entry: o = 0, nothing else
+      for (int j = tid; j < DV; j += NT) a.o[vec_v + j] = 0.f;
+      return;
+    }
+    sidx = (int64_t)slot * a.H + h;
+  }
+  float* S = a.S + sidx * (int64_t)DK * DV;
 
   // per-channel key-side vectors
   float kq = 0.f;

@@ -20,7 +20,99 @@ struct DecodeArgs {
   int B, H, Dk, Dv;
   bool f32_inputs;
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
+  const int* slots = nullptr;  // [B]: state pool slot of each entry (S is then [num_slots, H, Dk, Dv])
+  int num_slots = 0;
 };
+
+// Variable-length packed batch: N sequences packed along T of a [1, T, H, D]
+// layout. Chunks never cross a sequence boundary; chunk-indexed arrays
+// (records, chunk states, state gradients) are [H][max_chunks] with the
+// sequences' chunks in order, max_chunks = T / chunk + N bounding their count.
+struct Varlen {
+  const int64_t* cu = nullptr;       // [N+1] offsets, clamped non-decreasing within [0, T]; null: dense
+  const int* chunk_seq = nullptr;    // [max_chunks] sequence of global chunk g, -1 past the last chunk
+  const int* chunk_first = nullptr;  // [N+1] first global chunk of each sequence (prefix sums)
+  int nseq = 0;
+  int max_chunks = 0;
+};
+
+// Location of one chunk of a chunk-parallel grid. Dense: item = (b*H + h) * NC + n
+// (chunk fastest). Varlen: item = h * max_chunks + g (g the global chunk).
+struct ChunkLoc {
+  int64_t item;   // index into the chunk-indexed arrays
+  int64_t baseK;  // element offset of token 0 of the chunk's (batch row, head) in [., T, H, Dk]
+  int64_t baseV;  // same in [., T, H, Dv]
+  int t0;         // first token of the chunk (added to base* as (t0 + r) * H * D)
+  int Lr;         // valid rows, 0 < Lr <= C; 0: no chunk (varlen grid past the last chunk)
+};
+
+__device__ __forceinline__ ChunkLoc chunk_loc(const Varlen& vl, int T, int H, int Dk, int Dv, int C, int NC,
+                                              int item) {
+  ChunkLoc L;
+  L.item = item;
+  if (vl.cu == nullptr) {
+    const int bh = item / NC, n = item - bh * NC, bi = bh / H, h = bh - bi * H;
+    L.baseK = ((int64_t)bi * T * H + h) * Dk;
+    L.baseV = ((int64_t)bi * T * H + h) * Dv;
+    L.t0 = n * C;
+    L.Lr = min(C, T - L.t0);
+  } else {
+    const int h = item / vl.max_chunks, g = item - h * vl.max_chunks;
+    const int sq = vl.chunk_seq[g];
+    L.baseK = (int64_t)h * Dk;
+    L.baseV = (int64_t)h * Dv;
+    if (sq < 0) {
+      L.t0 = 0;
+      L.Lr = 0;
+    } else {
+      const int nl = g - vl.chunk_first[sq];
+      const int64_t s0 = vl.cu[sq], len = vl.cu[sq + 1] - s0;
+      L.t0 = (int)(s0 + (int64_t)nl * C);
+      const int64_t rest = len - (int64_t)nl * C;
+      L.Lr = (int)(rest < C ? rest : C);
+    }
+  }
+  return L;
+}
+
+// Workgroups of a chunk-parallel grid (one per chunk location) and of a chain
+// grid (one per (sequence or batch row, head)).
+__host__ __device__ inline int64_t chunk_items(const Varlen& vl, int B, int T, int H, int C) {
+  return vl.cu ? (int64_t)H * vl.max_chunks : (int64_t)B * H * ((T + C - 1) / C);
+}
+__host__ __device__ inline int seq_items(const Varlen& vl, int B, int H) { return (vl.cu ? vl.nseq : B) * H; }
+
+// Location of one (sequence, head) walked by a chain kernel: its chunks are
+// item0 .. item0 + nchunks - 1 in the chunk-indexed arrays, chunk n covers
+// tokens tok0 + n*C .. of length min(C, len - n*C); state index for S0/S_final.
+struct SeqLoc {
+  int64_t item0, state, baseK, baseV;
+  int tok0, len, nchunks;
+};
+
+// sb = b*H + h (dense) or seq*H + h (varlen)
+__device__ __forceinline__ SeqLoc seq_loc(const Varlen& vl, int T, int H, int Dk, int Dv, int C, int sb) {
+  SeqLoc S;
+  S.state = sb;
+  const int sq = sb / H, h = sb - sq * H;
+  if (vl.cu == nullptr) {
+    const int NC = (T + C - 1) / C;
+    S.item0 = (int64_t)sb * NC;
+    S.baseK = ((int64_t)sq * T * H + h) * Dk;
+    S.baseV = ((int64_t)sq * T * H + h) * Dv;
+    S.tok0 = 0;
+    S.len = T;
+    S.nchunks = NC;
+  } else {
+    S.item0 = (int64_t)h * vl.max_chunks + vl.chunk_first[sq];
+    S.baseK = (int64_t)h * Dk;
+    S.baseV = (int64_t)h * Dv;
+    S.tok0 = (int)vl.cu[sq];
+    S.len = (int)(vl.cu[sq + 1] - vl.cu[sq]);
+    S.nchunks = vl.chunk_first[sq + 1] - vl.chunk_first[sq];
+  }
+  return S;
+}
 
 struct FwdArgs {
   const void* q;
@@ -36,6 +128,7 @@ struct FwdArgs {
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
+  Varlen vl;               // packed variable-length batch (B = 1), or dense
 };
 
 // Segmented (two-level) forward chain: the pass and its buffers.
@@ -73,9 +166,16 @@ struct BwdArgs {
   const char* records = nullptr;  // backward records (T, P^T, Kh, Kb) for launch_bwd_grad
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations; db, dw, dlog_alpha are taken
                            // with respect to those
+  Varlen vl;               // packed variable-length batch (B = 1), or dense
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Packed variable-length batches: table bytes in a workspace, the bound on the
+// number of chunks, and the device-side plan that fills the tables and vl.
+int varlen_max_chunks(int N, int T, int C);
+size_t varlen_table_bytes(int N, int T, int C);
+hipError_t launch_varlen_plan(const int64_t* cu, int N, int T, int C, char* tables, Varlen& vl, hipStream_t s);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 // Two-stage forward: chunk-parallel records, then the sequential chain.

@@ -104,14 +104,14 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
 
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int NC = (T + C - 1) / C;
-  const int bh = blockIdx.x / NC, n = blockIdx.x - bh * NC;  // chunk fastest
-  const int bi = bh / H, h = bh - bi * H;
-  const int t0 = n * C, Lr = min(C, T - t0);
+  // (batch*head, chunk), chunk fastest; packed sequences: (head, global chunk)
+  const ChunkLoc cl = chunk_loc(a.vl, T, H, DK, Dv, C, NC, blockIdx.x);
+  if (cl.Lr <= 0) return;  // past the last chunk of a packed batch
+  const int t0 = cl.t0, Lr = cl.Lr;
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
-  const int64_t baseK = ((int64_t)bi * T * H + h) * DK;
-  const int64_t baseV = ((int64_t)bi * T * H + h) * Dv;
-  char* rec = rec_base + ((int64_t)bh * NC + n) * Rec::kBytes;
-  float* ut = ut_base + ((int64_t)bh * NC + n) * C * Dv;
+  const int64_t baseK = cl.baseK, baseV = cl.baseV;
+  char* rec = rec_base + cl.item * Rec::kBytes;
+  float* ut = ut_base + cl.item * C * Dv;
 
   // ---- loads: row r, channels sl*SW + 4*c4 .. +3 of every slice sl ----
   const int r = tid / TPR, c4 = tid - r * TPR;
@@ -478,8 +478,7 @@ static hipError_t launch_prep_t(const FwdArgs& a, char* rec, float* ut, hipStrea
   if constexpr (!PrepCfg<DK, C, F32IN, DIR>::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
-    const int NC = (a.T + C - 1) / C;
-    const int64_t grid = (int64_t)a.B * a.H * NC;
+    const int64_t grid = chunk_items(a.vl, a.B, a.T, a.H, C);
     hipLaunchKernelGGL((gdn2_prep_kernel<DK, C, F32IN, DIR>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut);
     return hipGetLastError();
   }

@@ -155,3 +155,91 @@ def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk
         st = lib.gdn2_bwd_chunked(*args, _stream(dev))
         _lib.check(st, "gdn2_bwd_chunked")
     return g
+
+
+def gdn2_varlen_max_chunks(N, T, chunk):
+    return _lib.load().gdn2_varlen_max_chunks(N, T, chunk)
+
+
+def gdn2_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, chunk=64, want_final_state=True,
+                    want_chunk_states=False, workspace=None, raw_gates=False):
+    """Packed variable-length forward: q, k, b, log_alpha [1,T,H,Dk], v, w [1,T,H,Dv]; cu_seqlens int64 [N+1]
+    on the device. Returns (o [1,T,H,Dv], S_final [N,H,Dk,Dv] or None, chunk_states
+    [H, max_chunks, Dk, Dv] or None)."""
+    lib = _lib.load()
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _check_inputs(("cu_seqlens",), (cu_seqlens,), torch.int64, dev)
+    N = cu_seqlens.numel() - 1
+    S0 = _f32_state(S0, "S0", dev, (N, H, Dk, Dv))
+    o = torch.zeros((1, T, H, Dv), dtype=torch.float32, device=dev)
+    S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
+    mc = lib.gdn2_varlen_max_chunks(N, T, chunk)
+    states = torch.empty((H, mc, Dk, Dv), dtype=torch.float32, device=dev) if want_chunk_states else None
+    need = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, N, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.gdn2_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens), N,
+                             _ptr(S0), _ptr(o), _ptr(S_final), _ptr(states), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), T, H, Dk, Dv, chunk, _dtype_code(q.dtype),
+                             _lib.GDN2_FLAG_RAW_GATES if raw_gates else 0, _stream(dev))
+    _lib.check(st, "gdn2_fwd_varlen")
+    return o, S_final, states
+
+
+def gdn2_bwd_varlen(q, k, v, log_alpha, b, w, dO, cu_seqlens, S0=None, dS_final=None, chunk_states=None, chunk=64,
+                    want_dS0=True, workspace=None, raw_gates=False):
+    """Packed variable-length backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw ([1,T,H,D] fp32,
+    zero outside every sequence) and dS0 ([N,H,Dk,Dv] or None)."""
+    lib = _lib.load()
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w", "dO"), (v, w, dO), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _check_inputs(("cu_seqlens",), (cu_seqlens,), torch.int64, dev)
+    N = cu_seqlens.numel() - 1
+    S0 = _f32_state(S0, "S0", dev, (N, H, Dk, Dv))
+    dS_final = _f32_state(dS_final, "dS_final", dev, (N, H, Dk, Dv))
+    mc = lib.gdn2_varlen_max_chunks(N, T, chunk)
+    chunk_states = _f32_state(chunk_states, "chunk_states", dev, (H, mc, Dk, Dv))
+    kshape, vshape = (1, T, H, Dk), (1, T, H, Dv)
+    g = {n: torch.zeros(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "db", "dlog_alpha")}
+    g.update({n: torch.zeros(vshape, dtype=torch.float32, device=dev) for n in ("dv", "dw")})
+    g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, N, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.gdn2_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens), N,
+                             _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]),
+                             _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), T, H, Dk, Dv, chunk,
+                             _dtype_code(q.dtype), _lib.GDN2_FLAG_RAW_GATES if raw_gates else 0, _stream(dev))
+    _lib.check(st, "gdn2_bwd_varlen")
+    return g
+
+
+def gdn2_decode_step_slots(q, k, v, log_alpha, b, w, S_pool, slots, o=None, raw_gates=False):
+    """One decode step for B entries whose states are S_pool[slots[b]] ([num_slots,H,Dk,Dv] fp32, in place);
+    slots int32 [B] on the device (an entry outside the pool gets o = 0). Returns o [B,H,Dv] fp32."""
+    lib = _lib.load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _check_inputs(("slots",), (slots,), torch.int32, dev)
+    _f32_state(S_pool, "S_pool", dev, (S_pool.shape[0], H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+    st = lib.gdn2_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S_pool),
+                                    _ptr(slots), S_pool.shape[0], _ptr(o), B, H, Dk, Dv, _dtype_code(q.dtype),
+                                    _lib.GDN2_FLAG_RAW_GATES if raw_gates else 0, _stream(dev))
+    _lib.check(st, "gdn2_decode_step_slots")
+    return o

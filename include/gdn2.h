@@ -192,6 +192,53 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
                         void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
                         int Dv, int chunk, int dt, unsigned flags, void* stream);
 
+/*
+ * Packed variable-length batches (row f3 of the build plan: what trainers and
+ * servers call). N sequences of different lengths are packed along T of a
+ * [1, T, H, D] layout: sequence n covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+ * (cu_seqlens: [N+1] int64 on the device, 8-byte aligned, normally 0 = cu[0] <=
+ * ... <= cu[N] = T). Each sequence runs the recurrence from its own entry
+ * state; chunks never cross a sequence boundary. The offsets are read on the
+ * device only (no host synchronisation); they are first made non-decreasing
+ * and clamped to [0, T], so no input can make a kernel read or write outside
+ * the tensors; tokens outside [cu[0], cu[N]) are left unwritten.
+ *
+ *   q, k, b, log_alpha [1,T,H,Dk]; v, w, dO [1,T,H,Dv]; o and gradients likewise
+ *   S0, S_final, dS_final, dS0  [N,H,Dk,Dv] fp32 (nullable as in the dense calls)
+ *   chunk_states [H, gdn2_varlen_max_chunks(N,T,chunk), Dk, Dv] fp32: the entry
+ *                state of every chunk, the sequences' chunks in order (entries past
+ *                the last chunk are not written)
+ *   workspace    gdn2_varlen_workspace_bytes(op, ...) bytes, 256-byte aligned (required)
+ *   flags        GDN2_FLAG_* as for the _ex calls
+ * Same kernels as the dense calls (two-stage forward, two-stage backward).
+ */
+int gdn2_varlen_max_chunks(int N, int T, int chunk);
+size_t gdn2_varlen_workspace_bytes(int op, int N, int T, int H, int Dk, int Dv, int chunk, int dt);
+int gdn2_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const void* b, const void* w, const long long* cu_seqlens, int N,
+                    const float* S0, float* o, float* S_final, float* chunk_states,
+                    void* workspace, size_t workspace_bytes, int T, int H, int Dk, int Dv,
+                    int chunk, int dt, unsigned flags, void* stream);
+int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const void* b, const void* w, const long long* cu_seqlens, int N,
+                    const float* S0, const void* dO, const float* dS_final,
+                    const float* chunk_states, float* dq, float* dk, float* dv,
+                    float* dlog_alpha, float* db, float* dw, float* dS0, void* workspace,
+                    size_t workspace_bytes, int T, int H, int Dk, int Dv, int chunk, int dt,
+                    unsigned flags, void* stream);
+
+/*
+ * gdn2_decode_step_slots -- one decode step for B sequences whose states live
+ * in a pool: entry b uses S_pool[slots[b]] ([num_slots, H, Dk, Dv] fp32, in
+ * place); slots [B] int32 on the device. An entry whose slot is negative or
+ * >= num_slots has no state: its o is set to zero and nothing else is touched.
+ * Entries must name distinct slots (two entries on one slot race).
+ */
+int gdn2_decode_step_slots(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const void* b, const void* w, float* S_pool, const int* slots,
+                           int num_slots, float* o, int B, int H, int Dk, int Dv, int dt,
+                           unsigned flags, void* stream);
+
 /* Workspace bytes an entry point needs for these sizes: the backward's
  * requirement, the forward's two-stage path (0 when that path does not cover
  * the sizes), 0 for decode. Returns 0 for invalid sizes as well; the call

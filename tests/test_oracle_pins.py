@@ -480,3 +480,56 @@ def test_raw_gate_decode_is_one_forward_step():
     o, S1 = oracle.forward_raw(q, k, v, a_raw, b_raw, w_raw, S0)
     od, Sd = oracle.decode_step_raw(q[:, 0], k[:, 0], v[:, 0], a_raw[:, 0], b_raw[:, 0], w_raw[:, 0], S0)
     assert maxrel(od, o[:, 0]) < TOL and maxrel(Sd, S1) < TOL
+
+
+# ----------------------------------------------------------------------------
+# packed variable-length batches
+# ----------------------------------------------------------------------------
+
+def test_varlen_with_equal_lengths_is_the_dense_batch():
+    """N sequences of one length packed along T equal the dense [N, L, H, D] batch (a reshape)."""
+    q, k, v, la, b, w, S0 = rnd_inputs(41, B=3, T=5)
+    pack = lambda x: np.ascontiguousarray(x.reshape(1, -1, *x.shape[2:]))  # noqa: E731
+    cu = np.arange(4) * 5
+    o, ST = oracle.forward(q, k, v, la, b, w, S0)
+    ov, STv = oracle.forward_varlen(*(pack(x) for x in (q, k, v, la, b, w)), cu, S0)
+    assert maxrel(ov, pack(o)) < TOL and maxrel(STv, ST) < TOL
+    rng = np.random.default_rng(3)
+    dO = rng.standard_normal(v.shape)
+    dS = rng.standard_normal(S0.shape)
+    g = oracle.backward(q, k, v, la, b, w, S0, dO, dS, checkpoint_every=2)
+    gv = oracle.backward_varlen(*(pack(x) for x in (q, k, v, la, b, w)), cu, S0, pack(dO), dS, checkpoint_every=2)
+    for n in ("dq", "dk", "dv", "db", "dw", "dlog_alpha"):
+        assert maxrel(gv[n], pack(g[n])) < TOL, n
+    assert maxrel(gv["dS0"], g["dS0"]) < TOL
+
+
+def test_varlen_boundaries_reset_the_state():
+    """An empty sequence passes its entry state through (and dS_final back); a sequence's outputs do not
+    depend on what is packed before it."""
+    q, k, v, la, b, w, _ = rnd_inputs(42, B=1, T=9, H=2)
+    rng = np.random.default_rng(4)
+    S0 = rng.standard_normal((3, 2, 3, 4))
+    cu = [0, 4, 4, 9]
+    o, ST = oracle.forward_varlen(q, k, v, la, b, w, cu, S0)
+    assert np.array_equal(ST[1], S0[1])
+    o3, S3 = oracle.forward(q[:, 4:], k[:, 4:], v[:, 4:], la[:, 4:], b[:, 4:], w[:, 4:], S0[2:3])
+    assert maxrel(o[:, 4:], o3) < TOL and maxrel(ST[2], S3[0]) < TOL
+    dS = rng.standard_normal(S0.shape)
+    g = oracle.backward_varlen(q, k, v, la, b, w, cu, S0, rng.standard_normal(v.shape), dS)
+    assert np.array_equal(g["dS0"][1], dS[1])
+
+
+def test_decode_slots_gather_and_scatter():
+    """Slot decode equals a dense decode on the gathered states, written back to the same slots;
+    entries without a slot leave the pool unchanged and output zero."""
+    q, k, v, la, b, w, _ = rnd_inputs(43, B=3, T=1)
+    rng = np.random.default_rng(6)
+    pool = rng.standard_normal((5, 2, 3, 4))
+    slots = [4, -1, 1]
+    o, new = oracle.decode_step_slots(q[:, 0], k[:, 0], v[:, 0], la[:, 0], b[:, 0], w[:, 0], pool, slots)
+    od, Sd = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], la[:, 0], b[:, 0], w[:, 0], pool[[4, 0, 1]])
+    assert maxrel(o[0], od[0]) < TOL and maxrel(o[2], od[2]) < TOL and np.all(o[1] == 0)
+    assert maxrel(new[4], Sd[0]) < TOL and maxrel(new[1], Sd[2]) < TOL
+    for s in (0, 2, 3):
+        assert np.array_equal(new[s], pool[s])
