@@ -1,7 +1,7 @@
 """Benchmark of the GDN-2 operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve] [--no-front-end]
-                    [--no-varlen]
+                    [--no-varlen] [--no-gate-granularity]
 
 A step is one training pass of the operator over one batch of synthetic input
 with the pages' layer shape: the chunked forward that also saves the chunk
@@ -13,8 +13,9 @@ separately and reported under "decode", and the long-sequence forward (B=1,
 H=16, d=128, T = 8K..64K: few heads, so the two-level chain) under
 "fwd_long_sequence_curve", and the same training step with pre-activation
 gates (fused gate front end against torch elementwise passes) under
-"front_end", and the same tokens as a packed batch of variable-length
-sequences under "varlen". Inputs are resident in HBM before any timed region.
+"front_end", the same tokens as a packed batch of variable-length
+sequences under "varlen", and the step with per-head scalar gates (KDA and
+Gated DeltaNet specialisations) under "gate_granularity". Inputs are resident in HBM before any timed region.
 
 Prints one JSON line: value = whole-job tokens/s of the forward+backward step,
 plus "roofline" for the dominant kernel (HIP events on the launch stream),
@@ -148,6 +149,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-front-end", action="store_true", help="skip the fused gate front end comparison")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length step")
+    ap.add_argument("--no-gate-granularity", action="store_true", help="skip the scalar-gate (KDA / GDN) steps")
     ap.add_argument("--no-curve", action="store_true", help="skip the long-sequence forward curve (T = 8K..64K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
@@ -335,6 +337,44 @@ def main():
                           "chain-rule passes after the plain entry points")
         out["front_end"] = fe
         del rd
+
+    if not args.no_gate_granularity:
+        # row f4, gate granularity: the config-4 step with per-head scalar gates ([B, T, H] tensors,
+        # broadcast inside the kernels): KDA (one beta for both gates) and Gated DeltaNet (also a scalar decay)
+        rng_g = torch.Generator(device="cpu").manual_seed(6)
+        beta = torch.sigmoid(torch.randn(B, T, H, generator=rng_g)).to(torch.bfloat16).to(dev)
+        adec = (-torch.nn.functional.softplus(torch.randn(B, T, H, generator=rng_g) - 2.0)).to(dev)
+        gsc = {n: torch.empty(B, T, H, device=dev) for n in ("db", "dw", "dlog_alpha")}
+
+        def scalar_step(flags, la):
+            st = lib.gdn2_fwd_chunked_ex(P(d["q"]), P(d["k"]), P(d["v"]), P(la), P(beta), P(beta), None, P(o), None,
+                                         P(states), P(ws_f), need_f, B, T, H, D, D, C, _lib.GDN2_BF16, flags, sh)
+            _lib.check(st, "gdn2_fwd_chunked_ex")
+            st = lib.gdn2_bwd_chunked_ex(P(d["q"]), P(d["k"]), P(d["v"]), P(la), P(beta), P(beta), None, P(d["dO"]),
+                                         None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
+                                         P(gsc["dlog_alpha"] if la is adec else grads["dlog_alpha"]),
+                                         P(gsc["db"]), P(gsc["dw"]), P(dS0), P(ws), need, B, T, H, D, D, C,
+                                         _lib.GDN2_BF16, flags, sh)
+            _lib.check(st, "gdn2_bwd_chunked_ex")
+
+        gg = {}
+        SB, SW, SD = _lib.GDN2_FLAG_SCALAR_B, _lib.GDN2_FLAG_SCALAR_W, _lib.GDN2_FLAG_SCALAR_DECAY
+        for name, flags, la in (("kda_ms_per_step", SB | SW, d["log_alpha"]),
+                                ("gated_deltanet_ms_per_step", SB | SW | SD, adec)):
+            scalar_step(flags, la)
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for _ in range(5):
+                scalar_step(flags, la)
+            g1.record(stream)
+            torch.cuda.synchronize()
+            gg[name] = round(g0.elapsed_time(g1) / 5, 4)
+        gg["channel_wise_ms_per_step"] = round(ms_step, 4)
+        gg["workload"] = ("config-4 training step with per-head scalar gates: KDA = one beta [B,T,H] for both "
+                          "gates, Gated DeltaNet = also a scalar decay [B,T,H]; channel-wise = the main step")
+        out["gate_granularity"] = gg
+        del beta, adec, gsc
 
     if not args.no_varlen:
         # row f3, packed variable-length batches: the same 8 x 4096 = 32768 tokens of H = 16 heads (d = 128,

@@ -27,6 +27,9 @@ GDN2_OP_DECODE = 1
 GDN2_OP_BWD = 2
 
 GDN2_FLAG_RAW_GATES = 1
+GDN2_FLAG_SCALAR_B = 2
+GDN2_FLAG_SCALAR_W = 4
+GDN2_FLAG_SCALAR_DECAY = 8
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

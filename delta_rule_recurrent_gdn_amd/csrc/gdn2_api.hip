@@ -12,7 +12,17 @@
 namespace {
 
 constexpr int kVersion = 200;  // 0.2.0: the _ex entry points (flags)
-constexpr unsigned kKnownFlags = GDN2_FLAG_RAW_GATES;
+constexpr unsigned kKnownFlags =
+    GDN2_FLAG_RAW_GATES | GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_DECAY;
+
+// the gate options of an argument block from the flags
+template <class Args>
+void set_gate_flags(Args& a, unsigned flags) {
+  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  a.scalar_b = (flags & GDN2_FLAG_SCALAR_B) != 0;
+  a.scalar_w = (flags & GDN2_FLAG_SCALAR_W) != 0;
+  a.scalar_decay = (flags & GDN2_FLAG_SCALAR_DECAY) != 0;
+}
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
@@ -200,7 +210,7 @@ int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float
   st = check_ptrs({q, k, v, log_alpha, b, w, o}, {S0, S_final, chunk_states});
   if (st != GDN2_OK) return st;
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
-  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  set_gate_flags(a, flags);
   if (!two_stage) return hip_status(gdn2::launch_fwd(a, s));
   const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
   if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
@@ -232,7 +242,7 @@ int gdn2_decode_step_ex(const void* q, const void* k, const void* v, const float
   st = check_ptrs({q, k, v, log_alpha, b, w, S, o}, {});
   if (st != GDN2_OK) return st;
   gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, S, o, B, H, Dk, Dv, dt == GDN2_F32};
-  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  set_gate_flags(a, flags);
   return hip_status(gdn2::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -249,7 +259,6 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if ((flags & ~kKnownFlags) != 0) return GDN2_ERR_UNSUPPORTED;
-  const bool raw = (flags & GDN2_FLAG_RAW_GATES) != 0;
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   const bool f32 = dt == GDN2_F32;
   const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
@@ -274,7 +283,7 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   char* rec = ws + 2 * plan.part;
   float* states = const_cast<float*>(chunk_states);
   gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, B, T, H, Dk, Dv, chunk, f32};
-  f.raw_gates = raw;
+  set_gate_flags(f, flags);
   if (states == nullptr) {
     states = reinterpret_cast<float*>(ws + plan.part);
     f.chunk_states = states;
@@ -292,7 +301,7 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
                   dS0, B, T, H, Dk, Dv, chunk, f32};
-  a.raw_gates = raw;
+  set_gate_flags(a, flags);
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
   a.records = rec;
@@ -362,7 +371,7 @@ int gdn2_fwd_varlen(const void* q, const void* k, const void* v, const float* lo
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, 1, T, H, Dk, Dv, chunk, f32};
-  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  set_gate_flags(a, flags);
   st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, a.vl, s));
   if (st != GDN2_OK) return st;
   char* rec = ws + p.tables;
@@ -395,9 +404,8 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   if (workspace == nullptr || workspace_bytes < p.need) return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
-  const bool raw = (flags & GDN2_FLAG_RAW_GATES) != 0;
   gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, 1, T, H, Dk, Dv, chunk, f32};
-  f.raw_gates = raw;
+  set_gate_flags(f, flags);
   st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, f.vl, s));
   if (st != GDN2_OK) return st;
   float* dS_chunks = reinterpret_cast<float*>(ws + p.tables);
@@ -414,7 +422,7 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
                   dS0, 1, T, H, Dk, Dv, chunk, f32};
-  a.raw_gates = raw;
+  set_gate_flags(a, flags);
   a.vl = f.vl;
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
@@ -436,7 +444,7 @@ int gdn2_decode_step_slots(const void* q, const void* k, const void* v, const fl
   if (slots == nullptr || (num_slots > 0 && S_pool == nullptr)) return GDN2_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(slots) & 3u) != 0) return GDN2_ERR_ALIGN;
   gdn2::DecodeArgs a{q, k, v, log_alpha, b, w, S_pool, o, B, H, Dk, Dv, dt == GDN2_F32};
-  a.raw_gates = (flags & GDN2_FLAG_RAW_GATES) != 0;
+  set_gate_flags(a, flags);
   a.slots = slots;
   a.num_slots = num_slots;
   return hip_status(gdn2::launch_decode(a, static_cast<hipStream_t>(stream)));

@@ -128,7 +128,7 @@ struct GradCfg {
   static constexpr int main_end(int endD_) {
     return endBase > tot_at(endD_) + KS::kTotBytes ? endBase : tot_at(endD_) + KS::kTotBytes;
   }
-  static constexpr int kTail = KS::kChanBytes + 2 * DK * 4 + kWaves * DK * 4;
+  static constexpr int kTail = KS::kChanBytes + 2 * DK * 4 + kWaves * DK * 4 + C * 8 * 4;
   static constexpr bool kStage = ((main_end(4 * C * DK * 4) + 15) & ~15) + kTail <= 160 * 1024;
   static constexpr int endD = (kStage ? 4 : 1) * C * DK * 4;
   static constexpr int oTOT = tot_at(endD);
@@ -137,7 +137,8 @@ struct GradCfg {
   static constexpr int oCH = (endMain + 15) & ~15;
   static constexpr int oEX = oCH + KS::kChanBytes;                 // float [2][DK] exit-term pieces
   static constexpr int oEXW = oEX + 2 * DK * 4;                    // float [kWaves][DK] per-wave partials
-  static constexpr int kLdsBytes = oEXW + kWaves * DK * 4;
+  static constexpr int oRED = oEXW + kWaves * DK * 4;              // float [C][8] per-token partial sums
+  static constexpr int kLdsBytes = oRED + C * 8 * 4;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
 
   static constexpr int NKT = NB * (DK / 16);                       // C x DK tiles
@@ -148,8 +149,10 @@ struct GradCfg {
 
 // One workgroup per (batch, head, chunk). T and P^T come from the backward
 // records (a.records), the exit-state gradient from the reverse chain.
-template <int DK, int C, bool F32IN, bool RAW>
+template <int DK, int C, bool F32IN, bool RAW, bool GS>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
+  // GS: some gate holds one value per (token, head); the per-channel case compiles without that code
+  const bool scalar_b = GS && a.scalar_b, scalar_w = GS && a.scalar_w, scalar_decay = GS && a.scalar_decay;
   using Cfg = GradCfg<DK, C, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   float* sTot = reinterpret_cast<float*>(smem + Cfg::oTOT);
   float* sEx = reinterpret_cast<float*>(smem + Cfg::oEX);
   float* sExW = reinterpret_cast<float*>(smem + Cfg::oEXW);
+  float* sRed = reinterpret_cast<float*>(smem + Cfg::oRED);  // scalar-gate gradients: [token][wave or block]
 
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
@@ -200,6 +204,14 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   KS ks;
   ks.init(tid);
   ks.raw = RAW;
+  ks.scalar_la = scalar_decay;
+  // per-head scalar gates ([., T, H]): element offset of token 0 of this (batch row, head); the b and w
+  // gates indexed as base + token * row + channel * stride in either layout
+  const int64_t baseS = baseK / DK;
+  const int64_t bBase = scalar_b ? baseS : baseK, bRow = scalar_b ? H : rowK;
+  const int bCs = scalar_b ? 0 : 1;
+  const int64_t wBase = scalar_w ? baseS : baseV, wRow = scalar_w ? H : rowV;
+  const int wCs = scalar_w ? 0 : 1;
   ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
 
@@ -307,7 +319,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         const int t = 16 * R + 4 * lg + e;
         const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc, safe = baseV + (int64_t)t0 * rowV + jc;
         vr[R][e] = ld_sel(static_cast<const InT*>(a.v), idx, safe, t < Lr);
-        wr[R][e] = ld_sel(static_cast<const InT*>(a.w), idx, safe, t < Lr);
+        wr[R][e] = ld_sel(static_cast<const InT*>(a.w), wBase + (int64_t)(t0 + t) * wRow + jc * wCs,
+                          wBase + (int64_t)t0 * wRow + jc * wCs, t < Lr);
       }
     __builtin_amdgcn_sched_barrier(0);
     RhsT s0f[UKd], dsf[UKd], dof[UCc];
@@ -377,14 +390,27 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < UCc; ++u)
         if (KU * u + KU - 1 >= 16 * R) unit_mma(acc, lds_unit(sTT, LDC, 16 * R, KU * u, C), rhs_c(dU, u));
+      float gw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * R + 4 * lg + e;
+        // pre-activation w: d/dw_raw = d/dw * w (1 - w)
+        gw[e] = t < Lr ? acc[e] * vv[R][e] * (RAW ? ww[R][e] * (1.f - ww[R][e]) : 1.f) : 0.f;
         if (t < Lr) {
           const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc;
-          // pre-activation w: d/dw_raw = d/dw * w (1 - w)
-          a.dw[idx] = acc[e] * vv[R][e] * (RAW ? ww[R][e] * (1.f - ww[R][e]) : 1.f);
+          if (!scalar_w) a.dw[idx] = gw[e];
           a.dv[idx] = acc[e] * ww[R][e];
+        }
+      }
+      if (scalar_w) {  // per-head w: the sum over this wave's 16 columns, then over the waves (below)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = gw[e];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          if (lr == 0) sRed[(16 * R + 4 * lg + e) * 8 + wid] = x;
         }
       }
     }
@@ -409,6 +435,13 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
+  if (scalar_w) {
+    for (int t = tid; t < Lr; t += NT) {
+      float x = 0.f;
+      for (int w = 0; w < Dv / 16; ++w) x += sRed[t * 8 + w];
+      a.dw[baseS + (int64_t)(t0 + t) * H] = x;
+    }
+  }
 
   // ---- key phase: contractions over the value axis ----
   //   dQs = dO S0^T, dKb = U dS^T, dU S0^T (C x DK);  dO U^T, dU (w v)^T (C x C)
@@ -477,7 +510,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool ok = t < Cfg::NKT && r < Lr;
       pq[i].set(e, a.q, idx, safe, ok);
       pk[i].set(e, a.k, idx, safe, ok);
-      pb[i].set(e, a.b, idx, safe, ok);
+      // b per channel, or one value per (token, head): base + token * row + channel * stride
+      const int64_t ib = bBase + (int64_t)(t0 + r) * bRow + c * bCs, sb = bBase + (int64_t)t0 * bRow + (c < DK ? c : 0) * bCs;
+      pb[i].set(e, a.b, ib, sb, ok);
     }
   }
   auto lds_rows = [&](const OpT* X, int row, int c0) -> RhsT2 {
@@ -502,7 +537,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool on = row < Lr && c0 < Dv;
       const int64_t idx = baseV + (int64_t)(t0 + (on ? row : 0)) * rowV + (on ? c0 : 0);
       const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + idx);
-      float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + idx);
+      const float4 y0 = load_la4(static_cast<const float*>(a.w), idx, baseS + (int64_t)(t0 + (on ? row : 0)) * H,
+                                 scalar_w);  // per-channel, or the token-head's value broadcast
+      float4 y = y0;
       if constexpr (RAW) y = make_float4(sigmoid_f(y.x), sigmoid_f(y.y), sigmoid_f(y.z), sigmoid_f(y.w));
       return on ? RhsT2{x.x * y.x, x.y * y.y, x.z * y.z, x.w * y.w} : RhsT2{};
     }
@@ -767,8 +804,8 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < KS::LA_RPS; ++i) {
       const int r = ks.la_sg * KS::LA_RPS + i;
-      araw[i] = *reinterpret_cast<const float4*>(a.log_alpha + baseK + (int64_t)(t0 + (r < Lr ? r : 0)) * rowK +
-                                                 ks.la_c);
+      const int rr = t0 + (r < Lr ? r : 0);
+      araw[i] = load_la4(a.log_alpha, baseK + (int64_t)rr * rowK + ks.la_c, baseS + (int64_t)rr * H, scalar_decay);
     }
   }
   // per-wave colsum partials of Kb * dKb (one wave per row block of each column block)
@@ -797,19 +834,54 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
           const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
           a.dq[idx] = gq[i][e];
           a.dk[idx] = gk[i][e];
-          a.db[idx] = gb[i][e];
+          if (!scalar_b) a.db[idx] = gb[i][e];
+        }
+      }
+      if (!Cfg::kStage && scalar_b) {  // per-head b, unstaged: sum over the tile's 16 channels, then the blocks
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = gb[i][e];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          if (lr == 0) sRed[(16 * R + 4 * lg + e) * 8 + cb] = x;
         }
       }
     }
   }
   __syncthreads();
+  if (scalar_b) {
+    if constexpr (Cfg::kStage) {
+      // per-head b: row sums of the staged gradient, BP threads per row (DK / BP channels each)
+      constexpr int BP = DK / 4 < 8 ? DK / 4 : 8, BCH = DK / BP;
+      for (int e = tid; e < C * BP; e += NT) {  // groups of BP lanes are wholly in or out
+        const int r = e / BP, part = e - r * BP;
+        float x = 0.f;
+#pragma unroll
+        for (int c = part * BCH; c < (part + 1) * BCH; c += 4) {
+          const float4 y = *reinterpret_cast<const float4*>(sOb + r * DK + c);
+          x += (y.x + y.y) + (y.z + y.w);
+        }
+#pragma unroll
+        for (int m = 1; m < BP; m *= 2) x += __shfl_xor(x, m);
+        if (part == 0 && r < Lr) a.db[baseS + (int64_t)(t0 + r) * H] = x;
+      }
+    } else {
+      for (int t = tid; t < Lr; t += NT) {
+        float x = 0.f;
+        for (int cb = 0; cb < KB16; ++cb) x += sRed[t * 8 + cb];
+        a.db[baseS + (int64_t)(t0 + t) * H] = x;
+      }
+    }
+  }
   for (int e = tid; Cfg::kStage && e < C * (DK / 4); e += NT) {
     const int r = e / (DK / 4), c4 = 4 * (e % (DK / 4));
     if (r < Lr) {
       const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c4;
       *reinterpret_cast<float4*>(a.dq + idx) = *reinterpret_cast<const float4*>(sOq + r * DK + c4);
       *reinterpret_cast<float4*>(a.dk + idx) = *reinterpret_cast<const float4*>(sOk + r * DK + c4);
-      *reinterpret_cast<float4*>(a.db + idx) = *reinterpret_cast<const float4*>(sOb + r * DK + c4);
+      if (!scalar_b) *reinterpret_cast<float4*>(a.db + idx) = *reinterpret_cast<const float4*>(sOb + r * DK + c4);
     }
   }
   // dlog_alpha: reverse cumulative sum over the chunk plus the exit term
@@ -847,16 +919,22 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < RPS; ++i) {
         const int r = sg * RPS + i;
-        if (r < Lr) {
-          const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
-          float4 d = make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
-          if constexpr (RAW) {
-            // log_alpha = -softplus(a_raw): d/da_raw = d/dlog_alpha * (-sigmoid(a_raw))
-            const float4 ar = araw[i];
-            d = make_float4(-d.x * sigmoid_f(ar.x), -d.y * sigmoid_f(ar.y), -d.z * sigmoid_f(ar.z),
-                            -d.w * sigmoid_f(ar.w));
-          }
-          *reinterpret_cast<float4*>(a.dlog_alpha + idx) = d;
+        const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
+        float4 d = make_float4(loc[i].x + ex[0], loc[i].y + ex[1], loc[i].z + ex[2], loc[i].w + ex[3]);
+        if constexpr (RAW) {
+          // log_alpha = -softplus(a_raw): d/da_raw = d/dlog_alpha * (-sigmoid(a_raw))
+          const float4 ar = araw[i];
+          d = make_float4(-d.x * sigmoid_f(ar.x), -d.y * sigmoid_f(ar.y), -d.z * sigmoid_f(ar.z),
+                          -d.w * sigmoid_f(ar.w));
+        }
+        if (!scalar_decay) {
+          if (r < Lr) *reinterpret_cast<float4*>(a.dlog_alpha + idx) = d;
+        } else {
+          // per-head decay: the sum over the row's channels, held by DK / 4 consecutive threads
+          float x = d.x + d.y + d.z + d.w;
+#pragma unroll
+          for (int m = 1; m < DK / 4; m *= 2) x += __shfl_xor(x, m);
+          if (c == 0 && r < Lr) a.dlog_alpha[baseS + (int64_t)(t0 + r) * H] = x;
         }
       }
     }
@@ -873,10 +951,15 @@ static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
   } else {
     if (a.records == nullptr) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)chunk_items(a.vl, a.B, a.T, a.H, C);
-    if (a.raw_gates)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true>), dim3(grid), dim3(512), 0, s, a);
+    const bool gs = a.scalar_b || a.scalar_w || a.scalar_decay;
+    if (a.raw_gates && gs)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, true>), dim3(grid), dim3(512), 0, s, a);
+    else if (a.raw_gates)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, false>), dim3(grid), dim3(512), 0, s, a);
+    else if (gs)
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, true>), dim3(grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false>), dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, false>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -99,6 +99,7 @@ struct KSide {
   int la_c, la_sg, qk_r, qk_c4;
   bool la_on, qk_on;
   bool raw = false;  // pre-activation gates: log_alpha = -softplus(input), b = sigmoid(input)
+  bool scalar_la = false, scalar_b = false;  // one value per (token, head), [., T, H], broadcast
 
   __device__ __forceinline__ void init(int tid) {
     la_c = LAW * (tid % (DK / LAW));  // first of the thread's channels
@@ -115,15 +116,16 @@ struct KSide {
 #pragma unroll
       for (int i = 0; i < LA_RPS; ++i) {
         const int r = la_sg * LA_RPS + i;
-        const float* src = log_alpha + baseK + (int64_t)(tn + r) * rowK + la_c;
+        const int64_t idx = baseK + (int64_t)(tn + r) * rowK + la_c;
+        const int64_t sidx = baseK / DK + (int64_t)(tn + r) * (rowK / DK);
         if constexpr (LAW == 4) {
-          const float4 x = r < Ln ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 x = r < Ln ? load_la4(log_alpha, idx, sidx, scalar_la) : make_float4(0.f, 0.f, 0.f, 0.f);
           la[i][0] = x.x;
           la[i][1] = x.y;
           la[i][2] = x.z;
           la[i][3] = x.w;
         } else {
-          la[i][0] = r < Ln ? *src : 0.f;
+          la[i][0] = r < Ln ? log_alpha[scalar_la ? sidx : idx] : 0.f;
         }
       }
       if (raw) {
@@ -143,15 +145,16 @@ struct KSide {
 #pragma unroll
       for (int i = 0; i < LA_RPS; ++i) {
         const int r = la_sg * LA_RPS + i;
-        const float* src = log_alpha + baseK + (int64_t)(tn + r) * rowK + la_c;
+        const int64_t idx = baseK + (int64_t)(tn + r) * rowK + la_c;
+        const int64_t sidx = baseK / DK + (int64_t)(tn + r) * (rowK / DK);
         if constexpr (LAW == 4) {
-          const float4 x = r < Ln ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 x = r < Ln ? load_la4(log_alpha, idx, sidx, scalar_la) : make_float4(0.f, 0.f, 0.f, 0.f);
           la[i][0] = x.x;
           la[i][1] = x.y;
           la[i][2] = x.z;
           la[i][3] = x.w;
         } else {
-          la[i][0] = r < Ln ? *src : 0.f;
+          la[i][0] = r < Ln ? log_alpha[scalar_la ? sidx : idx] : 0.f;
         }
       }
       if (raw) {
@@ -172,7 +175,7 @@ struct KSide {
             const int64_t idx = baseK + (int64_t)(tn + r) * rowK + s * SW + 4 * qk_c4;
             ld_raw(rq[s][i], q, idx);
             ld_raw(rk[s][i], k, idx);
-            ld_raw(rb[s][i], b, idx);
+            ld_raw_gate(rb[s][i], b, idx, baseK / DK + (int64_t)(tn + r) * (rowK / DK), scalar_b);
           } else {
             zero_raw(rq[s][i]);
             zero_raw(rk[s][i]);

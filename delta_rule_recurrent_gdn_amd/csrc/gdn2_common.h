@@ -130,6 +130,46 @@ __device__ __forceinline__ void ld_raw(Raw4<F32IN>& r, const void* base, int64_t
   if constexpr (F32IN) r.f = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
   else r.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
 }
+// Gates of one value per (token, head) ([., T, H] layout): the value at sidx
+// broadcast to every channel. These load the channels of a gate in either layout.
+template <bool F32IN>
+__device__ __forceinline__ void ld_raw_gate(Raw4<F32IN>& r, const void* base, int64_t idx, int64_t sidx, bool scalar) {
+  if (!scalar) {
+    ld_raw(r, base, idx);
+  } else if constexpr (F32IN) {
+    const float x = static_cast<const float*>(base)[sidx];
+    r.f = make_float4(x, x, x, x);
+  } else {
+    uint32_t x = static_cast<const uint16_t*>(base)[sidx];
+    x |= x << 16;
+    r.u = make_uint2(x, x);
+  }
+}
+template <bool F32IN>
+__device__ __forceinline__ void load4_gate(const void* base, int64_t idx, int64_t sidx, bool scalar, float (&out)[4]) {
+  if (!scalar) {
+    load4<F32IN>(base, idx, out);
+  } else {
+    const float x = load1<F32IN>(base, sidx);
+    out[0] = out[1] = out[2] = out[3] = x;
+  }
+}
+template <bool F32IN>
+__device__ __forceinline__ void load8_gate(const void* base, int64_t idx, int64_t sidx, bool scalar, float (&out)[8]) {
+  if (!scalar) {
+    load8<F32IN>(base, idx, out);
+  } else {
+    const float x = load1<F32IN>(base, sidx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = x;
+  }
+}
+__device__ __forceinline__ float4 load_la4(const float* base, int64_t idx, int64_t sidx, bool scalar) {
+  if (!scalar) return *reinterpret_cast<const float4*>(base + idx);
+  const float x = base[sidx];
+  return make_float4(x, x, x, x);
+}
+
 template <bool F32IN>
 __device__ __forceinline__ void ld_raw(Raw8<F32IN>& r, const void* base, int64_t idx) {
   if constexpr (F32IN) {
@@ -137,6 +177,19 @@ __device__ __forceinline__ void ld_raw(Raw8<F32IN>& r, const void* base, int64_t
     r.f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
   } else {
     r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+  }
+}
+template <bool F32IN>
+__device__ __forceinline__ void ld_raw_gate(Raw8<F32IN>& r, const void* base, int64_t idx, int64_t sidx, bool scalar) {
+  if (!scalar) {
+    ld_raw(r, base, idx);
+  } else if constexpr (F32IN) {
+    const float x = static_cast<const float*>(base)[sidx];
+    r.f0 = r.f1 = make_float4(x, x, x, x);
+  } else {
+    uint32_t x = static_cast<const uint16_t*>(base)[sidx];
+    x |= x << 16;
+    r.u = make_uint4(x, x, x, x);
   }
 }
 template <bool F32IN>

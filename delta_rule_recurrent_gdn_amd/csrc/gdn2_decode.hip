@@ -60,8 +60,9 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   if (tid < DK) {
     const float qv = load1<F32IN>(a.q, vec_k + tid);
     const float kv = load1<F32IN>(a.k, vec_k + tid);
-    float bv = load1<F32IN>(a.b, vec_k + tid);
-    const float la = a.log_alpha[vec_k + tid];
+    // per-head scalar gates ([B, H]): one value for every channel
+    float bv = load1<F32IN>(a.b, a.scalar_b ? bh : vec_k + tid);
+    const float la = a.log_alpha[a.scalar_decay ? bh : vec_k + tid];
     // pre-activation gates: b = sigmoid(b_raw), alpha = exp(-softplus(a_raw)) = sigmoid(-a_raw)
     if (a.raw_gates) bv = sigmoid_f(bv);
     s_alpha[tid] = a.raw_gates ? sigmoid_f(-la) : expf(la);
@@ -109,7 +110,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
 
   float vv[4], wg[4];
   load4<F32IN>(a.v, vec_v + 4 * j4, vv);
-  load4<F32IN>(a.w, vec_v + 4 * j4, wg);
+  load4_gate<F32IN>(a.w, vec_v + 4 * j4, bh, a.scalar_w, wg);
   if (a.raw_gates) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) wg[e] = sigmoid_f(wg[e]);

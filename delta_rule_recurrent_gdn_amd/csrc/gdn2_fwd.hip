@@ -142,6 +142,8 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
   KS ks;
   ks.init(tid);
   ks.raw = a.raw_gates;
+  ks.scalar_la = a.scalar_decay;
+  ks.scalar_b = a.scalar_b;
   constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
   const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
   Raw8<F32IN> rv[VW_RPT], rw[VW_RPT];
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
       if (r < Ln) {
         const int64_t idx = baseV + (int64_t)(tn + r) * rowV + 8 * vw_j8;
         ld_raw(rv[i], a.v, idx);
-        ld_raw(rw[i], a.w, idx);
+        ld_raw_gate(rw[i], a.w, idx, baseK / DK + (int64_t)(tn + r) * H, a.scalar_w);
       } else {
         zero_raw(rv[i]);
         zero_raw(rw[i]);

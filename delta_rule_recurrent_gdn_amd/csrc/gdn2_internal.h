@@ -22,6 +22,7 @@ struct DecodeArgs {
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
   const int* slots = nullptr;  // [B]: state pool slot of each entry (S is then [num_slots, H, Dk, Dv])
   int num_slots = 0;
+  bool scalar_b = false, scalar_w = false, scalar_decay = false;  // one value per (entry, head): [B, H]
 };
 
 // Variable-length packed batch: N sequences packed along T of a [1, T, H, D]
@@ -129,6 +130,8 @@ struct FwdArgs {
   bool f32_inputs;
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
   Varlen vl;               // packed variable-length batch (B = 1), or dense
+  // gates of one value per (token, head), [., T, H], broadcast over their channels
+  bool scalar_b = false, scalar_w = false, scalar_decay = false;
 };
 
 // Segmented (two-level) forward chain: the pass and its buffers.
@@ -167,6 +170,9 @@ struct BwdArgs {
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations; db, dw, dlog_alpha are taken
                            // with respect to those
   Varlen vl;               // packed variable-length batch (B = 1), or dense
+  // gates of one value per (token, head), [., T, H]; their gradients are then [., T, H] too
+  // (summed over the channels the value is broadcast to)
+  bool scalar_b = false, scalar_w = false, scalar_decay = false;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

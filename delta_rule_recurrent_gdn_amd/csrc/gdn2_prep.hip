@@ -123,10 +123,11 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
     const int c0 = sl * SW + 4 * c4;
     if (live && r < Lr) {
       const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c0;
+      const int64_t sidx = baseK / DK + (int64_t)(t0 + r) * H;  // per-head scalar gates: [., T, H]
       ld_raw(rq[sl], a.q, idx);
       ld_raw(rk[sl], a.k, idx);
-      ld_raw(rb[sl], a.b, idx);
-      const float4 x = *reinterpret_cast<const float4*>(a.log_alpha + idx);
+      ld_raw_gate(rb[sl], a.b, idx, sidx, a.scalar_b);
+      const float4 x = load_la4(a.log_alpha, idx, sidx, a.scalar_decay);
       g[sl][0] = x.x; g[sl][1] = x.y; g[sl][2] = x.z; g[sl][3] = x.w;
     } else {
       zero_raw(rq[sl]);
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
         if (rr < Lr) {
           const int64_t idx = baseV + (int64_t)(t0 + rr) * rowV + 8 * j8;
           load8<F32IN>(a.v, idx, vv);
-          load8<F32IN>(a.w, idx, ww);
+          load8_gate<F32IN>(a.w, idx, baseV / Dv + (int64_t)(t0 + rr) * H, a.scalar_w, ww);
           if (a.raw_gates) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) ww[q] = sigmoid_f(ww[q]);

@@ -44,6 +44,17 @@ def _f32_state(t, name, device, shape):
     return t
 
 
+def _flags(raw_gates, scalar_b, scalar_w, scalar_decay):
+    return ((_lib.GDN2_FLAG_RAW_GATES if raw_gates else 0) | (_lib.GDN2_FLAG_SCALAR_B if scalar_b else 0) |
+            (_lib.GDN2_FLAG_SCALAR_W if scalar_w else 0) | (_lib.GDN2_FLAG_SCALAR_DECAY if scalar_decay else 0))
+
+
+def _gate_shapes(lead, Dk, Dv, scalar_b, scalar_w, scalar_decay):
+    """Expected shapes of b, w, log_alpha: per channel, or one value per (token, head) when scalar."""
+    return {"b": lead if scalar_b else lead + (Dk,), "w": lead if scalar_w else lead + (Dv,),
+            "log_alpha": lead if scalar_decay else lead + (Dk,)}
+
+
 def _dtype_code(dtype):
     if dtype not in _DT:
         raise TypeError(f"inputs must be float32 or bfloat16, got {dtype}")
@@ -51,7 +62,8 @@ def _dtype_code(dtype):
 
 
 def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_state=True,
-                     want_chunk_states=False, single_pass=False, workspace=None, raw_gates=False):
+                     want_chunk_states=False, single_pass=False, workspace=None, raw_gates=False, scalar_b=False,
+                     scalar_w=False, scalar_decay=False):
     """Chunked forward. Returns (o, S_final or None, chunk_states or None).
 
     By default the two-stage path runs (chunk-parallel factors into a workspace,
@@ -59,7 +71,8 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     uint8 device tensor of at least gdn2_workspace_bytes(GDN2_OP_FWD, ...)
     bytes), else it is allocated here. single_pass=True runs the one-kernel
     path, which needs no workspace. raw_gates=True passes b, w, log_alpha as
-    pre-activations (gdn2_fwd_chunked_ex with GDN2_FLAG_RAW_GATES)."""
+    pre-activations (gdn2_fwd_chunked_ex with GDN2_FLAG_RAW_GATES); scalar_b / scalar_w /
+    scalar_decay pass that gate as one value per (token, head), [B, T, H] (GDN2_FLAG_SCALAR_*)."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -67,9 +80,11 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
     _check_inputs(("v", "w"), (v, w), q.dtype, dev)
     _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
-    for n, t, d in (("k", k, Dk), ("b", b, Dk), ("log_alpha", log_alpha, Dk), ("v", v, Dv), ("w", w, Dv)):
-        if tuple(t.shape) != (B, T, H, d):
-            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {(B, T, H, d)}")
+    gs = _gate_shapes((B, T, H), Dk, Dv, scalar_b, scalar_w, scalar_decay)
+    for n, t, shp in (("k", k, (B, T, H, Dk)), ("v", v, (B, T, H, Dv)), ("b", b, gs["b"]), ("w", w, gs["w"]),
+                      ("log_alpha", log_alpha, gs["log_alpha"])):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
     S0 = _f32_state(S0, "S0", dev, (B, H, Dk, Dv))
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
@@ -84,8 +99,9 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(S_final),
             _ptr(states), _ptr(workspace), ws_bytes, B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
-    if raw_gates:
-        st = lib.gdn2_fwd_chunked_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+    flags = _flags(raw_gates, scalar_b, scalar_w, scalar_decay)
+    if flags:
+        st = lib.gdn2_fwd_chunked_ex(*args, flags, _stream(dev))
         _lib.check(st, "gdn2_fwd_chunked_ex")
     else:
         st = lib.gdn2_fwd_chunked(*args, _stream(dev))
@@ -93,7 +109,8 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     return o, S_final, states
 
 
-def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None, raw_gates=False):
+def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                     scalar_decay=False):
     """One decode step; S ([B,H,Dk,Dv] fp32) is updated in place. Returns o [B,H,Dv] fp32.
     raw_gates=True passes b, w, log_alpha as pre-activations (gdn2_decode_step_ex)."""
     lib = _lib.load()
@@ -108,8 +125,9 @@ def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None, raw_gates=False):
         o = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S), _ptr(o), B, H, Dk, Dv,
             _dtype_code(q.dtype))
-    if raw_gates:
-        st = lib.gdn2_decode_step_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+    flags = _flags(raw_gates, scalar_b, scalar_w, scalar_decay)
+    if flags:
+        st = lib.gdn2_decode_step_ex(*args, flags, _stream(dev))
         _lib.check(st, "gdn2_decode_step_ex")
     else:
         st = lib.gdn2_decode_step(*args, _stream(dev))
@@ -122,7 +140,8 @@ def gdn2_workspace_bytes(op, B, T, H, Dk, Dv, chunk, dtype):
 
 
 def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk_states=None, chunk=64,
-                     want_dS0=True, workspace=None, raw_gates=False):
+                     want_dS0=True, workspace=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                     scalar_decay=False):
     """Chunked backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw (fp32) and dS0 (or None).
     raw_gates=True: b, w, log_alpha are pre-activations and db, dw, dlog_alpha the gradients with
     respect to them (gdn2_bwd_chunked_ex with GDN2_FLAG_RAW_GATES)."""
@@ -138,8 +157,10 @@ def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk
     NC = (T + chunk - 1) // chunk
     chunk_states = _f32_state(chunk_states, "chunk_states", dev, (B, H, NC, Dk, Dv))
     kshape, vshape = (B, T, H, Dk), (B, T, H, Dv)
-    g = {n: torch.empty(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "db", "dlog_alpha")}
-    g.update({n: torch.empty(vshape, dtype=torch.float32, device=dev) for n in ("dv", "dw")})
+    gs = _gate_shapes((B, T, H), Dk, Dv, scalar_b, scalar_w, scalar_decay)
+    g = {n: torch.empty(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk")}
+    g["dv"] = torch.empty(vshape, dtype=torch.float32, device=dev)
+    g.update({"d" + n: torch.empty(gs[n], dtype=torch.float32, device=dev) for n in ("b", "w", "log_alpha")})
     g["dS0"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dS0 else None
     need = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -148,8 +169,9 @@ def gdn2_bwd_chunked(q, k, v, log_alpha, b, w, dO, S0=None, dS_final=None, chunk
             _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]),
             _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H,
             Dk, Dv, chunk, _dtype_code(q.dtype))
-    if raw_gates:
-        st = lib.gdn2_bwd_chunked_ex(*args, _lib.GDN2_FLAG_RAW_GATES, _stream(dev))
+    flags = _flags(raw_gates, scalar_b, scalar_w, scalar_decay)
+    if flags:
+        st = lib.gdn2_bwd_chunked_ex(*args, flags, _stream(dev))
         _lib.check(st, "gdn2_bwd_chunked_ex")
     else:
         st = lib.gdn2_bwd_chunked(*args, _stream(dev))
@@ -162,7 +184,8 @@ def gdn2_varlen_max_chunks(N, T, chunk):
 
 
 def gdn2_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, chunk=64, want_final_state=True,
-                    want_chunk_states=False, workspace=None, raw_gates=False):
+                    want_chunk_states=False, workspace=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                    scalar_decay=False):
     """Packed variable-length forward: q, k, b, log_alpha [1,T,H,Dk], v, w [1,T,H,Dv]; cu_seqlens int64 [N+1]
     on the device. Returns (o [1,T,H,Dv], S_final [N,H,Dk,Dv] or None, chunk_states
     [H, max_chunks, Dk, Dv] or None)."""
@@ -186,13 +209,14 @@ def gdn2_fwd_varlen(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, chunk=64, wan
     st = lib.gdn2_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens), N,
                              _ptr(S0), _ptr(o), _ptr(S_final), _ptr(states), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), T, H, Dk, Dv, chunk, _dtype_code(q.dtype),
-                             _lib.GDN2_FLAG_RAW_GATES if raw_gates else 0, _stream(dev))
+                             _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
     _lib.check(st, "gdn2_fwd_varlen")
     return o, S_final, states
 
 
 def gdn2_bwd_varlen(q, k, v, log_alpha, b, w, dO, cu_seqlens, S0=None, dS_final=None, chunk_states=None, chunk=64,
-                    want_dS0=True, workspace=None, raw_gates=False):
+                    want_dS0=True, workspace=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                    scalar_decay=False):
     """Packed variable-length backward. Returns a dict with dq, dk, dv, dlog_alpha, db, dw ([1,T,H,D] fp32,
     zero outside every sequence) and dS0 ([N,H,Dk,Dv] or None)."""
     lib = _lib.load()
@@ -209,8 +233,10 @@ def gdn2_bwd_varlen(q, k, v, log_alpha, b, w, dO, cu_seqlens, S0=None, dS_final=
     mc = lib.gdn2_varlen_max_chunks(N, T, chunk)
     chunk_states = _f32_state(chunk_states, "chunk_states", dev, (H, mc, Dk, Dv))
     kshape, vshape = (1, T, H, Dk), (1, T, H, Dv)
-    g = {n: torch.zeros(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk", "db", "dlog_alpha")}
-    g.update({n: torch.zeros(vshape, dtype=torch.float32, device=dev) for n in ("dv", "dw")})
+    gs = _gate_shapes((1, T, H), Dk, Dv, scalar_b, scalar_w, scalar_decay)
+    g = {n: torch.zeros(kshape, dtype=torch.float32, device=dev) for n in ("dq", "dk")}
+    g["dv"] = torch.zeros(vshape, dtype=torch.float32, device=dev)
+    g.update({"d" + n: torch.zeros(gs[n], dtype=torch.float32, device=dev) for n in ("b", "w", "log_alpha")})
     g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dS0 else None
     need = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, N, T, H, Dk, Dv, chunk, _dtype_code(q.dtype))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -219,7 +245,7 @@ def gdn2_bwd_varlen(q, k, v, log_alpha, b, w, dO, cu_seqlens, S0=None, dS_final=
                              _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(chunk_states), _ptr(g["dq"]), _ptr(g["dk"]),
                              _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), T, H, Dk, Dv, chunk,
-                             _dtype_code(q.dtype), _lib.GDN2_FLAG_RAW_GATES if raw_gates else 0, _stream(dev))
+                             _dtype_code(q.dtype), _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
     _lib.check(st, "gdn2_bwd_varlen")
     return g
 

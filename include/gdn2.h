@@ -93,6 +93,19 @@ typedef enum { GDN2_OP_FWD = 0, GDN2_OP_DECODE = 1, GDN2_OP_BWD = 2 } gdn2_op;
  *   -dlog_alpha * sigmoid(a_raw). */
 #define GDN2_FLAG_RAW_GATES 1u
 
+/* GDN2_FLAG_SCALAR_B, _W, _DECAY -- gate granularity. The erase gate b, the
+ *   write gate w, or the decay log_alpha holds one value per (token, head)
+ *   instead of one per channel: layout [B,T,H] ([B,H] for decode, [1,T,H] for
+ *   packed batches), broadcast over the channels inside the kernels, which
+ *   read d times fewer bytes for it. The backward then returns that gate's
+ *   gradient in the same [.., H] layout (the sum over the channels). The
+ *   pages' reductions are these broadcasts: KDA has one scalar beta for both
+ *   gates (SCALAR_B | SCALAR_W with b = w = beta), Gated DeltaNet also a
+ *   scalar decay (| SCALAR_DECAY). Combines with GDN2_FLAG_RAW_GATES. */
+#define GDN2_FLAG_SCALAR_B 2u
+#define GDN2_FLAG_SCALAR_W 4u
+#define GDN2_FLAG_SCALAR_DECAY 8u
+
 /*
  * gdn2_fwd_chunked -- chunkwise WY forward over T tokens.
  *

@@ -50,3 +50,4 @@ alternative forms.
 from .gdn2 import forward, decode_step, backward  # noqa: F401
 from .front_end import gates_from_raw, forward_raw, decode_step_raw, backward_raw  # noqa: F401
 from .varlen import forward_varlen, backward_varlen, decode_step_slots  # noqa: F401
+from .gate_granularity import forward_gates, backward_gates  # noqa: F401

@@ -533,3 +533,63 @@ def test_decode_slots_gather_and_scatter():
     assert maxrel(new[4], Sd[0]) < TOL and maxrel(new[1], Sd[2]) < TOL
     for s in (0, 2, 3):
         assert np.array_equal(new[s], pool[s])
+
+
+# ----------------------------------------------------------------------------
+# gate granularity: per-head scalar gates
+# ----------------------------------------------------------------------------
+
+def test_scalar_gates_are_kda_and_gated_deltanet():
+    """Scalar b = w = beta is KDA, with a scalar decay as well Gated DeltaNet (the recurrences written out
+    above, independently of the oracle)."""
+    q, k, v, la, _, _, S0 = rnd_inputs(44, T=9, Dk=4, Dv=3)
+    rng = np.random.default_rng(45)
+    beta = rng.uniform(0.05, 1.0, size=q.shape[:3])
+    o, ST = oracle.forward_gates(q, k, v, la, beta, beta, S0, scalar_b=True, scalar_w=True)
+    o_ref, S_ref = _kda_reference(q, k, v, la, beta, S0)
+    assert maxrel(o, o_ref) < TOL and maxrel(ST, S_ref) < TOL
+    a = rng.uniform(0.5, 1.0, size=q.shape[:3])
+    o, ST = oracle.forward_gates(q, k, v, np.log(a), beta, beta, S0, scalar_b=True, scalar_w=True,
+                                 scalar_decay=True)
+    o_ref, S_ref = _gdn_reference(q, k, v, a, beta, S0)
+    assert maxrel(o, o_ref) < TOL and maxrel(ST, S_ref) < TOL
+
+
+@pytest.mark.parametrize("raw", [False, True])
+def test_scalar_gate_gradients_match_central_finite_differences(raw):
+    """Gradients with respect to per-head scalar b, w and decay (and the rest), against central
+    differences of forward_gates."""
+    rng = np.random.default_rng(46 + raw)
+    B, T, H, Dk, Dv = 1, 5, 1, 3, 2
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk)) * 0.6
+    v = rng.standard_normal((B, T, H, Dv))
+    la = rng.standard_normal((B, T, H)) - (1.0 if raw else 0.0)
+    la = la if raw else -np.abs(la) * 0.3
+    b = rng.standard_normal((B, T, H)) if raw else rng.uniform(0.1, 0.9, (B, T, H))
+    w = rng.standard_normal((B, T, H)) if raw else rng.uniform(0.1, 0.9, (B, T, H))
+    S0 = rng.standard_normal((B, H, Dk, Dv)) * 0.5
+    dO = rng.standard_normal(v.shape)
+    dS = rng.standard_normal(S0.shape)
+    flags = dict(scalar_b=True, scalar_w=True, scalar_decay=True, raw=raw)
+    g = oracle.backward_gates(q, k, v, la, b, w, S0, dO, dS, checkpoint_every=2, **flags)
+    inp = [q, k, v, la, b, w, S0]
+    names = ["dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0"]
+
+    def loss(xs):
+        o, ST = oracle.forward_gates(*xs, **flags)
+        return float(np.sum(o * dO) + np.sum(ST * dS))
+
+    h = 1e-6
+    for i, name in enumerate(names):
+        x = inp[i]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a_.copy() for a_ in inp]
+            xm = [a_.copy() for a_ in inp]
+            xp[i][idx] += h
+            xm[i][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert g[name].shape == x.shape, name
+        err = np.max(np.abs(g[name] - fd)) / max(1e-12, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
