@@ -43,13 +43,16 @@ def test_ex_entry_points_check_flags():
     U = _lib.GDN2_ERR_UNSUPPORTED
     fwd = lambda flags, B=1: lib.gdn2_fwd_chunked_ex(A, A, A, A, A, A, None, A, None, None, None, 0, B, 64, 2, 16,  # noqa
                                                       16, 16, 0, flags, None)
-    assert fwd(2) == U and fwd(1 << 31) == U
-    assert fwd(_lib.GDN2_FLAG_RAW_GATES, B=0) == _lib.GDN2_OK and fwd(0, B=0) == _lib.GDN2_OK
+    known = (_lib.GDN2_FLAG_RAW_GATES | _lib.GDN2_FLAG_SCALAR_B | _lib.GDN2_FLAG_SCALAR_W |
+             _lib.GDN2_FLAG_SCALAR_DECAY)
+    assert known == 15
+    assert fwd(16) == U and fwd(1 << 31) == U
+    assert fwd(known, B=0) == _lib.GDN2_OK and fwd(0, B=0) == _lib.GDN2_OK
     dec = lambda flags, B=4: lib.gdn2_decode_step_ex(A, A, A, A, A, A, A, A, B, 16, 128, 128, 1, flags, None)  # noqa
-    assert dec(4) == U and dec(_lib.GDN2_FLAG_RAW_GATES, B=0) == _lib.GDN2_OK
+    assert dec(32) == U and dec(known, B=0) == _lib.GDN2_OK
     bwd = lambda flags, B=1: lib.gdn2_bwd_chunked_ex(A, A, A, A, A, A, None, A, None, None, A, A, A, A, A, A,  # noqa
                                                       None, A, 1 << 20, B, 64, 2, 16, 16, 16, 0, flags, None)
-    assert bwd(8) == U and bwd(_lib.GDN2_FLAG_RAW_GATES, B=0) == _lib.GDN2_OK
+    assert bwd(64) == U and bwd(known, B=0) == _lib.GDN2_OK
 
 
 def test_workspace_bytes():
