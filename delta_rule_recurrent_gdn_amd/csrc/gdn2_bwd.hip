@@ -24,13 +24,14 @@
 //   dlog_alpha_t = sum_{s >= t in chunk} (q dq + 2 b db - k dk)_s + rowsum(S_exit * dS)
 //   rowsum(S_exit * dS) = exp(g_C) rowsum(S0 * dS) + colsum_r(Kb * dKb).
 //
-// Two kernels:
-//   * gdn2_bwd_dstate_kernel: one workgroup per (batch, head, value tile), chunks
-//     in reverse; carries dS (value columns are independent) and stores the exit
-//     gradient of every chunk; its final carry is dS0.
-//   * gdn2_bwd_grad_kernel: one workgroup per (batch, head, chunk), fully
-//     parallel; loops over value tiles accumulating the key-side partial
-//     products in registers, then forms every gradient of the chunk.
+// This file holds the chunk-parallel half: gdn2_bwd_grad_kernel, one workgroup
+// per (batch, head, chunk), which takes the chunk's entry state (saved by the
+// forward), the gradient of its exit state (from the reverse chain in
+// gdn2_chain.hip) and T, P^T, Kh, Kb from the backward record (gdn2_prep.hip),
+// and forms every per-token gradient of the chunk: a column phase (waves own
+// value columns; U, dU and d(w v) as register chains), a key phase (waves own
+// key-channel blocks; the contractions over the value axis), then dT, dA and
+// the products with the wide-range Gram factors in LDS.
 // Precision as in the forward: fp16 operands with fp32 accumulation, and a
 // two-term bf16 split for the products with the wide-range factors Kh', Qh', Kt'.
 
