@@ -116,14 +116,18 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // entry states ([H][max_chunks][Dk][Dv] each), then a records region for the
 // forward records (state recompute) and the backward ones.
 struct VarlenPlan {
-  size_t tables, part, records, need;
+  int L;             // segment length of the two-level chain (0: plain chain)
+  size_t tables, part, records, seg_off, need;
 };
 
 VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   VarlenPlan p{};
   const size_t mc = (size_t)gdn2::varlen_max_chunks(N, T, chunk);
-  p.tables = al256(gdn2::varlen_table_bytes(N, T, chunk));
-  const size_t fwd_rec = (size_t)H * mc * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * 4);
+  p.L = gdn2::varlen_seg_len(N, T, H, Dk, Dv, chunk);
+  p.tables = al256(gdn2::varlen_table_bytes(N, T, chunk, p.L));
+  // forward region: records, T (w v), then the two-level chain's segment maps
+  p.seg_off = al256((size_t)H * mc * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * 4));
+  const size_t fwd_rec = p.seg_off + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
   if (op == GDN2_OP_FWD) {
     p.records = al256(fwd_rec);
     p.need = p.tables + p.records;
@@ -372,13 +376,13 @@ int gdn2_fwd_varlen(const void* q, const void* k, const void* v, const float* lo
   char* ws = static_cast<char*>(workspace);
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, 1, T, H, Dk, Dv, chunk, f32};
   set_gate_flags(a, flags);
-  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, a.vl, s));
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, p.L, ws, a.vl, s));
   if (st != GDN2_OK) return st;
   char* rec = ws + p.tables;
   float* ut = reinterpret_cast<float*>(rec + (size_t)H * a.vl.max_chunks * gdn2::fwd_record_bytes(Dk, chunk, f32));
   st = hip_status(gdn2::launch_prep_fwd(a, rec, ut, s));
   if (st != GDN2_OK) return st;
-  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, nullptr, s));
+  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, p.L > 0 ? rec + p.seg_off : nullptr, s));
 }
 
 int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
@@ -406,7 +410,7 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   char* ws = static_cast<char*>(workspace);
   gdn2::FwdArgs f{q, k, v, log_alpha, b, w, S0, nullptr, nullptr, nullptr, 1, T, H, Dk, Dv, chunk, f32};
   set_gate_flags(f, flags);
-  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, ws, f.vl, s));
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, p.L, ws, f.vl, s));
   if (st != GDN2_OK) return st;
   float* dS_chunks = reinterpret_cast<float*>(ws + p.tables);
   char* rec = ws + p.tables + 2 * p.part;
@@ -417,7 +421,8 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
     f.chunk_states = states;
     float* ut = reinterpret_cast<float*>(rec + (size_t)H * f.vl.max_chunks * gdn2::fwd_record_bytes(Dk, chunk, f32));
     st = hip_status(gdn2::launch_prep_fwd(f, rec, ut, s));
-    if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, nullptr, s));
+    if (st == GDN2_OK)
+      st = hip_status(gdn2::launch_chain_fwd(f, rec, ut, p.L > 0 ? rec + p.seg_off : nullptr, s));
     if (st != GDN2_OK) return st;
   }
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,

@@ -74,18 +74,37 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int nbh = seq_items(a.vl, a.B, H);
   const int NC = (T + C - 1) / C;
-  int bh, cg, seg = 0, n_begin = 0, n_end = NC;
+  int bh, cg, n_begin = 0, n_end = NC;
+  int64_t segIdx = 0;               // this segment's slot in M, N, S_in
+  bool seg_first = true, seg_last = true;
   if constexpr (SEG) {
-    // block -> (batch*head, segment, column group); the columns are the value
-    // columns, followed in the map pass by DK identity columns
-    const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
+    // block -> (segment, column group); the columns are the value columns,
+    // followed in the map pass by DK identity columns. Dense: segments
+    // (batch*head, s), s < nseg (map pass: s < nseg - 1); packed sequences:
+    // (head, global segment), a sequence's last segment skipped by the map pass.
     const int ncg = ((sg.mode == kSegMap ? Dv + DK : Dv) + Cfg::kCols - 1) / Cfg::kCols;
     const int item = blockIdx.x / ncg;
     cg = blockIdx.x - item * ncg;
-    bh = item / nsb;
-    seg = item - bh * nsb;
-    n_begin = seg * sg.seg_len;
-    n_end = min(NC, n_begin + sg.seg_len);
+    int local;
+    if (a.vl.cu == nullptr) {
+      const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
+      bh = item / nsb;
+      local = item - bh * nsb;
+      segIdx = (int64_t)bh * sg.nseg + local;
+      seg_last = local == sg.nseg - 1;
+    } else {
+      const int h = item / a.vl.max_segs, gsg = item - h * a.vl.max_segs;
+      const int sq = a.vl.seg_seq[gsg];
+      if (sq < 0) return;  // past the last segment
+      local = gsg - a.vl.seg_first[sq];
+      seg_last = gsg == a.vl.seg_first[sq + 1] - 1;
+      if (sg.mode == kSegMap && seg_last) return;  // no map needed after a sequence's last segment
+      bh = sq * H + h;
+      segIdx = (int64_t)h * a.vl.max_segs + gsg;
+    }
+    seg_first = local == 0;
+    n_begin = local * sg.seg_len;
+    n_end = n_begin + sg.seg_len;  // clipped to the sequence below
   } else {
     // block -> (batch*head, column group); the column groups of one head share an XCD
     const int ncg = Dv / Cfg::kCols;
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   }
   // the (batch row or packed sequence, head) walked here: its chunks, tokens and states
   const SeqLoc sl = seq_loc(a.vl, T, H, DK, Dv, C, bh);
-  if (!SEG) n_end = sl.nchunks;
+  n_end = SEG ? min(n_end, sl.nchunks) : sl.nchunks;
   const int j0 = cg * Cfg::kCols + wid * 16 * NCT;  // first column of this wave
   // segmented: waves past the columns only copy records; identity columns (j0 >= Dv, map pass) have no input
   const bool active = !SEG || j0 < (sg.mode == kSegMap ? Dv + DK : Dv);
@@ -116,9 +135,9 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   if constexpr (SEG) {
     if (sg.mode == kSegMap) {
       Sent = nullptr;
-    } else if (seg > 0) {
+    } else if (!seg_first) {
       Sent = sg.S_in;
-      sOff = ((int64_t)bh * sg.nseg + seg) * DK * Dv + j0;
+      sOff = segIdx * DK * Dv + j0;
     }
   }
   f32x4 accS[RK][NCT];
@@ -306,7 +325,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
   if constexpr (SEG) {
     if (sg.mode == kSegMap && active) {
       // exit of a zero-entry segment: N (value columns) or M (identity columns)
-      const int64_t sb = (int64_t)bh * sg.nseg + seg;
+      const int64_t sb = segIdx;
       float* dst = ident ? sg.M + sb * DK * DK + (j0 - Dv) : sg.N + sb * DK * Dv + j0;
       const int ld = ident ? DK : Dv;
 #pragma unroll
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
           for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * R + 4 * lg + i) * ld + 16 * c + lr] = accS[R][c][i];
       return;
     }
-    if (seg != sg.nseg - 1 || !active) return;
+    if (!seg_last || !active) return;
   }
   if (a.S_final) {
 #pragma unroll
@@ -588,7 +607,8 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
 // matrix cores, N_s as the initial accumulator: wave w owns row tiles 2w and
 // 2w+1 (times DK / 128) of both 16-column tiles.
 template <int DK>
-__global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, SegArgs sg, int nbh, int Dv) {
+__global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
+                                                              Varlen vl, int H, int Dv) {
   constexpr int LDM = DK + 4, LDS_ = 32 + 4;
   constexpr int NM4 = DK * DK / 4;              // float4 of one M
   constexpr int MV = (NM4 + 255) / 256;         // per thread
@@ -598,6 +618,17 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   __shared__ __attribute__((aligned(16))) float sS[DK * LDS_];
   const int ncg = Dv / 32;
   const int bh = blockIdx.x / ncg, j0 = (blockIdx.x - bh * ncg) * 32;
+  // this (batch row or sequence, head)'s segments: slots base .. base + count - 1 of M, N, S_in
+  int64_t base;
+  int count;
+  if (vl.cu == nullptr) {
+    base = (int64_t)bh * sg.nseg;
+    count = sg.nseg;
+  } else {
+    const int sq = bh / H, h = bh - sq * H;
+    base = (int64_t)h * vl.max_segs + vl.seg_first[sq];
+    count = vl.seg_first[sq + 1] - vl.seg_first[sq];
+  }
   const int tid = threadIdx.x, wid = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   for (int e = tid; e < DK * 32; e += 256) {
     const int d = e >> 5, c = e & 31;
@@ -605,21 +636,29 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   }
   float4 mr[MV];
   auto load_m = [&](int s) {
-    const float4* M = reinterpret_cast<const float4*>(sg.M + ((int64_t)bh * sg.nseg + s) * DK * DK);
+    const float4* M = reinterpret_cast<const float4*>(sg.M + (base + s) * DK * DK);
 #pragma unroll
     for (int i = 0; i < MV; ++i)
       if (tid + 256 * i < NM4) mr[i] = M[tid + 256 * i];
   };
-  if (sg.nseg > 1) load_m(0);
-  for (int s = 0; s + 1 < sg.nseg; ++s) {
-    const int64_t sb = (int64_t)bh * sg.nseg + s;
+  if (count == 0) {  // an empty packed sequence has no segment to carry its state: S_final = S0
+    __syncthreads();
+    for (int e = tid; S_final && e < DK * 32; e += 256) {
+      const int d = e >> 5, c = e & 31;
+      S_final[((int64_t)bh * DK + d) * Dv + j0 + c] = sS[d * LDS_ + c];
+    }
+    return;
+  }
+  if (count > 1) load_m(0);
+  for (int s = 0; s + 1 < count; ++s) {
+    const int64_t sb = base + s;
 #pragma unroll
     for (int i = 0; i < MV; ++i) {
       const int e = tid + 256 * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
       if (e < NM4) *reinterpret_cast<float4*>(sM + row * LDM + c4) = mr[i];
     }
     __syncthreads();  // M_s and S_in(s) are in LDS
-    if (s + 2 < sg.nseg) load_m(s + 1);
+    if (s + 2 < count) load_m(s + 1);
     const float* N = sg.N + sb * DK * Dv + j0;
     f32x4 acc[RPW][2];
 #pragma unroll
@@ -696,28 +735,34 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
   if constexpr (!Cfg::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
-    const int NC = (a.T + C - 1) / C, nbh = a.B * a.H;
+    // G segments per (batch row, head) of a dense batch; a packed batch has
+    // a.vl.max_segs segment slots per head (from the plan's tables)
+    const bool packed = a.vl.cu != nullptr;
+    const int NC = (a.T + C - 1) / C, nbh = seq_items(a.vl, a.B, a.H);
+    const int64_t slots = packed ? (int64_t)a.H * a.vl.max_segs : (int64_t)nbh * G;
     SegArgs sg;
-    sg.nseg = G;
-    sg.seg_len = (NC + G - 1) / G;
+    sg.nseg = packed ? 0 : G;
+    sg.seg_len = packed ? a.vl.seg_len : (NC + G - 1) / G;
     sg.M = reinterpret_cast<float*>(seg);
-    sg.N = sg.M + (size_t)nbh * G * DK * DK;
-    sg.S_in = sg.N + (size_t)nbh * G * DK * a.Dv;
-    // (1) maps of segments 0 .. G-2
-    sg.mode = kSegMap;
+    sg.N = sg.M + (size_t)slots * DK * DK;
+    sg.S_in = sg.N + (size_t)slots * DK * a.Dv;
     const int ncg_map = (a.Dv + DK + Cfg::kCols - 1) / Cfg::kCols, ncg_run = (a.Dv + Cfg::kCols - 1) / Cfg::kCols;
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3(nbh * (G - 1) * ncg_map), dim3(512), 0,
-                       s, a, rec, ut, sg);
+    // (1) maps of every segment but the last of each (batch row or sequence, head)
+    sg.mode = kSegMap;
+    const int64_t map_items = packed ? slots : (int64_t)nbh * (G - 1);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(map_items * ncg_map)),
+                       dim3(512), 0, s, a, rec, ut, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // (2) entry states of segments 1 .. G-1
-    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, sg, nbh, a.Dv);
+    // (2) entry states of the later segments
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, a.S_final, sg,
+                       a.vl, a.H, a.Dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true entry state
     sg.mode = kSegRun;
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3(nbh * G * ncg_run), dim3(512), 0, s, a,
-                       rec, ut, sg);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(slots * ncg_run)),
+                       dim3(512), 0, s, a, rec, ut, sg);
     return hipGetLastError();
   }
 }
@@ -726,8 +771,12 @@ template <int DK, int C, bool F32IN>
 static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float* ut, char* seg, hipStream_t s) {
   const int nbh = seq_items(a.vl, a.B, a.H);
   {
-    const int G = seg && a.vl.cu == nullptr ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
-    if (G > 1) return launch_chain_seg<DK, C, F32IN>(a, rec, ut, seg, G, s);
+    if (a.vl.cu != nullptr) {
+      if (seg && a.vl.seg_len > 0) return launch_chain_seg<DK, C, F32IN>(a, rec, ut, seg, 0, s);
+    } else {
+      const int G = seg ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
+      if (G > 1) return launch_chain_seg<DK, C, F32IN>(a, rec, ut, seg, G, s);
+    }
   }
   if (a.Dv == 16) return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);
   // 32 columns per wave; as many waves per workgroup as keep >= 256 workgroups

@@ -35,6 +35,12 @@ struct Varlen {
   const int* chunk_first = nullptr;  // [N+1] first global chunk of each sequence (prefix sums)
   int nseq = 0;
   int max_chunks = 0;
+  // two-level chain inside the sequences (seg_len > 0): each sequence's chunks cut
+  // into segments of seg_len chunks; segment-indexed arrays are [H][max_segs]
+  const int* seg_first = nullptr;    // [N+1] first global segment of each sequence
+  const int* seg_seq = nullptr;      // [max_segs] sequence of global segment s, -1 past the last
+  int seg_len = 0;
+  int max_segs = 0;
 };
 
 // Location of one chunk of a chunk-parallel grid. Dense: item = (b*H + h) * NC + n
@@ -180,8 +186,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Packed variable-length batches: table bytes in a workspace, the bound on the
 // number of chunks, and the device-side plan that fills the tables and vl.
 int varlen_max_chunks(int N, int T, int C);
-size_t varlen_table_bytes(int N, int T, int C);
-hipError_t launch_varlen_plan(const int64_t* cu, int N, int T, int C, char* tables, Varlen& vl, hipStream_t s);
+// segment length of the two-level chain for a packed batch (0: plain chain), the
+// bound on the number of segments, and the bytes of the segment maps
+int varlen_seg_len(int N, int T, int H, int Dk, int Dv, int C);
+int varlen_max_segs(int N, int T, int C, int L);
+size_t varlen_seg_bytes(int N, int T, int H, int Dk, int Dv, int C);
+size_t varlen_table_bytes(int N, int T, int C, int L);
+hipError_t launch_varlen_plan(const int64_t* cu, int N, int T, int C, int L, char* tables, Varlen& vl,
+                              hipStream_t s);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 // Two-stage forward: chunk-parallel records, then the sequential chain.

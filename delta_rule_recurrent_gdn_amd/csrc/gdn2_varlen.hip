@@ -9,7 +9,10 @@
 //      [0, T], so every kernel reads inside the tensors whatever it is given;
 //   2. chunk_first[n] = sum over m < n of ceil((cu'[m+1] - cu'[m]) / C);
 //   3. chunk_seq[g] = the sequence of global chunk g, -1 for g >= chunk_first[N]
-//      up to max_chunks = T / C + N (which bounds chunk_first[N]).
+//      up to max_chunks = T / C + N (which bounds chunk_first[N]);
+//   4. for the two-level chain (segment length L > 0): seg_first[n] = sum over
+//      m < n of ceil(chunks_m / L) and seg_seq[s] = the sequence of global
+//      segment s, -1 past the last up to max_segs = max_chunks / L + N.
 
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
@@ -40,7 +43,8 @@ __device__ int64_t block_exclusive_scan(int64_t x, int64_t* sh, int64_t& total) 
 
 __global__ __launch_bounds__(kPlanThreads) void gdn2_varlen_plan_kernel(const int64_t* cu_in, int N, int T, int C,
                                                                           int max_chunks, int64_t* cu_out,
-                                                                          int* chunk_first, int* chunk_seq) {
+                                                                          int* chunk_first, int* chunk_seq, int L,
+                                                                          int max_segs, int* seg_first, int* seg_seq) {
   __shared__ int64_t sh[kPlanThreads];
   const int tid = threadIdx.x;
   // each thread owns offsets [o0, o1) of the N + 1 offsets
@@ -71,31 +75,81 @@ __global__ __launch_bounds__(kPlanThreads) void gdn2_varlen_plan_kernel(const in
   for (int n = o0; n < s1; ++n)
     for (int g = chunk_first[n]; g < chunk_first[n + 1]; ++g) chunk_seq[g] = n;
   for (int g = (int)tot + tid; g < max_chunks; g += kPlanThreads) chunk_seq[g] = -1;
+  if (L <= 0) return;
+  // 4. segments of L chunks inside each sequence
+  int64_t scnt = 0;
+  for (int n = o0; n < s1; ++n) scnt += (chunk_first[n + 1] - chunk_first[n] + L - 1) / L;
+  int64_t sfirst = block_exclusive_scan<false>(scnt, sh, tot);
+  for (int n = o0; n < s1; ++n) {
+    seg_first[n] = (int)sfirst;
+    sfirst += (chunk_first[n + 1] - chunk_first[n] + L - 1) / L;
+  }
+  if (tid == 0) seg_first[N] = (int)tot;
+  __syncthreads();
+  for (int n = o0; n < s1; ++n)
+    for (int g = seg_first[n]; g < seg_first[n + 1]; ++g) seg_seq[g] = n;
+  for (int g = (int)tot + tid; g < max_segs; g += kPlanThreads) seg_seq[g] = -1;
 }
 
 }  // namespace
 
 int varlen_max_chunks(int N, int T, int C) { return T / C + N; }
 
-// Table bytes inside a workspace: cu' [N+1] int64, chunk_first [N+1] int32,
-// chunk_seq [max_chunks] int32, each 256-byte aligned.
-size_t varlen_table_bytes(int N, int T, int C) {
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)(N + 1) * 8) + al((size_t)(N + 1) * 4) + al((size_t)varlen_max_chunks(N, T, C) * 4);
+// Two-level chain inside packed sequences: used when the (sequence, head)
+// chains alone have too few 32-column wave tiles to fill the GPU and the
+// batch holds at least 32 chunks; L chunks per segment, sized so that the
+// run pass has about 256 workgroups at T / C chunks, at least 8. The segment
+// machinery (compose kernel) needs Dv >= 32.
+int varlen_seg_len(int N, int T, int H, int Dk, int Dv, int C) {
+  (void)Dk;
+  const long nc = T / C;
+  if (Dv < 32 || nc < 32 || (long)N * H * (Dv / 32) >= 512) return 0;
+  long L = (nc * H * ((Dv + 127) / 128) + 255) / 256;
+  return (int)(L < 8 ? 8 : L);
 }
 
-hipError_t launch_varlen_plan(const int64_t* cu, int N, int T, int C, char* tables, Varlen& vl, hipStream_t s) {
+int varlen_max_segs(int N, int T, int C, int L) { return L > 0 ? varlen_max_chunks(N, T, C) / L + N : 0; }
+
+size_t varlen_seg_bytes(int N, int T, int H, int Dk, int Dv, int C) {
+  const int L = varlen_seg_len(N, T, H, Dk, Dv, C);
+  if (L == 0) return 0;
+  return (size_t)H * varlen_max_segs(N, T, C, L) * ((size_t)Dk * Dk + 2 * (size_t)Dk * Dv) * sizeof(float);
+}
+
+// Table bytes inside a workspace: cu' [N+1] int64, chunk_first [N+1] int32,
+// chunk_seq [max_chunks] int32, and with segments seg_first [N+1] and seg_seq
+// [max_segs] int32, each 256-byte aligned.
+size_t varlen_table_bytes(int N, int T, int C, int L) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  int64_t* cu_out = reinterpret_cast<int64_t*>(tables);
-  int* first = reinterpret_cast<int*>(tables + al((size_t)(N + 1) * 8));
-  int* seq = reinterpret_cast<int*>(tables + al((size_t)(N + 1) * 8) + al((size_t)(N + 1) * 4));
+  size_t b = al((size_t)(N + 1) * 8) + al((size_t)(N + 1) * 4) + al((size_t)varlen_max_chunks(N, T, C) * 4);
+  if (L > 0) b += al((size_t)(N + 1) * 4) + al((size_t)varlen_max_segs(N, T, C, L) * 4);
+  return b;
+}
+
+hipError_t launch_varlen_plan(const int64_t* cu, int N, int T, int C, int L, char* tables, Varlen& vl,
+                              hipStream_t s) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* p = tables;
+  int64_t* cu_out = reinterpret_cast<int64_t*>(p);
+  p += al((size_t)(N + 1) * 8);
+  int* first = reinterpret_cast<int*>(p);
+  p += al((size_t)(N + 1) * 4);
+  int* seq = reinterpret_cast<int*>(p);
+  p += al((size_t)varlen_max_chunks(N, T, C) * 4);
   vl.cu = cu_out;
   vl.chunk_first = first;
   vl.chunk_seq = seq;
   vl.nseq = N;
   vl.max_chunks = varlen_max_chunks(N, T, C);
+  vl.seg_len = L;
+  vl.max_segs = varlen_max_segs(N, T, C, L);
+  if (L > 0) {
+    vl.seg_first = reinterpret_cast<int*>(p);
+    p += al((size_t)(N + 1) * 4);
+    vl.seg_seq = reinterpret_cast<int*>(p);
+  }
   hipLaunchKernelGGL(gdn2_varlen_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, N, T, C, vl.max_chunks, cu_out,
-                     first, seq);
+                     first, seq, L, vl.max_segs, const_cast<int*>(vl.seg_first), const_cast<int*>(vl.seg_seq));
   return hipGetLastError();
 }
 

@@ -168,3 +168,54 @@ def test_decode_slots(dtype):
     assert rel_err(f64(Sp), ref_pool) <= tol
     for s in (1, 2, 4, 5, 7):  # untouched slots
         assert torch.equal(Sp[s].cpu(), pool[s])
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("fp32", 32, 64), ("bf16", 128, 128), ("bf16", 16, 64)])
+def test_varlen_two_level_chain(dtype, Dk, Dv):
+    """Few sequence-heads and at least 32 chunks: the packed forward cuts the long sequences into segments
+    (parallel segment maps, fp32 composition, re-run). Segments never cross a sequence boundary; empty and
+    one-segment sequences pass through."""
+    from delta_rule_recurrent_gdn_amd import _lib
+    lengths, C, H = [1500, 37, 900, 3, 0, 600], 32, 2
+    N, T = len(lengths), int(sum(lengths))
+    lib = _lib.load()
+    code = _lib.GDN2_F32 if dtype == "fp32" else _lib.GDN2_BF16
+    mc = gdn2_varlen_max_chunks(N, T, C)
+    per_chunk = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, C, 1, Dk, Dv, C, code)
+    ws = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, N, T, H, Dk, Dv, C, code)
+    assert ws > H * mc * per_chunk + H * (Dk * Dk + 2 * Dk * Dv) * 4  # segment maps present
+    inp, cu = _packed(lengths, H, Dk, Dv, dtype, seed=110 + Dk)
+    d = to_dev(inp)
+    o, Sf, cs = gdn2_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], cu.cuda(), d["S0"],
+                                chunk=C, want_chunk_states=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward_varlen(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], cu,
+                                         inp["S0"])
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    eo, es = rel_err(f64(o), o_ref), rel_err(f64(Sf), S_ref)
+    print(f"varlen two-level {dtype} Dk={Dk} Dv={Dv}: err o {eo:.2e} S {es:.2e}")
+    assert eo <= tol and es <= tol
+    cs64 = f64(cs)
+    starts = np.concatenate([[0], np.cumsum(lengths)])
+    cmap = _chunk_map(lengths, C)
+    for g in (0, 7, 8, 9, 30, 46, 47, 48, len(cmap) - 1):  # around segment and sequence boundaries
+        n, c, t = cmap[g]
+        if c == 0:
+            ref = f64(inp["S0"])[n]
+        else:
+            a = int(starts[n])
+            sl = {k_: v_[:, a:t] for k_, v_ in inp.items() if k_ != "S0"}
+            _, ref = oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["b"], sl["w"],
+                                    inp["S0"][n:n + 1])
+            ref = ref[0]
+        assert rel_err(cs64[:, g], ref) <= tol, (g, n, c)
+    # the backward's state recompute takes the same path
+    dO = torch.from_numpy(np.random.default_rng(5).standard_normal((1, T, H, Dv)).astype(np.float32))
+    dO = dO.to(synth.torch_dtype(dtype)).cuda()
+    g1 = gdn2_bwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO, cu.cuda(), S0=d["S0"],
+                         chunk_states=cs, chunk=C)
+    g2 = gdn2_bwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO, cu.cuda(), S0=d["S0"],
+                         chunk=C)
+    torch.cuda.synchronize()
+    for n_ in GRADS:
+        assert torch.equal(g1[n_], g2[n_]), n_
