@@ -62,6 +62,7 @@ struct BwdPlan {
   size_t part;     // one [B,H,NC,Dk,Dv] fp32 array, 256-byte aligned
   size_t records;  // records region (two-stage only): forward records for a
                    // state recompute, then the backward records
+  size_t seg;      // the two-level reverse chain's segment maps (0: not used)
   size_t need;
 };
 
@@ -76,8 +77,11 @@ BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
     p.records = rb > fw ? rb : fw;
   }
   // gradient of every chunk's exit state, room to recompute the chunk entry
-  // states when the caller passes none, and the records
-  p.need = 2 * p.part + p.records;
+  // states when the caller passes none, the records, and the reverse chain's
+  // segment maps for few heads and long sequences
+  p.records = (p.records + 255) & ~(size_t)255;
+  p.seg = p.two_stage ? gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk) : 0;
+  p.need = 2 * p.part + p.records + p.seg;
   return p;
 }
 
@@ -135,7 +139,8 @@ VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, b
     p.part = al256((size_t)H * mc * Dk * Dv * 4);
     const size_t bwd_rec = (size_t)H * mc * gdn2::record_bytes(Dk, chunk, f32, 1);
     p.records = al256(bwd_rec > fwd_rec ? bwd_rec : fwd_rec);
-    p.need = p.tables + 2 * p.part + p.records;
+    // then the reverse chain's segment maps
+    p.need = p.tables + 2 * p.part + p.records + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
   }
   return p;
 }
@@ -307,7 +312,8 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
                   dS0, B, T, H, Dk, Dv, chunk, f32};
   set_gate_flags(a, flags);
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
-  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
+  if (st == GDN2_OK)
+    st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? rec + plan.records : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;
@@ -430,7 +436,7 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   set_gate_flags(a, flags);
   a.vl = f.vl;
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
-  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, s));
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, p.L > 0 ? rec + p.records : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;

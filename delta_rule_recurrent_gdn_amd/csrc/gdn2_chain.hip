@@ -362,9 +362,18 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
 // units; dS and dU stay in accumulators as in the forward chain, and dO is
 // gathered straight into right-operand fragments, one chunk ahead.
 // dS_chunks[n] receives the exit-state gradient of chunk n; dS0 the final one.
+//
+// Segmented (two-level) form, the mirror image of the forward's: per chunk
+// dS_entry = (Diag(gamma) - W^T Kb) dS_exit + (terms in dO), so a segment maps
+// the gradient at its exit to the one at its entry, dS_in = M dS_out + N.
+// (1) every segment but the first in time runs from a zero exit gradient on
+// its value columns (-> N) and on DK identity columns without dO (-> M);
+// (2) a short pass composes dS_out(s-1) = M_s dS_out(s) + N_s backwards from
+// dS_final; (3) every segment runs again from its true exit gradient, writing
+// its chunks' exit gradients and (first segment) dS0.
 // ---------------------------------------------------------------------------
-template <int DK, int C, bool F32IN, int NCT, int NWV>
-__global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, const char* rec_base) {
+template <int DK, int C, bool F32IN, int NCT, int NWV, bool SEG>
+__global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, const char* rec_base, SegArgs sg) {
   using Rec = Record<DK, C, F32IN, 1>;
   using F = Frag<F32IN>;
   constexpr int RC = C / 16, RK = DK / 16, UK = Rec::UK, UC = Rec::UC;
@@ -378,30 +387,82 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
   const int Dv = a.Dv, T = a.T, H = a.H;
-  const int ncg = Dv / kCols;
   const int nbh = seq_items(a.vl, a.B, H);
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int bh = (slot / ncg) * 8 + xcd, cg = slot % ncg;
-  if (bh >= nbh) return;
+  int bh, cg, n_begin = 0, n_end = 1 << 30;
+  int64_t segIdx = 0;               // this segment's slot in M, N, S_in (here: exit gradients)
+  bool seg_first = true, seg_last = true;
+  if constexpr (SEG) {
+    // block -> (segment, column group) as in the forward's segmented chain, except that the map
+    // pass covers every segment but the FIRST of each (batch row or sequence, head)
+    const int ncg = ((sg.mode == kSegMap ? Dv + DK : Dv) + kCols - 1) / kCols;
+    const int item = blockIdx.x / ncg;
+    cg = blockIdx.x - item * ncg;
+    int local;
+    if (a.vl.cu == nullptr) {
+      const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
+      bh = item / nsb;
+      local = item - bh * nsb + (sg.mode == kSegMap ? 1 : 0);
+      segIdx = (int64_t)bh * sg.nseg + local;
+      seg_last = local == sg.nseg - 1;
+    } else {
+      const int h = item / a.vl.max_segs, gsg = item - h * a.vl.max_segs;
+      const int sq = a.vl.seg_seq[gsg];
+      if (sq < 0) return;  // past the last segment
+      local = gsg - a.vl.seg_first[sq];
+      seg_last = gsg == a.vl.seg_first[sq + 1] - 1;
+      if (sg.mode == kSegMap && local == 0) return;  // no map needed before a sequence's first segment
+      bh = sq * H + h;
+      segIdx = (int64_t)h * a.vl.max_segs + gsg;
+    }
+    seg_first = local == 0;
+    n_begin = local * sg.seg_len;
+    n_end = n_begin + sg.seg_len;
+  } else {
+    const int ncg = Dv / kCols;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bh = (slot / ncg) * 8 + xcd;
+    cg = slot % ncg;
+    if (bh >= nbh) return;
+  }
   // the (batch row or packed sequence, head) walked here: its chunks, tokens and states
   const SeqLoc sl = seq_loc(a.vl, T, H, DK, Dv, C, bh);
-  const int NC = sl.nchunks;
+  n_end = min(n_end, sl.nchunks);
   const int j0 = cg * kCols + wid * 16 * NCT;
+  // segmented: waves past the columns only copy records; identity columns (map pass) have no dO
+  const bool active = !SEG || j0 < (sg.mode == kSegMap ? Dv + DK : Dv);
+  const bool ident = SEG && j0 >= Dv;
+  const bool outs = !SEG || (sg.mode == kSegRun && active);  // exit gradients and dS0
+  const bool has_do = active && !ident;
   const int64_t rowV = (int64_t)H * Dv;
   const int64_t baseV = sl.baseV + j0;
   const int64_t stBase = sl.state * DK * Dv + j0;
   const char* recs = rec_base + sl.item0 * Rec::kBytes;
 
+  // carried gradient: dS_final (or zero); segmented map pass: zero, identity on the identity
+  // columns; segmented run: dS_final for the last segment, else the composed exit gradient
+  const float* Gent = a.dS_final;
+  int64_t gOff = stBase;
+  if constexpr (SEG) {
+    if (sg.mode == kSegMap) {
+      Gent = nullptr;
+    } else if (!seg_last) {
+      Gent = sg.S_in;
+      gOff = segIdx * DK * Dv + j0;
+    }
+  }
   f32x4 accD[RK][NCT];
 #pragma unroll
   for (int R = 0; R < RK; ++R)
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       accD[R][c] = zero4();
-      if (a.dS_final) {
+      if (ident) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accD[R][c][i] = (16 * R + 4 * lg + i == j0 - Dv + 16 * c + lr) ? 1.f : 0.f;
+      } else if (Gent && active) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          accD[R][c][i] = a.dS_final[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
+          accD[R][c][i] = Gent[gOff + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
       }
     }
 
@@ -425,20 +486,28 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
         }
   };
 
-  if (NC > 0) {  // an empty packed sequence has no chunk: dS0 = dS_final
-    dma_units(recs + (int64_t)(NC - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((NC - 1) & 1) * kBuf : 0),
+  if (n_begin < n_end) {  // an empty packed sequence has no chunk: dS0 = dS_final
+    dma_units(recs + (int64_t)(n_end - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((n_end - 1) & 1) * kBuf : 0),
               Rec::kChainUnits, wid, NWV);
-    load_do(NC - 1);
+    if (has_do) load_do(n_end - 1);
+  }
+  if (!has_do) {  // identity columns (and idle waves): no dO
+#pragma unroll
+    for (int u = 0; u < NDU; ++u)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int j = 0; j < NDE; ++j) rdo[u][c][j] = RawT(0);
   }
 
-  for (int n = NC - 1; n >= 0; --n) {
+  for (int n = n_end - 1; n >= n_begin; --n) {
     char* buf = smem + (NBUF == 2 ? (n & 1) * kBuf : 0);
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n+1
-    if (NBUF == 2 && n > 0)
+    if (NBUF == 2 && n > n_begin)
       dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * kBuf, Rec::kChainUnits, wid, NWV);
 
-    {
+    if (outs) {
       float* ws = a.dS_chunks + (sl.item0 + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)
@@ -460,7 +529,8 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
           if constexpr (F32IN) dof[u][c][j] = rdo[u][c][j];
           else dof[u][c][j] = static_cast<_Float16>(bf16_bits_to_f32(rdo[u][c][j]));
         }
-    if (n > 0) load_do(n - 1);
+    if (has_do && n > n_begin) load_do(n - 1);
+    if (active) {
 
     const uint4* uPT = reinterpret_cast<const uint4*>(buf + Rec::u0 * 1024) + l;
     const uint4* uKb = reinterpret_cast<const uint4*>(buf + Rec::u1 * 1024) + l;
@@ -564,12 +634,29 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
       }
     }
 
-    if (NBUF == 1 && n > 0) {
+    }  // active
+
+    if (NBUF == 1 && n > n_begin) {
       __syncthreads();  // every wave is done reading the single buffer
       dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem, Rec::kChainUnits, wid, NWV);
     }
   }
 
+  if constexpr (SEG) {
+    if (sg.mode == kSegMap && active) {
+      // entry gradient of a zero-exit segment: N (value columns) or M (identity columns)
+      float* dst = ident ? sg.M + segIdx * DK * DK + (j0 - Dv) : sg.N + segIdx * DK * Dv + j0;
+      const int ld = ident ? DK : Dv;
+#pragma unroll
+      for (int R = 0; R < RK; ++R)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * R + 4 * lg + i) * ld + 16 * c + lr] = accD[R][c][i];
+      return;
+    }
+    if (!seg_first || !active) return;
+  }
   if (a.dS0) {
 #pragma unroll
     for (int R = 0; R < RK; ++R)
@@ -607,8 +694,10 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
 // matrix cores, N_s as the initial accumulator: wave w owns row tiles 2w and
 // 2w+1 (times DK / 128) of both 16-column tiles.
 template <int DK>
+// reverse (the backward's exit gradients): S_in(s-1) = M_s S_in(s) + N_s from
+// S_in(count-1) = start (dS_final), empty sequences copying start to empty_out (dS0).
 __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
-                                                              Varlen vl, int H, int Dv) {
+                                                              Varlen vl, int H, int Dv, bool reverse) {
   constexpr int LDM = DK + 4, LDS_ = 32 + 4;
   constexpr int NM4 = DK * DK / 4;              // float4 of one M
   constexpr int MV = (NM4 + 255) / 256;         // per thread
@@ -635,8 +724,10 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     sS[d * LDS_ + c] = S0 ? S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
   }
   float4 mr[MV];
+  // step i reads the map of segment src(i) and writes the entry of the next one in walking order
+  auto src = [&](int i) { return reverse ? count - 1 - i : i; };
   auto load_m = [&](int s) {
-    const float4* M = reinterpret_cast<const float4*>(sg.M + (base + s) * DK * DK);
+    const float4* M = reinterpret_cast<const float4*>(sg.M + (base + src(s)) * DK * DK);
 #pragma unroll
     for (int i = 0; i < MV; ++i)
       if (tid + 256 * i < NM4) mr[i] = M[tid + 256 * i];
@@ -651,7 +742,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   }
   if (count > 1) load_m(0);
   for (int s = 0; s + 1 < count; ++s) {
-    const int64_t sb = base + s;
+    const int64_t sb = base + src(s);
 #pragma unroll
     for (int i = 0; i < MV; ++i) {
       const int e = tid + 256 * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
@@ -687,7 +778,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
       }
     }
     __syncthreads();  // every wave is done reading M_s and S_in(s)
-    float* out = sg.S_in + (sb + 1) * DK * Dv + j0;
+    float* out = sg.S_in + (reverse ? sb - 1 : sb + 1) * DK * Dv + j0;
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
       const int R = wid + 4 * t;
@@ -756,7 +847,7 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments
     hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, a.S_final, sg,
-                       a.vl, a.H, a.Dv);
+                       a.vl, a.H, a.Dv, false);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true entry state
@@ -820,14 +911,61 @@ static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStrea
     const int ncg = a.Dv / (16 * NCT * NWV);
     const int nbh = seq_items(a.vl, a.B, a.H);
     const int grid = ((nbh + 7) / 8) * 8 * ncg;
-    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, NCT, NWV>), dim3(grid), dim3(NWV * 64), 0, s, a, rec);
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, NCT, NWV, false>), dim3(grid), dim3(NWV * 64), 0, s, a,
+                       rec, SegArgs{});
+    return hipGetLastError();
+  }
+}
+
+// The two-level reverse chain: G segments per (batch row, head) of a dense
+// batch, or the packed batch's segment slots; seg holds M, N and the composed
+// exit gradients (fwd_seg_bytes / varlen_seg_bytes).
+template <int DK, int C, bool F32IN>
+static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* seg, int G, hipStream_t s) {
+  using Rec = Record<DK, C, F32IN, 1>;
+  constexpr int kCols = 16 * 8;  // 8 waves of 16 columns
+  if constexpr (Rec::kChainBytes > 160 * 1024) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    const bool packed = a.vl.cu != nullptr;
+    const int NC = (a.T + C - 1) / C, nbh = seq_items(a.vl, a.B, a.H);
+    const int64_t slots = packed ? (int64_t)a.H * a.vl.max_segs : (int64_t)nbh * G;
+    SegArgs sg;
+    sg.nseg = packed ? 0 : G;
+    sg.seg_len = packed ? a.vl.seg_len : (NC + G - 1) / G;
+    sg.M = reinterpret_cast<float*>(seg);
+    sg.N = sg.M + (size_t)slots * DK * DK;
+    sg.S_in = sg.N + (size_t)slots * DK * a.Dv;
+    const int ncg_map = (a.Dv + DK + kCols - 1) / kCols, ncg_run = (a.Dv + kCols - 1) / kCols;
+    // (1) maps of every segment but the first of each (batch row or sequence, head)
+    sg.mode = kSegMap;
+    const int64_t map_items = packed ? slots : (int64_t)nbh * (G - 1);
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(map_items * ncg_map)),
+                       dim3(512), 0, s, a, rec, sg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // (2) exit gradients of the earlier segments, composed backwards from dS_final
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.dS_final, a.dS0,
+                       sg, a.vl, a.H, a.Dv, true);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // (3) every segment from its true exit gradient
+    sg.mode = kSegRun;
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(slots * ncg_run)),
+                       dim3(512), 0, s, a, rec, sg);
     return hipGetLastError();
   }
 }
 
 template <int DK, int C, bool F32IN>
-static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, hipStream_t s) {
+static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, char* seg, hipStream_t s) {
   const int nbh = seq_items(a.vl, a.B, a.H);
+  if (a.vl.cu != nullptr) {
+    if (seg && a.vl.seg_len > 0) return launch_chain_bwd_seg<DK, C, F32IN>(a, rec, seg, 0, s);
+  } else {
+    const int G = seg ? fwd_segments(a.B, a.H, a.T, DK, a.Dv, C) : 1;
+    if (G > 1) return launch_chain_bwd_seg<DK, C, F32IN>(a, rec, seg, G, s);
+  }
   if (a.Dv == 16) return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
   const int tiles = a.Dv / 32;
   if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 2>(a, rec, s);
@@ -836,28 +974,28 @@ static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, hipStrea
 }
 
 template <int DK, bool F32IN>
-static hipError_t launch_chain_bwd_k(const BwdArgs& a, const char* rec, hipStream_t s) {
+static hipError_t launch_chain_bwd_k(const BwdArgs& a, const char* rec, char* seg, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_chain_bwd_c<DK, 16, F32IN>(a, rec, s);
-    case 32: return launch_chain_bwd_c<DK, 32, F32IN>(a, rec, s);
-    case 64: return launch_chain_bwd_c<DK, 64, F32IN>(a, rec, s);
+    case 16: return launch_chain_bwd_c<DK, 16, F32IN>(a, rec, seg, s);
+    case 32: return launch_chain_bwd_c<DK, 32, F32IN>(a, rec, seg, s);
+    case 64: return launch_chain_bwd_c<DK, 64, F32IN>(a, rec, seg, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool F32IN>
-static hipError_t launch_chain_bwd_f(const BwdArgs& a, const char* rec, hipStream_t s) {
+static hipError_t launch_chain_bwd_f(const BwdArgs& a, const char* rec, char* seg, hipStream_t s) {
   switch (a.Dk) {
-    case 16: return launch_chain_bwd_k<16, F32IN>(a, rec, s);
-    case 32: return launch_chain_bwd_k<32, F32IN>(a, rec, s);
-    case 64: return launch_chain_bwd_k<64, F32IN>(a, rec, s);
-    case 128: return launch_chain_bwd_k<128, F32IN>(a, rec, s);
+    case 16: return launch_chain_bwd_k<16, F32IN>(a, rec, seg, s);
+    case 32: return launch_chain_bwd_k<32, F32IN>(a, rec, seg, s);
+    case 64: return launch_chain_bwd_k<64, F32IN>(a, rec, seg, s);
+    case 128: return launch_chain_bwd_k<128, F32IN>(a, rec, seg, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_chain_bwd(const BwdArgs& a, const char* rec, hipStream_t s) {
-  return a.f32_inputs ? launch_chain_bwd_f<true>(a, rec, s) : launch_chain_bwd_f<false>(a, rec, s);
+hipError_t launch_chain_bwd(const BwdArgs& a, const char* rec, char* seg, hipStream_t s) {
+  return a.f32_inputs ? launch_chain_bwd_f<true>(a, rec, seg, s) : launch_chain_bwd_f<false>(a, rec, seg, s);
 }
 
 }  // namespace gdn2

@@ -146,3 +146,24 @@ def test_bwd_gdn_special_case_matches_oracle():
     ref = _oracle_bwd(inp)
     for name in GRADS + ("dS0",):
         assert rel_err(f64(g[name]), ref[name]) <= TOL_F32, name
+
+
+@pytest.mark.parametrize("B,H,T,Dk,Dv,C,dtype", [
+    (1, 2, 33 * 16 + 5, 32, 32, 16, "fp32"),     # 34 chunks: 4 segments
+    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # config-shaped heads: 5 segments
+    (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16 identity columns after 64 value columns
+    (1, 1, 36 * 32, 64, 128, 32, "fp32"),
+])
+@pytest.mark.parametrize("use_states", [True, False], ids=["saved_states", "recomputed_states"])
+def test_bwd_two_level_reverse_chain(B, H, T, Dk, Dv, C, dtype, use_states):
+    """Few heads and at least 32 chunks: the reverse chain runs in segments (parallel segment maps of the
+    exit-gradient, fp32 composition from dS_final backwards, re-run); every gradient against the oracle."""
+    inp = synth.make_inputs(B, T, H, Dk, Dv, dtype, seed=120 + Dk + C, s0_std=0.3, grad=True)
+    dS = torch.from_numpy(np.random.default_rng(Dk + 1).standard_normal((B, H, Dk, Dv)).astype(np.float32))
+    g = _gpu_bwd(inp, C, dS, use_states=use_states)
+    ref = _oracle_bwd(inp, dS)
+    tol = TOL_F32 if dtype == "fp32" else TOL_GRAD
+    errs = {n: rel_err(f64(g[n]), ref[n]) for n in GRADS + ("dS0",)}
+    print("two-level bwd", (B, H, T, Dk, Dv, C, dtype), {k: f"{v:.1e}" for k, v in errs.items()})
+    for n, e in errs.items():
+        assert e <= tol, (n, e)

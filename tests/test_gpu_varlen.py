@@ -219,3 +219,10 @@ def test_varlen_two_level_chain(dtype, Dk, Dv):
     torch.cuda.synchronize()
     for n_ in GRADS:
         assert torch.equal(g1[n_], g2[n_]), n_
+    # against the oracle (the reverse chain is segmented as well)
+    dO_host = dO.cpu()
+    ref = oracle.backward_varlen(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], cu, inp["S0"],
+                                 dO_host)
+    gtol = TOL_F32 if dtype == "fp32" else TOL_GRAD
+    for n_ in GRADS:
+        assert rel_err(f64(g1[n_]), ref[n_]) <= gtol, n_
