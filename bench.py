@@ -176,9 +176,9 @@ def main():
     import synth
     from delta_rule_recurrent_gdn_amd import _lib, gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked
 
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS["fwd+bwd-B8-H16-T4096-d128"]
     B, T, H, D, C = cfg["B"], cfg["T"], cfg["H"], cfg["Dk"], cfg["chunk"]
-    inp = synth.config_inputs(4)
+    inp = synth.workload_inputs("fwd+bwd-B8-H16-T4096-d128")
     # the oracle baseline runs first, in forked worker processes, before this
     # process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(inp, heads=16)
@@ -198,48 +198,71 @@ def main():
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     need_f = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, _lib.GDN2_BF16)
     ws_f = torch.empty(max(need_f, 1), dtype=torch.uint8, device=dev)
+    # the training pair: the forward's record pass also writes the backward's records
+    need_r = lib.gdn2_records_bytes(B, T, H, D, D, C, _lib.GDN2_BF16)
+    recs = torch.empty(need_r, dtype=torch.uint8, device=dev)
+    need_br = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, _lib.GDN2_BF16)
+    ws_br = torch.empty(need_br, dtype=torch.uint8, device=dev)
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     sh = stream.cuda_stream
 
-    def fwd(single_pass=False):
+    def fwd(flags=0, x=d):
+        st = lib.gdn2_fwd_chunked_train(P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["b"]), P(x["w"]),
+                                        None, P(o), None, P(states), P(recs), need_r, P(ws_f), need_f, B, T, H, D, D,
+                                        C, _lib.GDN2_BF16, flags, sh)
+        _lib.check(st, "gdn2_fwd_chunked_train")
+
+    def bwd(flags=0, x=d, gb=None, gw=None, gla=None):
+        st = lib.gdn2_bwd_chunked_records(P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["b"]), P(x["w"]),
+                                          None, P(x["dO"]), None, P(states), P(recs), need_r, P(grads["dq"]),
+                                          P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"] if gla is None else gla),
+                                          P(grads["db"] if gb is None else gb), P(grads["dw"] if gw is None else gw),
+                                          P(dS0), P(ws_br), need_br,
+                                          B, T, H, D, D, C, _lib.GDN2_BF16, flags, sh)
+        _lib.check(st, "gdn2_bwd_chunked_records")
+
+    # the separate entry points (each call with its own record pass), for comparison
+    def fwd_sep(single_pass=False):
         wsp, wsn = (None, 0) if single_pass else (P(ws_f), need_f)
         st = lib.gdn2_fwd_chunked(P(d["q"]), P(d["k"]), P(d["v"]), P(d["log_alpha"]), P(d["b"]), P(d["w"]), None,
                                   P(o), None, P(states), wsp, wsn, B, T, H, D, D, C, _lib.GDN2_BF16, sh)
         _lib.check(st, "gdn2_fwd_chunked")
 
-    def bwd():
+    def bwd_sep():
         st = lib.gdn2_bwd_chunked(P(d["q"]), P(d["k"]), P(d["v"]), P(d["log_alpha"]), P(d["b"]), P(d["w"]), None,
                                   P(d["dO"]), None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
                                   P(grads["dlog_alpha"]), P(grads["db"]), P(grads["dw"]), P(dS0), P(ws), need,
                                   B, T, H, D, D, C, _lib.GDN2_BF16, sh)
         _lib.check(st, "gdn2_bwd_chunked")
 
-    def step():
-        fwd()
-        bwd()
+    def timed_pair(f, b, n, warm):
+        """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream)."""
+        for _ in range(warm):
+            f()
+            b()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
+        ev[0].record(stream)
+        for i in range(n):
+            f()
+            ev[2 * i + 1].record(stream)
+            b()
+            ev[2 * i + 2].record(stream)
+        torch.cuda.synchronize()
+        tf = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)) / n
+        tb = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n)) / n
+        return tf, tb, ev[0].elapsed_time(ev[-1]) / n
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     t_wall = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        fwd()
-        ev[2 * i + 1].record(stream)
-        bwd()
-        ev[2 * i + 2].record(stream)
-    torch.cuda.synchronize()
+    t_fwd, t_bwd, ms_step = timed_pair(fwd, bwd, args.steps, args.warmup)
     wall = time.perf_counter() - t_wall
-    t_fwd = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps  # ms
-    t_bwd = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
-    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    s_fwd, s_bwd, s_step = timed_pair(fwd_sep, bwd_sep, min(args.steps, 10), 1)
     # the single-pass forward (no workspace), timed on its own for comparison
-    fwd(single_pass=True)
+    fwd_sep(single_pass=True)
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record(stream)
     for _ in range(args.steps):
-        fwd(single_pass=True)
+        fwd_sep(single_pass=True)
     s1.record(stream)
     torch.cuda.synchronize()
     t_fwd_single = s0.elapsed_time(s1) / args.steps
@@ -252,13 +275,14 @@ def main():
     # dominant launch: the entry-point call with the larger share of the step
     # (each call is its kernels back to back on one stream)
     if t_fwd >= t_bwd:
-        tkey = "fwd_launch_traffic_bytes"
-        dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked launch (gdn2_prep_kernel forward records + gdn2_chain_fwd_kernel, "
-                                     "chunk states saved)", t_fwd, by_f, F_f)
+        tkey = "train_fwd_launch_traffic_bytes"
+        dom, t_dom, by_dom, f_dom = ("gdn2_fwd_chunked_train launch (gdn2_prep_kernel forward and backward records "
+                                     "+ gdn2_chain_fwd_kernel, chunk states saved)", t_fwd, by_f, F_f)
     else:
-        tkey = "bwd_launch_traffic_bytes"
-        dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked launch (gdn2_prep_kernel backward records + "
-                                     "gdn2_chain_bwd_kernel + gdn2_bwd_grad_kernel)", t_bwd, by_b, F_b)
+        tkey = "bwd_records_launch_traffic_bytes"
+        dom, t_dom, by_dom, f_dom = ("gdn2_bwd_chunked_records launch (gdn2_chain_bwd_kernel + "
+                                     "gdn2_bwd_grad_kernel; its records come from the training forward)", t_bwd,
+                                     by_b, F_b)
     achieved = by_dom / (t_dom / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(tkey), "kernel": dom,
@@ -269,13 +293,17 @@ def main():
         "metric": "GDN-2 fwd+bwd tokens/s (H=16,d=128,T=4K) + % MFMA peak; decode % HBM peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded normal / sigmoid / -softplus draws, config 4 recipe)",
-        "config": {"workload": "GDN-2 chunked forward (saving chunk states) + gate-aware backward, "
+        "dtype": "bf16", "data": "synthetic (seeded normal / sigmoid / -softplus draws, workload "
+                                 "fwd+bwd-B8-H16-T4096-d128, seed 4)",
+        "config": {"workload": "GDN-2 training step: gdn2_fwd_chunked_train (chunkwise forward saving chunk "
+                               "states and the backward records) + gdn2_bwd_chunked_records (gate-aware backward), "
                                "B=8 H=16 T=4096 d_k=d_v=128 chunk=64, bf16 q/k/v/b/w/dO, fp32 log_alpha, "
                                "fp32 outputs and gradients",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,
                    "parallelism": "single GPU"},
         "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4), "fwd_single_pass_ms": round(t_fwd_single, 4),
+        "separate_calls": {"fwd_ms": round(s_fwd, 4), "bwd_ms": round(s_bwd, 4), "ms_per_step": round(s_step, 4),
+                           "note": "gdn2_fwd_chunked + gdn2_bwd_chunked, each with its own record pass"},
         "mfma_frac": round(mfma, 4),
         "hbm_frac_step": round((by_f + by_b) / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline,
@@ -283,7 +311,7 @@ def main():
     }
 
     if not args.no_front_end:
-        # row f1, the fused gate front end: the same training step with the gates passed as pre-activations
+        # the fused gate front end: the same training step with the gates passed as pre-activations
         # (b, w = sigmoid(.), log_alpha = -softplus(.) inside the kernels; gradients with respect to the
         # pre-activations), against the same step with the activations and their chain rule done as torch
         # elementwise passes around the plain entry points
@@ -293,29 +321,16 @@ def main():
         FLAG = _lib.GDN2_FLAG_RAW_GATES
 
         def raw_step():
-            st = lib.gdn2_fwd_chunked_ex(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(rd["log_alpha"]), P(rd["b"]),
-                                         P(rd["w"]), None, P(o), None, P(states), P(ws_f), need_f, B, T, H, D, D, C,
-                                         _lib.GDN2_BF16, FLAG, sh)
-            _lib.check(st, "gdn2_fwd_chunked_ex")
-            st = lib.gdn2_bwd_chunked_ex(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(rd["log_alpha"]), P(rd["b"]),
-                                         P(rd["w"]), None, P(rd["dO"]), None, P(states), P(grads["dq"]),
-                                         P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"]), P(grads["db"]),
-                                         P(grads["dw"]), P(dS0), P(ws), need, B, T, H, D, D, C, _lib.GDN2_BF16,
-                                         FLAG, sh)
-            _lib.check(st, "gdn2_bwd_chunked_ex")
+            fwd(FLAG, rd)
+            bwd(FLAG, rd)
 
         def unfused_step():
             bb = torch.sigmoid(rd["b"])
             ww = torch.sigmoid(rd["w"])
             la = -torch.nn.functional.softplus(rd["log_alpha"])
-            st = lib.gdn2_fwd_chunked(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(la), P(bb), P(ww), None, P(o), None,
-                                      P(states), P(ws_f), need_f, B, T, H, D, D, C, _lib.GDN2_BF16, sh)
-            _lib.check(st, "gdn2_fwd_chunked")
-            st = lib.gdn2_bwd_chunked(P(rd["q"]), P(rd["k"]), P(rd["v"]), P(la), P(bb), P(ww), None, P(rd["dO"]),
-                                      None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
-                                      P(grads["dlog_alpha"]), P(grads["db"]), P(grads["dw"]), P(dS0), P(ws), need,
-                                      B, T, H, D, D, C, _lib.GDN2_BF16, sh)
-            _lib.check(st, "gdn2_bwd_chunked")
+            act = dict(rd, b=bb, w=ww, log_alpha=la)
+            fwd(0, act)
+            bwd(0, act)
             grads["db"].mul_(bb * (1 - bb))
             grads["dw"].mul_(ww * (1 - ww))
             grads["dlog_alpha"].mul_(-torch.sigmoid(rd["log_alpha"]))
@@ -332,14 +347,14 @@ def main():
             torch.cuda.synchronize()
             fe[name] = round(f0.elapsed_time(f1) / 5, 4)
         fe["fused_tokens_per_s"] = round(tokens / (fe["fused_ms_per_step"] / 1e3), 1)
-        fe["workload"] = ("config-4 training step (forward saving chunk states + backward) with pre-activation "
-                          "gates b, w (bf16) and a (fp32); unfused = torch sigmoid / softplus passes before and "
-                          "chain-rule passes after the plain entry points")
+        fe["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with pre-activation gates b, w "
+                          "(bf16) and a (fp32); unfused = torch sigmoid / softplus passes before and chain-rule "
+                          "passes after the same entry points without the flag")
         out["front_end"] = fe
         del rd
 
     if not args.no_gate_granularity:
-        # row f4, gate granularity: the config-4 step with per-head scalar gates ([B, T, H] tensors,
+        # gate granularity: the same training step with per-head scalar gates ([B, T, H] tensors,
         # broadcast inside the kernels): KDA (one beta for both gates) and Gated DeltaNet (also a scalar decay)
         rng_g = torch.Generator(device="cpu").manual_seed(6)
         beta = torch.sigmoid(torch.randn(B, T, H, generator=rng_g)).to(torch.bfloat16).to(dev)
@@ -347,15 +362,9 @@ def main():
         gsc = {n: torch.empty(B, T, H, device=dev) for n in ("db", "dw", "dlog_alpha")}
 
         def scalar_step(flags, la):
-            st = lib.gdn2_fwd_chunked_ex(P(d["q"]), P(d["k"]), P(d["v"]), P(la), P(beta), P(beta), None, P(o), None,
-                                         P(states), P(ws_f), need_f, B, T, H, D, D, C, _lib.GDN2_BF16, flags, sh)
-            _lib.check(st, "gdn2_fwd_chunked_ex")
-            st = lib.gdn2_bwd_chunked_ex(P(d["q"]), P(d["k"]), P(d["v"]), P(la), P(beta), P(beta), None, P(d["dO"]),
-                                         None, P(states), P(grads["dq"]), P(grads["dk"]), P(grads["dv"]),
-                                         P(gsc["dlog_alpha"] if la is adec else grads["dlog_alpha"]),
-                                         P(gsc["db"]), P(gsc["dw"]), P(dS0), P(ws), need, B, T, H, D, D, C,
-                                         _lib.GDN2_BF16, flags, sh)
-            _lib.check(st, "gdn2_bwd_chunked_ex")
+            x = dict(d, log_alpha=la, b=beta, w=beta)
+            fwd(flags, x)
+            bwd(flags, x, gb=gsc["db"], gw=gsc["dw"], gla=gsc["dlog_alpha"] if la is adec else None)
 
         gg = {}
         SB, SW, SD = _lib.GDN2_FLAG_SCALAR_B, _lib.GDN2_FLAG_SCALAR_W, _lib.GDN2_FLAG_SCALAR_DECAY
@@ -371,13 +380,14 @@ def main():
             torch.cuda.synchronize()
             gg[name] = round(g0.elapsed_time(g1) / 5, 4)
         gg["channel_wise_ms_per_step"] = round(ms_step, 4)
-        gg["workload"] = ("config-4 training step with per-head scalar gates: KDA = one beta [B,T,H] for both "
-                          "gates, Gated DeltaNet = also a scalar decay [B,T,H]; channel-wise = the main step")
+        gg["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with per-head scalar gates: KDA = "
+                          "one beta [B,T,H] for both gates, Gated DeltaNet = also a scalar decay [B,T,H]; "
+                          "channel-wise = the main step")
         out["gate_granularity"] = gg
         del beta, adec, gsc
 
     if not args.no_varlen:
-        # row f3, packed variable-length batches: the same 8 x 4096 = 32768 tokens of H = 16 heads (d = 128,
+        # packed variable-length batches: the same 8 x 4096 = 32768 tokens of H = 16 heads (d = 128,
         # chunk 64, bf16) cut into documents of seeded lengths (uniform 256 .. 8192, the last one takes the
         # remainder), packed along T; one training step = gdn2_fwd_varlen (saving chunk states) +
         # gdn2_bwd_varlen
@@ -426,8 +436,8 @@ def main():
         del vstates, vws_f, vws_b, vo
 
     if not args.no_decode:
-        c3 = synth.CONFIGS[3]
-        dec = synth.config_inputs(3)
+        c3 = synth.WORKLOADS["decode-B256-H16-d128-128steps"]
+        dec = synth.workload_inputs("decode-B256-H16-d128-128steps")
         dd = {k: v.to(dev) for k, v in dec.items()}
         S = dd["S0"].clone()
         od = torch.empty(c3["B"], c3["H"], c3["Dv"], device=dev)
@@ -461,11 +471,12 @@ def main():
         del dd, dec, xs, S
 
     if not args.no_curve:
-        # config 2: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk states) at each T.
+        # the long-sequence sweep: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk
+        # states) at each T.
         # Few heads and long sequences: the two-stage forward takes the two-level chain here.
         curve = {}
-        for Tc in synth.CONFIGS[2]["T"]:
-            ci = synth.config_inputs(2, T=Tc)
+        for Tc in synth.WORKLOADS["fwd-long-B1-H16-d128"]["T"]:
+            ci = synth.workload_inputs("fwd-long-B1-H16-d128", T=Tc)
             cd = {k: v.to(dev) for k, v in ci.items()}
             oc = torch.empty(1, Tc, 16, D, device=dev)
             Sf = torch.empty(1, 16, D, D, device=dev)

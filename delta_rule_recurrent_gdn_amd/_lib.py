@@ -25,6 +25,7 @@ GDN2_BF16 = 1
 GDN2_OP_FWD = 0
 GDN2_OP_DECODE = 1
 GDN2_OP_BWD = 2
+GDN2_OP_BWD_RECORDS = 3
 
 GDN2_FLAG_RAW_GATES = 1
 GDN2_FLAG_SCALAR_B = 2
@@ -47,6 +48,11 @@ SIGNATURES = {
                               _I, _I, _I, _I, _I, _I, _I, _P]),
     "gdn2_bwd_chunked_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                  _I, _I, _I, _I, _I, _I, _I, _U, _P]),
+    "gdn2_records_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "gdn2_fwd_chunked_train": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _I, _I, _I, _I, _I,
+                                    _I, _I, _U, _P]),
+    "gdn2_bwd_chunked_records": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _SZ, _I, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_varlen_max_chunks": (_I, [_I, _I, _I]),
     "gdn2_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gdn2_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _U,

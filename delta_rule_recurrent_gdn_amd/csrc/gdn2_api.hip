@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: the _ex entry points (flags)
+constexpr int kVersion = 300;  // 0.3.0: the training pair (forward writes the backward records)
 constexpr unsigned kKnownFlags =
     GDN2_FLAG_RAW_GATES | GDN2_FLAG_SCALAR_B | GDN2_FLAG_SCALAR_W | GDN2_FLAG_SCALAR_DECAY;
 
@@ -88,6 +88,15 @@ BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
 size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   return bwd_plan(B, T, H, Dk, Dv, chunk, f32).need;
 }
+
+// The training pair: the backward records (written by the training forward)
+// and the workspace of the backward that reads them (state gradients, then the
+// reverse chain's segment maps).
+size_t train_records(int B, int T, int H, int Dk, int chunk, bool f32) {
+  return (size_t)B * H * ((T + chunk - 1) / chunk) * gdn2::record_bytes(Dk, chunk, f32, 1);
+}
+
+size_t bwd_records_workspace(const BwdPlan& p) { return p.part + p.seg; }
 
 // Two-stage forward workspace: records, then T (w*v) for every chunk, then
 // (256-byte aligned) the segment maps and entry states of the two-level chain
@@ -194,7 +203,19 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
     if (!chunk_ok(chunk) || T == 0) return 0;
     return fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
   }
+  if (op == GDN2_OP_BWD_RECORDS) {
+    if (!chunk_ok(chunk) || T == 0) return 0;
+    const BwdPlan p = bwd_plan(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+    return p.two_stage ? bwd_records_workspace(p) : 0;
+  }
   return 0;
+}
+
+size_t gdn2_records_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dt) {
+  if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK || !chunk_ok(chunk) || T == 0) return 0;
+  const bool f32 = dt == GDN2_F32;
+  if (!bwd_plan(B, T, H, Dk, Dv, chunk, f32).two_stage) return 0;
+  return train_records(B, T, H, Dk, chunk, f32);
 }
 
 int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
@@ -314,6 +335,79 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK)
     st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? rec + plan.records : nullptr, s));
+  a.records = rec;
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
+  return st;
+}
+
+int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                           const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
+                           void* records, size_t records_bytes, void* workspace, size_t workspace_bytes, int B,
+                           int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
+  int st = check_common(B, T, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
+  const bool f32 = dt == GDN2_F32;
+  if (!bwd_plan(B, T, H, Dk, Dv, chunk, f32).two_stage) return GDN2_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {  // no chunks, no records: S_T = S0
+    st = check_ptrs({}, {S0, S_final});
+    if (st != GDN2_OK) return st;
+    if (S_final == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(S_final, S0, (int64_t)B * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, o, chunk_states, records}, {S0, S_final});
+  if (st != GDN2_OK) return st;
+  const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, f32);
+  if (workspace == nullptr || workspace_bytes < need || records_bytes < train_records(B, T, H, Dk, chunk, f32))
+    return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
+    return GDN2_ERR_ALIGN;
+  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, f32};
+  set_gate_flags(a, flags);
+  char* rec = static_cast<char*>(workspace);
+  float* ut = reinterpret_cast<float*>(rec + (size_t)B * H * ((T + chunk - 1) / chunk) *
+                                                 gdn2::fwd_record_bytes(Dk, chunk, f32));
+  st = hip_status(gdn2::launch_prep_train(a, rec, ut, static_cast<char*>(records), s));
+  if (st != GDN2_OK) return st;
+  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, fwd_seg_ptr(rec, B, T, H, Dk, Dv, chunk, f32), s));
+}
+
+int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                             const void* w, const float* S0, const void* dO, const float* dS_final,
+                             const float* chunk_states, const void* records, size_t records_bytes, float* dq,
+                             float* dk, float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
+                             void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv,
+                             int chunk, int dt, unsigned flags, void* stream) {
+  int st = check_common(B, T, H, Dk, Dv, dt);
+  if (st != GDN2_OK) return st;
+  if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
+  const bool f32 = dt == GDN2_F32;
+  const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
+  if (!plan.two_stage) return GDN2_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {  // S_T = S0, so dS0 = dS_final
+    st = check_ptrs({}, {dS_final, dS0});
+    if (st != GDN2_OK) return st;
+    if (dS0 == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(dS0, dS_final, (int64_t)B * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, dO, chunk_states, records, dq, dk, dv, dlog_alpha, db, dw},
+                  {S0, dS_final, dS0});
+  if (st != GDN2_OK) return st;
+  if (workspace == nullptr || workspace_bytes < bwd_records_workspace(plan) ||
+      records_bytes < train_records(B, T, H, Dk, chunk, f32))
+    return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
+    return GDN2_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  const char* rec = static_cast<const char*>(records);
+  gdn2::BwdArgs a{q,  k,  v,  log_alpha,  b,  w,  dO, dS_final, chunk_states, reinterpret_cast<float*>(ws),
+                  dq, dk, dv, dlog_alpha, db, dw, dS0, B, T, H, Dk, Dv, chunk, f32};
+  set_gate_flags(a, flags);
+  st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? ws + plan.part : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;

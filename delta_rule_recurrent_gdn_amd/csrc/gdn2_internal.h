@@ -214,6 +214,10 @@ size_t record_bytes(int Dk, int chunk, bool f32_inputs, int dir);
 // which writes a.dS_chunks and a.dS0; launch_bwd_grad then forms the
 // per-token gradients.
 hipError_t launch_prep_bwd(const FwdArgs& a, char* rec, hipStream_t stream);
+// Training forward's record pass: the forward records and T (w v) as
+// launch_prep_fwd, and in the same pass the backward records into brec (as
+// launch_prep_bwd would write them).
+hipError_t launch_prep_train(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t stream);
 // seg: nullable buffer of fwd_seg_bytes() (dense) or varlen_seg_bytes() (packed)
 // bytes; used (two-level reverse chain) under the same conditions as the forward's.
 hipError_t launch_chain_bwd(const BwdArgs& a, const char* rec, char* seg, hipStream_t stream);

@@ -38,22 +38,26 @@
 
 namespace gdn2 {
 
-// DIR 0: forward record (+ T (w v)); DIR 1: backward record (no value side).
+// DIR 0: forward record (+ T (w v)); DIR 1: backward record (no value side);
+// DIR 2: both records and T (w v) from one pass (the training forward).
 template <int DK, int C, bool F32IN, int DIR>
 struct PrepCfg {
   static constexpr int NT = 512, NW = NT / kWave;
   using KS = KSide<DK, C, F32IN, NT>;  // slice geometry and the blocked inversion
   using OpT = typename KS::OpT;
-  using Rec = Record<DK, C, F32IN, DIR>;
+  using Rec = Record<DK, C, F32IN, DIR == 1 ? 1 : 0>;  // the record `rec` points at
+  using RecB = Record<DK, C, F32IN, 1>;                // the backward record (DIR 1, 2)
   using F = Frag<F32IN>;
   static constexpr int NB = KS::NB, SW = KS::SW, NSL = KS::NSL;
   static constexpr int LDC = KS::LDC, LDCF = KS::LDCF, LDSW = KS::LDSW;
   static constexpr int OPB = sizeof(OpT);
-  static constexpr int DVM = DIR == 0 ? 128 : 0;  // largest value width staged
+  static constexpr int DVM = DIR != 1 ? 128 : 0;  // largest value width staged
   // thread -> (row, 4 channels of every slice): TPR threads per row
   static constexpr int TPR = SW / 4;
   static constexpr int RPW = kWave / TPR;        // rows per wave
-  static constexpr int NGT = KS::NGT, GPW = KS::GPW;
+  // Gram tiles: the strict-lower A tiles, then the causal term's tiles in the
+  // orientation of each record written (DIR 2: both, half again as many)
+  static constexpr int NGT = KS::NGT, NGT2 = DIR == 2 ? NGT + NGT / 2 : NGT, GPW = (NGT2 + NW - 1) / NW;
   // LDS
   static constexpr int oCH = 0;                                    // float [4][DK] g_m, g_C, exp(g_m), exp(g_C-g_m)
   static constexpr int oTOT = oCH + 4 * DK * 4;                    // float [NW][DK] per-wave cumsum totals
@@ -80,16 +84,29 @@ __device__ __forceinline__ int unit_off4(int r, int k0, int nu) {
   return ((r >> 4) * nu + u) * F::kUnitBytes + 16 * ((r & 15) + 16 * g) + 8 * half;
 }
 
+// Gram tile t: kind 0 = a strict-lower tile of A, 1 = a causal-term tile computed
+// as P^T (its accumulators are the forward record's P units), 2 = one computed as
+// P (the backward record's P^T units); (R, I) its block in the lower triangle.
+template <int DIR, int NGT>
+__device__ __forceinline__ int gram_tile(int t, int& R, int& I) {
+  constexpr int HALF = NGT / 2;
+  const int kind = t < HALF ? 0 : (DIR == 0 ? 1 : (DIR == 1 ? 2 : (t < NGT ? 1 : 2)));
+  tri_index(t < HALF ? t : (t < NGT ? t - HALF : t - NGT), R, I);
+  return kind;
+}
+
 template <int DK, int C, bool F32IN, int DIR>
-__global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base) {
+__global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base,
+                                                            char* brec_base) {
   using Cfg = PrepCfg<DK, C, F32IN, DIR>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   using Rec = typename Cfg::Rec;
+  using RecB = typename Cfg::RecB;
   using F = Frag<F32IN>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, SW = Cfg::SW, NSL = Cfg::NSL, TPR = Cfg::TPR;
   constexpr int LDC = Cfg::LDC, LDCF = Cfg::LDCF, LDSW = Cfg::LDSW;
-  constexpr int NGT = Cfg::NGT, GPW = Cfg::GPW;
+  constexpr int NGT = Cfg::NGT, NGT2 = Cfg::NGT2, GPW = Cfg::GPW;
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   float* sCh = reinterpret_cast<float*>(smem + Cfg::oCH);
@@ -110,7 +127,8 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
   const int t0 = cl.t0, Lr = cl.Lr;
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
   const int64_t baseK = cl.baseK, baseV = cl.baseV;
-  char* rec = rec_base + cl.item * Rec::kBytes;
+  char* rec = rec_base + cl.item * Rec::kBytes;  // forward record (DIR 0, 2), backward record (DIR 1)
+  char* recB = DIR == 1 ? rec : (DIR == 2 ? brec_base + cl.item * RecB::kBytes : nullptr);
   float* ut = ut_base + cl.item * C * Dv;
 
   // ---- loads: row r, channels sl*SW + 4*c4 .. +3 of every slice sl ----
@@ -137,7 +155,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
     }
   }
   // (w v)^T for the whole value width, into its own LDS region
-  if constexpr (DIR == 0) {
+  if constexpr (DIR != 1) {
     const int vpr = Dv / 8;
 #pragma unroll
     for (int i = 0; i < Cfg::VW_PT; ++i) {
@@ -244,14 +262,16 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       }
       // the token-major factor (forward: decayed q; backward: k decayed to the
       // chunk end) straight into its record units; the channel-major one
-      // (forward: k decayed to the chunk end; backward: decayed q) staged transposed
+      // (forward: k decayed to the chunk end; backward: decayed q) staged transposed.
+      // DIR 2 writes both token-major factors and stages the forward's channel-major
+      // one here, the backward's after the inversion.
       {
-        const float* tm = DIR == 0 ? qs : kb;
-        const float* cm = DIR == 0 ? kb : qs;
+        const float* tm = DIR == 1 ? kb : qs;
+        const float* cm = DIR == 1 ? qs : kb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(cm[i]);
-        auto put = [&](int ubase, const float (&x)[4]) {
-          char* dst = rec + ubase * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
+        auto put = [&](char* rbase, int ubase, const float (&x)[4]) {
+          char* dst = rbase + ubase * F::kUnitBytes + unit_off4<F32IN>(r, c0, Rec::UK);
           if constexpr (F32IN) {
             *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
           } else {
@@ -265,12 +285,13 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
         float tmv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmv[i] = tm[i];
-        put(Rec::u1, tmv);
-        if constexpr (DIR == 1) {  // b k exp(g) for the gradient kernel
+        put(rec, Rec::u1, tmv);
+        if constexpr (DIR == 2) put(recB, RecB::u1, kb);
+        if constexpr (DIR != 0) {  // b k exp(g) for the gradient kernel
           float kh[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) kh[i] = khm[i] * egm[i];
-          put(Rec::u5, kh);
+          put(recB, RecB::u5, kh);
         }
       }
       if constexpr (F32IN) {
@@ -298,16 +319,16 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int t = wid + NW * i;
-      if (t < NGT) {
-        const bool isP = t >= NGT / 2;
+      if (t < NGT2) {
         int R, I;
-        tri_index(isP ? t - NGT / 2 : t, R, I);
+        const int kind = gram_tile<DIR, NGT>(t, R, I);
+        const bool isP = kind != 0;
         if constexpr (F32IN) {
           const float* sl0 = reinterpret_cast<const float*>(sSL);
           const float* Kh = sl0;
           const float* Qh = sl0 + C * LDSW;
           const float* Kt = sl0 + 2 * (C * LDSW);
-          if (isP && DIR == 0) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
+          if (kind == 1) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
           else if (isP) mma_nt_k<SW>(accG[i], Qh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
           else mma_nt_k<SW>(accG[i], Kh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
         } else {
@@ -315,7 +336,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
           const __bf16* Kh = sl0;
           const __bf16* Qh = sl0 + 2 * (C * LDSW);
           const __bf16* Kt = sl0 + 4 * (C * LDSW);
-          if (isP && DIR == 0)
+          if (kind == 1)
             mma_nt_split_k<SW>(accG[i], Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW,
                                Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW);
           else if (isP)
@@ -339,11 +360,10 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int t = wid + NW * i;
-      if (t < NGT) {
-        const bool isP = t >= NGT / 2;
+      if (t < NGT2) {
         int R, I;
-        tri_index(isP ? t - NGT / 2 : t, R, I);
-        if (!isP) {
+        const int kind = gram_tile<DIR, NGT>(t, R, I);
+        if (kind == 0) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = 16 * R + 4 * lg + e, col = 16 * I + lr;
@@ -356,12 +376,13 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
           float pv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool keep = DIR == 0 ? (I < R || 4 * lg + e <= lr) : (I < R || lr <= 4 * lg + e);
+            const bool keep = kind == 1 ? (I < R || 4 * lg + e <= lr) : (I < R || lr <= 4 * lg + e);
             pv[e] = keep ? accG[i][e] : 0.f;
           }
-          const int urow = DIR == 0 ? 16 * R + lr : 16 * I + lr;
-          const int ukk = DIR == 0 ? 16 * I + 4 * lg : 16 * R + 4 * lg;
-          char* dst = rec + (DIR == 0 ? Rec::u3 : Rec::u0) * F::kUnitBytes + unit_off4<F32IN>(urow, ukk, Rec::UC);
+          const int urow = kind == 1 ? 16 * R + lr : 16 * I + lr;
+          const int ukk = kind == 1 ? 16 * I + 4 * lg : 16 * R + 4 * lg;
+          char* dst = kind == 1 ? rec + Rec::u3 * F::kUnitBytes + unit_off4<F32IN>(urow, ukk, Rec::UC)
+                                : recB + RecB::u0 * F::kUnitBytes + unit_off4<F32IN>(urow, ukk, RecB::UC);
           if constexpr (F32IN) {
             *reinterpret_cast<float4*>(dst) = make_float4(pv[0], pv[1], pv[2], pv[3]);
           } else {
@@ -372,9 +393,9 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
             // the other half of a diagonal unit lies on the zero side of the diagonal
             // (forward: the next block; backward: the previous one) or past the chunk
             if (I == R) {
-              if (DIR == 0 && (R & 1) == 0) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
-              if (DIR == 1 && (R & 1) == 1) *reinterpret_cast<uint2*>(dst - 8) = make_uint2(0u, 0u);
-              if (DIR == 1 && (R & 1) == 0 && R + 1 == NB) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+              if (kind == 1 && (R & 1) == 0) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
+              if (kind == 2 && (R & 1) == 1) *reinterpret_cast<uint2*>(dst - 8) = make_uint2(0u, 0u);
+              if (kind == 2 && (R & 1) == 0 && R + 1 == NB) *reinterpret_cast<uint2*>(dst + 8) = make_uint2(0u, 0u);
             }
           }
         }
@@ -387,7 +408,31 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
   ks.invert(sAf, sXs);  // begins and ends with a barrier
 
   // ---- backward: T units for the per-chunk gradient kernel ----
-  if constexpr (DIR == 1) write_units_f32<F32IN>(sAf, LDCF, C, C, rec + Rec::u4 * F::kUnitBytes, wid, NW);
+  if constexpr (DIR != 0) write_units_f32<F32IN>(sAf, LDCF, C, C, recB + RecB::u4 * F::kUnitBytes, wid, NW);
+
+  // ---- both records: the backward's channel-major factor (decayed q) through the
+  //      same staging buffer, free since the inversion's first barrier ----
+  if constexpr (DIR == 2) {
+    if (live) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const int c0 = sl * SW + 4 * c4;
+        float qv[4];
+        cvt(rq[sl], qv);
+        const float4 gm4 = *reinterpret_cast<const float4*>(sCh + c0);
+        const float4 eg4 = *reinterpret_cast<const float4*>(sCh + 2 * DK + c0);
+        const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w}, egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = __expf(g[sl][i] - gm[i]);
+          sT1[(c0 + i) * LDC + r] = static_cast<OpT>(qv[i] * e1 * egm[i]);
+        }
+      }
+    }
+    __syncthreads();
+    write_units<F32IN>(sT1, LDC, DK, C, recB + RecB::u2 * F::kUnitBytes, wid, NW);
+    __syncthreads();
+  }
 
   // ---- Kh^T = (b k exp(g))^T over the dead Kb^T staging ----
   if (live) {
@@ -408,7 +453,7 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
   __syncthreads();
 
   // ---- forward: -W units from W^T tiles (channel blocks 2u, 2u+1, or u for fp32) ----
-  if constexpr (DIR == 0) {
+  if constexpr (DIR != 1) {
     constexpr int CPU = F32IN ? 1 : 2;
     constexpr int NWU = (C / 16) * Rec::UK;
     for (int t = wid; t < NWU; t += NW) {
@@ -438,14 +483,14 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
   }
   // ---- backward: -W^T units from W tiles (rows t, column d): the accumulator
   //      lane (d, g) holds tokens 4g+e, which are -W^T's unit slots ----
-  if constexpr (DIR == 1) {
+  if constexpr (DIR != 0) {
     const int lr = l & 15, lg = l >> 4;
     constexpr int NWT = (C / 16) * (DK / 16);
     for (int t = wid; t < NWT; t += NW) {
       const int R = t / (DK / 16), cb = t - R * (DK / 16);
       f32x4 acc = zero4();
       mma_nt_xf32<OpT>(acc, sAf + 16 * R * LDCF, LDCF, sT1 + 16 * cb * LDC, LDC, 16 * (R + 1));
-      char* dst = rec + Rec::u3 * F::kUnitBytes + unit_off4<F32IN>(16 * cb + lr, 16 * R + 4 * lg, Rec::UC);
+      char* dst = recB + RecB::u3 * F::kUnitBytes + unit_off4<F32IN>(16 * cb + lr, 16 * R + 4 * lg, RecB::UC);
       if constexpr (F32IN) {
         *reinterpret_cast<float4*>(dst) = make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
       } else {
@@ -457,13 +502,14 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
       }
     }
   }
-  {
-    float* gam = reinterpret_cast<float*>(rec + Rec::uG * F::kUnitBytes);
-    for (int c = tid; c < DK; c += NT) gam[c] = __expf(sCh[DK + c]);
+  for (int c = tid; c < DK; c += NT) {
+    const float gc = __expf(sCh[DK + c]);
+    reinterpret_cast<float*>(rec + Rec::uG * F::kUnitBytes)[c] = gc;
+    if constexpr (DIR == 2) reinterpret_cast<float*>(recB + RecB::uG * F::kUnitBytes)[c] = gc;
   }
 
   // ---- Ut = T (w v): accumulator tiles straight to the workspace ----
-  if constexpr (DIR == 0) {
+  if constexpr (DIR != 1) {
     const int nvt = Dv / 16, ntile = (C / 16) * nvt;
     for (int t = wid; t < ntile; t += NW) {
       const int R = t / nvt, jb = t - R * nvt;
@@ -475,51 +521,61 @@ __global__ __launch_bounds__(512, 2) void gdn2_prep_kernel(FwdArgs a, char* rec_
 }
 
 template <int DK, int C, bool F32IN, int DIR>
-static hipError_t launch_prep_t(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+static hipError_t launch_prep_t(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t s) {
   if constexpr (!PrepCfg<DK, C, F32IN, DIR>::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
     const int64_t grid = chunk_items(a.vl, a.B, a.T, a.H, C);
-    hipLaunchKernelGGL((gdn2_prep_kernel<DK, C, F32IN, DIR>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut);
+    hipLaunchKernelGGL((gdn2_prep_kernel<DK, C, F32IN, DIR>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut,
+                       brec);
     return hipGetLastError();
   }
 }
 
 template <int DK, bool F32IN, int DIR>
-static hipError_t launch_prep_c(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+static hipError_t launch_prep_c(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_prep_t<DK, 16, F32IN, DIR>(a, rec, ut, s);
-    case 32: return launch_prep_t<DK, 32, F32IN, DIR>(a, rec, ut, s);
-    case 64: return launch_prep_t<DK, 64, F32IN, DIR>(a, rec, ut, s);
+    case 16: return launch_prep_t<DK, 16, F32IN, DIR>(a, rec, ut, brec, s);
+    case 32: return launch_prep_t<DK, 32, F32IN, DIR>(a, rec, ut, brec, s);
+    case 64: return launch_prep_t<DK, 64, F32IN, DIR>(a, rec, ut, brec, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool F32IN, int DIR>
-static hipError_t launch_prep_f(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
+static hipError_t launch_prep_f(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t s) {
   switch (a.Dk) {
-    case 16: return launch_prep_c<16, F32IN, DIR>(a, rec, ut, s);
-    case 32: return launch_prep_c<32, F32IN, DIR>(a, rec, ut, s);
-    case 64: return launch_prep_c<64, F32IN, DIR>(a, rec, ut, s);
-    case 128: return launch_prep_c<128, F32IN, DIR>(a, rec, ut, s);
+    case 16: return launch_prep_c<16, F32IN, DIR>(a, rec, ut, brec, s);
+    case 32: return launch_prep_c<32, F32IN, DIR>(a, rec, ut, brec, s);
+    case 64: return launch_prep_c<64, F32IN, DIR>(a, rec, ut, brec, s);
+    case 128: return launch_prep_c<128, F32IN, DIR>(a, rec, ut, brec, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prep_fwd(const FwdArgs& a, char* rec, float* ut, hipStream_t s) {
-  return a.f32_inputs ? launch_prep_f<true, 0>(a, rec, ut, s) : launch_prep_f<false, 0>(a, rec, ut, s);
+  return a.f32_inputs ? launch_prep_f<true, 0>(a, rec, ut, nullptr, s)
+                      : launch_prep_f<false, 0>(a, rec, ut, nullptr, s);
 }
 
 hipError_t launch_prep_bwd(const FwdArgs& a, char* rec, hipStream_t s) {
-  return a.f32_inputs ? launch_prep_f<true, 1>(a, rec, nullptr, s) : launch_prep_f<false, 1>(a, rec, nullptr, s);
+  return a.f32_inputs ? launch_prep_f<true, 1>(a, rec, nullptr, nullptr, s)
+                      : launch_prep_f<false, 1>(a, rec, nullptr, nullptr, s);
+}
+
+hipError_t launch_prep_train(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t s) {
+  return a.f32_inputs ? launch_prep_f<true, 2>(a, rec, ut, brec, s) : launch_prep_f<false, 2>(a, rec, ut, brec, s);
 }
 
 template <int DK, bool F32IN>
 static bool prep_fits_c(int chunk) {
   switch (chunk) {
-    case 16: return PrepCfg<DK, 16, F32IN, 0>::kFits && PrepCfg<DK, 16, F32IN, 1>::kFits;
-    case 32: return PrepCfg<DK, 32, F32IN, 0>::kFits && PrepCfg<DK, 32, F32IN, 1>::kFits;
-    case 64: return PrepCfg<DK, 64, F32IN, 0>::kFits && PrepCfg<DK, 64, F32IN, 1>::kFits;
+    case 16: return PrepCfg<DK, 16, F32IN, 0>::kFits && PrepCfg<DK, 16, F32IN, 1>::kFits &&
+                    PrepCfg<DK, 16, F32IN, 2>::kFits;
+    case 32: return PrepCfg<DK, 32, F32IN, 0>::kFits && PrepCfg<DK, 32, F32IN, 1>::kFits &&
+                    PrepCfg<DK, 32, F32IN, 2>::kFits;
+    case 64: return PrepCfg<DK, 64, F32IN, 0>::kFits && PrepCfg<DK, 64, F32IN, 1>::kFits &&
+                    PrepCfg<DK, 64, F32IN, 2>::kFits;
   }
   return false;
 }

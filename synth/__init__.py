@@ -23,21 +23,21 @@ Layouts: q, k, b, log_alpha [B, T, H, Dk]; v, w, dO [B, T, H, Dv]; S0 [B, H, Dk,
 import numpy as np
 import torch
 
-# The five workloads. Shapes follow the pages' layer (16 heads, d_k = d_v = 128,
-# sequence length 4K) plus a tiny fp32 case, a long-sequence sweep and a decode
-# batch.
-CONFIGS = {
-    0: dict(name="tiny-fp32-fwd", B=1, H=2, T=64, Dk=16, Dv=16, chunk=16, dtype="fp32", seed=0,
-            s0_std=None, grad=False),
-    1: dict(name="fwd-B8-H16-T4096-d128", B=8, H=16, T=4096, Dk=128, Dv=128, chunk=64, dtype="bf16",
-            seed=1, s0_std=None, grad=False),
-    2: dict(name="fwd-long-B1-H16-d128", B=1, H=16, T=(8192, 16384, 32768, 65536), Dk=128, Dv=128,
-            chunk=64, dtype="bf16", seed=2, s0_std=0.02, grad=False),
-    3: dict(name="decode-B256-H16-d128-128steps", B=256, H=16, Dk=128, Dv=128, steps=128, dtype="bf16",
-            seed=3, s0_std=0.02),
-    4: dict(name="fwd+bwd-B8-H16-T4096-d128", B=8, H=16, T=4096, Dk=128, Dv=128, chunk=64, dtype="bf16",
-            seed=4, s0_std=None, grad=True),
+# The five workloads, by name. Shapes follow the pages' layer (16 heads,
+# d_k = d_v = 128, sequence length 4K) plus a tiny fp32 case, a long-sequence
+# sweep and a decode batch.
+WORKLOADS = {
+    "tiny-fp32-fwd": dict(B=1, H=2, T=64, Dk=16, Dv=16, chunk=16, dtype="fp32", seed=0, s0_std=None, grad=False),
+    "fwd-B8-H16-T4096-d128": dict(B=8, H=16, T=4096, Dk=128, Dv=128, chunk=64, dtype="bf16", seed=1,
+                                  s0_std=None, grad=False),
+    "fwd-long-B1-H16-d128": dict(B=1, H=16, T=(8192, 16384, 32768, 65536), Dk=128, Dv=128, chunk=64,
+                                 dtype="bf16", seed=2, s0_std=0.02, grad=False),
+    "decode-B256-H16-d128-128steps": dict(B=256, H=16, Dk=128, Dv=128, steps=128, dtype="bf16", seed=3,
+                                          s0_std=0.02),
+    "fwd+bwd-B8-H16-T4096-d128": dict(B=8, H=16, T=4096, Dk=128, Dv=128, chunk=64, dtype="bf16", seed=4,
+                                      s0_std=None, grad=True),
 }
+
 
 _TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -114,15 +114,15 @@ def make_decode_inputs(B, H, Dk, Dv, steps, dtype="bf16", seed=3, s0_std=0.02, r
                 w=_cast(w, dtype), log_alpha=torch.from_numpy(la), S0=torch.from_numpy(S0))
 
 
-def config_inputs(idx, T=None):
-    """Inputs of one of the five workloads (for config 2 pass the sequence length T)."""
-    c = CONFIGS[idx]
-    if idx == 3:
+def workload_inputs(name, T=None):
+    """Inputs of one of the named workloads (the long-sequence sweep takes its sequence length T)."""
+    c = WORKLOADS[name]
+    if "steps" in c:
         return make_decode_inputs(c["B"], c["H"], c["Dk"], c["Dv"], c["steps"], c["dtype"], c["seed"],
                                   c["s0_std"])
-    if idx == 2:
+    if isinstance(c["T"], tuple):
         if T is None:
-            raise ValueError("config 2 needs T")
+            raise ValueError(f"{name} needs the sequence length T")
     else:
         T = c["T"]
     return make_inputs(c["B"], T, c["H"], c["Dk"], c["Dv"], c["dtype"], c["seed"], c["s0_std"], c["grad"])

@@ -60,9 +60,9 @@ def test_bwd_sweep_small(dtype, Dk, Dv, C):
         assert e <= tol, (name, e)
 
 
-def test_config4_sampled_pairs():
+def test_training_B8_H16_T4096_sampled_pairs():
     """B=8, H=16, T=4096, d=128, chunk 64, bf16, dO ~ N(0,1): every gradient of sampled (b, h) pairs."""
-    inp = synth.config_inputs(4)
+    inp = synth.workload_inputs("fwd+bwd-B8-H16-T4096-d128")
     g = _gpu_bwd(inp, 64)
     pairs = [(0, 0), (5, 11), (7, 15)]
     args = [take_pairs(inp[n], pairs) for n in ("q", "k", "v", "log_alpha", "b", "w")]
@@ -73,7 +73,7 @@ def test_config4_sampled_pairs():
         errs[name] = rel_err(gp, ref[name])
     gs = np.stack([f64(g["dS0"])[b, h] for b, h in pairs])[:, None]
     errs["dS0"] = rel_err(gs, ref["dS0"])
-    print("config4 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    print("B8 H16 T4096 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     for name, e in errs.items():
         assert e <= TOL_GRAD, (name, e)
     for name in GRADS:
@@ -150,7 +150,7 @@ def test_bwd_gdn_special_case_matches_oracle():
 
 @pytest.mark.parametrize("B,H,T,Dk,Dv,C,dtype", [
     (1, 2, 33 * 16 + 5, 32, 32, 16, "fp32"),     # 34 chunks: 4 segments
-    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # config-shaped heads: 5 segments
+    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # d = 128 heads: 5 segments
     (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16 identity columns after 64 value columns
     (1, 1, 36 * 32, 64, 128, 32, "fp32"),
 ])

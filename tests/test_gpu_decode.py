@@ -30,11 +30,11 @@ def test_decode_small(dtype, Dk, Dv):
         assert rel_err(f64(S), S_ref) <= tol
 
 
-def test_config3_decode_128_steps_sampled():
+def test_decode_B256_H16_128_steps_sampled():
     """B=256, H=16, d=128, fp32 state ~ 0.02 N(0,1), 128 consecutive steps; the oracle follows
     a sample of sequences through all steps (every head of each sampled sequence)."""
-    c = synth.CONFIGS[3]
-    inp = synth.config_inputs(3)
+    c = synth.WORKLOADS["decode-B256-H16-d128-128steps"]
+    inp = synth.workload_inputs("decode-B256-H16-d128-128steps")
     dev = {n: inp[n].to(DEV) for n in inp}
     S = dev["S0"].clone()
     seqs = [0, 77, 255]
@@ -50,7 +50,7 @@ def test_config3_decode_128_steps_sampled():
         o_ref, S_ref = oracle.decode_step(*args, S_ref)
         errs.append(rel_err(f64(o_gpu[t]), o_ref))
     es = rel_err(f64(S[seqs]), S_ref)
-    print(f"config3 max err o {max(errs):.3e} S {es:.3e}")
+    print(f"decode B256 H16 max err o {max(errs):.3e} S {es:.3e}")
     assert max(errs) <= TOL_BF16 and es <= TOL_BF16
 
 

@@ -27,12 +27,12 @@ PATHS = pytest.mark.parametrize("single", [False, True], ids=["two_stage", "sing
 
 
 @PATHS
-def test_config0_tiny_fp32_exact(single):
+def test_tiny_fp32_exact(single):
     """B=1, H=2, T=64, d=16, chunk 16, fp32, seed 0: every output against the stepwise oracle."""
-    inp = synth.config_inputs(0)
+    inp = synth.workload_inputs("tiny-fp32-fwd")
     o, S, _ = _run(inp, 16, single=single)
     o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], None)
-    print("config0 err o %.3e S %.3e" % (rel_err(f64(o), o_ref), rel_err(f64(S), S_ref)))
+    print("tiny fp32 err o %.3e S %.3e" % (rel_err(f64(o), o_ref), rel_err(f64(S), S_ref)))
     assert rel_err(f64(o), o_ref) <= TOL_F32
     assert rel_err(f64(S), S_ref) <= TOL_F32
 
@@ -73,29 +73,29 @@ def test_sweep_small(dtype, Dk, Dv, C, single):
 
 
 @PATHS
-def test_config1_sampled_pairs(single):
+def test_fwd_B8_H16_T4096_sampled_pairs(single):
     """B=8, H=16, T=4096, d=128, chunk 64, bf16: all outputs of sampled (b, h) pairs."""
-    inp = synth.config_inputs(1)
+    inp = synth.workload_inputs("fwd-B8-H16-T4096-d128")
     o, S, _ = _run(inp, 64, single=single)
     pairs = [(0, 0), (3, 7), (7, 15), (5, 2)]
     o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
     eo, es = rel_err(gpu_pairs(o, pairs), o_ref), rel_err(gpu_state_pairs(S, pairs), S_ref)
     floor = rel_err(o_ref.astype(np.float32).astype(np.float64), o_ref)
-    print(f"config1 err o {eo:.3e} S {es:.3e} (fp32 output floor {floor:.1e})")
+    print(f"B8 H16 T4096 err o {eo:.3e} S {es:.3e} (fp32 output floor {floor:.1e})")
     assert eo <= TOL_BF16 and es <= TOL_BF16
     assert np.isfinite(f64(o)).all() and np.isfinite(f64(S)).all()
 
 
 @pytest.mark.parametrize("T", [8192, 65536])
 @PATHS
-def test_config2_long_sequence_sampled(T, single):
+def test_long_sequence_B1_H16_sampled(T, single):
     """B=1, H=16, T up to 64K, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1)."""
-    inp = synth.config_inputs(2, T=T)
+    inp = synth.workload_inputs("fwd-long-B1-H16-d128", T=T)
     o, S, _ = _run(inp, 64, single=single)
     pairs = [(0, 0), (0, 9)] if T <= 8192 else [(0, 5)]
     o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
     eo, es = rel_err(gpu_pairs(o, pairs), o_ref), rel_err(gpu_state_pairs(S, pairs), S_ref)
-    print(f"config2 T={T} err o {eo:.3e} S {es:.3e}")
+    print(f"long sequence T={T} err o {eo:.3e} S {es:.3e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
@@ -191,7 +191,7 @@ def test_two_stage_matches_single_pass(Dk, Dv, C, dtype):
 SEGMENTED = [
     # B, H, T, Dk, Dv, C, dtype
     (1, 2, 33 * 16 + 5, 32, 32, 16, "fp32"),     # 34 chunks, ragged tail, 4 segments
-    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # config-shaped heads, 5 segments
+    (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # d = 128 heads, 5 segments
     (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16: 16 identity columns after 64 value columns
     (1, 2, 48 * 32 + 31, 128, 32, 32, "bf16"),   # map pass of 160 columns: two column groups
     (1, 1, 36 * 32, 64, 128, 32, "fp32"),
