@@ -249,11 +249,11 @@ int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const 
                              int dt, unsigned flags, void* stream);
 
 /*
- * Packed variable-length batches (row f3 of the build plan: what trainers and
- * servers call). N sequences of different lengths are packed along T of a
- * [1, T, H, D] layout: sequence n covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
- * (cu_seqlens: [N+1] int64 on the device, 8-byte aligned, normally 0 = cu[0] <=
- * ... <= cu[N] = T). Each sequence runs the recurrence from its own entry
+ * Packed variable-length batches (the form trainers on concatenated documents
+ * and serving batches use; [README] training-setup list). N sequences of
+ * different lengths are packed along T of a [1, T, H, D] layout: sequence n
+ * covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens: [N+1] int64 on
+ * the device, 8-byte aligned, normally 0 = cu[0] <= ... <= cu[N] = T). Each sequence runs the recurrence from its own entry
  * state; chunks never cross a sequence boundary. The offsets are read on the
  * device only (no host synchronisation); they are first made non-decreasing
  * and clamped to [0, T], so no input can make a kernel read or write outside
