@@ -199,7 +199,9 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   const int64_t baseK = cl.baseK, baseV = cl.baseV;
   const int64_t stOff = cl.item * DK * Dv;
   const float* S0g = a.chunk_states + stOff;
-  const float* dSg = a.dS_chunks + stOff;
+  // exit-state gradients: fp16 for 16-bit inputs (every use rounds them to fp16 operands anyway)
+  using SdT = typename std::conditional<F32IN, float, _Float16>::type;
+  const SdT* dSg = static_cast<const SdT*>(a.dS_chunks) + stOff;
 
   // ---- key-side preparation ----
   KS ks;
@@ -474,13 +476,20 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const bool on = c0 < Dv;
       const int cs = on ? c0 : 0;  // unconditional loads, zeroed below
       const float* ps = S0g + (int64_t)d * Dv + cs;
-      const float* pd = dSg + (int64_t)d * Dv + cs;
+      const SdT* pd = dSg + (int64_t)d * Dv + cs;
 #pragma unroll
       for (int j4 = 0; j4 < NV; j4 += 4) {
         const float4 a4 = *reinterpret_cast<const float4*>(ps + j4);
-        const float4 b4 = *reinterpret_cast<const float4*>(pd + j4);
         xs[j4] = a4.x; xs[j4 + 1] = a4.y; xs[j4 + 2] = a4.z; xs[j4 + 3] = a4.w;
-        xd[j4] = b4.x; xd[j4 + 1] = b4.y; xd[j4 + 2] = b4.z; xd[j4 + 3] = b4.w;
+        if constexpr (F32IN) {
+          const float4 b4 = *reinterpret_cast<const float4*>(pd + j4);
+          xd[j4] = b4.x; xd[j4 + 1] = b4.y; xd[j4 + 2] = b4.z; xd[j4 + 3] = b4.w;
+        }
+      }
+      if constexpr (!F32IN) {  // NV = 8 halves: one 16-byte load
+        const f16x8 h8 = *reinterpret_cast<const f16x8*>(pd);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) xd[j] = static_cast<float>(h8[j]);
       }
 #pragma unroll
       for (int j = 0; j < NV; ++j) {

@@ -508,13 +508,14 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_bwd_kernel(BwdArgs a, con
       dma_units(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * kBuf, Rec::kChainUnits, wid, NWV);
 
     if (outs) {
-      float* ws = a.dS_chunks + (sl.item0 + n) * DK * Dv + j0;
+      using SdT = typename std::conditional<F32IN, float, _Float16>::type;
+      SdT* ws = static_cast<SdT*>(a.dS_chunks) + (sl.item0 + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ws[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = accD[R][c][i];
+          for (int i = 0; i < 4; ++i) ws[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = static_cast<SdT>(accD[R][c][i]);
     }
 
     // this chunk's dO fragments; the previous chunk's start loading

@@ -162,7 +162,8 @@ struct BwdArgs {
   const void* dO;
   const float* dS_final;     // nullable
   const float* chunk_states; // required here (the C ABI fills it in when the caller passes none)
-  float* dS_chunks;          // workspace [B,H,NC,Dk,Dv]: gradient of each chunk's exit state
+  void* dS_chunks;           // workspace [B,H,NC,Dk,Dv]: gradient of each chunk's exit state, fp32 for
+                             // fp32 inputs, fp16 for bf16 inputs (the precision of its matrix-core uses)
   float* dq;
   float* dk;
   float* dv;
