@@ -198,7 +198,8 @@ def main():
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     need_f = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, _lib.GDN2_BF16)
     ws_f = torch.empty(max(need_f, 1), dtype=torch.uint8, device=dev)
-    # the training pair: the forward's record pass also writes the backward's records
+    # the training pair: the forward's record pass also writes the backward's records, and its chain the
+    # chunk entry states (fp16) beside them
     need_r = lib.gdn2_records_bytes(B, T, H, D, D, C, _lib.GDN2_BF16)
     recs = torch.empty(need_r, dtype=torch.uint8, device=dev)
     need_br = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, _lib.GDN2_BF16)
@@ -208,13 +209,13 @@ def main():
 
     def fwd(flags=0, x=d):
         st = lib.gdn2_fwd_chunked_train(P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["b"]), P(x["w"]),
-                                        None, P(o), None, P(states), P(recs), need_r, P(ws_f), need_f, B, T, H, D, D,
-                                        C, _lib.GDN2_BF16, flags, sh)
+                                        None, P(o), None, P(recs), need_r, P(ws_f), need_f, B, T, H, D, D, C,
+                                        _lib.GDN2_BF16, flags, sh)
         _lib.check(st, "gdn2_fwd_chunked_train")
 
     def bwd(flags=0, x=d, gb=None, gw=None, gla=None):
         st = lib.gdn2_bwd_chunked_records(P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["b"]), P(x["w"]),
-                                          None, P(x["dO"]), None, P(states), P(recs), need_r, P(grads["dq"]),
+                                          P(x["dO"]), None, P(recs), need_r, P(grads["dq"]),
                                           P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"] if gla is None else gla),
                                           P(grads["db"] if gb is None else gb), P(grads["dw"] if gw is None else gw),
                                           P(dS0), P(ws_br), need_br,
@@ -295,8 +296,9 @@ def main():
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded normal / sigmoid / -softplus draws, workload "
                                  "fwd+bwd-B8-H16-T4096-d128, seed 4)",
-        "config": {"workload": "GDN-2 training step: gdn2_fwd_chunked_train (chunkwise forward saving chunk "
-                               "states and the backward records) + gdn2_bwd_chunked_records (gate-aware backward), "
+        "config": {"workload": "GDN-2 training step: gdn2_fwd_chunked_train (chunkwise forward saving the "
+                               "backward records and fp16 chunk entry states) + gdn2_bwd_chunked_records "
+                               "(gate-aware backward), "
                                "B=8 H=16 T=4096 d_k=d_v=128 chunk=64, bf16 q/k/v/b/w/dO, fp32 log_alpha, "
                                "fp32 outputs and gradients",
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,

@@ -49,10 +49,10 @@ SIGNATURES = {
     "gdn2_bwd_chunked_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                  _I, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_records_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
-    "gdn2_fwd_chunked_train": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _I, _I, _I, _I, _I,
-                                    _I, _I, _U, _P]),
-    "gdn2_bwd_chunked_records": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P,
-                                      _P, _SZ, _I, _I, _I, _I, _I, _I, _I, _U, _P]),
+    "gdn2_fwd_chunked_train": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _I, _I, _I, _I, _I, _I,
+                                    _I, _U, _P]),
+    "gdn2_bwd_chunked_records": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                      _I, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_varlen_max_chunks": (_I, [_I, _I, _I]),
     "gdn2_varlen_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gdn2_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _I, _U,

@@ -52,6 +52,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; 
 
 size_t state_bytes(int B, int H, int Dk, int Dv) { return (size_t)B * H * Dk * Dv * sizeof(float); }
 
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32);
 
 // Backward plan: the two-stage reverse pass (chunk-parallel records, then the
@@ -89,11 +91,18 @@ size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   return bwd_plan(B, T, H, Dk, Dv, chunk, f32).need;
 }
 
-// The training pair: the backward records (written by the training forward)
-// and the workspace of the backward that reads them (state gradients, then the
-// reverse chain's segment maps).
-size_t train_records(int B, int T, int H, int Dk, int chunk, bool f32) {
-  return (size_t)B * H * ((T + chunk - 1) / chunk) * gdn2::record_bytes(Dk, chunk, f32, 1);
+// The training pair's records buffer: the backward records, then (256-byte
+// aligned) every chunk's entry state, fp32 for fp32 inputs and fp16 for 16-bit
+// ones (the precision of their matrix-core uses in the backward); and the
+// workspace of the backward that reads them (state gradients, then the reverse
+// chain's segment maps).
+size_t train_states_offset(int B, int T, int H, int Dk, int chunk, bool f32) {
+  return al256((size_t)B * H * ((T + chunk - 1) / chunk) * gdn2::record_bytes(Dk, chunk, f32, 1));
+}
+
+size_t train_records(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  return train_states_offset(B, T, H, Dk, chunk, f32) +
+         (size_t)B * H * ((T + chunk - 1) / chunk) * Dk * Dv * (f32 ? 4 : 2);
 }
 
 size_t bwd_records_workspace(const BwdPlan& p) { return p.part + p.seg; }
@@ -121,8 +130,6 @@ char* fwd_seg_ptr(char* ws, int B, int T, int H, int Dk, int Dv, int chunk, bool
   if (gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk) == 0) return nullptr;
   return ws + fwd_seg_offset(B, T, H, Dv, Dk, chunk, f32);
 }
-
-size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Packed variable-length batches: [tables][...] workspaces. Forward: records
 // and T (w v) over [H][max_chunks]; backward: state gradients and recomputed
@@ -215,7 +222,7 @@ size_t gdn2_records_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dt
   if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK || !chunk_ok(chunk) || T == 0) return 0;
   const bool f32 = dt == GDN2_F32;
   if (!bwd_plan(B, T, H, Dk, Dv, chunk, f32).two_stage) return 0;
-  return train_records(B, T, H, Dk, chunk, f32);
+  return train_records(B, T, H, Dk, Dv, chunk, f32);
 }
 
 int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
@@ -341,9 +348,9 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
 }
 
 int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                           const void* w, const float* S0, float* o, float* S_final, float* chunk_states,
-                           void* records, size_t records_bytes, void* workspace, size_t workspace_bytes, int B,
-                           int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
+                           const void* w, const float* S0, float* o, float* S_final, void* records,
+                           size_t records_bytes, void* workspace, size_t workspace_bytes, int B, int T, int H,
+                           int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
@@ -357,14 +364,17 @@ int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const fl
     if (S_final == nullptr) return GDN2_OK;
     return hip_status(gdn2::launch_copy_or_zero(S_final, S0, (int64_t)B * H * Dk * Dv, s));
   }
-  st = check_ptrs({q, k, v, log_alpha, b, w, o, chunk_states, records}, {S0, S_final});
+  st = check_ptrs({q, k, v, log_alpha, b, w, o, records}, {S0, S_final});
   if (st != GDN2_OK) return st;
   const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, f32);
-  if (workspace == nullptr || workspace_bytes < need || records_bytes < train_records(B, T, H, Dk, chunk, f32))
+  if (workspace == nullptr || workspace_bytes < need || records_bytes < train_records(B, T, H, Dk, Dv, chunk, f32))
     return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
     return GDN2_ERR_ALIGN;
-  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, f32};
+  char* states = static_cast<char*>(records) + train_states_offset(B, T, H, Dk, chunk, f32);
+  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, f32 ? reinterpret_cast<float*>(states) : nullptr,
+                  B, T, H, Dk, Dv, chunk, f32};
+  if (!f32) a.states16 = reinterpret_cast<_Float16*>(states);
   set_gate_flags(a, flags);
   char* rec = static_cast<char*>(workspace);
   float* ut = reinterpret_cast<float*>(rec + (size_t)B * H * ((T + chunk - 1) / chunk) *
@@ -375,11 +385,10 @@ int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const fl
 }
 
 int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
-                             const void* w, const float* S0, const void* dO, const float* dS_final,
-                             const float* chunk_states, const void* records, size_t records_bytes, float* dq,
-                             float* dk, float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
-                             void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk, int Dv,
-                             int chunk, int dt, unsigned flags, void* stream) {
+                             const void* w, const void* dO, const float* dS_final, const void* records,
+                             size_t records_bytes, float* dq, float* dk, float* dv, float* dlog_alpha, float* db,
+                             float* dw, float* dS0, void* workspace, size_t workspace_bytes, int B, int T, int H,
+                             int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
   int st = check_common(B, T, H, Dk, Dv, dt);
   if (st != GDN2_OK) return st;
   if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
@@ -394,18 +403,19 @@ int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const 
     if (dS0 == nullptr) return GDN2_OK;
     return hip_status(gdn2::launch_copy_or_zero(dS0, dS_final, (int64_t)B * H * Dk * Dv, s));
   }
-  st = check_ptrs({q, k, v, log_alpha, b, w, dO, chunk_states, records, dq, dk, dv, dlog_alpha, db, dw},
-                  {S0, dS_final, dS0});
+  st = check_ptrs({q, k, v, log_alpha, b, w, dO, records, dq, dk, dv, dlog_alpha, db, dw}, {dS_final, dS0});
   if (st != GDN2_OK) return st;
   if (workspace == nullptr || workspace_bytes < bwd_records_workspace(plan) ||
-      records_bytes < train_records(B, T, H, Dk, chunk, f32))
+      records_bytes < train_records(B, T, H, Dk, Dv, chunk, f32))
     return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
     return GDN2_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   const char* rec = static_cast<const char*>(records);
-  gdn2::BwdArgs a{q,  k,  v,  log_alpha,  b,  w,  dO, dS_final, chunk_states, reinterpret_cast<float*>(ws),
-                  dq, dk, dv, dlog_alpha, db, dw, dS0, B, T, H, Dk, Dv, chunk, f32};
+  const char* states = rec + train_states_offset(B, T, H, Dk, chunk, f32);
+  gdn2::BwdArgs a{q,  k,  v,  log_alpha,  b,  w,  dO, dS_final, f32 ? reinterpret_cast<const float*>(states) : nullptr,
+                  reinterpret_cast<float*>(ws), dq, dk, dv, dlog_alpha, db, dw, dS0, B, T, H, Dk, Dv, chunk, f32};
+  if (!f32) a.states16 = reinterpret_cast<const _Float16*>(states);
   set_gate_flags(a, flags);
   st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? ws + plan.part : nullptr, s));
   a.records = rec;

@@ -150,7 +150,7 @@ struct GradCfg {
 
 // One workgroup per (batch, head, chunk). T and P^T come from the backward
 // records (a.records), the exit-state gradient from the reverse chain.
-template <int DK, int C, bool F32IN, bool RAW, bool GS>
+template <int DK, int C, bool F32IN, bool RAW, bool GS, bool S16>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   // GS: some gate holds one value per (token, head); the per-channel case compiles without that code
   const bool scalar_b = GS && a.scalar_b, scalar_w = GS && a.scalar_w, scalar_decay = GS && a.scalar_decay;
@@ -198,7 +198,12 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
   const int64_t baseK = cl.baseK, baseV = cl.baseV;
   const int64_t stOff = cl.item * DK * Dv;
-  const float* S0g = a.chunk_states + stOff;
+  // chunk entry states: fp32, or fp16 (S16: the training pair's own copy, 16-bit inputs)
+  using S0T = typename std::conditional<S16, _Float16, float>::type;
+  static_assert(!S16 || !F32IN, "fp16 states go with 16-bit inputs");
+  const S0T* S0g;
+  if constexpr (S16) S0g = a.states16 + stOff;
+  else S0g = a.chunk_states + stOff;
   // exit-state gradients: fp16 for 16-bit inputs (every use rounds them to fp16 operands anyway)
   using SdT = typename std::conditional<F32IN, float, _Float16>::type;
   const SdT* dSg = static_cast<const SdT*>(a.dS_chunks) + stOff;
@@ -475,12 +480,19 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       float xs[NV], xd[NV];
       const bool on = c0 < Dv;
       const int cs = on ? c0 : 0;  // unconditional loads, zeroed below
-      const float* ps = S0g + (int64_t)d * Dv + cs;
+      const S0T* ps = S0g + (int64_t)d * Dv + cs;
       const SdT* pd = dSg + (int64_t)d * Dv + cs;
+      if constexpr (S16) {  // NV = 8 halves: one 16-byte load
+        const f16x8 h8 = *reinterpret_cast<const f16x8*>(ps);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) xs[j] = static_cast<float>(h8[j]);
+      }
 #pragma unroll
       for (int j4 = 0; j4 < NV; j4 += 4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(ps + j4);
-        xs[j4] = a4.x; xs[j4 + 1] = a4.y; xs[j4 + 2] = a4.z; xs[j4 + 3] = a4.w;
+        if constexpr (!S16) {
+          const float4 a4 = *reinterpret_cast<const float4*>(ps + j4);
+          xs[j4] = a4.x; xs[j4 + 1] = a4.y; xs[j4 + 2] = a4.z; xs[j4 + 3] = a4.w;
+        }
         if constexpr (F32IN) {
           const float4 b4 = *reinterpret_cast<const float4*>(pd + j4);
           xd[j4] = b4.x; xd[j4 + 1] = b4.y; xd[j4 + 2] = b4.z; xd[j4 + 3] = b4.w;
@@ -962,14 +974,31 @@ static hipError_t launch_grad_t(const BwdArgs& a, hipStream_t s) {
     if (a.records == nullptr) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)chunk_items(a.vl, a.B, a.T, a.H, C);
     const bool gs = a.scalar_b || a.scalar_w || a.scalar_decay;
+    if (a.states16 != nullptr) {
+      if constexpr (F32IN) {
+        return hipErrorInvalidValue;  // fp16 states go with 16-bit inputs
+      } else {
+        if (a.raw_gates && gs)
+          hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, true, true>), dim3(grid), dim3(512), 0, s, a);
+        else if (a.raw_gates)
+          hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, false, true>), dim3(grid), dim3(512), 0, s, a);
+        else if (gs)
+          hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, true, true>), dim3(grid), dim3(512), 0, s, a);
+        else
+          hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, false, true>), dim3(grid), dim3(512), 0, s,
+                             a);
+        return hipGetLastError();
+      }
+    }
+    if (a.chunk_states == nullptr) return hipErrorInvalidValue;
     if (a.raw_gates && gs)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, true>), dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, true, false>), dim3(grid), dim3(512), 0, s, a);
     else if (a.raw_gates)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, false>), dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, true, false, false>), dim3(grid), dim3(512), 0, s, a);
     else if (gs)
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, true>), dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, true, false>), dim3(grid), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, false>), dim3(grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gdn2_bwd_grad_kernel<DK, C, F32IN, false, false, false>), dim3(grid), dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }

@@ -184,7 +184,16 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
       dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem + ((n + 1 - n_begin) & 1) * Rec::kBytes, Rec::kUnits,
                 wid, NWV);
 
-    if (a.chunk_states && outs) {
+    if (a.states16 && outs) {
+      _Float16* cs = a.states16 + (sl.item0 + n) * DK * Dv + j0;
+#pragma unroll
+      for (int R = 0; R < RK; ++R)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            cs[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = static_cast<_Float16>(accS[R][c][i]);
+    } else if (a.chunk_states && outs) {
       float* cs = a.chunk_states + (sl.item0 + n) * DK * Dv + j0;
 #pragma unroll
       for (int R = 0; R < RK; ++R)

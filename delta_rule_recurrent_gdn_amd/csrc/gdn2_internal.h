@@ -135,6 +135,8 @@ struct FwdArgs {
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations (sigmoid, sigmoid, -softplus)
+  _Float16* states16 = nullptr;  // two-stage chain only: the chunk entry states in fp16 (instead of
+                                 // chunk_states), for the training pair's backward
   Varlen vl;               // packed variable-length batch (B = 1), or dense
   // gates of one value per (token, head), [., T, H], broadcast over their channels
   bool scalar_b = false, scalar_w = false, scalar_decay = false;
@@ -174,6 +176,8 @@ struct BwdArgs {
   int B, T, H, Dk, Dv, chunk;
   bool f32_inputs;
   const char* records = nullptr;  // backward records (T, P^T, Kh, Kb) for launch_bwd_grad
+  const _Float16* states16 = nullptr;  // the chunk entry states in fp16 (16-bit inputs): read instead of
+                                       // chunk_states by launch_bwd_grad
   bool raw_gates = false;  // b, w, log_alpha hold pre-activations; db, dw, dlog_alpha are taken
                            // with respect to those
   Varlen vl;               // packed variable-length batch (B = 1), or dense

@@ -196,9 +196,9 @@ def _nbytes(t):
 
 def gdn2_fwd_chunked_train(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_state=True, workspace=None,
                            records=None, raw_gates=False, scalar_b=False, scalar_w=False, scalar_decay=False):
-    """Training forward (gdn2_fwd_chunked_train): the two-stage forward with the chunk entry states saved,
-    whose chunk-parallel pass also writes the backward's per-chunk records. Returns (o, S_final or None,
-    chunk_states, records); pass chunk_states and records to gdn2_bwd_chunked_records with the same inputs.
+    """Training forward (gdn2_fwd_chunked_train): the two-stage forward whose chunk-parallel pass also writes
+    the backward's per-chunk records and whose chain stores every chunk's entry state with them. Returns
+    (o, S_final or None, records); pass records to gdn2_bwd_chunked_records with the same inputs.
     `workspace` and `records` may supply the buffers (uint8 device tensors of at least
     gdn2_workspace_bytes(GDN2_OP_FWD, ...) and gdn2_records_bytes(...) bytes)."""
     lib = _lib.load()
@@ -216,25 +216,21 @@ def gdn2_fwd_chunked_train(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_fin
     S0 = _f32_state(S0, "S0", dev, (B, H, Dk, Dv))
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=dev)
     S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
-    NC = (T + chunk - 1) // chunk
-    states = torch.empty((B, H, NC, Dk, Dv), dtype=torch.float32, device=dev)
     dt = _dtype_code(q.dtype)
     workspace = _scratch(workspace, lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, Dk, Dv, chunk, dt), dev)
     records = _scratch(records, lib.gdn2_records_bytes(B, T, H, Dk, Dv, chunk, dt), dev)
     st = lib.gdn2_fwd_chunked_train(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), _ptr(o),
-                                    _ptr(S_final), _ptr(states), _ptr(records), _nbytes(records), _ptr(workspace),
+                                    _ptr(S_final), _ptr(records), _nbytes(records), _ptr(workspace),
                                     _nbytes(workspace), B, T, H, Dk, Dv, chunk, dt,
                                     _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
     _lib.check(st, "gdn2_fwd_chunked_train")
-    return o, S_final, states, records
+    return o, S_final, records
 
 
-def gdn2_bwd_chunked_records(q, k, v, log_alpha, b, w, dO, chunk_states, records, dS_final=None, chunk=64,
-                             want_dS0=True, workspace=None, raw_gates=False, scalar_b=False, scalar_w=False,
-                             scalar_decay=False):
+def gdn2_bwd_chunked_records(q, k, v, log_alpha, b, w, dO, records, dS_final=None, chunk=64, want_dS0=True,
+                             workspace=None, raw_gates=False, scalar_b=False, scalar_w=False, scalar_decay=False):
     """Backward from the training forward's records (gdn2_bwd_chunked_records): the reverse chain and the
-    per-chunk gradients, without the backward's own record pass. Same results as gdn2_bwd_chunked.
-    Returns the dict of gdn2_bwd_chunked."""
+    per-chunk gradients, without the backward's own record pass. Returns the dict of gdn2_bwd_chunked."""
     lib = _lib.load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -243,8 +239,6 @@ def gdn2_bwd_chunked_records(q, k, v, log_alpha, b, w, dO, chunk_states, records
     _check_inputs(("v", "w", "dO"), (v, w, dO), q.dtype, dev)
     _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
     dS_final = _f32_state(dS_final, "dS_final", dev, (B, H, Dk, Dv))
-    NC = (T + chunk - 1) // chunk
-    chunk_states = _f32_state(chunk_states, "chunk_states", dev, (B, H, NC, Dk, Dv))
     if records is None or records.device != dev or records.dtype != torch.uint8:
         raise ValueError("records must be the uint8 device tensor returned by gdn2_fwd_chunked_train")
     gs = _gate_shapes((B, T, H), Dk, Dv, scalar_b, scalar_w, scalar_decay)
@@ -255,12 +249,11 @@ def gdn2_bwd_chunked_records(q, k, v, log_alpha, b, w, dO, chunk_states, records
     dt = _dtype_code(q.dtype)
     workspace = _scratch(workspace, lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, Dk, Dv, chunk, dt),
                          dev)
-    st = lib.gdn2_bwd_chunked_records(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), None, _ptr(dO),
-                                      _ptr(dS_final), _ptr(chunk_states), _ptr(records), _nbytes(records),
-                                      _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
-                                      _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace),
-                                      _nbytes(workspace), B, T, H, Dk, Dv, chunk, dt,
-                                      _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
+    st = lib.gdn2_bwd_chunked_records(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(dO),
+                                      _ptr(dS_final), _ptr(records), _nbytes(records), _ptr(g["dq"]), _ptr(g["dk"]),
+                                      _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+                                      _ptr(g["dS0"]), _ptr(workspace), _nbytes(workspace), B, T, H, Dk, Dv, chunk,
+                                      dt, _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
     _lib.check(st, "gdn2_bwd_chunked_records")
     return g
 

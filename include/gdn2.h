@@ -206,8 +206,8 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
                         int Dv, int chunk, int dt, unsigned flags, void* stream);
 
 /*
- * Training pair -- the forward also writes what the backward's reverse pass
- * needs, so the backward skips its own chunk-parallel record pass.
+ * Training pair -- the forward also writes everything the backward needs, so
+ * the backward skips its own chunk-parallel record pass.
  *
  * The backward's per-chunk records (the causal q-k term, the decayed q and k,
  * W, T and the decayed b*k, in the orientation of the reverse pass) depend on
@@ -215,38 +215,45 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
  * factor they are made of. gdn2_fwd_chunked_train runs that kernel once for
  * both directions: it writes the forward's records to `workspace` (as
  * gdn2_fwd_chunked_ex does) and the backward's to `records`, then runs the
- * forward chain. gdn2_bwd_chunked_records then runs the reverse chain and the
- * per-chunk gradient kernel from `records`. Results are those of
- * gdn2_fwd_chunked_ex and gdn2_bwd_chunked_ex on the same inputs, bit for bit.
+ * forward chain, which also stores every chunk's entry state in `records`.
+ * gdn2_bwd_chunked_records then runs the reverse chain and the per-chunk
+ * gradient kernel from `records`.
+ *
+ * The entry states are kept at the precision the backward consumes them in:
+ * fp32 for fp32 inputs, fp16 for 16-bit inputs (every matrix-core product
+ * that uses them rounds them to fp16 operands). Results equal those of
+ * gdn2_fwd_chunked_ex followed by gdn2_bwd_chunked_ex on the same inputs bit
+ * for bit, except dlog_alpha with 16-bit inputs: its rowsum(S_entry * dS_exit)
+ * term then takes the fp16 entry state, a difference of at most
+ * 2^-12 sum|S_entry * dS_exit| per key channel and chunk (up to 3e-3 of
+ * rms(dlog_alpha) in the parity tests; the error against the float64 oracle
+ * on a B=8 H=16 T=4096 batch is unchanged).
  *
  *   records       device buffer of at least gdn2_records_bytes(...) bytes,
- *                 256-byte aligned, owned by the caller; written by
+ *                 256-byte aligned, owned by the caller, opaque; written by
  *                 gdn2_fwd_chunked_train, read by gdn2_bwd_chunked_records,
  *                 which must get the same inputs, sizes and flags (it does not
  *                 check: other contents give meaningless gradients)
- *   chunk_states  required by both calls (the forward's output, the backward's input)
  *   workspace     forward: gdn2_workspace_bytes(GDN2_OP_FWD, ...) bytes;
  *                 backward: gdn2_workspace_bytes(GDN2_OP_BWD_RECORDS, ...) bytes;
  *                 both 256-byte aligned, contents on entry ignored
- *   S0            forward: as gdn2_fwd_chunked; backward: not read (the first
- *                 chunk's entry state in chunk_states is S0)
- * Other arguments as gdn2_fwd_chunked_ex / gdn2_bwd_chunked_ex. Both return
- * GDN2_ERR_UNSUPPORTED for sizes the two-stage backward does not cover
+ * Other arguments as gdn2_fwd_chunked_ex / gdn2_bwd_chunked_ex (S0 enters
+ * only the forward: the first chunk's entry state in `records` is S0). Both
+ * return GDN2_ERR_UNSUPPORTED for sizes the two-stage backward does not cover
  * (gdn2_records_bytes returns 0 for them).
  */
 size_t gdn2_records_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dt);
 int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const float* log_alpha,
                            const void* b, const void* w, const float* S0, float* o, float* S_final,
-                           float* chunk_states, void* records, size_t records_bytes, void* workspace,
+                           void* records, size_t records_bytes, void* workspace,
                            size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
                            int dt, unsigned flags, void* stream);
 int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const float* log_alpha,
-                             const void* b, const void* w, const float* S0, const void* dO,
-                             const float* dS_final, const float* chunk_states, const void* records,
-                             size_t records_bytes, float* dq, float* dk, float* dv, float* dlog_alpha,
-                             float* db, float* dw, float* dS0, void* workspace,
-                             size_t workspace_bytes, int B, int T, int H, int Dk, int Dv, int chunk,
-                             int dt, unsigned flags, void* stream);
+                             const void* b, const void* w, const void* dO, const float* dS_final,
+                             const void* records, size_t records_bytes, float* dq, float* dk,
+                             float* dv, float* dlog_alpha, float* db, float* dw, float* dS0,
+                             void* workspace, size_t workspace_bytes, int B, int T, int H, int Dk,
+                             int Dv, int chunk, int dt, unsigned flags, void* stream);
 
 /*
  * Packed variable-length batches (the form trainers on concatenated documents

@@ -169,30 +169,34 @@ def test_bwd_argument_errors():
 
 def test_training_pair_sizes_and_argument_errors():
     """gdn2_records_bytes: per chunk the backward record (57 units of 1 KB for the reverse chain, then
-    T: 8 and the decayed b*k: 16, at d = 128, chunk 64, bf16); the backward from records needs only the
-    exit-state gradients. Both calls check their buffers before launching."""
+    T: 8 and the decayed b*k: 16, at d = 128, chunk 64, bf16), then every chunk's entry state (fp16 for
+    16-bit inputs); the backward from records needs only the exit-state gradients. Both calls check their
+    buffers before launching."""
     lib = _lib.load()
     B, T, H, D, C = 8, 4096, 16, 128, 64
     nc = T // C
     rb = lib.gdn2_records_bytes(B, T, H, D, D, C, 1)
-    assert rb == B * H * nc * 81 * 1024
+    assert rb == B * H * nc * 81 * 1024 + B * H * nc * D * D * 2
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, 1) == B * H * nc * D * D * 4
     assert lib.gdn2_records_bytes(B, T, H, 48, D, C, 1) == 0 and lib.gdn2_records_bytes(B, 0, H, D, D, C, 1) == 0
-    rb = lib.gdn2_records_bytes(1, 64, 2, 16, 16, 16, 0)
+    # fp32 inputs keep fp32 entry states
+    rb32 = lib.gdn2_records_bytes(1, 64, 2, 16, 16, 16, 0)
+    rb16 = lib.gdn2_records_bytes(1, 64, 2, 16, 16, 16, 1)
+    assert rb32 > 0 and rb16 > 0
+    rb = rb32
     fw = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, 64, 2, 16, 16, 16, 0)
     bw = lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, 1, 64, 2, 16, 16, 16, 0)
-    assert rb > 0 and fw > 0 and bw > 0
+    assert fw > 0 and bw > 0
 
-    def fwd(cs=A, rec=A, rec_bytes=rb, ws=A, ws_bytes=fw, flags=0, B=1, T=64):
-        return lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, cs, rec, rec_bytes, ws, ws_bytes, B, T,
-                                          2, 16, 16, 16, 0, flags, None)
+    def fwd(rec=A, rec_bytes=rb, ws=A, ws_bytes=fw, flags=0, B=1, T=64):
+        return lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, rec, rec_bytes, ws, ws_bytes, B, T, 2, 16,
+                                          16, 16, 0, flags, None)
 
-    def bwd(cs=A, rec=A, rec_bytes=rb, ws=A, ws_bytes=bw, flags=0):
-        return lib.gdn2_bwd_chunked_records(A, A, A, A, A, A, None, A, None, cs, rec, rec_bytes, A, A, A, A, A, A,
-                                            None, ws, ws_bytes, 1, 64, 2, 16, 16, 16, 0, flags, None)
+    def bwd(rec=A, rec_bytes=rb, ws=A, ws_bytes=bw, flags=0):
+        return lib.gdn2_bwd_chunked_records(A, A, A, A, A, A, A, None, rec, rec_bytes, A, A, A, A, A, A, None, ws,
+                                            ws_bytes, 1, 64, 2, 16, 16, 16, 0, flags, None)
 
     for call in (fwd, bwd):
-        assert call(cs=None) == _lib.GDN2_ERR_NULL          # chunk states are required by both
         assert call(rec=None) == _lib.GDN2_ERR_NULL
         assert call(rec_bytes=rb - 1) == _lib.GDN2_ERR_WORKSPACE
         assert call(ws=None) == _lib.GDN2_ERR_WORKSPACE
@@ -203,5 +207,5 @@ def test_training_pair_sizes_and_argument_errors():
     assert bwd(ws_bytes=bw - 1) == _lib.GDN2_ERR_WORKSPACE
     assert fwd(B=0) == _lib.GDN2_OK
     # fp32 inputs at d = 128 need chunk <= 32 (the two-stage kernels do not cover chunk 64)
-    assert lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, A, A, rb, A, fw, 1, 64, 2, 128, 128, 64, 0, 0,
+    assert lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, A, rb, A, fw, 1, 64, 2, 128, 128, 64, 0, 0,
                                       None) == _lib.GDN2_ERR_UNSUPPORTED

@@ -1,11 +1,19 @@
 """GPU parity of the training pair (gdn2_fwd_chunked_train / gdn2_bwd_chunked_records): the forward's
-chunk-parallel pass also writes the backward's per-chunk records, and the backward starts from them.
+chunk-parallel pass also writes the backward's per-chunk records, its chain stores every chunk's entry
+state with them (fp16 for 16-bit inputs), and the backward starts from them.
 
 The fused pass forms every record value with the same operations, in the same order, as the separate
-forward and backward record passes, so the pair's results equal gdn2_fwd_chunked (two-stage, saving chunk
-states) followed by gdn2_bwd_chunked bit for bit. The equality is checked across the supported key widths,
-chunk sizes, both input dtypes, ragged lengths, the two-level chains, pre-activation and scalar gates. One
-shape is also checked against the float64 oracle, through the C ABI."""
+forward and backward record passes, and every matrix-core use of an entry state rounds it to fp16 in both
+paths, so the pair's results equal gdn2_fwd_chunked (two-stage, saving chunk states) followed by
+gdn2_bwd_chunked bit for bit, with one exception: with 16-bit inputs the rowsum(S_entry * dS_exit) term of
+dlog_alpha takes the fp16 entry state. Its difference is bounded by 2^-12 sum|S_entry * dS_exit| per key
+channel and chunk; that sum runs to about ten times rms(dlog_alpha) on these inputs (initial states of
+std 0.2), and the measured difference is at most 2.7e-3 of rms(dlog_alpha), so the bar is 5e-3. On the
+B=8 H=16 T=4096 training workload the pair's dlog_alpha error against the oracle equals the separate
+path's (4.35e-3, last test). The equality is checked
+across the supported key widths, chunk sizes, both input dtypes, ragged lengths, the two-level chains,
+pre-activation and scalar gates. One shape is also checked against the float64 oracle, through the C
+ABI."""
 
 import numpy as np
 import pytest
@@ -15,23 +23,29 @@ import oracle
 import synth
 from delta_rule_recurrent_gdn_amd import (gdn2_bwd_chunked, gdn2_bwd_chunked_records, gdn2_fwd_chunked,
                                           gdn2_fwd_chunked_train)
-from tests.helpers import TOL_GRAD, f64, rel_err, to_dev
+from tests.helpers import TOL_GRAD, f64, rel_err, take_pairs, to_dev
 
 pytestmark = pytest.mark.gpu
 GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
+DLA_BAR = 5e-3  # 16-bit inputs: dlog_alpha of the pair against the separate calls (see above)
 
 
 def _pair_equals_separate(inp, C, dS=None, **kw):
     d = to_dev(inp)
     x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
-    o1, S1, c1, rec = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C, **kw)
-    g1 = gdn2_bwd_chunked_records(*x, d["dO"], c1, rec, dS_final=dS, chunk=C, **kw)
+    o1, S1, rec = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C, **kw)
+    g1 = gdn2_bwd_chunked_records(*x, d["dO"], rec, dS_final=dS, chunk=C, **kw)
     o2, S2, c2 = gdn2_fwd_chunked(*x, d["S0"], chunk=C, want_chunk_states=True, **kw)
     g2 = gdn2_bwd_chunked(*x, d["dO"], S0=d["S0"], dS_final=dS, chunk_states=c2, chunk=C, **kw)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(c1, c2)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
     for n in GRADS:
-        assert torch.equal(g1[n], g2[n]), n
+        if n == "dlog_alpha" and d["q"].dtype == torch.bfloat16:
+            e = rel_err(f64(g1[n]), f64(g2[n]))
+            print(f"pair dlog_alpha vs separate: {e:.2e}")
+            assert e <= DLA_BAR, e
+        else:
+            assert torch.equal(g1[n], g2[n]), n
     return o1, S1, g1
 
 
@@ -80,3 +94,25 @@ def test_training_pair_against_oracle():
                           inp["dO"], dS)
     for n in GRADS:
         assert rel_err(f64(g[n]), ref[n]) <= TOL_GRAD, n
+
+
+def test_training_pair_B8_H16_T4096_sampled_pairs():
+    """The benchmarked training step (B=8, H=16, T=4096, d=128, chunk 64, bf16) through the pair: every
+    gradient of sampled (b, h) pairs against the float64 oracle."""
+    inp = synth.workload_inputs("fwd+bwd-B8-H16-T4096-d128")
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    _, _, rec = gdn2_fwd_chunked_train(*x, None, chunk=64)
+    g = gdn2_bwd_chunked_records(*x, d["dO"], rec, chunk=64)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (5, 11), (7, 15)]
+    args = [take_pairs(inp[n], pairs) for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    ref = oracle.backward(*args, None, take_pairs(inp["dO"], pairs))
+    errs = {}
+    for name in GRADS[:-1]:
+        gp = np.stack([f64(g[name])[b, :, h] for b, h in pairs])[:, :, None, :]
+        errs[name] = rel_err(gp, ref[name])
+    errs["dS0"] = rel_err(np.stack([f64(g["dS0"])[b, h] for b, h in pairs])[:, None], ref["dS0"])
+    print("pair B8 H16 T4096 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL_GRAD, (name, e)
