@@ -97,7 +97,9 @@ struct FwdCfg {
   static constexpr int VW_RPT = (C + VW_RPP - 1) / VW_RPP;
 };
 
-template <int DK, int C, int BV, bool F32IN>
+// FL: some gate option (pre-activation or per-head scalar gates) is on; without
+// it every gate-option branch of the loads folds away.
+template <int DK, int C, int BV, bool F32IN, bool FL>
 __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<DK, C, BV, F32IN>;
   using KS = typename Cfg::KS;
@@ -141,9 +143,10 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
 
   KS ks;
   ks.init(tid);
-  ks.raw = a.raw_gates;
-  ks.scalar_la = a.scalar_decay;
-  ks.scalar_b = a.scalar_b;
+  const bool raw_gates = FL && a.raw_gates, scalar_w = FL && a.scalar_w;
+  ks.raw = raw_gates;
+  ks.scalar_la = FL && a.scalar_decay;
+  ks.scalar_b = FL && a.scalar_b;
   constexpr int VW_RPP = Cfg::VW_RPP, VW_RPT = Cfg::VW_RPT;
   const int vw_r = tid / (BV / 8), vw_j8 = tid % (BV / 8);
   Raw8<F32IN> rv[VW_RPT], rw[VW_RPT];
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
       if (r < Ln) {
         const int64_t idx = baseV + (int64_t)(tn + r) * rowV + 8 * vw_j8;
         ld_raw(rv[i], a.v, idx);
-        ld_raw_gate(rw[i], a.w, idx, baseK / DK + (int64_t)(tn + r) * H, a.scalar_w);
+        ld_raw_gate(rw[i], a.w, idx, baseK / DK + (int64_t)(tn + r) * H, scalar_w);
       } else {
         zero_raw(rv[i]);
         zero_raw(rw[i]);
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
         float vv[8], ww[8];
         cvt(rv[i], vv);
         cvt(rw[i], ww);
-        if (a.raw_gates) {
+        if (raw_gates) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) ww[e] = sigmoid_f(ww[e]);  // v is zero on padding rows
         }
@@ -334,7 +337,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int nv = a.Dv / BV;
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * nv;
-    hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
+    if (a.raw_gates || a.scalar_b || a.scalar_w || a.scalar_decay)
+      hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN, true>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN, false>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
     return hipGetLastError();
   }
 }
