@@ -175,6 +175,29 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
     if (has_ut) load_ut(n_begin, utn);
   }
 
+  // o of chunk n is stored at the start of step n + 1: every step begins by
+  // waiting for all of the wave's vector-memory operations (the next record and
+  // T (w v) loads), and stores count among them, so stores issued at the end of
+  // a step would put their full write latency on the chain. (Not in the
+  // segmented kernel, whose 8-wave workgroups have no registers to spare.)
+  constexpr bool kDefer = !SEG;
+  f32x4 oPrev[RC][NCT];
+  int t0Prev = 0, LrPrev = 0;
+  bool oPend = false;
+  auto store_o = [&]() {
+#pragma unroll
+    for (int R = 0; R < RC; ++R)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * R + 4 * lg + i;
+        if (r < LrPrev) {
+          float* op = a.o + baseV + (int64_t)(t0Prev + r) * rowV + lr;
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) op[16 * c] = oPrev[R][c][i];
+        }
+      }
+  };
+
   for (int n = n_begin; n < n_end; ++n) {
     const int t0 = sl.tok0 + n * C, Lr = min(C, sl.len - n * C);
     char* buf = smem + (Cfg::NBUF == 2 ? ((n - n_begin) & 1) * Rec::kBytes : 0);
@@ -183,6 +206,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
     if (Cfg::NBUF == 2 && n + 1 < n_end)
       dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem + ((n + 1 - n_begin) & 1) * Rec::kBytes, Rec::kUnits,
                 wid, NWV);
+    if (oPend) store_o();
 
     if (a.states16 && outs) {
       _Float16* cs = a.states16 + (sl.item0 + n) * DK * Dv + j0;
@@ -311,18 +335,20 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
       }
     }
 
-    // ---- o (not written when the caller only wants states) ----
+    // ---- o (not written when the caller only wants states): stored next step ----
+    if (a.o && outs) {
 #pragma unroll
-    for (int R = 0; R < RC && a.o && outs; ++R)
+      for (int R = 0; R < RC; ++R)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * R + 4 * lg + i;
-        if (r < Lr) {
-          float* op = a.o + baseV + (int64_t)(t0 + r) * rowV + lr;
-#pragma unroll
-          for (int c = 0; c < NCT; ++c) op[16 * c] = accO[R][c][i];
-        }
+        for (int c = 0; c < NCT; ++c) oPrev[R][c] = accO[R][c];
+      t0Prev = t0;
+      LrPrev = Lr;
+      oPend = true;
+      if constexpr (!kDefer) {
+        store_o();
+        oPend = false;
       }
+    }
     }  // active
 
     if (Cfg::NBUF == 1 && n + 1 < n_end) {
@@ -330,6 +356,7 @@ __global__ __launch_bounds__(NWV * 64) void gdn2_chain_fwd_kernel(FwdArgs a, con
       dma_units(recs + (int64_t)(n + 1) * Rec::kBytes, smem, Rec::kUnits, wid, NWV);
     }
   }
+  if (oPend) store_o();  // the last chunk's o
 
   if constexpr (SEG) {
     if (sg.mode == kSegMap && active) {
