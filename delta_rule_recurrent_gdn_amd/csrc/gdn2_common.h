@@ -34,6 +34,12 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource on the gfx9 family (gfx950 included): 32-bit
+// data format, no swizzle, so offsets are plain byte offsets; accesses past
+// num_records read zero and are not written.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 constexpr int kWave = 64;
 

@@ -27,6 +27,7 @@ struct DecodeShape {
   static constexpr int kRowGroups = kThreads / kCols4;
   static constexpr int kRowsPerThread = DK / kRowGroups;
   static_assert(kRowsPerThread >= 1 && kRowGroups * kRowsPerThread == DK, "decode tiling");
+  static_assert((kRowsPerThread & (kRowsPerThread - 1)) == 0, "rows per thread: a power of two");
 };
 
 template <int DK, int DV, bool F32IN>
@@ -55,6 +56,29 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   }
   float* S = a.S + sidx * (int64_t)DK * DV;
 
+  // stream the state rows owned by this thread, first, so that their latency and
+  // that of the per-channel vectors below overlap (the vectors' LDS writes wait
+  // for every load issued before them); through a buffer resource over this
+  // head's state: one VGPR offset and a scalar row offset per access
+  const int j4 = tid % C4, rg = tid / C4;
+  const __amdgpu_buffer_rsrc_t Sr = __builtin_amdgcn_make_buffer_rsrc(S, 0, DK * DV * 4, kBufferRsrcWord3);
+  const int voff = (rg * DV + 4 * j4) * 4;
+  constexpr int kRowStep = RG * DV * 4;  // bytes between a thread's rows
+  // slot i holds the thread's row step (i + rot) mod RPT: neighbouring workgroups
+  // start at different 4 KiB pieces of their states, which all begin on 64 KiB
+  // boundaries (the same offsets at the same time otherwise)
+  const int rot = (int)(blockIdx.x & (RPT - 1));
+  auto row_of = [&](int i) { return (i + rot) & (RPT - 1); };
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(Sr, voff, row_of(i) * kRowStep, 0));
+  // this thread's 4 value columns of v and w, in flight with the state
+  float vv[4], wg[4];
+  load4<F32IN>(a.v, vec_v + 4 * j4, vv);
+  load4_gate<F32IN>(a.w, vec_v + 4 * j4, bh, a.scalar_w, wg);
+  __builtin_amdgcn_sched_barrier(0);
+
   // per-channel key-side vectors
   float kq = 0.f;
   if (tid < DK) {
@@ -75,17 +99,12 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   for (int off = kWave / 2; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
   if ((tid & (kWave - 1)) == 0) s_wsum[tid / kWave] = kq;
 
-  // stream the state rows owned by this thread
-  const int j4 = tid % C4, rg = tid / C4;
-  float4 s[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const float4*>(S + (rg + RG * i) * DV + 4 * j4);
   __syncthreads();
 
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int c = rg + RG * i;
+    const int c = rg + RG * row_of(i);
     const float al = s_alpha[c], e = s_e[c], qc = s_q[c];
     s[i].x *= al; s[i].y *= al; s[i].z *= al; s[i].w *= al;
     r.x += e * s[i].x; r.y += e * s[i].y; r.z += e * s[i].z; r.w += e * s[i].w;
@@ -97,7 +116,9 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
 
   r = make_float4(0.f, 0.f, 0.f, 0.f);
   p = r;
-#pragma unroll
+  // two row groups per step: unrolled fully, the compiler holds every partial at
+  // once beside the state rows (64 more VGPRs, one workgroup fewer per CU)
+#pragma unroll 2
   for (int g = 0; g < RG; ++g) {
     const float4 x = *reinterpret_cast<const float4*>(&s_red_r[g][4 * j4]);
     const float4 y = *reinterpret_cast<const float4*>(&s_red_p[g][4 * j4]);
@@ -108,9 +129,6 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
 #pragma unroll
   for (int wv = 0; wv < NWAVES; ++wv) kqs += s_wsum[wv];
 
-  float vv[4], wg[4];
-  load4<F32IN>(a.v, vec_v + 4 * j4, vv);
-  load4_gate<F32IN>(a.w, vec_v + 4 * j4, bh, a.scalar_w, wg);
   if (a.raw_gates) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) wg[e] = sigmoid_f(wg[e]);
@@ -122,10 +140,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::kThreads)) void gdn2_decode_k
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int c = rg + RG * i;
+    const int c = rg + RG * row_of(i);
     const float kc = s_k[c];
     const float4 n = make_float4(s[i].x + kc * u.x, s[i].y + kc * u.y, s[i].z + kc * u.z, s[i].w + kc * u.w);
-    *reinterpret_cast<float4*>(S + c * DV + 4 * j4) = n;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, n), Sr, voff, row_of(i) * kRowStep, 0);
   }
 }
 
