@@ -24,12 +24,13 @@ def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
     good = text.replace(text.split("sources_sha256: ")[1].split("\n")[0], bench.kernel_sources_sha256())
     prof.write_text(good)
-    got = bench.measured_traffic("bwd_launch_traffic_bytes")
+    got = bench.measured_traffic("bwd_records_launch_traffic_bytes")
     assert isinstance(got, int) and got > 3_221_225_472  # at least the algorithmic bytes
+    assert isinstance(bench.measured_traffic("train_fwd_launch_traffic_bytes"), int)
     prof.write_text(good.replace(bench.kernel_sources_sha256(), "0" * 64))
-    assert bench.measured_traffic("bwd_launch_traffic_bytes") is None
+    assert bench.measured_traffic("bwd_records_launch_traffic_bytes") is None
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "missing.md"))
-    assert bench.measured_traffic("bwd_launch_traffic_bytes") is None
+    assert bench.measured_traffic("bwd_records_launch_traffic_bytes") is None
 
 
 def test_byte_and_flop_models_match_the_stated_per_token_figures():

@@ -161,3 +161,34 @@ def test_packed_training_pair_two_level_chains():
 
 def test_packed_training_pair_raw_gates():
     _varlen_pair_equals_separate([100, 0, 70], 2, 64, 64, 32, "bf16", seed=122, raw_gates=True)
+
+
+def test_packed_training_pair_scalar_gates():
+    """Gated DeltaNet-style gates (one b = w and one decay per token-head) on a packed batch through the pair,
+    against the separate calls and against the float64 oracle fed the broadcast gates."""
+    lengths, C, H, D = [45, 0, 70, 13], 32, 2, 32
+    T = int(sum(lengths))
+    rng = np.random.default_rng(123)
+    inp = synth.make_inputs(1, T, H, D, D, "fp32", seed=123, grad=True)
+    beta = torch.from_numpy(rng.uniform(0.05, 0.95, (1, T, H)).astype(np.float32))
+    la = torch.from_numpy(-np.log1p(np.exp(rng.standard_normal((1, T, H)) - 2)).astype(np.float32))
+    inp.update(b=beta, w=beta.clone(), log_alpha=la)
+    S0 = torch.from_numpy((0.2 * rng.standard_normal((len(lengths), H, D, D))).astype(np.float32))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64))
+    kw = dict(scalar_b=True, scalar_w=True, scalar_decay=True)
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o1, S1, rec = gdn2_fwd_varlen_train(*x, cu.cuda(), S0.cuda(), chunk=C, **kw)
+    g1 = gdn2_bwd_varlen_records(*x, d["dO"], cu.cuda(), rec, chunk=C, **kw)
+    o2, S2, cs = gdn2_fwd_varlen(*x, cu.cuda(), S0.cuda(), chunk=C, want_chunk_states=True, **kw)
+    g2 = gdn2_bwd_varlen(*x, d["dO"], cu.cuda(), S0=S0.cuda(), chunk_states=cs, chunk=C, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for n in GRADS:
+        assert torch.equal(g1[n], g2[n]), n
+    ex = lambda t: t[..., None].expand(*t.shape, D).contiguous()  # noqa: E731
+    ref = oracle.backward_varlen(inp["q"], inp["k"], inp["v"], ex(la), ex(beta), ex(beta), cu, S0, inp["dO"])
+    for n in ("db", "dw", "dlog_alpha"):
+        ref[n] = ref[n].sum(-1)
+    for n in GRADS:
+        assert rel_err(f64(g1[n]), ref[n]) <= 1e-4, n
