@@ -296,6 +296,26 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
+  // fp16 entry states (S16): the key phase's rows of S0 and dS (this wave's
+  // key-channel block, 8 value columns per lane group and step) are fetched
+  // right after the column phase's gathers, so that they arrive during the
+  // column phase instead of opening the key phase with a wait (not with
+  // per-head scalar gates, whose reductions leave no registers for them)
+  constexpr bool kEarly = S16 && !GS;
+  constexpr int kNStepE = kEarly ? Cfg::DVM / 32 : 1;
+  f16x8 eS[kNStepE], eD[kNStepE];
+  auto fetch_rows = [&]() {
+    if constexpr (kEarly) {
+      const int d = 16 * (wid % KB16) + lr;
+#pragma unroll
+      for (int st = 0; st < kNStepE; ++st) {
+        const int c0 = 32 * st + 8 * lg, cs = c0 < Dv ? c0 : 0;
+        eS[st] = *reinterpret_cast<const f16x8*>(S0g + (int64_t)d * Dv + cs);
+        eD[st] = *reinterpret_cast<const f16x8*>(dSg + (int64_t)d * Dv + cs);
+      }
+    }
+  };
+  if (16 * wid >= Dv) fetch_rows();  // a wave with no value columns
   if (16 * wid < Dv) {
     const int jc = 16 * wid + lr;
     using RhsT = typename std::conditional<F32IN, f32x4, f16x8>::type;
@@ -330,6 +350,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
         wr[R][e] = ld_sel(static_cast<const InT*>(a.w), wBase + (int64_t)(t0 + t) * wRow + jc * wCs,
                           wBase + (int64_t)t0 * wRow + jc * wCs, t < Lr);
       }
+    fetch_rows();
     __builtin_amdgcn_sched_barrier(0);
     RhsT s0f[UKd], dsf[UKd], dof[UCc];
     float vv[RC][4], ww[RC][4];
@@ -482,7 +503,13 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
       const int cs = on ? c0 : 0;  // unconditional loads, zeroed below
       const S0T* ps = S0g + (int64_t)d * Dv + cs;
       const SdT* pd = dSg + (int64_t)d * Dv + cs;
-      if constexpr (S16) {  // NV = 8 halves: one 16-byte load
+      if constexpr (kEarly) {  // fetched with the column phase's gathers
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          xs[j] = static_cast<float>(eS[st][j]);
+          xd[j] = static_cast<float>(eD[st][j]);
+        }
+      } else if constexpr (S16) {  // NV = 8 halves: one 16-byte load
         const f16x8 h8 = *reinterpret_cast<const f16x8*>(ps);
 #pragma unroll
         for (int j = 0; j < NV; ++j) xs[j] = static_cast<float>(h8[j]);
@@ -498,7 +525,7 @@ __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
           xd[j4] = b4.x; xd[j4 + 1] = b4.y; xd[j4 + 2] = b4.z; xd[j4 + 3] = b4.w;
         }
       }
-      if constexpr (!F32IN) {  // NV = 8 halves: one 16-byte load
+      if constexpr (!F32IN && !kEarly) {  // NV = 8 halves: one 16-byte load
         const f16x8 h8 = *reinterpret_cast<const f16x8*>(pd);
 #pragma unroll
         for (int j = 0; j < NV; ++j) xd[j] = static_cast<float>(h8[j]);
