@@ -118,6 +118,14 @@ def test_training_pair_B8_H16_T4096_sampled_pairs():
     print("pair B8 H16 T4096 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     for name, e in errs.items():
         assert e <= TOL_GRAD, (name, e)
+    # no atomics anywhere on the path: a second pair gives the same bits
+    o1, _, rec2 = gdn2_fwd_chunked_train(*x, None, chunk=64)
+    g2 = gdn2_bwd_chunked_records(*x, d["dO"], rec2, chunk=64)
+    o2, _, _ = gdn2_fwd_chunked_train(*x, None, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for name in GRADS:
+        assert torch.equal(g[name], g2[name]), name
 
 
 def _varlen_pair_equals_separate(lengths, H, Dk, Dv, C, dtype, seed, **kw):
