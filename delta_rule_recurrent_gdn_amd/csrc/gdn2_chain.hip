@@ -76,7 +76,10 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
   constexpr int RC = Cfg::RC, RK = Cfg::RK, UK = Rec::UK, UC = Rec::UC;
   constexpr int KU = F::KU;
 
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
+  // two record buffers (one when two do not fit), as separate arrays: see the step loop
+  __shared__ __attribute__((aligned(1024))) char smemA[Rec::kBytes];
+  __shared__ __attribute__((aligned(1024))) char smemB[Cfg::NBUF == 2 ? Rec::kBytes : 16];
+  char* const smem = smemA;
 
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
@@ -188,10 +191,10 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       dma_units(src, dst, Rec::kUnits, wid, NWV);
     }
   };
-  f32x4 utn[RC][NCT];
+  f32x4 utA[RC][NCT], utB[RC][NCT];
   if (n_begin < n_end) {  // an empty packed sequence has no chunk: S_final = S0
     dma(recs + (int64_t)n_begin * Rec::kBytes, smem);
-    if (has_ut) load_ut(n_begin, utn);
+    if (has_ut) load_ut(n_begin, utA);
   }
 
   // o of chunk n is stored at the start of step n + 1: every step begins by
@@ -217,13 +220,15 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       }
   };
 
-  for (int n = n_begin; n < n_end; ++n) {
+  // one chain step: record n in buf, the next record's copy into nbuf; T (w v) of chunk n in utc, the next
+  // chunk's loaded into utx
+  auto step = [&](const int n, char* buf, char* nbuf, f32x4 (&utc)[RC][NCT], f32x4 (&utx)[RC][NCT])
+                  __attribute__((always_inline)) {
     const int t0 = sl.tok0 + n * C, Lr = min(C, sl.len - n * C);
-    char* buf = smem + (Cfg::NBUF == 2 ? ((n - n_begin) & 1) * Rec::kBytes : 0);
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n-1
     if (Cfg::NBUF == 2 && n + 1 < n_end)
-      dma(recs + (int64_t)(n + 1) * Rec::kBytes, smem + ((n + 1 - n_begin) & 1) * Rec::kBytes);
+      dma(recs + (int64_t)(n + 1) * Rec::kBytes, nbuf);
     if (oPend) store_o();
 
     if (a.states16 && outs) {
@@ -250,10 +255,10 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
     for (int R = 0; R < RC; ++R)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        accU[R][c] = has_ut ? utn[R][c] : zero4();
+        accU[R][c] = has_ut ? utc[R][c] : zero4();
         accO[R][c] = zero4();
       }
-    if (has_ut && n + 1 < n_end) load_ut(n + 1, utn);
+    if (has_ut && n + 1 < n_end) load_ut(n + 1, utx);
     if (active) {
 
     const uint4* uW = reinterpret_cast<const uint4*>(buf + Rec::u0 * 1024) + l;
@@ -373,6 +378,15 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       __syncthreads();  // every wave is done reading the single buffer
       dma(recs + (int64_t)(n + 1) * Rec::kBytes, smem);
     }
+  };
+  // Steps in pairs, so that every record copy and every LDS read names its buffer, and every T (w v) load
+  // its registers, statically. With the buffer chosen at run time the compiler waited, before the first
+  // LDS read of each step, for every vector-memory operation then in flight (the next record's copy
+  // included), and moving the loaded T (w v) into the registers of the next step forced the same wait.
+  char* const nextA = Cfg::NBUF == 2 ? smemB : smemA;
+  for (int n = n_begin; n < n_end; n += 2) {
+    step(n, smemA, nextA, utA, utB);
+    if (n + 1 < n_end) step(n + 1, nextA, smemA, utB, utA);
   }
   if (oPend) store_o();  // the last chunk's o
 
@@ -438,7 +452,10 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
   constexpr int NBUF = 2 * kBuf <= 160 * 1024 ? 2 : 1;
   constexpr int kCols = 16 * NCT * NWV;
 
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kBuf];
+  // record buffers as separate arrays, as in the forward chain
+  __shared__ __attribute__((aligned(1024))) char smemA[kBuf];
+  __shared__ __attribute__((aligned(1024))) char smemB[NBUF == 2 ? kBuf : 16];
+  char* const smem = smemA;
 
   const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
@@ -531,12 +548,17 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
       }
     }
 
-  // dO of chunk nn as right-operand fragments (contraction over the chunk's tokens)
+  // dO of chunk nn as right-operand fragments (contraction over the chunk's tokens): fetched one step
+  // ahead as raw values (rows past the sequence read the chunk's first row) and zeroed past the sequence
+  // when they are used, so that nothing waits for the loads in the step that issues them
   constexpr int NDU = F32IN ? RC : UC;    // fragments per column tile
   constexpr int NDE = F32IN ? 4 : 8;      // elements per fragment
-  using RawT = typename std::conditional<F32IN, float, uint16_t>::type;
-  RawT rdo[NDU][NCT][NDE];
-  auto load_do = [&](int nn) {
+  // (bf16 bits one per register: packed two to a register, the loads are waited for at once; the
+  // segmented kernel's 8-wave workgroups keep them packed, with one dO set, for want of registers)
+  using RawT = typename std::conditional<F32IN, float, typename std::conditional<SEG, uint16_t, uint32_t>::type>::type;
+  auto do_row = [&](int u, int j) { return F32IN ? 16 * u + 4 * lg + j : KU * u + F::kslot(lg, j); };
+  RawT rdoA[NDU][NCT][NDE], rdoB[NDU][NCT][NDE];
+  auto load_do = [&](int nn, RawT (&dst)[NDU][NCT][NDE]) {
     const int tn = sl.tok0 + nn * C, Ln = min(C, sl.len - nn * C);
 #pragma unroll
     for (int u = 0; u < NDU; ++u)
@@ -544,32 +566,28 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
         for (int j = 0; j < NDE; ++j) {
-          const int t = F32IN ? 16 * u + 4 * lg + j : KU * u + F::kslot(lg, j);
+          const int t = do_row(u, j);
           const int64_t idx = baseV + (int64_t)(tn + t) * rowV + 16 * c + lr;
           const int64_t safe = baseV + (int64_t)tn * rowV + 16 * c + lr;  // the chunk's first row
-          rdo[u][c][j] = ld_sel(static_cast<const RawT*>(a.dO), idx, safe, t < Ln);
+          if constexpr (SEG) dst[u][c][j] = ld_sel(static_cast<const RawT*>(a.dO), idx, safe, t < Ln);
+          else if constexpr (F32IN) dst[u][c][j] = static_cast<const float*>(a.dO)[t < Ln ? idx : safe];
+          else dst[u][c][j] = static_cast<const uint16_t*>(a.dO)[t < Ln ? idx : safe];
         }
   };
 
   if (n_begin < n_end) {  // an empty packed sequence has no chunk: dS0 = dS_final
-    dma(recs + (int64_t)(n_end - 1) * Rec::kBytes, smem + (NBUF == 2 ? ((n_end - 1) & 1) * kBuf : 0));
-    if (has_do) load_do(n_end - 1);
-  }
-  if (!has_do) {  // identity columns (and idle waves): no dO
-#pragma unroll
-    for (int u = 0; u < NDU; ++u)
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int j = 0; j < NDE; ++j) rdo[u][c][j] = RawT(0);
+    dma(recs + (int64_t)(n_end - 1) * Rec::kBytes, smem);
+    if (has_do) load_do(n_end - 1, rdoA);
   }
 
-  for (int n = n_end - 1; n >= n_begin; --n) {
-    char* buf = smem + (NBUF == 2 ? (n & 1) * kBuf : 0);
+  // one chain step: record n in buf, the previous record's copy into nbuf; dO of chunk n in rdc, the
+  // previous chunk's loaded into rdx
+  auto step = [&](const int n, char* buf, char* nbuf, RawT (&rdc)[NDU][NCT][NDE], RawT (&rdx)[NDU][NCT][NDE])
+                  __attribute__((always_inline)) {
     wait_vm_all();
     __syncthreads();  // record n is in LDS; every wave is done with chunk n+1
     if (NBUF == 2 && n > n_begin)
-      dma(recs + (int64_t)(n - 1) * Rec::kBytes, smem + ((n - 1) & 1) * kBuf);
+      dma(recs + (int64_t)(n - 1) * Rec::kBytes, nbuf);
 
     if (outs) {
       using SdT = typename std::conditional<F32IN, float, _Float16>::type;
@@ -582,19 +600,22 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
           for (int i = 0; i < 4; ++i) ws[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = static_cast<SdT>(accD[R][c][i]);
     }
 
-    // this chunk's dO fragments; the previous chunk's start loading
+    // this chunk's dO fragments (zero past the sequence, and on the identity columns and idle waves);
+    // the previous chunk's start loading
     using DoF = typename std::conditional<F32IN, f32x4, f16x8>::type;
     DoF dof[NDU][NCT];
+    const int Ln = min(C, sl.len - n * C);
 #pragma unroll
     for (int u = 0; u < NDU; ++u)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
         for (int j = 0; j < NDE; ++j) {
-          if constexpr (F32IN) dof[u][c][j] = rdo[u][c][j];
-          else dof[u][c][j] = static_cast<_Float16>(bf16_bits_to_f32(rdo[u][c][j]));
+          const bool ok = has_do && (SEG || do_row(u, j) < Ln);  // (segmented: zeroed at the load)
+          if constexpr (F32IN) dof[u][c][j] = ok ? rdc[u][c][j] : 0.f;
+          else dof[u][c][j] = static_cast<_Float16>(ok ? bf16_bits_to_f32(rdc[u][c][j]) : 0.f);
         }
-    if (has_do && n > n_begin) load_do(n - 1);
+    if (has_do && n > n_begin) load_do(n - 1, rdx);
     if (active) {
 
     const uint4* uPT = reinterpret_cast<const uint4*>(buf + Rec::u0 * 1024) + l;
@@ -704,6 +725,21 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
     if (NBUF == 1 && n > n_begin) {
       __syncthreads();  // every wave is done reading the single buffer
       dma(recs + (int64_t)(n - 1) * Rec::kBytes, smem);
+    }
+  };
+  // steps in pairs: static buffers and dO registers (see the forward chain's step loop); the segmented
+  // kernel's 8-wave workgroups have no registers for the pairs (spills), so it takes one step per
+  // iteration with one dO set
+  char* const nextA = NBUF == 2 ? smemB : smemA;
+  if constexpr (SEG) {
+    for (int n = n_end - 1; n >= n_begin; --n) {
+      const bool odd = ((n_end - 1 - n) & 1) != 0;
+      step(n, odd ? nextA : smemA, odd ? smemA : nextA, rdoA, rdoA);
+    }
+  } else {
+    for (int n = n_end - 1; n >= n_begin; n -= 2) {
+      step(n, smemA, nextA, rdoA, rdoB);
+      if (n - 1 >= n_begin) step(n - 1, nextA, smemA, rdoB, rdoA);
     }
   }
 
