@@ -54,10 +54,10 @@ __device__ __forceinline__ void dma_units(const char* src, char* dst, int units,
 }
 
 // Helper waves of the plain reverse chain (one workgroup per CU): they take the
-// record copies off the column waves, which also gather dO, on SIMDs that would
-// otherwise be idle (1.52 -> 1.50 ms for the B8 H16 T4096 backward). The forward
-// chain has none: it is bound by its per-CU share of HBM bandwidth, and helper
-// copies competing with the column waves' stores made it slower (0.93 -> 0.97 ms).
+// record copies off the column waves, which also gather dO (1.41 -> 1.38 ms for
+// the B8 H16 T4096 backward; four helpers: 1.39 ms). The forward chain has none:
+// its four column waves need more than the 256 registers a wave may hold when a
+// SIMD runs two, and with two column waves helpers made it slower.
 constexpr int kChainHelpers = 2;
 
 // all vector-memory operations of this wave have completed (gfx9 encoding:
@@ -771,8 +771,8 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dispatch: NCT = 2 (32 columns per wave) when Dv allows, NWV waves so that
-// the grid has at least ~256 workgroups when it can
+// dispatch: NCT column tiles of 16 per wave, NWV column waves per workgroup,
+// shaped so that the grid has at least ~256 workgroups when it can
 // ---------------------------------------------------------------------------
 template <int DK, int C, bool F32IN, int NCT, int NWV>
 static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float* ut, hipStream_t s) {
@@ -972,9 +972,11 @@ static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float*
     }
   }
   if (a.Dv == 16) return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);
-  // 32 columns per wave; as many waves per workgroup as keep >= 256 workgroups
-  const int tiles = a.Dv / 32;  // wave tiles per head
-  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_t<DK, C, F32IN, 2, 2>(a, rec, ut, s);
+  // 64 columns per workgroup, over four waves (one per SIMD), while that keeps >= 256 workgroups (two
+  // waves of 32 columns: 0.89 -> 0.84 ms for the B8 H16 T4096 training forward); else 32 columns per
+  // one-wave workgroup, or 16 for few heads
+  const int tiles = a.Dv / 32;  // 32-column tiles per head
+  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_t<DK, C, F32IN, 1, 4>(a, rec, ut, s);
   if (nbh * tiles >= 256) return launch_chain_t<DK, C, F32IN, 2, 1>(a, rec, ut, s);
   return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);  // few heads: 16 columns per workgroup
 }
@@ -1069,8 +1071,10 @@ static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, char* se
     if (G > 1) return launch_chain_bwd_seg<DK, C, F32IN>(a, rec, seg, G, s);
   }
   if (a.Dv == 16) return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
+  // workgroup shapes as in the forward chain (four waves of 16 columns: 1.44 -> 1.39 ms for the B8 H16
+  // T4096 backward), plus the helper waves
   const int tiles = a.Dv / 32;
-  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 2>(a, rec, s);
+  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 1, 4>(a, rec, s);
   if (nbh * tiles >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 1>(a, rec, s);
   return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
 }

@@ -25,7 +25,8 @@ import synth
 from delta_rule_recurrent_gdn_amd import (gdn2_bwd_chunked, gdn2_bwd_chunked_records, gdn2_bwd_varlen,
                                           gdn2_bwd_varlen_records, gdn2_fwd_chunked, gdn2_fwd_chunked_train,
                                           gdn2_fwd_varlen, gdn2_fwd_varlen_train)
-from tests.helpers import TOL_GRAD, f64, rel_err, take_pairs, to_dev
+from tests.helpers import (TOL_BF16, TOL_F32, TOL_GRAD, f64, gpu_pairs, gpu_state_pairs, oracle_fwd_pairs, rel_err,
+                           take_pairs, take_state_pairs, to_dev)
 
 pytestmark = pytest.mark.gpu
 GRADS = ("dq", "dk", "dv", "dlog_alpha", "db", "dw", "dS0")
@@ -96,6 +97,32 @@ def test_training_pair_against_oracle():
                           inp["dO"], dS)
     for n in GRADS:
         assert rel_err(f64(g[n]), ref[n]) <= TOL_GRAD, n
+
+
+@pytest.mark.parametrize("B,H,T,Dk,Dv,C,dtype", [
+    (4, 32, 2 * 64 + 5, 128, 128, 64, "bf16"),  # 128 (batch, head) pairs of 128 value columns
+    (8, 32, 3 * 32 + 7, 64, 64, 32, "bf16"),    # 256 pairs of 64
+    (4, 32, 2 * 32 + 3, 64, 128, 32, "fp32"),
+])
+def test_many_heads_four_wave_chains(B, H, T, Dk, Dv, C, dtype):
+    """Enough (batch, head) pairs for the chains' four-wave workgroups (16 value columns a wave), with a
+    ragged last chunk: the pair against the separate calls, and sampled pairs of every output and gradient
+    against the float64 oracle."""
+    inp = synth.make_inputs(B, T, H, Dk, Dv, dtype, seed=130 + Dk + C, s0_std=0.2, grad=True)
+    dS = torch.from_numpy(np.random.default_rng(131).standard_normal((B, H, Dk, Dv)).astype(np.float32))
+    o, S, g = _pair_equals_separate(inp, C, dS=dS.cuda())
+    pairs = [(0, 0), (B // 2, H - 1), (B - 1, 17)]
+    o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
+    tol = TOL_F32 if dtype == "fp32" else TOL_BF16
+    assert rel_err(gpu_pairs(o, pairs), o_ref) <= tol and rel_err(gpu_state_pairs(S, pairs), S_ref) <= tol
+    args = [take_pairs(inp[n], pairs) for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    ref = oracle.backward(*args, take_state_pairs(inp["S0"], pairs), take_pairs(inp["dO"], pairs),
+                          take_state_pairs(dS, pairs))
+    gtol = tol if dtype == "fp32" else TOL_GRAD
+    for name in GRADS[:-1]:
+        e = rel_err(np.stack([f64(g[name])[b, :, h] for b, h in pairs])[:, :, None, :], ref[name])
+        assert e <= gtol, (name, e)
+    assert rel_err(np.stack([f64(g["dS0"])[b, h] for b, h in pairs])[:, None], ref["dS0"]) <= gtol
 
 
 def test_training_pair_B8_H16_T4096_sampled_pairs():
