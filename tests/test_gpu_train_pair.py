@@ -194,6 +194,12 @@ def test_packed_training_pair_two_level_chains():
     _varlen_pair_equals_separate([1500, 37, 900, 3, 0, 600], 2, 64, 64, 32, "bf16", seed=121)
 
 
+def test_packed_training_pair_many_sequences():
+    """256 (sequence, head) pairs of 128 value columns: the chains' four-wave workgroups in the packed layout."""
+    _varlen_pair_equals_separate([37, 0, 1, 64, 65, 130, 16, 93, 7, 128, 3, 70, 64, 1, 90, 33], 16, 128, 128, 64,
+                                 "bf16", seed=142)
+
+
 def test_packed_training_pair_raw_gates():
     _varlen_pair_equals_separate([100, 0, 70], 2, 64, 64, 32, "bf16", seed=122, raw_gates=True)
 

@@ -226,3 +226,25 @@ def test_varlen_two_level_chain(dtype, Dk, Dv):
     gtol = TOL_F32 if dtype == "fp32" else TOL_GRAD
     for n_ in GRADS:
         assert rel_err(f64(g1[n_]), ref[n_]) <= gtol, n_
+
+
+def test_varlen_many_sequences_four_wave_chains():
+    """16 ragged sequences of 16 heads (256 (sequence, head) pairs of 128 value columns): the chains take
+    their four-wave workgroups in the packed layout; outputs, states and every gradient against the
+    oracle's per-sequence definition."""
+    lengths = [37, 0, 1, 64, 65, 130, 16, 93, 7, 128, 3, 70, 64, 1, 90, 33]
+    C, H, D = 64, 16, 128
+    inp, cu = _packed(lengths, H, D, D, "bf16", seed=140, grad=True)
+    dS = torch.from_numpy(np.random.default_rng(141).standard_normal((len(lengths), H, D, D)).astype(np.float32))
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o, S, cs = gdn2_fwd_varlen(*x, cu.cuda(), d["S0"], chunk=C, want_chunk_states=True)
+    g = gdn2_bwd_varlen(*x, d["dO"], cu.cuda(), S0=d["S0"], dS_final=dS.cuda(), chunk_states=cs, chunk=C)
+    torch.cuda.synchronize()
+    args = [inp[n] for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    o_ref, S_ref = oracle.forward_varlen(*args, cu, inp["S0"])
+    assert rel_err(f64(o), o_ref) <= TOL_BF16 and rel_err(f64(S), S_ref) <= TOL_BF16
+    ref = oracle.backward_varlen(*args, cu, inp["S0"], inp["dO"], dS)
+    for n in GRADS:
+        e = rel_err(f64(g[n]), ref[n])
+        assert e <= TOL_GRAD, (n, e)
