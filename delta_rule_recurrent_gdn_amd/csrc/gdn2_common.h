@@ -418,12 +418,15 @@ __device__ __forceinline__ void mma_nt_yf32(f32x4& acc, const T* X, int ldx, con
   }
 }
 
-// Same with X fp32 (converted) and Y 16-bit.
+// Same with X fp32 (converted) and Y 16-bit. A 16-bit Y may hold each row's 8-element blocks permuted:
+// block b of row srow0 + r stored at block b ^ (((srow0 + r) / 8) & smask) (smask 0: plain rows).
 template <typename T>
-__device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx, const T* Y, int ldy, int K) {
+__device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx, const T* Y, int ldy, int K,
+                                            int srow0 = 0, int smask = 0) {
   const int l = lane_id();
   const int r = l & 15, g = l >> 4;
   if constexpr (sizeof(T) == 2) {
+    const int sw = 8 * (((srow0 + r) >> 3) & smask);
     typedef T v8 __attribute__((ext_vector_type(8)));
     typedef T v4 __attribute__((ext_vector_type(4)));
     int k0 = 0;
@@ -433,7 +436,7 @@ __device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx,
       v8 a;
       a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
       a[4] = static_cast<T>(x1.x); a[5] = static_cast<T>(x1.y); a[6] = static_cast<T>(x1.z); a[7] = static_cast<T>(x1.w);
-      const v8 b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+      const v8 b = *reinterpret_cast<const v8*>(Y + r * ldy + ((k0 + 8 * g) ^ sw));
       acc = mfma16x16x32(a, b, acc);
     }
     if (k0 < K) {
@@ -443,7 +446,7 @@ __device__ __forceinline__ void mma_nt_xf32(f32x4& acc, const float* X, int ldx,
         const float4 x1 = *reinterpret_cast<const float4*>(X + r * ldx + k0 + 8 * g + 4);
         a[0] = static_cast<T>(x0.x); a[1] = static_cast<T>(x0.y); a[2] = static_cast<T>(x0.z); a[3] = static_cast<T>(x0.w);
         a[4] = static_cast<T>(x1.x); a[5] = static_cast<T>(x1.y); a[6] = static_cast<T>(x1.z); a[7] = static_cast<T>(x1.w);
-        b = *reinterpret_cast<const v8*>(Y + r * ldy + k0 + 8 * g);
+        b = *reinterpret_cast<const v8*>(Y + r * ldy + ((k0 + 8 * g) ^ sw));
       }
       acc = mfma16x16x32(a, b, acc);
     }

@@ -69,6 +69,10 @@ struct PrepCfg {
                                                                               : KS::kAfBytes + KS::kXsBytes);
   static constexpr int oT1 = oR + ((endR + 15) & ~15);            // OpT [DK][LDC]: Kb^T, later Kh^T
   static constexpr int oWVT = oT1 + DK * LDC * OPB;                // OpT [DVM][LDC] (w v)^T
+  // (w v)^T row j holds its 8-token blocks permuted, block b at b ^ ((j / 8) & kWvSwz): the staging
+  // writes of one wave cover 16 rows 8 apart, which would otherwise all start in the same LDS bank
+  // (16-way conflicts; 2-way with the permutation). 16-bit operands only.
+  static constexpr int kWvSwz = F32IN ? 0 : C / 8 - 1;
   static constexpr int kLdsBytes = oWVT + DVM * LDC * OPB;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
   static constexpr int VW_PT = (C * DVM / 8 + NT - 1) / NT;
@@ -174,8 +178,9 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
 #pragma unroll
           for (int q = 0; q < 8; ++q) vv[q] = ww[q] = 0.f;
         }
+        const int rs = rr ^ (8 * (j8 & Cfg::kWvSwz));  // rows 8 * j8 + q: (row / 8) = j8
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sWVT[(8 * j8 + q) * LDC + rr] = static_cast<OpT>(ww[q] * vv[q]);
+        for (int q = 0; q < 8; ++q) sWVT[(8 * j8 + q) * LDC + rs] = static_cast<OpT>(ww[q] * vv[q]);
       }
     }
   }
@@ -514,7 +519,8 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
     for (int t = wid; t < ntile; t += NW) {
       const int R = t / nvt, jb = t - R * nvt;
       f32x4 acc = zero4();
-      mma_nt_xf32<OpT>(acc, sAf + 16 * R * LDCF, LDCF, sWVT + 16 * jb * LDC, LDC, 16 * (R + 1));
+      mma_nt_xf32<OpT>(acc, sAf + 16 * R * LDCF, LDCF, sWVT + 16 * jb * LDC, LDC, 16 * (R + 1), 16 * jb,
+                       Cfg::kWvSwz);
       *reinterpret_cast<float4*>(ut + (int64_t)t * 256 + 4 * l) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
