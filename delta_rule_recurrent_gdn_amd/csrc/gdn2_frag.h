@@ -124,25 +124,33 @@ __device__ __forceinline__ void write_units_f32(const float* X, int ld, int M, i
 
 // Unpack unit (R, u) of a record matrix [M][K] into row-major LDS copies:
 // X[row][k] (ldx) and, when XT is not null, XT[k][row] (ldt); indices past K skipped.
-template <bool F32IN, typename OpT>
+// VEC: X's row takes the lane's slots as runs of 4 consecutive contraction indices, one vector store
+// each, instead of one store per element.
+template <bool F32IN, bool VEC, typename OpT>
 __device__ __forceinline__ void unpack_unit(const uint4& v, int R, int u, int K, OpT* X, int ldx, OpT* XT, int ldt) {
   using F = Frag<F32IN>;
   const int l = lane_id(), r = 16 * R + (l & 15), g = l >> 4;
   if constexpr (F32IN) {
     const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+    if constexpr (VEC) *reinterpret_cast<uint4*>(X + r * ldx + F::KU * u + F::kslot(g, 0)) = v;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = F::KU * u + F::kslot(g, j);
-      X[r * ldx + k] = x[j];
+      if constexpr (!VEC) X[r * ldx + k] = x[j];
       if (XT) XT[k * ldt + r] = x[j];
     }
   } else {
     const f16x8 h = __builtin_bit_cast(f16x8, v);
+    if constexpr (VEC) {  // slots 0-3 and 4-7; K is a multiple of 16, so a run lies wholly below K or not
+      const int k0 = F::KU * u + F::kslot(g, 0), k1 = F::KU * u + F::kslot(g, 4);
+      if (k0 < K) *reinterpret_cast<uint2*>(X + r * ldx + k0) = make_uint2(v.x, v.y);
+      if (k1 < K) *reinterpret_cast<uint2*>(X + r * ldx + k1) = make_uint2(v.z, v.w);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = F::KU * u + F::kslot(g, j);
       if (k < K) {
-        X[r * ldx + k] = h[j];
+        if constexpr (!VEC) X[r * ldx + k] = h[j];
         if (XT) XT[k * ldt + r] = h[j];
       }
     }
