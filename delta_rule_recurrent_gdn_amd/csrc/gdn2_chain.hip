@@ -906,7 +906,10 @@ int fwd_segments(int B, int H, int T, int Dk, int Dv, int chunk) {
   const int NC = (T + chunk - 1) / chunk;
   const long nbh = (long)B * H;
   if (nbh * (Dv / 32) >= 512) return 1;     // enough 32-column wave tiles already
-  long g = 256 / (nbh * ((Dv + 127) / 128)); // about one run-pass workgroup per CU
+  // about one run-pass workgroup per two CUs: with pipelined chain steps, fewer and longer segments cost
+  // less than the extra map and composition work of more (B1 H16 d128: T = 8K 0.36 -> 0.31 ms, 16K
+  // 0.57 -> 0.52 ms; equal at 32K and 64K; one per CU at 64K was not faster)
+  long g = 128 / (nbh * ((Dv + 127) / 128));
   if (g > NC / 8) g = NC / 8;                // at least 8 chunks per segment
   if (g > 64) g = 64;
   if (g < 4) return 1;

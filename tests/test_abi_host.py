@@ -77,12 +77,12 @@ def test_workspace_bytes():
 def test_workspace_bytes_two_level_forward():
     """Few heads and a long sequence: the forward workspace also holds the two-level chain's segment
     maps M [Dk x Dk], zero-entry exit states N and composed entry states [Dk x Dv] (fp32), 256-byte
-    aligned after the records and T (w v). 16 heads x 1024 chunks -> 16 segments of 64 chunks."""
+    aligned after the records and T (w v). 16 heads x 1024 chunks -> 8 segments of 128 chunks."""
     lib = _lib.load()
     B, T, H, D, C = 1, 65536, 16, 128, 64
     nc = T // C
     base = B * H * nc * (57 * 1024 + C * D * 4)
-    seg = B * H * 16 * (D * D + 2 * D * D) * 4
+    seg = B * H * 8 * (D * D + 2 * D * D) * 4
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == (base + 255) // 256 * 256 + seg
     # 128 heads fill the GPU with the plain chain: no segment buffers (the B=8 H=16 T=4096 training figure above)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 8, 4096, 16, D, D, C, 1) == 8 * 16 * 64 * (57 * 1024 + C * D * 4)
