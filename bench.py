@@ -236,6 +236,19 @@ def main():
                                   B, T, H, D, D, C, _lib.GDN2_BF16, sh)
         _lib.check(st, "gdn2_bwd_chunked")
 
+    def timed_ms(fn, n=10, warm=3):
+        """Average ms of fn over n calls after warm untimed ones (HIP events on the launch stream)."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     def timed_pair(f, b, n, warm):
         """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream)."""
         for _ in range(warm):
@@ -339,15 +352,7 @@ def main():
 
         fe = {}
         for name, fn in (("fused_ms_per_step", raw_step), ("unfused_ms_per_step", unfused_step)):
-            fn()
-            torch.cuda.synchronize()
-            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            f0.record(stream)
-            for _ in range(5):
-                fn()
-            f1.record(stream)
-            torch.cuda.synchronize()
-            fe[name] = round(f0.elapsed_time(f1) / 5, 4)
+            fe[name] = round(timed_ms(fn), 4)
         fe["fused_tokens_per_s"] = round(tokens / (fe["fused_ms_per_step"] / 1e3), 1)
         fe["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with pre-activation gates b, w "
                           "(bf16) and a (fp32); unfused = torch sigmoid / softplus passes before and chain-rule "
@@ -372,15 +377,7 @@ def main():
         SB, SW, SD = _lib.GDN2_FLAG_SCALAR_B, _lib.GDN2_FLAG_SCALAR_W, _lib.GDN2_FLAG_SCALAR_DECAY
         for name, flags, la in (("kda_ms_per_step", SB | SW, d["log_alpha"]),
                                 ("gated_deltanet_ms_per_step", SB | SW | SD, adec)):
-            scalar_step(flags, la)
-            torch.cuda.synchronize()
-            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            g0.record(stream)
-            for _ in range(5):
-                scalar_step(flags, la)
-            g1.record(stream)
-            torch.cuda.synchronize()
-            gg[name] = round(g0.elapsed_time(g1) / 5, 4)
+            gg[name] = round(timed_ms(lambda: scalar_step(flags, la)), 4)
         gg["channel_wise_ms_per_step"] = round(ms_step, 4)
         gg["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with per-head scalar gates: KDA = "
                           "one beta [B,T,H] for both gates, Gated DeltaNet = also a scalar decay [B,T,H]; "
@@ -440,15 +437,7 @@ def main():
 
         vt = {}
         for name, fn in (("pair", varlen_pair_step), ("separate", varlen_step)):
-            fn()
-            torch.cuda.synchronize()
-            v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            v0.record(stream)
-            for _ in range(5):
-                fn()
-            v1.record(stream)
-            torch.cuda.synchronize()
-            vt[name] = v0.elapsed_time(v1) / 5
+            vt[name] = timed_ms(fn)
         vms = vt["pair"]
         out["varlen"] = {"workload": f"packed batch of {N} sequences (lengths uniform 256..8192, seed 5) totalling "
                                      f"{B * T} tokens, H=16 d=128 chunk 64 bf16: training step "
