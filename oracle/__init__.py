@@ -11,18 +11,19 @@ Sources (the web pages on the method; cited by these tags everywhere):
 * [README]  "Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention",
             the NVlabs/GatedDeltaNet-2 README: the gate bullet list (erase
             gate, write gate, channel-wise decay, strict generalization) and
-            the update-rule paragraph that follows it. The page text is missing
-            the update equation itself; the paragraph after it says that the
-            right factor of the rank-one erase is channel-selective on the key
-            axis and the write term channel-selective on the value axis.
+            the update-rule paragraph that follows it. The extracted page text
+            lacks the update equation; the paragraph places the erase gate on
+            the key side (it multiplies k in the erase, b * k) and the write
+            gate on the value side (it multiplies v in the write, w * v).
 * [WIKI]    the AI-research-wiki summary of the same paper: TL;DR and
             "Key findings" (chunkwise WY algorithm absorbing channel-wise
             decay into asymmetric erase factors).
 * [NEWS]    the aiexpert.news article "Gated DeltaNet-2: finer-grained state
             editing for linear attention": method paragraph.
 * [ABS]     the arXiv 2605.22791 abstract (paper-index page and its mirror):
-            "fast-weight update view", delta rule subtracts the current read
-            before writing, reductions to KDA and Gated DeltaNet.
+            the update read as a fast-weight write, the delta rule removing
+            what the state currently returns for a key before writing to it,
+            and the reductions to KDA and Gated DeltaNet.
 
 The recurrence implemented, per batch row and head, with S_t a d_k x d_v
 matrix (the form fixed from [README] update-rule paragraph and [ABS]):
@@ -33,8 +34,9 @@ matrix (the form fixed from [README] update-rule paragraph and [ABS]):
 with b_t in [0,1]^{d_k} the erase gate, w_t in [0,1]^{d_v} the write gate and
 alpha_t = exp(log_alpha_t) the channel-wise decay on the key axis.
 
-Readings of points the pages leave open (each also listed in the design doc):
-decay is applied before the erase read ([README] "decayed state"); the output
+Readings of points the pages leave open:
+decay is applied before the erase read (the [README] gate list has the erase
+gate act on the state after decay); the output
 reads the updated state S_t; q is used as given (no scaling, no normalisation);
 gates are post-activation values and gradients are taken with respect to them.
 

@@ -29,12 +29,13 @@ def _f64(x):
 def _step(S, q_t, k_t, v_t, la_t, b_t, w_t):
     """One recurrence step for all (batch, head) pairs at once.
 
-    Fast-weight update view ([ABS]): decay the state first ([README] gate list:
-    the erase gate acts on "the decayed state"), read it through the erase key
-    e_t = b_t * k_t (the right factor of the rank-one erase is channel-selective
-    on the key axis, [README] update-rule paragraph), subtract that read from the
-    gated write w_t * v_t (delta rule: the current read is subtracted before
-    writing, [ABS]), write the difference along k_t, then read out with q_t.
+    The update as a fast-weight write ([ABS]): decay the state first (the
+    [README] gate list has the erase gate act on the state after decay), read
+    it through the erase key e_t = b_t * k_t (the erase gate scales the key-side
+    factor of the rank-one erase, [README] update-rule paragraph), take that
+    read away from the gated write w_t * v_t (the delta rule removes the
+    current read before writing, [ABS]), write the difference along k_t, then
+    read out with q_t.
 
     Expanding (I - k e^T) D S + k (w*v)^T gives exactly D S + k (w*v - (D S)^T e)^T,
     which is what is computed here.
