@@ -57,16 +57,20 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32);
 
 // Backward plan: the two-stage reverse pass (chunk-parallel records, then the
-// register-resident reverse chain) where the kernels cover the sizes, else the
-// single-kernel reverse pass.
+// register-resident reverse chain), where the kernels cover the sizes (two_stage;
+// otherwise the backward calls return GDN2_ERR_UNSUPPORTED).
 struct BwdPlan {
   bool two_stage;
   size_t part;     // one [B,H,NC,Dk,Dv] fp32 array, 256-byte aligned
   size_t records;  // records region (two-stage only): forward records for a
                    // state recompute, then the backward records
   size_t seg;      // the two-level reverse chain's segment maps (0: not used)
+  size_t gsc;      // 16-bit inputs: partial maxima of the upstream gradients (grad_scale), 0 for fp32
   size_t need;
 };
+
+// the upstream-gradient partial maxima of nst (sequence, head) pairs (16-bit inputs only)
+size_t gscale_bytes(int nst, bool f32) { return f32 ? 0 : al256((size_t)nst * gdn2::kGradScaleSplit * 4); }
 
 BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   BwdPlan p{};
@@ -82,14 +86,12 @@ BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   // states when the caller passes none, the records, and the reverse chain's
   // segment maps for few heads and long sequences
   p.records = (p.records + 255) & ~(size_t)255;
-  p.seg = p.two_stage ? gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk) : 0;
-  p.need = 2 * p.part + p.records + p.seg;
+  p.seg = al256(p.two_stage ? gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk) : 0);
+  p.gsc = gscale_bytes(B * H, f32);
+  p.need = 2 * p.part + p.records + p.seg + p.gsc;
   return p;
 }
 
-size_t bwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
-  return bwd_plan(B, T, H, Dk, Dv, chunk, f32).need;
-}
 
 // The training pair's records buffer: the backward records, then (256-byte
 // aligned) every chunk's entry state, fp32 for fp32 inputs and fp16 for 16-bit
@@ -105,7 +107,8 @@ size_t train_records(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
          (size_t)B * H * ((T + chunk - 1) / chunk) * Dk * Dv * (f32 ? 4 : 2);
 }
 
-size_t bwd_records_workspace(const BwdPlan& p) { return p.part + p.seg; }
+// the training pair's backward workspace: state gradients, segment maps, upstream-gradient maxima
+size_t bwd_records_workspace(const BwdPlan& p) { return p.part + p.seg + p.gsc; }
 
 // Two-stage forward workspace: records, then T (w*v) for every chunk, then
 // (256-byte aligned) the segment maps and entry states of the two-level chain
@@ -137,7 +140,7 @@ char* fwd_seg_ptr(char* ws, int B, int T, int H, int Dk, int Dv, int chunk, bool
 // forward records (state recompute) and the backward ones.
 struct VarlenPlan {
   int L;             // segment length of the two-level chain (0: plain chain)
-  size_t tables, part, records, seg_off, need;
+  size_t tables, part, records, seg_off, gsc_off, need;  // gsc_off: upstream-gradient maxima (backward)
 };
 
 VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, bool f32) {
@@ -155,13 +158,15 @@ VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, b
     // the backward from the training pair's records: state gradients, then the
     // reverse chain's segment maps
     p.part = al256((size_t)H * mc * Dk * Dv * 4);
-    p.need = p.tables + p.part + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
+    p.gsc_off = p.tables + p.part + al256(gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk));
+    p.need = p.gsc_off + gscale_bytes(N * H, f32);
   } else {
     p.part = al256((size_t)H * mc * Dk * Dv * 4);
     const size_t bwd_rec = (size_t)H * mc * gdn2::record_bytes(Dk, chunk, f32, 1);
     p.records = al256(bwd_rec > fwd_rec ? bwd_rec : fwd_rec);
-    // then the reverse chain's segment maps
-    p.need = p.tables + 2 * p.part + p.records + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
+    // then the reverse chain's segment maps, then the upstream-gradient maxima
+    p.gsc_off = p.tables + 2 * p.part + p.records + al256(gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk));
+    p.need = p.gsc_off + gscale_bytes(N * H, f32);
   }
   return p;
 }
@@ -209,7 +214,8 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
   if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK) return 0;
   if (op == GDN2_OP_BWD) {
     if (!chunk_ok(chunk) || T == 0) return 0;
-    return bwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+    const BwdPlan p = bwd_plan(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+    return p.two_stage ? p.need : 0;
   }
   if (op == GDN2_OP_FWD) {
     if (!chunk_ok(chunk) || T == 0) return 0;
@@ -344,7 +350,12 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   gdn2::BwdArgs a{q, k, v, log_alpha, b, w, dO, dS_final, states, dS_chunks, dq, dk, dv, dlog_alpha, db, dw,
                   dS0, B, T, H, Dk, Dv, chunk, f32};
   set_gate_flags(a, flags);
-  st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
+  if (!f32) {
+    float* part = reinterpret_cast<float*>(ws + 2 * plan.part + plan.records + plan.seg);
+    st = hip_status(gdn2::launch_grad_scale(a, part, s));
+    a.gscale = part;
+  }
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK)
     st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? rec + plan.records : nullptr, s));
   a.records = rec;
@@ -422,7 +433,12 @@ int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const 
                   reinterpret_cast<float*>(ws), dq, dk, dv, dlog_alpha, db, dw, dS0, B, T, H, Dk, Dv, chunk, f32};
   if (!f32) a.states16 = reinterpret_cast<const _Float16*>(states);
   set_gate_flags(a, flags);
-  st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? ws + plan.part : nullptr, s));
+  if (!f32) {
+    float* part = reinterpret_cast<float*>(ws + plan.part + plan.seg);
+    st = hip_status(gdn2::launch_grad_scale(a, part, s));
+    a.gscale = part;
+  }
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, plan.seg ? ws + plan.part : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
   return st;
@@ -561,7 +577,12 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
                   dS0, 1, T, H, Dk, Dv, chunk, f32};
   set_gate_flags(a, flags);
   a.vl = f.vl;
-  st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
+  if (!f32) {
+    float* part = reinterpret_cast<float*>(ws + p.gsc_off);
+    st = hip_status(gdn2::launch_grad_scale(a, part, s));
+    a.gscale = part;
+  }
+  if (st == GDN2_OK) st = hip_status(gdn2::launch_prep_bwd(f, rec, s));
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, p.L > 0 ? rec + p.records : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));
@@ -643,6 +664,11 @@ int gdn2_bwd_varlen_records(const void* q, const void* k, const void* v, const f
   if (!f32) a.states16 = reinterpret_cast<const _Float16*>(states);
   set_gate_flags(a, flags);
   st = hip_status(gdn2::launch_varlen_plan(cu_seqlens, N, T, chunk, p.L, ws, a.vl, s));
+  if (st == GDN2_OK && !f32) {
+    float* part = reinterpret_cast<float*>(ws + p.gsc_off);
+    st = hip_status(gdn2::launch_grad_scale(a, part, s));
+    a.gscale = part;
+  }
   if (st == GDN2_OK) st = hip_status(gdn2::launch_chain_bwd(a, rec, p.L > 0 ? ws + p.tables + p.part : nullptr, s));
   a.records = rec;
   if (st == GDN2_OK) st = hip_status(gdn2::launch_bwd_grad(a, s));

@@ -500,6 +500,8 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
   // the (batch row or packed sequence, head) walked here: its chunks, tokens and states
   const SeqLoc sl = seq_loc(a.vl, T, H, DK, Dv, C, bh);
   n_end = min(n_end, sl.nchunks);
+  // 16-bit inputs: dO and dS_final enter times a power of two (grad_scale), dS0 leaves without it
+  const float gsc = F32IN ? 1.f : grad_scale(a.gscale, sl.state);
   const int j0 = cg * kCols + wid * 16 * NCT;
   // segmented: waves past the columns only copy records; identity columns (map pass) have no dO;
   // plain: the helper waves (NHW, as in the forward chain) only copy records
@@ -542,9 +544,10 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
 #pragma unroll
         for (int i = 0; i < 4; ++i) accD[R][c][i] = (16 * R + 4 * lg + i == j0 - Dv + 16 * c + lr) ? 1.f : 0.f;
       } else if (Gent && active) {
+        const float gin = Gent == a.dS_final ? gsc : 1.f;  // a composed exit gradient is already scaled
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          accD[R][c][i] = Gent[gOff + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
+          accD[R][c][i] = gin * Gent[gOff + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr];
       }
     }
 
@@ -613,7 +616,7 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
         for (int j = 0; j < NDE; ++j) {
           const bool ok = has_do && (SEG || do_row(u, j) < Ln);  // (segmented: zeroed at the load)
           if constexpr (F32IN) dof[u][c][j] = ok ? rdc[u][c][j] : 0.f;
-          else dof[u][c][j] = static_cast<_Float16>(ok ? bf16_bits_to_f32(rdc[u][c][j]) : 0.f);
+          else dof[u][c][j] = static_cast<_Float16>(ok ? gsc * bf16_bits_to_f32(rdc[u][c][j]) : 0.f);
         }
     if (has_do && n > n_begin) load_do(n - 1, rdx);
     if (active) {
@@ -760,13 +763,14 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
   }
   if (!active) return;  // helper waves
   if (a.dS0) {
+    const float inv = 1.f / gsc;  // exact: a power of two
 #pragma unroll
     for (int R = 0; R < RK; ++R)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          a.dS0[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = accD[R][c][i];
+          a.dS0[stBase + (int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] = inv * accD[R][c][i];
   }
 }
 
@@ -798,8 +802,11 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
 template <int DK>
 // reverse (the backward's exit gradients): S_in(s-1) = M_s S_in(s) + N_s from
 // S_in(count-1) = start (dS_final), empty sequences copying start to empty_out (dS0).
+// gscale (reverse, 16-bit inputs): start is dS_final, taken times grad_scale() as the reverse chain
+// takes it; an empty sequence's dS0 is written without the scale.
 __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
-                                                              Varlen vl, int H, int Dv, bool reverse) {
+                                                              Varlen vl, int H, int Dv, bool reverse,
+                                                              const float* gscale) {
   constexpr int LDM = DK + 4, LDS_ = 32 + 4;
   constexpr int NM4 = DK * DK / 4;              // float4 of one M
   constexpr int MV = (NM4 + 255) / 256;         // per thread
@@ -821,9 +828,10 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     count = vl.seg_first[sq + 1] - vl.seg_first[sq];
   }
   const int tid = threadIdx.x, wid = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const float gsc = grad_scale(gscale, bh);
   for (int e = tid; e < DK * 32; e += 256) {
     const int d = e >> 5, c = e & 31;
-    sS[d * LDS_ + c] = S0 ? S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
+    sS[d * LDS_ + c] = S0 ? gsc * S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
   }
   float4 mr[MV];
   // step i reads the map of segment src(i) and writes the entry of the next one in walking order
@@ -838,7 +846,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     __syncthreads();
     for (int e = tid; S_final && e < DK * 32; e += 256) {
       const int d = e >> 5, c = e & 31;
-      S_final[((int64_t)bh * DK + d) * Dv + j0 + c] = sS[d * LDS_ + c];
+      S_final[((int64_t)bh * DK + d) * Dv + j0 + c] = sS[d * LDS_ + c] / gsc;
     }
     return;
   }
@@ -952,7 +960,7 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments
     hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, a.S_final, sg,
-                       a.vl, a.H, a.Dv, false);
+                       a.vl, a.H, a.Dv, false, static_cast<const float*>(nullptr));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true entry state
@@ -1053,7 +1061,7 @@ static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* 
     if (e != hipSuccess) return e;
     // (2) exit gradients of the earlier segments, composed backwards from dS_final
     hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.dS_final, a.dS0,
-                       sg, a.vl, a.H, a.Dv, true);
+                       sg, a.vl, a.H, a.Dv, true, a.gscale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true exit gradient

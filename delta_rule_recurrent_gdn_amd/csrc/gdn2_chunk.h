@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "gdn2_common.h"
+#include "gdn2_wide.h"
 
 namespace gdn2 {
 
@@ -189,7 +190,10 @@ struct KSide {
   // Gate preprocessing: g (sG, fp32 [C][DK]) and the per-channel constants in
   // sChan = {g_m, g_C, exp(g_m), exp(g_C - g_m)} (each [DK]). The caller must
   // have synchronised since the last readers of sG/sChan/sTot. Ends synchronised.
-  __device__ __forceinline__ void gates(float* sTot, float* sG, float* sChan) {
+  // Returns (in every thread) whether the chunk is a wide-decay one: on some
+  // channel |g - g_m| exceeds kWideSpan (gdn2_wide.h).
+  __device__ __forceinline__ bool gates(float* sTot, float* sG, float* sChan) {
+    bool far = false;
     if (la_on) {
       float run[LAW];
 #pragma unroll
@@ -198,7 +202,7 @@ struct KSide {
       for (int i = 0; i < LA_RPS; ++i)
 #pragma unroll
         for (int j = 0; j < LAW; ++j) {
-          run[j] += la[i][j];
+          run[j] += la_floor(la[i][j]);  // per-token log-decay floor (gdn2_wide.h)
           la[i][j] = run[j];
         }
       st_lanes(sTot + la_sg * DK + la_c, run);
@@ -223,7 +227,10 @@ struct KSide {
       for (int i = 0; i < LA_RPS; ++i) {
         float g[LAW];
 #pragma unroll
-        for (int j = 0; j < LAW; ++j) g[j] = la[i][j] + off[j];
+        for (int j = 0; j < LAW; ++j) {
+          g[j] = la[i][j] + off[j];
+          far = far || fabsf(g[j] - gmid[j]) > kWideSpan;
+        }
         st_lanes(sG + (la_sg * LA_RPS + i) * DK + la_c, g);
       }
       if (la_sg == 0) {
@@ -239,6 +246,51 @@ struct KSide {
         st_lanes(sChan + 3 * DK + la_c, e2);
       }
     }
+    return __builtin_amdgcn_readfirstlane(__syncthreads_or(far)) != 0;  // uniform: a scalar branch
+  }
+
+  // Wide-decay chunks (gdn2_wide.h): from log_alpha rows fetched again by
+  // load_la(), the cumulative log-decay from the start of each row's 16-token
+  // block into sG (fp32 [C][DK]), the block totals into sBs [NB][DK] and the
+  // pair scales into sPS. Same synchronisation contract as gates().
+  __device__ __forceinline__ void gates_block(float* sTot, float* sG, float* sBs, float* sPS) {
+    constexpr int SPB = 16 / LA_RPS;  // cumsum segments per 16-token block
+    static_assert(LA_RPS <= 16 && 16 % LA_RPS == 0, "segments tile the blocks");
+    if (la_on) {
+      float run[LAW];
+#pragma unroll
+      for (int j = 0; j < LAW; ++j) run[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < LA_RPS; ++i)
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) {
+          run[j] += la_floor(la[i][j]);
+          la[i][j] = run[j];
+        }
+      st_lanes(sTot + la_sg * DK + la_c, run);
+    }
+    __syncthreads();
+    if (la_on) {
+      float off[LAW];
+#pragma unroll
+      for (int j = 0; j < LAW; ++j) off[j] = 0.f;
+      for (int sgi = (la_sg / SPB) * SPB; sgi < la_sg; ++sgi) {
+        float tt[LAW];
+        ld_lanes(tt, sTot + sgi * DK + la_c);
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) off[j] += tt[j];
+      }
+#pragma unroll
+      for (int i = 0; i < LA_RPS; ++i) {
+        float g[LAW];
+#pragma unroll
+        for (int j = 0; j < LAW; ++j) g[j] = la[i][j] + off[j];
+        st_lanes(sG + (la_sg * LA_RPS + i) * DK + la_c, g);
+        if (la_sg % SPB == SPB - 1 && i == LA_RPS - 1) st_lanes(sBs + (la_sg / SPB) * DK + la_c, g);
+      }
+    }
+    __syncthreads();
+    wide_pair_scales<NB, DK, NT>(sBs, sPS);
     __syncthreads();
   }
 

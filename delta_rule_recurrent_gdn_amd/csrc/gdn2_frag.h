@@ -66,6 +66,14 @@ struct Record {
   static_assert(DK * 4 <= 1024, "exp(g_C) must fit one unit");
 };
 
+// Byte offset of the wide-decay flag of a record (gdn2_wide.h): the last word of the exp(g_C)
+// unit, which uses its first DK floats only. The fast record pass writes it for every chunk it
+// covers (1: the chunk's record comes from the wide pass instead).
+template <class R>
+__host__ __device__ constexpr int wide_flag_offset() {
+  return R::uG * 1024 + 1020;
+}
+
 // Write the units of a row-major matrix X [M][K] (operand type, leading
 // dimension ld, in LDS) to dst (global): unit (R, u) at dst + (R * units(K) + u) KB.
 // Units are dealt round-robin to the nw waves starting at wave w0.

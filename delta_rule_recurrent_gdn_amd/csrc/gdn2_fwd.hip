@@ -71,11 +71,17 @@ struct FwdCfg {
   static constexpr int oST = oWVT + BV * LDC * OPB;                // OpT [BV][LDK]  S^T
   static constexpr int oCH = oST + BV * LDK * OPB;                 // float [4][DK]  per-channel gate constants
   static constexpr int oTOT = oCH + KS::kChanBytes;                // float cumsum segment totals
-  static constexpr int oX = oTOT + KS::kTotBytes;                  // start of the phase-shared region
+  static constexpr int oBS = oTOT + KS::kTotBytes;                 // float [NB][DK] block totals (wide chunks)
+  static constexpr int oPS = oBS + NB * DK * 4;                    // float [npair][DK] pair scales (wide chunks)
+  static constexpr int oX = oPS + wide_npair(NB) * DK * 4;         // start of the phase-shared region
   // phase F (gate preprocessing + Gram)
   static constexpr int oG = oX;
   static constexpr int oSL = oG + KS::kGBytes;
-  static constexpr int endF = oSL + KS::kSlicesBytes;
+  // wide-decay chunks use the slice region for b k, q and k of one channel slice (fp32 [C][LDW]
+  // each), then for the diagonal-block tables of A and P ([C][16] each)
+  static constexpr int LDW = KS::SW + 4;
+  static constexpr int kWideSl = 3 * C * LDW * 4 > 2 * C * 16 * 4 ? 3 * C * LDW * 4 : 2 * C * 16 * 4;
+  static constexpr int endF = oSL + (KS::kSlicesBytes > kWideSl ? KS::kSlicesBytes : kWideSl);
   // phase W (after the Gram products)
   static constexpr int oAf = oX;                                   // float [C][LDCF]  A, then T
   static constexpr int oPm = oAf + KS::kAfBytes;                   // OpT [C][LDC]   P
@@ -83,7 +89,12 @@ struct FwdCfg {
   static constexpr int oUT = oWm + C * LDK * OPB;                  // OpT [BV][LDC]  U^T
   static constexpr int oXs = oUT + BV * LDC * OPB;                 // float inversion scratch
   static constexpr int endW = oXs + KS::kXsBytes;
-  static constexpr int kLdsBytes = endF > endW ? endF : endW;
+  // the fp32 state handed from the fast to the slow chunk loop: below sST if it fits there, else
+  // from the gate constants on (extending the allocation where needed); either way over buffers
+  // written only after the slow loop's first barrier
+  static constexpr int oSt = DK * BV * 4 <= oST ? 0 : oCH;
+  static constexpr int endSt = oSt + DK * BV * 4;
+  static constexpr int kLdsBytes = endF > endW ? (endF > endSt ? endF : endSt) : (endW > endSt ? endW : endSt);
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
 
   static constexpr int NUT = NB * (BV / 16);                       // U / O tiles
@@ -97,17 +108,188 @@ struct FwdCfg {
   static constexpr int VW_RPT = (C + VW_RPP - 1) / VW_RPP;
 };
 
+// A wide-decay chunk (gdn2_wide.h): its Gram matrices and decayed key-side
+// operands with block-referenced decay factors, in place of KSide::factors_gram
+// and gram_store -- A -> sAf (strict lower), P -> sPm (row-major, lower incl.),
+// q exp(g) -> sQs, (b k exp(g))^T -> sKhT, (k exp(g_C - g))^T -> sKbT. The
+// chunk's inputs are read again from global memory and every intermediate
+// lives in LDS.
+template <int DK, int C, int BV, bool F32IN, bool FL>
+__device__ __forceinline__ void fwd_wide_chunk(const FwdArgs& a, int64_t baseK, int t0, int Lr, char* smem) {
+  using Cfg = FwdCfg<DK, C, BV, F32IN>;
+  using KS = typename Cfg::KS;
+  using OpT = typename Cfg::OpT;
+  constexpr int NT = kFwdThreads, NW = Cfg::kWaves, NB = Cfg::NB;
+  constexpr int SW = KS::SW, NSL = KS::NSL, NGT = KS::NGT, GPW = KS::GPW;
+  constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDW = Cfg::LDW;
+  OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
+  OpT* sQs = reinterpret_cast<OpT*>(smem + Cfg::oQs);
+  OpT* sKbT = reinterpret_cast<OpT*>(smem + Cfg::oKbT);
+  float* sG = reinterpret_cast<float*>(smem + Cfg::oG);
+  float* sW = reinterpret_cast<float*>(smem + Cfg::oSL);
+  float* sBs = reinterpret_cast<float*>(smem + Cfg::oBS);
+  float* sPS = reinterpret_cast<float*>(smem + Cfg::oPS);
+  float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
+  OpT* sPm = reinterpret_cast<OpT*>(smem + Cfg::oPm);
+  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
+  const int lr = l & 15, lg = l >> 4;
+  const int H = a.H;
+  const int64_t rowK = (int64_t)H * DK, baseS = baseK / DK;
+  const bool raw = FL && a.raw_gates, sla = FL && a.scalar_decay, sbg = FL && a.scalar_b;
+
+  // log-decay (floored), then the cumulative sum inside each 16-token block and the block totals
+#pragma unroll 1
+  for (int e = tid; e < C * DK; e += NT) {
+    const int r = e / DK, c = e - r * DK;
+    float x = 0.f;
+    if (r < Lr) {
+      x = a.log_alpha[sla ? baseS + (int64_t)(t0 + r) * H : baseK + (int64_t)(t0 + r) * rowK + c];
+      if (raw) x = neg_softplus_f(x);
+      x = la_floor(x);
+    }
+    sG[e] = x;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int e = tid; e < NB * DK; e += NT) {
+    const int R = e / DK, c = e - R * DK;
+    float run = 0.f;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      run += sG[(16 * R + i) * DK + c];
+      sG[(16 * R + i) * DK + c] = run;
+    }
+    sBs[e] = run;
+  }
+  __syncthreads();
+  wide_pair_scales<NB, DK, NT>(sBs, sPS);
+  __syncthreads();
+
+  // per channel slice: b k, q and k (fp32) and the decayed key-side operands; the off-diagonal
+  // Gram tiles on fp32 matrix cores with the block-referenced decay factors applied as the
+  // operands are read; the diagonal blocks pair by pair, thread (row r, columns j and j + 8)
+  float* sBK = sW;
+  float* sQ = sW + C * LDW;
+  float* sK = sW + 2 * C * LDW;
+  f32x4 accG[GPW];
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) accG[i] = zero4();
+  const int pr = tid / 8, pj = tid % 8;  // pairwise: row pr (< C), block columns pj and pj + 8
+  float da0 = 0.f, da1 = 0.f, dp0 = 0.f, dp1 = 0.f;
+#pragma unroll 1
+  for (int sl = 0; sl < NSL; ++sl) {
+#pragma unroll 1
+    for (int e = tid; e < C * SW; e += NT) {
+      const int r = e / SW, cs = e - r * SW, c = sl * SW + cs;
+      float qv = 0.f, kv = 0.f, bv = 0.f;
+      if (r < Lr) {
+        const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c;
+        qv = load1<F32IN>(a.q, idx);
+        kv = load1<F32IN>(a.k, idx);
+        bv = load1<F32IN>(a.b, sbg ? baseS + (int64_t)(t0 + r) * H : idx);
+        if (raw) bv = sigmoid_f(bv);
+      }
+      const int R = r >> 4;
+      const float gb = sG[r * DK + c], bs = sBs[R * DK + c];
+      const float eg = __expf(wide_before<NB, DK>(sBs, R, c) + gb);        // exp(g)
+      const float ec = __expf((bs - gb) + wide_after<NB, DK>(sBs, R, c));  // exp(g_C - g)
+      sBK[r * LDW + cs] = bv * kv;
+      sQ[r * LDW + cs] = qv;
+      sK[r * LDW + cs] = kv;
+      sQs[r * LDK + c] = static_cast<OpT>(qv * eg);
+      sKhT[c * LDC + r] = static_cast<OpT>(bv * kv * eg);
+      sKbT[c * LDC + r] = static_cast<OpT>(kv * ec);
+    }
+    __syncthreads();
+    // off-diagonal tiles: acc += sum_c (X_rc exp(gb_rc)) s_RI,c (k_ic exp(Bs_I,c - gb_ic))
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int t = wid + NW * i;
+      if (t < NGT) {
+        const bool isP = t >= NGT / 2;
+        int R, I;
+        tri_index(isP ? t - NGT / 2 : t, R, I);
+        if (I < R) {
+          const float* X = isP ? sQ : sBK;
+          const int rr = 16 * R + lr, ii = 16 * I + lr;
+#pragma unroll 1
+          for (int k0 = 0; k0 < SW; k0 += 4) {
+            const int c = sl * SW + k0 + lg;
+            float x = X[rr * LDW + k0 + lg] * __expf(sG[rr * DK + c]);
+            if (I + 2 <= R) x *= sPS[wide_pair(R, I) * DK + c];
+            const float y = sK[ii * LDW + k0 + lg] * __expf(sBs[I * DK + c] - sG[ii * DK + c]);
+            accG[i] = mfma16x16x4(x, y, accG[i]);
+          }
+        }
+      }
+    }
+    // diagonal blocks: A_ri and P_ri for i = 16 (r / 16) + pj and + 8, over the slice's channels
+    if (pr < C) {
+      const int rb = pr & ~15, rl = pr & 15;
+#pragma unroll 1
+      for (int cs = 0; cs < SW; ++cs) {
+        const int c = sl * SW + cs;
+        const float gr = sG[pr * DK + c], bkr = sBK[pr * LDW + cs], qr = sQ[pr * LDW + cs];
+        if (pj <= rl) {
+          const int i = rb + pj;
+          const float t = sK[i * LDW + cs] * __expf(gr - sG[i * DK + c]);
+          da0 += pj < rl ? bkr * t : 0.f;
+          dp0 += qr * t;
+        }
+        if (pj + 8 <= rl) {
+          const int i = rb + pj + 8;
+          const float t = sK[i * LDW + cs] * __expf(gr - sG[i * DK + c]);
+          da1 += pj + 8 < rl ? bkr * t : 0.f;
+          dp1 += qr * t;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // the diagonal blocks into the owners' accumulators
+  float* tA = sW;
+  float* tP = sW + C * 16;
+  if (pr < C) {
+    tA[pr * 16 + pj] = da0;
+    tA[pr * 16 + pj + 8] = da1;
+    tP[pr * 16 + pj] = dp0;
+    tP[pr * 16 + pj + 8] = dp1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int t = wid + NW * i;
+    if (t < NGT) {
+      const bool isP = t >= NGT / 2;
+      int R, I;
+      tri_index(isP ? t - NGT / 2 : t, R, I);
+      if (I == R) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accG[i][e] += (isP ? tP : tA)[(16 * R + 4 * lg + e) * 16 + lr];
+      }
+    }
+  }
+  __syncthreads();
+  KS().template gram_store<false>(accG, sAf, sPm);
+}
+
 // FL: some gate option (pre-activation or per-head scalar gates) is on; without
 // it every gate-option branch of the loads folds away.
-template <int DK, int C, int BV, bool F32IN, bool FL>
-__global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
+//
+// The chunk loop of one workgroup from chunk n0. SLOW = false: from chunk 0 and
+// S0, with no code for wide-decay chunks: at the first one it leaves the fp32
+// state in LDS (sSt, over per-chunk buffers) and returns the chunk's index
+// (NC when the sequence is done). SLOW = true: from chunk n0 and the state in
+// sSt, every chunk on, the wide ones through fwd_wide_chunk -- reached only
+// through the called function below, so the fast loop keeps its registers.
+template <int DK, int C, int BV, bool F32IN, bool FL, bool SLOW>
+__device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) {
   using Cfg = FwdCfg<DK, C, BV, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   constexpr int NW = Cfg::kWaves, NB = Cfg::NB;
   constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF;
-
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
+  float* sSt = reinterpret_cast<float*>(smem + Cfg::oSt);  // [DK][BV] fp32 state between the two loops
   OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
   OpT* sQs = reinterpret_cast<OpT*>(smem + Cfg::oQs);
   OpT* sKbT = reinterpret_cast<OpT*>(smem + Cfg::oKbT);
@@ -131,7 +313,7 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
   const int nbh = a.B * a.H;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int bh = (slot / nv) * 8 + xcd, vt = slot % nv;
-  if (bh >= nbh) return;
+  if (bh >= nbh) return 0;
   const int bi = bh / a.H, h = bh - bi * a.H;
   const int j0 = vt * BV;
   const int Dv = a.Dv, T = a.T, H = a.H;
@@ -175,7 +357,10 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
     accS[i] = zero4();
     if (t < Cfg::NST) {
       const int cb = t / (BV / 16), jb = t % (BV / 16);
-      if (a.S0) {
+      if (SLOW) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[i][e] = sSt[(16 * cb + 4 * lg + e) * BV + 16 * jb + lr];
+      } else if (a.S0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           accS[i][e] = a.S0[stBase + (int64_t)(16 * cb + 4 * lg + e) * Dv + 16 * jb + lr];
@@ -183,9 +368,10 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
       store_tile_t(sST + 16 * jb * LDK + 16 * cb, LDK, accS[i]);
     }
   }
-  load_chunk(0);
+  load_chunk(n0);
 
-  for (int n = 0; n < NC; ++n) {
+  int nstop = NC;
+  for (int n = n0; n < NC; ++n) {
     const int t0 = n * C;
     const int Lr = min(C, T - t0);
 
@@ -219,22 +405,31 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
         for (int e = 0; e < 8; ++e) sWVT[(8 * vw_j8 + e) * LDC + r] = static_cast<OpT>(ww[e] * vv[e]);
       }
     }
-    ks.gates(sTot, sG, sCh);
-
-    // ---- (2)+(3a) factors and the Gram products A, P ----
-    f32x4 accG[KS::GPW];
-    ks.factors_gram(sG, sCh, sSL, accG,
-                    [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
-                        const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
-                      (void)e1;
-                      st4(sQs + r * LDK + c0, qv[0] * eg[0], qv[1] * eg[1], qv[2] * eg[2], qv[3] * eg[3]);
+    // gates() also reports a wide-decay chunk: on some channel the cumulative decay from the chunk
+    // middle leaves the range that the middle-referenced factors can carry (gdn2_wide.h)
+    const bool wide = ks.gates(sTot, sG, sCh);
+    if (!SLOW && wide) {  // the rest of the sequence is the slow loop's
+      nstop = n;
+      break;
+    }
+    if (SLOW && wide) {
+      fwd_wide_chunk<DK, C, BV, F32IN, FL>(a, baseK, t0, Lr, smem);
+    } else {
+      // ---- (2)+(3a) factors and the Gram products A, P ----
+      f32x4 accG[KS::GPW];
+      ks.factors_gram(sG, sCh, sSL, accG,
+                      [&](int r, int c0, const float (&qv)[4], const float (&kv)[4], const float (&bv)[4],
+                          const float (&e1)[4], const float (&eg)[4], const float (&ec)[4]) {
+                        (void)e1;
+                        st4(sQs + r * LDK + c0, qv[0] * eg[0], qv[1] * eg[1], qv[2] * eg[2], qv[3] * eg[3]);
 #pragma unroll
-                      for (int i = 0; i < 4; ++i) {
-                        sKhT[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * eg[i]);
-                        sKbT[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * ec[i]);
-                      }
-                    });
-    ks.template gram_store<false>(accG, sAf, sPm);
+                        for (int i = 0; i < 4; ++i) {
+                          sKhT[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * eg[i]);
+                          sKbT[(c0 + i) * LDC + r] = static_cast<OpT>(kv[i] * ec[i]);
+                        }
+                      });
+      ks.template gram_store<false>(accG, sAf, sPm);
+    }
 
     // ---- (3b) T = (I + A)^-1 ----
     ks.invert(sAf, sXs);
@@ -312,6 +507,19 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
     }
   }
 
+  if (!SLOW && nstop < NC) {  // hand the fp32 state over to the slow loop
+#pragma unroll
+    for (int i = 0; i < Cfg::SPW; ++i) {
+      const int t = wid + NW * i;
+      if (t < Cfg::NST) {
+        const int cb = t / (BV / 16), jb = t % (BV / 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sSt[(16 * cb + 4 * lg + e) * BV + 16 * jb + lr] = accS[i][e];
+      }
+    }
+    __syncthreads();
+    return nstop;
+  }
   if (a.S_final) {
 #pragma unroll
     for (int i = 0; i < Cfg::SPW; ++i) {
@@ -324,6 +532,22 @@ __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
       }
     }
   }
+  return NC;
+}
+
+// The slow loop as a called function (its registers do not add to the fast loop's). The arguments
+// are taken by value: a reference would make the kernel keep its own copy in private memory.
+template <int DK, int C, int BV, bool F32IN, bool FL>
+__device__ __attribute__((noinline)) void fwd_chunks_slow(FwdArgs a, char* smem, int n0) {
+  fwd_chunks<DK, C, BV, F32IN, FL, true>(a, smem, n0);
+}
+
+template <int DK, int C, int BV, bool F32IN, bool FL>
+__global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
+  using Cfg = FwdCfg<DK, C, BV, F32IN>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
+  const int n = fwd_chunks<DK, C, BV, F32IN, FL, false>(a, smem, 0);
+  if (n < (a.T + C - 1) / C) fwd_chunks_slow<DK, C, BV, F32IN, FL>(a, smem, n);
 }
 
 // ---------------------------------------------------------------------------

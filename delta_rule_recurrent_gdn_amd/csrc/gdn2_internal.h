@@ -47,6 +47,7 @@ struct Varlen {
 // (chunk fastest). Varlen: item = h * max_chunks + g (g the global chunk).
 struct ChunkLoc {
   int64_t item;   // index into the chunk-indexed arrays
+  int64_t state;  // (batch row or sequence) * H + head: index of its states [., H, Dk, Dv]
   int64_t baseK;  // element offset of token 0 of the chunk's (batch row, head) in [., T, H, Dk]
   int64_t baseV;  // same in [., T, H, Dv]
   int t0;         // first token of the chunk (added to base* as (t0 + r) * H * D)
@@ -59,6 +60,7 @@ __device__ __forceinline__ ChunkLoc chunk_loc(const Varlen& vl, int T, int H, in
   L.item = item;
   if (vl.cu == nullptr) {
     const int bh = item / NC, n = item - bh * NC, bi = bh / H, h = bh - bi * H;
+    L.state = bh;
     L.baseK = ((int64_t)bi * T * H + h) * Dk;
     L.baseV = ((int64_t)bi * T * H + h) * Dv;
     L.t0 = n * C;
@@ -66,6 +68,7 @@ __device__ __forceinline__ ChunkLoc chunk_loc(const Varlen& vl, int T, int H, in
   } else {
     const int h = item / vl.max_chunks, g = item - h * vl.max_chunks;
     const int sq = vl.chunk_seq[g];
+    L.state = (int64_t)(sq < 0 ? 0 : sq) * H + h;
     L.baseK = (int64_t)h * Dk;
     L.baseV = (int64_t)h * Dv;
     if (sq < 0) {
@@ -184,7 +187,27 @@ struct BwdArgs {
   // gates of one value per (token, head), [., T, H]; their gradients are then [., T, H] too
   // (summed over the channels the value is broadcast to)
   bool scalar_b = false, scalar_w = false, scalar_decay = false;
+  // 16-bit inputs: partial maxima of |dO| and |dS_final| per (sequence, head), kGradScaleSplit each
+  // (gdn2_grad_scale_kernel); the backward kernels scale dO and dS_final by grad_scale() of them
+  const float* gscale = nullptr;
 };
+
+// Upstream-gradient scaling of the 16-bit backward. The backward is linear in (dO, dS_final) jointly,
+// and their matrix-core operands are fp16 (range 6.1e-5 .. 65504 for normal numbers, while bf16 inputs
+// span fp32's range): every (sequence, head) runs on dO and dS_final times a power of two that brings
+// their largest magnitude into [1, 2), and every gradient is multiplied back on its store (exact).
+constexpr int kGradScaleSplit = 8;  // partial maxima per (sequence, head)
+__device__ __forceinline__ float grad_scale(const float* part, int64_t st) {
+  if (part == nullptr) return 1.f;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGradScaleSplit; ++i) m = fmaxf(m, part[st * kGradScaleSplit + i]);
+  if (!(m > 0.f) || !(m <= 3.4e38f)) return 1.f;  // all zero, or not finite: unscaled
+  int e = ilogbf(m);
+  e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  return ldexpf(1.f, -e);
+}
+hipError_t launch_grad_scale(const BwdArgs& a, float* part, hipStream_t s);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -35,6 +35,7 @@
 #include "gdn2_chunk.h"
 #include "gdn2_frag.h"
 #include "gdn2_internal.h"
+#include "gdn2_wide.h"
 
 namespace gdn2 {
 
@@ -65,15 +66,23 @@ struct PrepCfg {
   static constexpr int oSL = oR;                                   // Gram factor slices (factor phase)
   static constexpr int oAf = oR;                                   // float [C][LDCF] A, then T (after the Gram)
   static constexpr int oXs = oAf + KS::kAfBytes;
-  static constexpr int endR = (KS::kSlicesBytes > KS::kAfBytes + KS::kXsBytes ? KS::kSlicesBytes
-                                                                              : KS::kAfBytes + KS::kXsBytes);
+  // wide-decay chunks: per slice, three fp32 factors [C][LDW], then k and the block-relative
+  // cumulative decay [C][LDW] with the diagonal-block tables [C][16] of A and P
+  static constexpr int LDW = SW + 4;
+  static constexpr int kWideFac = 3 * C * LDW * 4;
+  static constexpr int kWideDiag = 2 * C * LDW * 4 + 2 * C * 16 * 4;
+  static constexpr int kSlR = KS::kSlicesBytes > kWideFac ? (KS::kSlicesBytes > kWideDiag ? KS::kSlicesBytes : kWideDiag)
+                                                          : (kWideFac > kWideDiag ? kWideFac : kWideDiag);
+  static constexpr int endR = (kSlR > KS::kAfBytes + KS::kXsBytes ? kSlR : KS::kAfBytes + KS::kXsBytes);
   static constexpr int oT1 = oR + ((endR + 15) & ~15);            // OpT [DK][LDC]: Kb^T, later Kh^T
   static constexpr int oWVT = oT1 + DK * LDC * OPB;                // OpT [DVM][LDC] (w v)^T
   // (w v)^T row j holds its 8-token blocks permuted, block b at b ^ ((j / 8) & kWvSwz): the staging
   // writes of one wave cover 16 rows 8 apart, which would otherwise all start in the same LDS bank
   // (16-way conflicts; 2-way with the permutation). 16-bit operands only.
   static constexpr int kWvSwz = F32IN ? 0 : C / 8 - 1;
-  static constexpr int kLdsBytes = oWVT + DVM * LDC * OPB;
+  static constexpr int oBS = oWVT + DVM * LDC * OPB;               // float [NB][DK] block totals (wide path)
+  static constexpr int oPS = oBS + NB * DK * 4;                    // float [npair][DK] pair scales (wide path)
+  static constexpr int kLdsBytes = oPS + wide_npair(NB) * DK * 4;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
   static constexpr int VW_PT = (C * DVM / 8 + NT - 1) / NT;
 };
@@ -99,9 +108,12 @@ __device__ __forceinline__ int gram_tile(int t, int& R, int& I) {
   return kind;
 }
 
-template <int DK, int C, bool F32IN, int DIR>
-__global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base,
-                                                            char* brec_base) {
+// One chunk (item) of the chunk-parallel record pass. WIDE = false: the fast path, which only
+// flags a wide-decay chunk (and leaves its record to the WIDE = true pass); WIDE = true: the
+// block-referenced factors of gdn2_wide.h, exact for any decay. smem: Cfg::kLdsBytes of LDS.
+template <int DK, int C, bool F32IN, int DIR, bool WIDE>
+__device__ __forceinline__ void prep_chunk(const FwdArgs& a, char* rec_base, float* ut_base, char* brec_base,
+                                           int item, char* smem) {
   using Cfg = PrepCfg<DK, C, F32IN, DIR>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
@@ -112,7 +124,6 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
   constexpr int LDC = Cfg::LDC, LDCF = Cfg::LDCF, LDSW = Cfg::LDSW;
   constexpr int NGT = Cfg::NGT, NGT2 = Cfg::NGT2, GPW = Cfg::GPW;
 
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
   float* sCh = reinterpret_cast<float*>(smem + Cfg::oCH);
   float* sTot = reinterpret_cast<float*>(smem + Cfg::oTOT);
   char* sSL = smem + Cfg::oSL;
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int NC = (T + C - 1) / C;
   // (batch*head, chunk), chunk fastest; packed sequences: (head, global chunk)
-  const ChunkLoc cl = chunk_loc(a.vl, T, H, DK, Dv, C, NC, blockIdx.x);
+  const ChunkLoc cl = chunk_loc(a.vl, T, H, DK, Dv, C, NC, item);
   if (cl.Lr <= 0) return;  // past the last chunk of a packed batch
   const int t0 = cl.t0, Lr = cl.Lr;
   const int64_t rowK = (int64_t)H * DK, rowV = (int64_t)H * Dv;
@@ -193,6 +204,11 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
 #pragma unroll
       for (int j = 0; j < 4; ++j) g[sl][j] = neg_softplus_f(g[sl][j]);
   }
+  // per-token log-decay floor (padding rows hold 0)
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[sl][j] = la_floor(g[sl][j]);
 
   // ---- gates: inclusive cumsum over the rows of the chunk ----
   // within the wave (rows r = lane / TPR of this wave), then across waves
@@ -225,11 +241,83 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
     if (r == C - 1) *reinterpret_cast<float4*>(sCh + DK + c0) = make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
   }
   __syncthreads();
+  // a wide-decay chunk: on some channel the cumulative decay from the chunk middle leaves the range
+  // that the middle-referenced factors can carry (gdn2_wide.h)
+  bool far = false;
+  if (!WIDE && live) {
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) far = far || fabsf(g[sl][j] - sCh[sl * SW + 4 * c4 + j]) > kWideSpan;
+  }
   for (int c = tid; c < DK; c += NT) {
     sCh[2 * DK + c] = __expf(sCh[c]);
     sCh[3 * DK + c] = __expf(sCh[DK + c] - sCh[c]);
   }
-  __syncthreads();
+  float* sBs = reinterpret_cast<float*>(smem + Cfg::oBS);
+  float* sPS = reinterpret_cast<float*>(smem + Cfg::oPS);
+  if constexpr (!WIDE) {
+    const bool wide = __builtin_amdgcn_readfirstlane(__syncthreads_or(far)) != 0;  // uniform: a scalar branch
+    if (tid == 0) {
+      *reinterpret_cast<int*>(rec + wide_flag_offset<Rec>()) = wide ? 1 : 0;
+      if constexpr (DIR == 2) *reinterpret_cast<int*>(recB + wide_flag_offset<RecB>()) = wide ? 1 : 0;
+    }
+    if (wide) return;  // the whole workgroup: the wide pass writes this chunk's record
+  } else {
+    __syncthreads();
+    // g <- cumulative log-decay from the start of the row's 16-token block, from the log-decays
+    // again (no difference of two long sums is ever formed); block totals; pair scales
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int c0 = sl * SW + 4 * c4;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (live && r < Lr) {
+        const int64_t idx = baseK + (int64_t)(t0 + r) * rowK + c0;
+        x = load_la4(a.log_alpha, idx, baseK / DK + (int64_t)(t0 + r) * H, a.scalar_decay);
+      }
+      g[sl][0] = x.x; g[sl][1] = x.y; g[sl][2] = x.z; g[sl][3] = x.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (a.raw_gates && live && r < Lr) g[sl][j] = neg_softplus_f(g[sl][j]);
+        g[sl][j] = la_floor(g[sl][j]);
+      }
+    }
+#pragma unroll
+    for (int off = TPR; off < kWave; off *= 2) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y = __shfl_up(g[sl][j], off, kWave);
+          if (l >= off) g[sl][j] += y;
+        }
+    }
+    if constexpr (Cfg::RPW < 16) {  // a 16-token block spans two waves: the odd one adds the even one's total
+      if (l >= kWave - TPR) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+          *reinterpret_cast<float4*>(sTot + wid * DK + sl * SW + 4 * c4) =
+              make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+      }
+      __syncthreads();
+      if (wid & 1) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          const float4 t4 = *reinterpret_cast<const float4*>(sTot + (wid - 1) * DK + sl * SW + 4 * c4);
+          g[sl][0] += t4.x; g[sl][1] += t4.y; g[sl][2] += t4.z; g[sl][3] += t4.w;
+        }
+      }
+    }
+    if (live && (r & 15) == 15) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+        *reinterpret_cast<float4*>(sBs + (r >> 4) * DK + sl * SW + 4 * c4) =
+            make_float4(g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+    }
+    __syncthreads();
+    wide_pair_scales<NB, DK, NT>(sBs, sPS);
+    __syncthreads();
+  }
 
   // ---- factors and the Gram products, one channel slice at a time ----
   // A tiles (R, I) from Kh' Kt'^T; the causal term as P^T tiles (I, R) from
@@ -237,9 +325,11 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
   f32x4 accG[GPW];
 #pragma unroll
   for (int i = 0; i < GPW; ++i) accG[i] = zero4();
+  constexpr int LDW = Cfg::LDW;
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
     const int cl = 4 * c4, c0 = sl * SW + cl;
+    float wbk[4] = {0.f, 0.f, 0.f, 0.f}, wq[4] = {0.f, 0.f, 0.f, 0.f};  // WIDE: b k and q of the row
     if (live) {
       float qv[4], kv[4], bv[4];
       cvt(rq[sl], qv);
@@ -249,21 +339,42 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
 #pragma unroll
         for (int i = 0; i < 4; ++i) bv[i] = sigmoid_f(bv[i]);  // k is zero on padding rows
       }
-      const float4 gm4 = *reinterpret_cast<const float4*>(sCh + c0);
-      const float4 eg4 = *reinterpret_cast<const float4*>(sCh + 2 * DK + c0);
-      const float4 ec4 = *reinterpret_cast<const float4*>(sCh + 3 * DK + c0);
-      const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-      const float egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w}, egcm[4] = {ec4.x, ec4.y, ec4.z, ec4.w};
-      float khm[4], qhm[4], ktm[4], qs[4], kb[4];
+      float khm[4], qhm[4], ktm[4], qs[4], kb[4], kh[4];
+      if constexpr (!WIDE) {
+        const float4 gm4 = *reinterpret_cast<const float4*>(sCh + c0);
+        const float4 eg4 = *reinterpret_cast<const float4*>(sCh + 2 * DK + c0);
+        const float4 ec4 = *reinterpret_cast<const float4*>(sCh + 3 * DK + c0);
+        const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+        const float egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w}, egcm[4] = {ec4.x, ec4.y, ec4.z, ec4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e1 = __expf(g[sl][i] - gm[i]);     // exp(g - g_m)
-        const float e2 = __builtin_amdgcn_rcpf(e1);     // exp(g_m - g)
-        khm[i] = bv[i] * kv[i] * e1;
-        qhm[i] = qv[i] * e1;
-        ktm[i] = kv[i] * e2;
-        qs[i] = qv[i] * e1 * egm[i];                    // q exp(g)
-        kb[i] = kv[i] * egcm[i] * e2;                   // k exp(g_C - g)
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = __expf(g[sl][i] - gm[i]);     // exp(g - g_m)
+          const float e2 = __builtin_amdgcn_rcpf(e1);     // exp(g_m - g)
+          khm[i] = bv[i] * kv[i] * e1;
+          qhm[i] = qv[i] * e1;
+          ktm[i] = kv[i] * e2;
+          qs[i] = qv[i] * e1 * egm[i];                    // q exp(g)
+          kb[i] = kv[i] * egcm[i] * e2;                   // k exp(g_C - g)
+          kh[i] = khm[i] * egm[i];                        // b k exp(g)
+        }
+      } else {
+        // block-referenced factors (all <= 1): rows at their block start, columns at their block end
+        const int R = r >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gb = g[sl][i], bs = sBs[R * DK + c0 + i];
+          const float E = __expf(gb), Fc = __expf(bs - gb);
+          const float eg = __expf(wide_before<NB, DK>(sBs, R, c0 + i) + gb);        // exp(g)
+          const float ec = __expf((bs - gb) + wide_after<NB, DK>(sBs, R, c0 + i));  // exp(g_C - g)
+          wbk[i] = bv[i] * kv[i];
+          wq[i] = qv[i];
+          khm[i] = wbk[i] * E;
+          qhm[i] = qv[i] * E;
+          ktm[i] = kv[i] * Fc;
+          qs[i] = qv[i] * eg;
+          kb[i] = kv[i] * ec;
+          kh[i] = wbk[i] * eg;
+        }
       }
       // the token-major factor (forward: decayed q; backward: k decayed to the
       // chunk end) straight into its record units; the channel-major one
@@ -292,14 +403,14 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
         for (int i = 0; i < 4; ++i) tmv[i] = tm[i];
         put(rec, Rec::u1, tmv);
         if constexpr (DIR == 2) put(recB, RecB::u1, kb);
-        if constexpr (DIR != 0) {  // b k exp(g) for the gradient kernel
-          float kh[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) kh[i] = khm[i] * egm[i];
-          put(recB, RecB::u5, kh);
-        }
+        if constexpr (DIR != 0) put(recB, RecB::u5, kh);  // b k exp(g) for the gradient kernel
       }
-      if constexpr (F32IN) {
+      if constexpr (WIDE) {
+        float* s0 = reinterpret_cast<float*>(sSL) + r * LDW + cl;
+        st4(s0 + 0 * (C * LDW), khm[0], khm[1], khm[2], khm[3]);
+        st4(s0 + 1 * (C * LDW), qhm[0], qhm[1], qhm[2], qhm[3]);
+        st4(s0 + 2 * (C * LDW), ktm[0], ktm[1], ktm[2], ktm[3]);
+      } else if constexpr (F32IN) {
         float* s0 = reinterpret_cast<float*>(sSL) + r * LDSW + cl;
         st4(s0 + 0 * (C * LDSW), khm[0], khm[1], khm[2], khm[3]);
         st4(s0 + 1 * (C * LDSW), qhm[0], qhm[1], qhm[2], qhm[3]);
@@ -321,40 +432,100 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
       }
     }
     __syncthreads();
+    if constexpr (!WIDE) {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < NGT2) {
-        int R, I;
-        const int kind = gram_tile<DIR, NGT>(t, R, I);
-        const bool isP = kind != 0;
-        if constexpr (F32IN) {
-          const float* sl0 = reinterpret_cast<const float*>(sSL);
-          const float* Kh = sl0;
-          const float* Qh = sl0 + C * LDSW;
-          const float* Kt = sl0 + 2 * (C * LDSW);
-          if (kind == 1) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
-          else if (isP) mma_nt_k<SW>(accG[i], Qh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
-          else mma_nt_k<SW>(accG[i], Kh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
-        } else {
-          const __bf16* sl0 = reinterpret_cast<const __bf16*>(sSL);
-          const __bf16* Kh = sl0;
-          const __bf16* Qh = sl0 + 2 * (C * LDSW);
-          const __bf16* Kt = sl0 + 4 * (C * LDSW);
-          if (kind == 1)
-            mma_nt_split_k<SW>(accG[i], Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW,
-                               Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW);
-          else if (isP)
-            mma_nt_split_k<SW>(accG[i], Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW,
-                               Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
-          else
-            mma_nt_split_k<SW>(accG[i], Kh + 16 * R * LDSW, Kh + C * LDSW + 16 * R * LDSW, LDSW,
-                               Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
+      for (int i = 0; i < GPW; ++i) {
+        const int t = wid + NW * i;
+        if (t < NGT2) {
+          int R, I;
+          const int kind = gram_tile<DIR, NGT>(t, R, I);
+          const bool isP = kind != 0;
+          if constexpr (F32IN) {
+            const float* sl0 = reinterpret_cast<const float*>(sSL);
+            const float* Kh = sl0;
+            const float* Qh = sl0 + C * LDSW;
+            const float* Kt = sl0 + 2 * (C * LDSW);
+            if (kind == 1) mma_nt_k<SW>(accG[i], Kt + 16 * I * LDSW, LDSW, Qh + 16 * R * LDSW, LDSW);
+            else if (isP) mma_nt_k<SW>(accG[i], Qh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
+            else mma_nt_k<SW>(accG[i], Kh + 16 * R * LDSW, LDSW, Kt + 16 * I * LDSW, LDSW);
+          } else {
+            const __bf16* sl0 = reinterpret_cast<const __bf16*>(sSL);
+            const __bf16* Kh = sl0;
+            const __bf16* Qh = sl0 + 2 * (C * LDSW);
+            const __bf16* Kt = sl0 + 4 * (C * LDSW);
+            if (kind == 1)
+              mma_nt_split_k<SW>(accG[i], Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW,
+                                 Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW);
+            else if (isP)
+              mma_nt_split_k<SW>(accG[i], Qh + 16 * R * LDSW, Qh + C * LDSW + 16 * R * LDSW, LDSW,
+                                 Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
+            else
+              mma_nt_split_k<SW>(accG[i], Kh + 16 * R * LDSW, Kh + C * LDSW + 16 * R * LDSW, LDSW,
+                                 Kt + 16 * I * LDSW, Kt + C * LDSW + 16 * I * LDSW, LDSW);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+    } else {
+      // off-diagonal tiles on fp32 matrix cores from the block-referenced factors, the row
+      // factor scaled by the decay of the blocks in between (pair scale)
+      const float* Kh = reinterpret_cast<const float*>(sSL);
+      const float* Qh = Kh + C * LDW;
+      const float* Kt = Kh + 2 * (C * LDW);
+#pragma unroll
+      for (int i = 0; i < GPW; ++i) {
+        const int t = wid + NW * i;
+        if (t < NGT2) {
+          int R, I;
+          const int kind = gram_tile<DIR, NGT>(t, R, I);
+          if (I < R) {
+            const float* s = I + 2 <= R ? sPS + wide_pair(R, I) * DK + sl * SW : nullptr;
+            if (kind == 1) mma_nt_f32s<SW>(accG[i], Kt + 16 * I * LDW, LDW, Qh + 16 * R * LDW, LDW, s);
+            else if (kind == 2) mma_nt_f32s<SW>(accG[i], Qh + 16 * R * LDW, LDW, Kt + 16 * I * LDW, LDW, s);
+            else mma_nt_f32s<SW>(accG[i], Kh + 16 * R * LDW, LDW, Kt + 16 * I * LDW, LDW, s);
+          }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      // diagonal blocks exactly, pair by pair: k and the block-relative decay of every row, then
+      // the row sums into tables that the owners of the diagonal tiles add
+      float* sKw = reinterpret_cast<float*>(sSL);
+      float* sGw = sKw + C * LDW;
+      float* tA = sGw + C * LDW;
+      float* tP = tA + C * 16;
+      if (live) {
+        float kv[4];
+        cvt(rk[sl], kv);
+        st4(sKw + r * LDW + cl, kv[0], kv[1], kv[2], kv[3]);
+        st4(sGw + r * LDW + cl, g[sl][0], g[sl][1], g[sl][2], g[sl][3]);
+      }
+      __syncthreads();
+      {
+        const float gbr[4] = {g[sl][0], g[sl][1], g[sl][2], g[sl][3]};
+        gram_diag_pairwise<TPR, C>(r, live, cl, wbk, wq, gbr, sKw, sGw, LDW, tA, tP);
+      }
+      __syncthreads();
+      {
+        const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+          const int t = wid + NW * i;
+          if (t < NGT2) {
+            int R, I;
+            const int kind = gram_tile<DIR, NGT>(t, R, I);
+            if (I == R) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int ar = 16 * R + 4 * lg + e, ac = 16 * R + lr;  // accumulator row, column
+                accG[i][e] += kind == 0 ? tA[ar * 16 + lr] : kind == 1 ? tP[ac * 16 + 4 * lg + e] : tP[ar * 16 + lr];
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- channel-major factor units; A -> LDS (strict lower); the causal term's
@@ -429,8 +600,15 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
         const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w}, egm[4] = {eg4.x, eg4.y, eg4.z, eg4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e1 = __expf(g[sl][i] - gm[i]);
-          sT1[(c0 + i) * LDC + r] = static_cast<OpT>(qv[i] * e1 * egm[i]);
+          // the same operations in the same order as the separate backward record pass (bitwise equal records)
+          float qs;
+          if constexpr (WIDE) {
+            qs = qv[i] * __expf(wide_before<NB, DK>(sBs, r >> 4, c0 + i) + g[sl][i]);
+          } else {
+            const float e1 = __expf(g[sl][i] - gm[i]);
+            qs = qv[i] * e1 * egm[i];
+          }
+          sT1[(c0 + i) * LDC + r] = static_cast<OpT>(qs);
         }
       }
     }
@@ -452,7 +630,11 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
         for (int i = 0; i < 4; ++i) bv[i] = sigmoid_f(bv[i]);  // k is zero on padding rows
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sT1[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * __expf(g[sl][i]));
+      for (int i = 0; i < 4; ++i) {
+        // g is block-relative on the wide path
+        const float gg = WIDE ? wide_before<NB, DK>(sBs, r >> 4, c0 + i) + g[sl][i] : g[sl][i];
+        sT1[(c0 + i) * LDC + r] = static_cast<OpT>(bv[i] * kv[i] * __expf(gg));
+      }
     }
   }
   __syncthreads();
@@ -526,14 +708,61 @@ __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_
   }
 }
 
+// The record pass: one workgroup per chunk on the fast path (two per CU at d_k = 128, chunk 64).
+// The LDS of the wide-path tables is not part of it.
+template <int DK, int C, bool F32IN, int DIR>
+__global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base,
+                                                            char* brec_base) {
+  __shared__ __attribute__((aligned(16))) char smem[PrepCfg<DK, C, F32IN, DIR>::oBS];
+  prep_chunk<DK, C, F32IN, DIR, false>(a, rec_base, ut_base, brec_base, blockIdx.x, smem);
+}
+
+// The chunks the record pass flagged as wide-decay, recomputed exactly. Workgroup w covers items
+// w, w + gridDim.x, ...: it reads their flags in parallel, lists the flagged ones in LDS and
+// processes them one after another (each result depends on its chunk alone, so the list order
+// does not matter). With no wide chunk every workgroup only reads its flags.
+template <int DK, int C, bool F32IN, int DIR>
+__global__ __launch_bounds__(512) void gdn2_prep_wide_kernel(FwdArgs a, char* rec_base, float* ut_base,
+                                                              char* brec_base, int nitems) {
+  using Cfg = PrepCfg<DK, C, F32IN, DIR>;
+  using Rec = typename Cfg::Rec;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
+  __shared__ int list[kWideBatch];
+  __shared__ int count;
+  const int per = (nitems + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int k0 = 0; k0 < per; k0 += kWideBatch) {
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    const int k = k0 + (int)threadIdx.x;
+    const int64_t item = blockIdx.x + (int64_t)k * gridDim.x;
+    if (threadIdx.x < kWideBatch && k < per && item < nitems) {
+      const int f = *reinterpret_cast<const int*>(rec_base + item * Rec::kBytes + wide_flag_offset<Rec>());
+      if (f == 1) list[atomicAdd(&count, 1)] = (int)item;
+    }
+    __syncthreads();
+    const int n = count;
+    for (int j = 0; j < n; ++j) {
+      prep_chunk<DK, C, F32IN, DIR, true>(a, rec_base, ut_base, brec_base, list[j], smem);
+      __syncthreads();
+    }
+    __syncthreads();
+  }
+}
+
 template <int DK, int C, bool F32IN, int DIR>
 static hipError_t launch_prep_t(const FwdArgs& a, char* rec, float* ut, char* brec, hipStream_t s) {
   if constexpr (!PrepCfg<DK, C, F32IN, DIR>::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
     const int64_t grid = chunk_items(a.vl, a.B, a.T, a.H, C);
+    if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((gdn2_prep_kernel<DK, C, F32IN, DIR>), dim3((unsigned)grid), dim3(512), 0, s, a, rec, ut,
                        brec);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int wgrid = grid < kWideGrid ? (int)grid : kWideGrid;
+    hipLaunchKernelGGL((gdn2_prep_wide_kernel<DK, C, F32IN, DIR>), dim3((unsigned)wgrid), dim3(512), 0, s, a, rec,
+                       ut, brec, (int)grid);
     return hipGetLastError();
   }
 }

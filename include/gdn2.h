@@ -12,11 +12,11 @@
  * channel-wise decay on the key axis. Sources: the NVlabs/GatedDeltaNet-2
  * README ("Gated DeltaNet-2: Decoupling Erase and Write in Linear Attention"),
  * its gate bullet list and the update-rule paragraph after it (the page text
- * lacks the equation; the paragraph states that the right factor of the
- * rank-one erase is key-channel-selective and the write is value-channel-
- * selective), and the arXiv 2605.22791 abstract (fast-weight update view,
- * delta rule, reductions to KDA and Gated DeltaNet, chunkwise WY algorithm,
- * gate-aware backward, constant-memory decoding).
+ * lacks the equation; the paragraph puts the erase gate on the key side of the
+ * rank-one erase and the write gate on the value side of the write), and the
+ * arXiv 2605.22791 abstract (the update as a fast-weight write, the delta
+ * rule, the reductions to KDA and Gated DeltaNet, the chunkwise WY algorithm,
+ * the gate-aware backward, decoding in constant memory).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -38,16 +38,29 @@
  *   tensors as passed. Nothing is clamped or range-checked; q is not scaled.
  * - Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
  *   B, H >= 1; T >= 0 (T = 0 writes S_final = S0 and nothing else). A ragged
- *   last chunk is handled exactly.
+ *   last chunk is handled exactly. One exception: the backward (and the
+ *   training pair) with fp32 inputs at Dk = 128 and chunk 64 is not built
+ *   (GDN2_ERR_UNSUPPORTED; gdn2_workspace_bytes and gdn2_records_bytes return
+ *   0 for it); fp32 inputs run it at chunk 32.
  * - Numerics: fp32 inputs are computed with fp32 matrix-core products. bf16
  *   inputs use fp16 matrix-core operands for the value-side products and a
  *   two-term bf16 split for the decay-scaled key Gram matrices, always with
- *   fp32 accumulation and an fp32 state. The in-chunk decay factors are taken
- *   relative to the middle of the chunk, so within every chunk the cumulative
- *   log-decay of each channel from the chunk middle to either end must stay
- *   above -87 (exp of it must be a normal fp32 number) -- at chunk 64 that is
- *   an average log_alpha above about -2.7 per token; use a smaller chunk for
- *   stronger decay.
+ *   fp32 accumulation and an fp32 state.
+ *   Decay range: any log_alpha <= 0 is exact, -inf (a channel reset)
+ *   included. The chunked calls floor each token's log_alpha at -20 (a decay
+ *   factor of at least exp(-20) ~ 2.1e-9 per token, below fp32 resolution
+ *   next to any term of order one); decode applies exp(log_alpha) as given.
+ *   Chunks where some channel's cumulative log-decay from the chunk middle
+ *   exceeds 60 in magnitude take a slower exact path (decay factors taken
+ *   per 16-token block, the diagonal blocks pair by pair); the others a fast
+ *   one. Both give the same results to rounding.
+ *   Magnitudes: the bf16 backward multiplies dO and dS_final, per (batch row
+ *   or sequence, head), by the power of two that brings their largest
+ *   magnitude into [1, 2) (a pre-pass over dO), and every gradient back on its
+ *   store, so the fp16 operand range does not limit the upstream gradients'
+ *   scale; the forward's fp16 operands hold v, w*v, U and the state, whose
+ *   products must stay within fp16's range (|v| and |S0| up to 2^12 are
+ *   tested).
  * - Results are deterministic (no floating-point atomics): identical inputs
  *   give bitwise identical outputs.
  * - A nullable input means zeros; a nullable output means "not written".

@@ -62,8 +62,13 @@ def test_workspace_bytes():
     # backward: exit-state gradients and room for recomputed entry states (one [B,H,NC,D,D] fp32 array
     # each), then a records region that holds the forward records (for a state recompute) and later the
     # backward ones: 57 units of 1 KB per chunk plus T (w v)
+    # backward records: 57 units of 1 KB per chunk plus T (w v); for 16-bit inputs, at the end, the
+    # partial maxima of the upstream gradients: 8 floats per (batch, head), 256-byte aligned
     rec = lambda n: B * H * n * (57 * 1024 + C * D * 4)  # noqa: E731
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4 + rec(nc)
+    gsc = (B * H * 8 * 4 + 255) // 256 * 256
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4 + rec(nc) + gsc
+    # fp32 inputs: no upstream-gradient scaling
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 64, 64, C, 0) > 0
     # two-stage forward: per chunk a record of 57 units of 1 KB (W, decayed q: 16 each; decayed k^T: 16;
     # causal term: 8; exp(g_last): 1) plus T (w v) in fp32
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 4)
@@ -71,7 +76,10 @@ def test_workspace_bytes():
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == B * H * nc * (113 * 1024 + C * D * 4)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4 + rec(2)
+    # fp32 inputs at d_k = 128, chunk 64: the backward is not built, so no workspace size either
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 0) == 0
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, 0) == 0
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4 + rec(2) + gsc
 
 
 def test_workspace_bytes_two_level_forward():
@@ -177,7 +185,7 @@ def test_training_pair_sizes_and_argument_errors():
     nc = T // C
     rb = lib.gdn2_records_bytes(B, T, H, D, D, C, 1)
     assert rb == B * H * nc * 81 * 1024 + B * H * nc * D * D * 2
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, 1) == B * H * nc * D * D * 4
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, 1) == B * H * nc * D * D * 4 + B * H * 32
     assert lib.gdn2_records_bytes(B, T, H, 48, D, C, 1) == 0 and lib.gdn2_records_bytes(B, 0, H, D, D, C, 1) == 0
     # fp32 inputs keep fp32 entry states
     rb32 = lib.gdn2_records_bytes(1, 64, 2, 16, 16, 16, 0)
