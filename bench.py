@@ -1,13 +1,17 @@
 """Benchmark of the GDN-2 operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-curve] [--no-front-end]
-                    [--no-varlen] [--no-gate-granularity]
+                    [--no-varlen] [--no-gate-granularity] [--no-prefill] [--no-flush] [--decode-only]
 
 A step is one training pass of the operator over one batch of synthetic input
 with the pages' layer shape: the chunked forward that also saves the chunk
 entry states, then the gate-aware chunked backward (B=8, H=16, T=4096,
 d_k=d_v=128, chunk 64, bf16 q/k/v/b/w/dO, fp32 log_alpha). W untimed steps,
-then K timed steps between two synchronisations. The one-token decode step
+then K timed steps between two synchronisations; before every step a 512 MiB
+scratch buffer is written (outside the step's events) so that no step starts
+with its inputs in L2 or the Infinity Cache. The forward alone on the same
+shape (prefill: no chunk states, the configuration's own seeded inputs) is
+reported under "prefill". The one-token decode step
 (B=256 sequences, H=16, d=128, fp32 state, 128 consecutive steps) is timed
 separately and reported under "decode", and the long-sequence forward (B=1,
 H=16, d=128, T = 8K..64K: few heads, so the two-level chain) under
@@ -35,6 +39,18 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0        # HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16/fp16 matrix cores, TFLOP/s
+FLUSH_BYTES = 512 << 20      # written between timed steps: twice the 256 MB Infinity Cache
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 # FLOP and byte models per token-head at chunk C, d_k = d_v = d (algorithmic,
 # dense-counted; redundant recompute is not counted).
@@ -135,9 +151,99 @@ def cpu_baseline(inp, heads):
     H = inp["q"].shape[2]
     # tokens of the workload carry H heads each: the sample covers heads/H of T tokens
     tokens = T * heads / H
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"batch row 0, {heads} of {H} heads, T={T}: float64 stepwise forward + reverse-mode "
                       f"backward, one process per head ({dt:.1f} s wall)"}
+
+
+def _oracle_fwd_worker(args):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    with threadpool_limits(limits=1):
+        oracle.forward(*args, None)
+    return args[0].shape[1]
+
+
+def cpu_baseline_prefill(inp, heads):
+    """Time the oracle forward on batch row 0, `heads` heads, full T, over a process pool."""
+    import multiprocessing as mp
+
+    import torch
+
+    cores = min(len(os.sched_getaffinity(0)), 16, heads)
+    f = lambda t: t[0:1, :, :heads].to(torch.float64).numpy()  # noqa: E731
+    full = [f(inp[n]) for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    jobs = [tuple(x[:, :, h:h + 1].copy() for x in full) for h in range(heads)]
+    t = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        pool.map(_oracle_fwd_worker, jobs, chunksize=1)
+    dt = time.perf_counter() - t
+    T, H = full[0].shape[1], inp["q"].shape[2]
+    return {"value": T * heads / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"batch row 0, {heads} of {H} heads, T={T}: float64 stepwise forward, one process per head "
+                      f"({dt:.1f} s wall)"}
+
+
+def cpu_baseline_decode(dec, steps):
+    """Time the oracle's decode step over every (sequence, head) of the decode batch for `steps` steps
+    (numpy vectorised over the pairs, one process, BLAS threads as the host sets them)."""
+    import oracle
+
+    S = dec["S0"]
+    t = time.perf_counter()
+    for i in range(steps):
+        _, S = oracle.decode_step(*(dec[n][i] for n in ("q", "k", "v", "log_alpha", "b", "w")), S)
+    dt = time.perf_counter() - t
+    B = dec["q"].shape[1]
+    return {"value": B * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"{steps} of the 128 decode steps, all {B} sequences x {dec['q'].shape[2]} heads: float64 "
+                      f"oracle decode step vectorised over the pairs in one process ({dt:.1f} s wall)"}
+
+
+def run_decode(lib, _lib, dev, stream):
+    """The one-token decode (B=256 sequences, H=16, d=128, fp32 state, bf16 token inputs) over its 128
+    consecutive steps: microseconds per step against the HBM roofline (the state exceeds the Infinity Cache,
+    so no flush is needed between steps)."""
+    import torch
+
+    import synth
+
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    sh = stream.cuda_stream
+    c3 = synth.WORKLOADS["decode-B256-H16-d128-128steps"]
+    dec = synth.workload_inputs("decode-B256-H16-d128-128steps")
+    dd = {k: v.to(dev) for k, v in dec.items()}
+    S = dd["S0"].clone()
+    od = torch.empty(c3["B"], c3["H"], c3["Dv"], device=dev)
+    steps = c3["steps"]
+    xs = [[dd[n][t] for n in ("q", "k", "v", "log_alpha", "b", "w")] for t in range(steps)]
+
+    def dstep(t):
+        x = xs[t]
+        st = lib.gdn2_decode_step(P(x[0]), P(x[1]), P(x[2]), P(x[3]), P(x[4]), P(x[5]), P(S), P(od),
+                                  c3["B"], c3["H"], c3["Dk"], c3["Dv"], _lib.GDN2_BF16, sh)
+        _lib.check(st, "gdn2_decode_step")
+
+    for t in range(8):
+        dstep(t)
+    S.copy_(dd["S0"])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(steps):
+        dstep(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byt = decode_bytes(c3["B"], c3["H"], c3["Dk"])
+    gbs = byt / (us / 1e6) / 1e9
+    return {"workload": "one-token decode, B=256 H=16 d=128, fp32 state 256x16x128x128, "
+                        "bf16 token inputs, 128 consecutive steps",
+            "us_per_step": round(us, 2), "tokens_per_s": round(c3["B"] / (us / 1e6), 1),
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_step": int(byt)}
 
 
 def main():
@@ -151,6 +257,10 @@ def main():
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length step")
     ap.add_argument("--no-gate-granularity", action="store_true", help="skip the scalar-gate (KDA / GDN) steps")
     ap.add_argument("--no-curve", action="store_true", help="skip the long-sequence forward curve (T = 8K..64K)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the forward-only (prefill) row")
+    ap.add_argument("--no-flush", action="store_true", help="no cache flush between timed training steps")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode section (for hardware-counter runs of the decode kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -174,19 +284,31 @@ def main():
         return
 
     import synth
-    from delta_rule_recurrent_gdn_amd import _lib, gdn2_bwd_chunked, gdn2_decode_step, gdn2_fwd_chunked
+    from delta_rule_recurrent_gdn_amd import _lib
+
+    if args.decode_only:
+        dev = torch.device("cuda:0")
+        lib = _lib.load()
+        print(json.dumps({"decode": run_decode(lib, _lib, dev, torch.cuda.current_stream(dev))}), flush=True)
+        return
 
     cfg = synth.WORKLOADS["fwd+bwd-B8-H16-T4096-d128"]
     B, T, H, D, C = cfg["B"], cfg["T"], cfg["H"], cfg["Dk"], cfg["chunk"]
     inp = synth.workload_inputs("fwd+bwd-B8-H16-T4096-d128")
-    # the oracle baseline runs first, in forked worker processes, before this
+    pre = None if args.no_prefill else synth.workload_inputs("fwd-B8-H16-T4096-d128")
+    # the oracle baselines run first, in forked worker processes, before this
     # process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(inp, heads=16)
+    cpu_pre = None if (args.no_cpu or pre is None) else cpu_baseline_prefill(pre, heads=16)
+    cpu_dec = None
+    if not args.no_cpu and not args.no_decode:
+        cpu_dec = cpu_baseline_decode(synth.workload_inputs("decode-B256-H16-d128-128steps"), steps=4)
 
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev)
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, device=dev)
 
     # preallocated outputs and workspace: the timed region only launches kernels
     NC = (T + C - 1) // C
@@ -249,28 +371,58 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    def timed_pair(f, b, n, warm):
-        """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream)."""
+    def timed_pair(f, b, n, warm, fl=None):
+        """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream).
+        With fl, the buffer fl is written before every step, outside the step's events."""
         for _ in range(warm):
             f()
             b()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
-        ev[0].record(stream)
+        if fl is None:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n + 1)]
+            ev[0].record(stream)
+            for i in range(n):
+                f()
+                ev[2 * i + 1].record(stream)
+                b()
+                ev[2 * i + 2].record(stream)
+            torch.cuda.synchronize()
+            tf = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)) / n
+            tb = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n)) / n
+            return tf, tb, ev[0].elapsed_time(ev[-1]) / n
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         for i in range(n):
+            fl.fill_(float(i))
+            ev[i][0].record(stream)
             f()
-            ev[2 * i + 1].record(stream)
+            ev[i][1].record(stream)
             b()
-            ev[2 * i + 2].record(stream)
+            ev[i][2].record(stream)
         torch.cuda.synchronize()
-        tf = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)) / n
-        tb = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(n)) / n
-        return tf, tb, ev[0].elapsed_time(ev[-1]) / n
+        tf = sum(e[0].elapsed_time(e[1]) for e in ev) / n
+        tb = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+        return tf, tb, tf + tb
+
+    def timed_flushed(fn, n=10, warm=3):
+        """Average ms of fn over n calls, the flush buffer written before each (outside the events)."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(float(i))
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n
 
     t_wall = time.perf_counter()
-    t_fwd, t_bwd, ms_step = timed_pair(fwd, bwd, args.steps, args.warmup)
+    t_fwd, t_bwd, ms_step = timed_pair(fwd, bwd, args.steps, args.warmup, flush)
     wall = time.perf_counter() - t_wall
-    s_fwd, s_bwd, s_step = timed_pair(fwd_sep, bwd_sep, min(args.steps, 10), 1)
+    _, _, ms_step_nf = timed_pair(fwd, bwd, min(args.steps, 10), 1) if flush is not None else (0, 0, ms_step)
+    s_fwd, s_bwd, s_step = timed_pair(fwd_sep, bwd_sep, min(args.steps, 10), 1, flush)
     # the single-pass forward (no workspace), timed on its own for comparison
     fwd_sep(single_pass=True)
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -317,13 +469,51 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,
                    "parallelism": "single GPU"},
         "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4), "fwd_single_pass_ms": round(t_fwd_single, 4),
+        "cache_flush": None if flush is None else f"{FLUSH_BYTES >> 20} MiB written before every timed step",
+        "ms_per_step_back_to_back": round(ms_step_nf, 4),
         "separate_calls": {"fwd_ms": round(s_fwd, 4), "bwd_ms": round(s_bwd, 4), "ms_per_step": round(s_step, 4),
                            "note": "gdn2_fwd_chunked + gdn2_bwd_chunked, each with its own record pass"},
         "mfma_frac": round(mfma, 4),
+        # at this path's arithmetic intensity, HBM caps the matrix-core fraction (by the FLOP model) at this
+        # value even at full HBM bandwidth
+        "mfma_frac_ceiling_at_hbm_peak": round((F_f + F_b) / ((by_f + by_b) / (PEAK_HBM_GBS * 1e9))
+                                               / (PEAK_BF16_TFLOPS * 1e12), 4),
         "hbm_frac_step": round((by_f + by_b) / (ms_step / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
+
+    if pre is not None:
+        # prefill: the forward alone on the per-layer training shape (B=8 H=16 T=4096 d=128 chunk 64,
+        # bf16, S0 = 0, seed 1), returning o only (no chunk states, no final state)
+        pdv = {k: (v.to(dev) if v is not None else None) for k, v in pre.items()}
+        po = torch.empty(B, T, H, D, device=dev)
+
+        def prefill_call(single_pass=False):
+            wsp, wsn = (None, 0) if single_pass else (P(ws_f), need_f)
+            st = lib.gdn2_fwd_chunked(P(pdv["q"]), P(pdv["k"]), P(pdv["v"]), P(pdv["log_alpha"]), P(pdv["b"]),
+                                      P(pdv["w"]), None, P(po), None, None, wsp, wsn, B, T, H, D, D, C,
+                                      _lib.GDN2_BF16, sh)
+            _lib.check(st, "gdn2_fwd_chunked")
+
+        tp = timed_flushed(prefill_call, n=min(args.steps, 10))
+        tp1 = timed_flushed(lambda: prefill_call(True), n=min(args.steps, 10))
+        Fp, Bp = F_f, fwd_bytes(C, D, save_states=False) * th
+        pr = {"workload": "forward only (prefill) of the per-layer training shape: gdn2_fwd_chunked two-stage "
+                          "path, B=8 H=16 T=4096 d_k=d_v=128 chunk 64, bf16 q/k/v/b/w, fp32 log_alpha, fp32 o, "
+                          "no chunk states, seeded inputs of that workload (seed 1)",
+              "ms": round(tp, 4), "tokens_per_s": round(B * T / (tp / 1e3), 1),
+              "mfma_frac": round(Fp / (tp / 1e3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+              "hbm_frac": round(Bp / (tp / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+              "roofline_frac": round(max(Fp / (PEAK_BF16_TFLOPS * 1e12), Bp / (PEAK_HBM_GBS * 1e9)) / (tp / 1e3), 4),
+              "mfma_frac_ceiling_at_hbm_peak": round(Fp / (Bp / (PEAK_HBM_GBS * 1e9)) / (PEAK_BF16_TFLOPS * 1e12), 4),
+              "algorithmic_flops": int(Fp), "algorithmic_bytes": int(Bp),
+              "single_pass_ms": round(tp1, 4),
+              "single_pass_tokens_per_s": round(B * T / (tp1 / 1e3), 1)}
+        if cpu_pre is not None:
+            pr["cpu_baseline"] = cpu_pre
+        out["prefill"] = pr
+        del pdv, po
 
     if not args.no_front_end:
         # the fused gate front end: the same training step with the gates passed as pre-activations
@@ -447,39 +637,9 @@ def main():
         del vstates, vws_f, vws_b, vo, vrec, vws_r
 
     if not args.no_decode:
-        c3 = synth.WORKLOADS["decode-B256-H16-d128-128steps"]
-        dec = synth.workload_inputs("decode-B256-H16-d128-128steps")
-        dd = {k: v.to(dev) for k, v in dec.items()}
-        S = dd["S0"].clone()
-        od = torch.empty(c3["B"], c3["H"], c3["Dv"], device=dev)
-        steps = c3["steps"]
-        xs = [[dd[n][t] for n in ("q", "k", "v", "log_alpha", "b", "w")] for t in range(steps)]
-
-        def dstep(t):
-            x = xs[t]
-            st = lib.gdn2_decode_step(P(x[0]), P(x[1]), P(x[2]), P(x[3]), P(x[4]), P(x[5]), P(S), P(od),
-                                      c3["B"], c3["H"], c3["Dk"], c3["Dv"], _lib.GDN2_BF16, sh)
-            _lib.check(st, "gdn2_decode_step")
-
-        for t in range(8):
-            dstep(t)
-        S.copy_(dd["S0"])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for t in range(steps):
-            dstep(t)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        byt = decode_bytes(c3["B"], c3["H"], c3["Dk"])
-        gbs = byt / (us / 1e6) / 1e9
-        out["decode"] = {"workload": "one-token decode, B=256 H=16 d=128, fp32 state 256x16x128x128, "
-                                     "bf16 token inputs, 128 consecutive steps",
-                         "us_per_step": round(us, 2), "tokens_per_s": round(c3["B"] / (us / 1e6), 1),
-                         "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "algorithmic_bytes_per_step": int(byt)}
-        del dd, dec, xs, S
+        out["decode"] = run_decode(lib, _lib, dev, stream)
+        if cpu_dec is not None:
+            out["decode"]["cpu_baseline"] = cpu_dec
 
     if not args.no_curve:
         # the long-sequence sweep: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk
