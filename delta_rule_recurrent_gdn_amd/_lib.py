@@ -32,6 +32,8 @@ GDN2_FLAG_SCALAR_B = 2
 GDN2_FLAG_SCALAR_W = 4
 GDN2_FLAG_SCALAR_DECAY = 8
 
+GDN2_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024  # the device array of gdn2_fwd_chunked_noalloc
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -66,6 +68,7 @@ SIGNATURES = {
                                      _SZ, _I, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_decode_step_slots": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _U, _P]),
     "gdn2_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "gdn2_fwd_chunked_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gdn2_status_string": (ctypes.c_char_p, [_I]),
     "gdn2_version": (_I, []),
 }

@@ -347,6 +347,29 @@ int gdn2_decode_step_slots(const void* q, const void* k, const void* v, const fl
  * itself reports them. */
 size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chunk, int dt);
 
+/*
+ * gdn2_fwd_chunked_noalloc -- gdn2_fwd_chunked's two-stage path for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a device array owned by the
+ * library, GDN2_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the first
+ * load of the library's device code until the process ends. Arguments as
+ * gdn2_fwd_chunked without the workspace pair; results are identical to
+ * gdn2_fwd_chunked with a workspace (the same kernels).
+ *
+ * Sizes whose forward workspace, gdn2_workspace_bytes(GDN2_OP_FWD, ...), exceeds
+ * GDN2_NOALLOC_SCRATCH_BYTES return GDN2_ERR_WORKSPACE before any device work;
+ * sizes that need no workspace run the single-pass kernel. The call allocates
+ * nothing: its first call on a device only looks up that device's copy of the
+ * array (with that device current). Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (concurrent streams, threads) race
+ * and must be ordered by the caller; nothing in the array needs to be cleared.
+ */
+#define GDN2_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int gdn2_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const void* b, const void* w, const float* S0, float* o, float* S_final,
+                             float* chunk_states, int B, int T, int H, int Dk, int Dv, int chunk,
+                             int dt, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gdn2_status_string(int status);
 
