@@ -1,0 +1,148 @@
+"""Operand-precision budget of the chunked forward (CPU, numpy and the oracle only).
+
+The bf16 path runs its matrix-core products on 16-bit operands with fp32 accumulation. Which 16-bit format
+each operand takes is a design choice; this file is its evidence. The chunkwise WY forward (the refactoring
+of tests/chunked_model.py, with the Gram factors referenced to the chunk middle as the kernels form them) is
+evaluated in float64 with every product operand rounded by one of three policies, and compared with the
+float64 oracle on inputs drawn like the B = 8, H = 16, T = 4096, d = 128 workload (one row, two heads,
+T = 512):
+
+* "bf16": every operand bf16 (8-bit mantissa, fp32's range);
+* "fp16": every operand fp16 (11-bit mantissa, normal range 6.1e-5 .. 65504);
+* "kernel": the Gram factors, whose entries span exp(+-half-chunk decay), as a two-term bf16 split
+  (hi = bf16(x), lo = bf16(x - hi): about 16 mantissa bits over fp32's range); every other operand fp16.
+
+Findings pinned here: bf16 operands alone miss the 2e-2 output bar; fp16 operands meet it but overflow once
+the half-chunk decay passes ln(65504) ~ 11.1; the kernel policy meets it with margin at both decay levels.
+The backward's upstream gradients are covered by the same kind of check: fp16 operands of dO ~ 1e-7 lose
+most of their mantissa, and a power-of-two prescale (exact) restores it.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import TOL_BF16, rel_err
+
+
+def bf16(x):
+    """Round to bfloat16 (nearest even) and back to float64."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def fp16(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def split(x):
+    """bf16 hi/lo pair, summed back (what a product of the pair against an operand accumulates)."""
+    hi = bf16(x)
+    return hi + bf16(np.asarray(x, np.float64) - hi)
+
+
+POLICIES = {"bf16": (bf16, bf16), "fp16": (fp16, fp16), "kernel": (split, fp16)}  # (Gram factors, others)
+
+
+def chunk_fwd_rounded(S0, q, k, v, la, b, w, rg, rv):
+    """One chunk of the WY forward with product operands rounded: rg for the Gram factors, rv otherwise."""
+    L = q.shape[0]
+    g = np.cumsum(la, axis=0)
+    gm = g[(L - 1) // 2]                      # chunk-middle reference per key channel
+    gC = g[-1]
+    with np.errstate(over="ignore", invalid="ignore"):
+        Khm = b * k * np.exp(g - gm)          # Gram factors: Kh = Khm e^{gm}, Kt = Ktm e^{-gm}
+        Ktm = k * np.exp(gm - g)
+        Qhm = q * np.exp(g - gm)
+        A = np.tril(rg(Khm) @ rg(Ktm).T, -1)
+        P = np.tril(rg(Qhm) @ rg(Ktm).T)
+    T = np.linalg.inv(np.eye(L) + A)          # fp32 in the kernel: exact here
+    Kh = b * k * np.exp(g)                    # bounded by |k|: decay factors <= 1
+    Qh = q * np.exp(g)
+    Kb = k * np.exp(gC - g)
+    W = rv(T) @ rv(Kh)
+    U = rv(T) @ rv(w * v) - rv(W) @ rv(S0)
+    O = rv(Qh) @ rv(S0) + rv(P) @ rv(U)
+    S1 = np.exp(gC)[:, None] * S0 + rv(Kb).T @ rv(U)
+    return O, S1
+
+
+def chunked_forward_rounded(inp, C, policy):
+    rg, rv = POLICIES[policy]
+    q, k, v, la, b, w = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v", "log_alpha", "b", "w"))
+    B, T, H, _ = q.shape
+    o = np.zeros(v.shape)
+    for bi in range(B):
+        for h in range(H):
+            S = np.zeros((q.shape[-1], v.shape[-1]))
+            for s in range(0, T, C):
+                e = min(s + C, T)
+                sl = (bi, slice(s, e), h)
+                o[sl], S = chunk_fwd_rounded(S, q[sl], k[sl], v[sl], la[sl], b[sl], w[sl], rg, rv)
+    return o
+
+
+def _inputs(strong):
+    inp = synth.make_inputs(1, 512, 2, 128, 128, "bf16", seed=1)
+    if strong:  # a quarter of the key channels forget fast: log_alpha = -1.5 per token (half-chunk decay 48)
+        la = inp["log_alpha"].clone()
+        la[..., ::4] = -1.5
+        inp["log_alpha"] = la
+    return inp
+
+
+@pytest.fixture(scope="module")
+def errors():
+    out = {}
+    for strong in (False, True):
+        inp = _inputs(strong)
+        o_ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"])
+        for pol in POLICIES:
+            o = chunked_forward_rounded(inp, 64, pol)
+            out[(strong, pol)] = rel_err(o, o_ref) if np.isfinite(o).all() else float("inf")
+    return out
+
+
+def test_bf16_operands_miss_the_bar(errors):
+    assert errors[(False, "bf16")] > TOL_BF16, errors
+
+
+def test_fp16_operands_meet_the_bar_at_mild_decay_only(errors):
+    assert errors[(False, "fp16")] < TOL_BF16 / 2, errors
+    assert not np.isfinite(errors[(True, "fp16")]), errors  # exp(48) > 65504: the Gram factors overflow
+
+
+def test_kernel_policy_meets_the_bar_at_both_decay_levels(errors):
+    for strong in (False, True):
+        assert errors[(strong, "kernel")] < TOL_BF16 / 2, errors
+    assert errors[(False, "kernel")] < errors[(False, "bf16")] / 3, errors
+
+
+def test_model_is_exact_without_rounding():
+    """The rounded model with identity rounding is the WY forward itself (guards the model, not a policy)."""
+    inp = _inputs(True)
+    POLICIES["exact"] = (lambda x: x, lambda x: x)
+    try:
+        o = chunked_forward_rounded(inp, 64, "exact")
+    finally:
+        del POLICIES["exact"]
+    o_ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"])
+    assert rel_err(o, o_ref) < 1e-9
+
+
+@pytest.mark.parametrize("scale", [1e-7, 1e-3, 1.0, 1e3])
+def test_upstream_gradient_prescale(scale):
+    """dU = P^T dO with dO of magnitude `scale` as fp16 operands: direct vs power-of-two prescaled."""
+    rng = np.random.default_rng(7)
+    dO = bf16(scale * rng.standard_normal((64, 128)))
+    Pt = fp16(np.tril(rng.uniform(-0.3, 0.3, (64, 64))).T)
+    ref = Pt @ dO
+    direct = Pt @ fp16(dO)
+    s = 2.0 ** -np.floor(np.log2(np.max(np.abs(dO))))    # brings max |dO| into [1, 2)
+    pre = (Pt @ fp16(s * dO)) / s
+    e_pre = rel_err(pre, ref)
+    assert e_pre < 2e-3
+    if scale <= 1e-7:
+        assert rel_err(direct, ref) > 0.1  # most of the mantissa lost below fp16's normal range
