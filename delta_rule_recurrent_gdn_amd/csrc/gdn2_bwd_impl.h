@@ -242,6 +242,71 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   const int bCs = scalar_b ? 0 : 1;
   const int64_t wBase = scalar_w ? baseS : baseV, wRow = scalar_w ? H : rowV;
   const int wCs = scalar_w ? 0 : 1;
+  // the column phase's gathers (this wave's 16 value columns: rows of S0 and dS in operand slots, dO,
+  // v, w) are issued here as well, ahead of the record units, so that one memory latency covers both
+  using Fr = Frag<F32IN>;
+  constexpr int KU = Fr::KU, UKd = Fr::units(DK), UCc = Fr::units(C), RC = C / 16;
+  using RhsT = typename std::conditional<F32IN, f32x4, f16x8>::type;
+  constexpr int NE = F32IN ? 4 : 8;
+  using InT = typename std::conditional<F32IN, float, __bf16>::type;
+  const int jc = 16 * wid + lr;
+  float s0r[UKd][NE], dsr[UKd][NE];
+  InT dor[UCc][NE], vr[RC][4], wr[RC][4];
+  if (16 * wid < Dv) {
+#pragma unroll
+    for (int u = 0; u < UKd; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int d = KU * u + Fr::kslot(lg, j);
+        s0r[u][j] = ld_sel(S0g, (int64_t)d * Dv + jc, jc, d < DK);
+        dsr[u][j] = ld_sel(dSg, (int64_t)d * Dv + jc, jc, d < DK);
+      }
+#pragma unroll
+    for (int u = 0; u < UCc; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int t = KU * u + Fr::kslot(lg, j);
+        dor[u][j] = ld_sel(static_cast<const InT*>(a.dO), baseV + (int64_t)(t0 + t) * rowV + jc,
+                           baseV + (int64_t)t0 * rowV + jc, t < Lr);
+      }
+#pragma unroll
+    for (int R = 0; R < RC; ++R)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * R + 4 * lg + e;
+        const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc, safe = baseV + (int64_t)t0 * rowV + jc;
+        vr[R][e] = ld_sel(static_cast<const InT*>(a.v), idx, safe, t < Lr);
+        wr[R][e] = ld_sel(static_cast<const InT*>(a.w), wBase + (int64_t)(t0 + t) * wRow + jc * wCs,
+                          wBase + (int64_t)t0 * wRow + jc * wCs, t < Lr);
+      }
+  }
+  // T (and T^T) and P^T from the record's units; P^T units that lie wholly
+  // below the diagonal are not stored (zero). The loads are issued before the gate cumsum, so that their
+  // latency passes during it; they are unpacked after it
+  using F = Frag<F32IN>;
+  const char* rec = a.records + cl.item * Rec::kBytes;
+  // units: T, P^T (chunk x chunk), then Kh, Kb (chunk x Dk); every load of
+  // the wave first, then the unpacking
+  constexpr int NU = Rec::RC * Rec::UC, NK = Rec::RC * Rec::UK, NUT = 2 * NU + 2 * NK;
+  constexpr int UPW = (NUT + NW - 1) / NW;
+  // (The unit index arithmetic is written out here: the same arithmetic in a
+  // lambda with reference out-parameters, inside these unrolled loops,
+  // compiled to code that unpacked wrong units for some sizes on gfx950.)
+  uint4 uv[UPW];
+  int uw[UPW], uR[UPW], uu[UPW];
+#pragma unroll
+  for (int p = 0; p < UPW; ++p) {
+    const int t = wid + NW * p;
+    const int which = t < NU ? 0 : t < 2 * NU ? 1 : t < 2 * NU + NK ? 2 : 3;
+    const int tt = which == 0 ? t : which == 1 ? t - NU : which == 2 ? t - 2 * NU : t - 2 * NU - NK;
+    const int nu = which < 2 ? Rec::UC : Rec::UK;
+    const int ub = which == 0 ? Rec::u4 : which == 1 ? Rec::u0 : which == 2 ? Rec::u5 : Rec::u1;
+    uw[p] = t < NUT ? which : -1;
+    uR[p] = tt / nu;
+    uu[p] = tt - uR[p] * nu;
+    const int64_t off = t < NUT ? (int64_t)(ub + tt) * F::kUnitBytes : 0;  // past the units: any valid unit
+    uv[p] = *reinterpret_cast<const uint4*>(rec + off + 16 * l);
+  }
   ks.load_la(a.log_alpha, baseK, rowK, t0, Lr);
   ks.gates(sTot, sG, sCh);
   float* sBs = reinterpret_cast<float*>(smem + Cfg::oBS);
@@ -276,32 +341,6 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
     if constexpr (WIDE) return __expf((sBs[R * DK + c] - e1) + wide_after<NB, DK>(sBs, R, c));
     else return sCh[3 * DK + c] * __builtin_amdgcn_rcpf(e1);
   };
-  // T (and T^T) and P^T from the record's units; P^T units that lie wholly
-  // below the diagonal are not stored (zero)
-  using F = Frag<F32IN>;
-  const char* rec = a.records + cl.item * Rec::kBytes;
-  // units: T, P^T (chunk x chunk), then Kh, Kb (chunk x Dk); every load of
-  // the wave first, then the unpacking
-  constexpr int NU = Rec::RC * Rec::UC, NK = Rec::RC * Rec::UK, NUT = 2 * NU + 2 * NK;
-  constexpr int UPW = (NUT + NW - 1) / NW;
-  // (The unit index arithmetic is written out here: the same arithmetic in a
-  // lambda with reference out-parameters, inside these unrolled loops,
-  // compiled to code that unpacked wrong units for some sizes on gfx950.)
-  uint4 uv[UPW];
-  int uw[UPW], uR[UPW], uu[UPW];
-#pragma unroll
-  for (int p = 0; p < UPW; ++p) {
-    const int t = wid + NW * p;
-    const int which = t < NU ? 0 : t < 2 * NU ? 1 : t < 2 * NU + NK ? 2 : 3;
-    const int tt = which == 0 ? t : which == 1 ? t - NU : which == 2 ? t - 2 * NU : t - 2 * NU - NK;
-    const int nu = which < 2 ? Rec::UC : Rec::UK;
-    const int ub = which == 0 ? Rec::u4 : which == 1 ? Rec::u0 : which == 2 ? Rec::u5 : Rec::u1;
-    uw[p] = t < NUT ? which : -1;
-    uR[p] = tt / nu;
-    uu[p] = tt - uR[p] * nu;
-    const int64_t off = t < NUT ? (int64_t)(ub + tt) * F::kUnitBytes : 0;  // past the units: any valid unit
-    uv[p] = *reinterpret_cast<const uint4*>(rec + off + 16 * l);
-  }
 #pragma unroll
   for (int p = 0; p < UPW; ++p) {
     const int which = uw[p], R = uR[p], u = uu[p];
@@ -324,8 +363,6 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   // (lane layout of gdn2_frag.h); the left operands are row-major LDS rows
   // read in the same slot order. dw, dv leave from here; U and dU go to LDS
   // for the contractions over the value axis.
-  using Fr = Frag<F32IN>;
-  constexpr int KU = Fr::KU, UKd = Fr::units(DK), UCc = Fr::units(C), RC = C / 16;
   __syncthreads();  // Kh, Kb, T, T^T, P^T are in LDS; the gate buffer is dead
   auto lds_unit = [&](const OpT* X, int ld, int row0, int k0, int K) -> uint4 {
     const OpT* p = X + (row0 + lr) * ld + k0 + 4 * lg;
@@ -359,39 +396,6 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   };
   if (16 * wid >= Dv) fetch_rows();  // a wave with no value columns
   if (16 * wid < Dv) {
-    const int jc = 16 * wid + lr;
-    using RhsT = typename std::conditional<F32IN, f32x4, f16x8>::type;
-    constexpr int NE = F32IN ? 4 : 8;
-    // every gather first, in flight together; conversions after the fence
-    using InT = typename std::conditional<F32IN, float, __bf16>::type;
-    float s0r[UKd][NE], dsr[UKd][NE];
-    InT dor[UCc][NE], vr[RC][4], wr[RC][4];
-#pragma unroll
-    for (int u = 0; u < UKd; ++u)
-#pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        const int d = KU * u + Fr::kslot(lg, j);
-        s0r[u][j] = ld_sel(S0g, (int64_t)d * Dv + jc, jc, d < DK);
-        dsr[u][j] = ld_sel(dSg, (int64_t)d * Dv + jc, jc, d < DK);
-      }
-#pragma unroll
-    for (int u = 0; u < UCc; ++u)
-#pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        const int t = KU * u + Fr::kslot(lg, j);
-        dor[u][j] = ld_sel(static_cast<const InT*>(a.dO), baseV + (int64_t)(t0 + t) * rowV + jc,
-                           baseV + (int64_t)t0 * rowV + jc, t < Lr);
-      }
-#pragma unroll
-    for (int R = 0; R < RC; ++R)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * R + 4 * lg + e;
-        const int64_t idx = baseV + (int64_t)(t0 + t) * rowV + jc, safe = baseV + (int64_t)t0 * rowV + jc;
-        vr[R][e] = ld_sel(static_cast<const InT*>(a.v), idx, safe, t < Lr);
-        wr[R][e] = ld_sel(static_cast<const InT*>(a.w), wBase + (int64_t)(t0 + t) * wRow + jc * wCs,
-                          wBase + (int64_t)t0 * wRow + jc * wCs, t < Lr);
-      }
     fetch_rows();
     __builtin_amdgcn_sched_barrier(0);
     RhsT s0f[UKd], dsf[UKd], dof[UCc];

@@ -34,9 +34,10 @@ namespace gdn2 {
 
 constexpr float kLaFloor = -20.f;
 constexpr float kWideSpan = 60.f;
-// workgroups of a wide-chunk pass: each reads the flags of about items / kWideGrid chunks,
-// kWideBatch at a time
-constexpr int kWideGrid = 1024;
+// workgroups of a wide-chunk pass: one per compute unit (the pass's LDS admits one workgroup per
+// CU, so more would only queue); each reads the flags of about items / kWideGrid chunks, kWideBatch
+// at a time, in parallel
+constexpr int kWideGrid = 256;
 constexpr int kWideBatch = 64;
 
 // NaN stays NaN (an fmaxf would replace it)

@@ -86,13 +86,13 @@ def test_fwd_B8_H16_T4096_sampled_pairs(single):
     assert np.isfinite(f64(o)).all() and np.isfinite(f64(S)).all()
 
 
-@pytest.mark.parametrize("T", [8192, 65536])
+@pytest.mark.parametrize("T", [8192, 16384, 32768, 65536])
 @PATHS
 def test_long_sequence_B1_H16_sampled(T, single):
     """B=1, H=16, T up to 64K, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1)."""
     inp = synth.workload_inputs("fwd-long-B1-H16-d128", T=T)
     o, S, _ = _run(inp, 64, single=single)
-    pairs = [(0, 0), (0, 9)] if T <= 8192 else [(0, 5)]
+    pairs = [(0, 0), (0, 9)] if T <= 8192 else [(0, 5)] if T == 65536 else [(0, 3), (0, 14)]
     o_ref, S_ref = oracle_fwd_pairs(inp, pairs)
     eo, es = rel_err(gpu_pairs(o, pairs), o_ref), rel_err(gpu_state_pairs(S, pairs), S_ref)
     print(f"long sequence T={T} err o {eo:.3e} S {es:.3e}")
