@@ -8,7 +8,7 @@ with the pages' layer shape: the chunked forward that also saves the chunk
 entry states, then the gate-aware chunked backward (B=8, H=16, T=4096,
 d_k=d_v=128, chunk 64, bf16 q/k/v/b/w/dO, fp32 log_alpha). W untimed steps,
 then K timed steps between two synchronisations; before every step a 512 MiB
-scratch buffer is written (outside the step's events) so that no step starts
+scratch buffer is read (outside the step's events) so that no step starts
 with its inputs in L2 or the Infinity Cache. The forward alone on the same
 shape (prefill: no chunk states, the configuration's own seeded inputs) is
 reported under "prefill". The one-token decode step
@@ -39,7 +39,13 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0        # HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16/fp16 matrix cores, TFLOP/s
-FLUSH_BYTES = 512 << 20      # written between timed steps: twice the 256 MB Infinity Cache
+FLUSH_BYTES = 512 << 20      # read between timed steps: twice the 256 MB Infinity Cache
+
+
+def evict_caches(buf):
+    """Read `buf` (FLUSH_BYTES) on the current stream: every L2 and Infinity Cache line is then one of its
+    clean lines, so the next kernel's data comes from HBM and no dirty flush data is written back meanwhile."""
+    buf.sum()
 
 
 def cpu_model():
@@ -237,13 +243,29 @@ def run_decode(lib, _lib, dev, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    # the same steps with FLUSH_BYTES read before each (outside its events): no state line can come
+    # from the Infinity Cache, so this time is the HBM-served one
+    flush = torch.ones(FLUSH_BYTES // 4, device=dev)
+    S.copy_(dd["S0"])
+    nfl = 32
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nfl)]
+    for t in range(nfl):
+        evict_caches(flush)
+        ev[t][0].record(stream)
+        dstep(t)
+        ev[t][1].record(stream)
+    torch.cuda.synchronize()
+    us_fl = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / nfl
     byt = decode_bytes(c3["B"], c3["H"], c3["Dk"])
     gbs = byt / (us / 1e6) / 1e9
     return {"workload": "one-token decode, B=256 H=16 d=128, fp32 state 256x16x128x128, "
                         "bf16 token inputs, 128 consecutive steps",
             "us_per_step": round(us, 2), "tokens_per_s": round(c3["B"] / (us / 1e6), 1),
             "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-            "algorithmic_bytes_per_step": int(byt)}
+            "algorithmic_bytes_per_step": int(byt),
+            "flushed_us_per_step": round(us_fl, 2),
+            "flushed_hbm_frac": round(byt / (us_fl / 1e6) / 1e9 / PEAK_HBM_GBS, 4),
+            "flushed_note": f"{nfl} steps, each after {FLUSH_BYTES >> 20} MiB read (Infinity Cache evicted)"}
 
 
 def main():
@@ -308,7 +330,7 @@ def main():
     d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev)
-    flush = None if args.no_flush else torch.empty(FLUSH_BYTES // 4, device=dev)
+    flush = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, device=dev)
 
     # preallocated outputs and workspace: the timed region only launches kernels
     NC = (T + C - 1) // C
@@ -373,7 +395,7 @@ def main():
 
     def timed_pair(f, b, n, warm, fl=None):
         """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream).
-        With fl, the buffer fl is written before every step, outside the step's events."""
+        With fl, the buffer fl is read before every step (evict_caches), outside the step's events."""
         for _ in range(warm):
             f()
             b()
@@ -392,7 +414,7 @@ def main():
             return tf, tb, ev[0].elapsed_time(ev[-1]) / n
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         for i in range(n):
-            fl.fill_(float(i))
+            evict_caches(fl)
             ev[i][0].record(stream)
             f()
             ev[i][1].record(stream)
@@ -404,14 +426,14 @@ def main():
         return tf, tb, tf + tb
 
     def timed_flushed(fn, n=10, warm=3):
-        """Average ms of fn over n calls, the flush buffer written before each (outside the events)."""
+        """Average ms of fn over n calls, the flush buffer read before each (outside the events)."""
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for i in range(n):
             if flush is not None:
-                flush.fill_(float(i))
+                evict_caches(flush)
             ev[i][0].record(stream)
             fn()
             ev[i][1].record(stream)
@@ -469,7 +491,7 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": D, "d_v": D, "chunk": C,
                    "parallelism": "single GPU"},
         "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4), "fwd_single_pass_ms": round(t_fwd_single, 4),
-        "cache_flush": None if flush is None else f"{FLUSH_BYTES >> 20} MiB written before every timed step",
+        "cache_flush": None if flush is None else f"{FLUSH_BYTES >> 20} MiB read before every timed step",
         "ms_per_step_back_to_back": round(ms_step_nf, 4),
         "separate_calls": {"fwd_ms": round(s_fwd, 4), "bwd_ms": round(s_bwd, 4), "ms_per_step": round(s_step, 4),
                            "note": "gdn2_fwd_chunked + gdn2_bwd_chunked, each with its own record pass"},
