@@ -322,6 +322,9 @@ def main():
     # process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(inp, heads=16)
     cpu_pre = None if (args.no_cpu or pre is None) else cpu_baseline_prefill(pre, heads=16)
+    cpu_long = None
+    if not args.no_cpu and not args.no_curve:
+        cpu_long = cpu_baseline_prefill(synth.workload_inputs("fwd-long-B1-H16-d128", T=8192), heads=16)
     cpu_dec = None
     if not args.no_cpu and not args.no_decode:
         cpu_dec = cpu_baseline_decode(synth.workload_inputs("decode-B256-H16-d128-128steps"), steps=4)
@@ -682,15 +685,7 @@ def main():
                                           D, C, _lib.GDN2_BF16, sh)
                 _lib.check(st, "gdn2_fwd_chunked")
 
-            cf()
-            torch.cuda.synchronize()
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            for _ in range(3):
-                cf()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            ms = a0.elapsed_time(a1) / 3
+            ms = timed_flushed(cf, n=10, warm=2)
             byt = fwd_bytes(C, D, save_states=False) * Tc * 16
             gbs = byt / (ms / 1e3) / 1e9
             curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1),
@@ -698,6 +693,8 @@ def main():
                               "segments": _segments_from_workspace(lib, _lib, Tc, D, C)}
             del cd, ci
         out["fwd_long_sequence_curve"] = curve
+        if cpu_long is not None:
+            out["fwd_long_sequence_cpu_baseline"] = cpu_long
 
     if cpu is not None:
         out["cpu_baseline"] = cpu

@@ -1247,7 +1247,7 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
 template <int DK, int C, bool F32IN, bool RAW, bool GS, bool S16>
 __global__ __launch_bounds__(512) void gdn2_bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GradCfg<DK, C, F32IN>::kLdsBytes];
-  grad_chunk<DK, C, F32IN, RAW, GS, S16, false>(a, blockIdx.x, smem);
+  grad_chunk<DK, C, F32IN, RAW, GS, S16, false>(a, chunk_item_of_block(a.vl, a.T, a.H, C, blockIdx.x), smem);
 }
 
 // One wide-pass item as a called function, so that its register allocation does

@@ -92,6 +92,19 @@ __host__ __device__ inline int64_t chunk_items(const Varlen& vl, int B, int T, i
 }
 __host__ __device__ inline int seq_items(const Varlen& vl, int B, int H) { return (vl.cu ? vl.nseq : B) * H; }
 
+// The item (chunk_loc's index) that workgroup blk of a chunk-parallel pass takes: head fastest, so that the
+// workgroups in flight together read whole token rows of q, k, v, ... ([., T, H, D]: all heads of a token
+// are adjacent) instead of one head's slice of many rows.
+__device__ __forceinline__ int chunk_item_of_block(const Varlen& vl, int T, int H, int C, int blk) {
+  if (vl.cu == nullptr) {
+    const int NC = (T + C - 1) / C;
+    const int bi = blk / (NC * H), rem = blk - bi * (NC * H), n = rem / H, h = rem - n * H;
+    return (bi * H + h) * NC + n;
+  }
+  const int g = blk / H, h = blk - g * H;
+  return h * vl.max_chunks + g;
+}
+
 // Location of one (sequence, head) walked by a chain kernel: its chunks are
 // item0 .. item0 + nchunks - 1 in the chunk-indexed arrays, chunk n covers
 // tokens tok0 + n*C .. of length min(C, len - n*C); state index for S0/S_final.

@@ -714,7 +714,8 @@ template <int DK, int C, bool F32IN, int DIR>
 __global__ __launch_bounds__(512, 4) void gdn2_prep_kernel(FwdArgs a, char* rec_base, float* ut_base,
                                                             char* brec_base) {
   __shared__ __attribute__((aligned(16))) char smem[PrepCfg<DK, C, F32IN, DIR>::oBS];
-  prep_chunk<DK, C, F32IN, DIR, false>(a, rec_base, ut_base, brec_base, blockIdx.x, smem);
+  prep_chunk<DK, C, F32IN, DIR, false>(a, rec_base, ut_base, brec_base,
+                                       chunk_item_of_block(a.vl, a.T, a.H, C, blockIdx.x), smem);
 }
 
 // The chunks the record pass flagged as wide-decay, recomputed exactly. Workgroup w covers items
