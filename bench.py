@@ -268,6 +268,43 @@ def run_decode(lib, _lib, dev, stream):
             "flushed_note": f"{nfl} steps, each after {FLUSH_BYTES >> 20} MiB read (Infinity Cache evicted)"}
 
 
+def run_curve(lib, _lib, dev, sh, timed, Ts):
+    """The long-sequence forward (B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1), no chunk states) at
+    each T in Ts, timed by timed(fn) (ms). Few heads and long sequences: the two-level chain."""
+    import torch
+
+    import synth
+
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    D, C = 128, 64
+    # the long-sequence sweep: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk
+    # states) at each T.
+    # Few heads and long sequences: the two-stage forward takes the two-level chain here.
+    curve = {}
+    for Tc in Ts:
+        ci = synth.workload_inputs("fwd-long-B1-H16-d128", T=Tc)
+        cd = {k: v.to(dev) for k, v in ci.items()}
+        oc = torch.empty(1, Tc, 16, D, device=dev)
+        Sf = torch.empty(1, 16, D, D, device=dev)
+        nwc = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, Tc, 16, D, D, C, _lib.GDN2_BF16)
+        wc = torch.empty(max(nwc, 1), dtype=torch.uint8, device=dev)
+
+        def cf():
+            st = lib.gdn2_fwd_chunked(P(cd["q"]), P(cd["k"]), P(cd["v"]), P(cd["log_alpha"]), P(cd["b"]),
+                                      P(cd["w"]), P(cd["S0"]), P(oc), P(Sf), None, P(wc), nwc, 1, Tc, 16, D,
+                                      D, C, _lib.GDN2_BF16, sh)
+            _lib.check(st, "gdn2_fwd_chunked")
+
+        ms = timed(cf)
+        byt = fwd_bytes(C, D, save_states=False) * Tc * 16
+        gbs = byt / (ms / 1e3) / 1e9
+        curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1),
+                          "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "segments": _segments_from_workspace(lib, _lib, Tc, D, C)}
+        del cd, ci
+    return curve
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +320,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="no cache flush between timed training steps")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode section (for hardware-counter runs of the decode kernel)")
+    ap.add_argument("--curve-only", type=int, default=0, metavar="T",
+                    help="only the long-sequence forward at this T, 3 runs (for hardware-counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -307,6 +346,26 @@ def main():
 
     import synth
     from delta_rule_recurrent_gdn_amd import _lib
+
+    if args.curve_only:
+        dev = torch.device("cuda:0")
+        lib = _lib.load()
+        stream = torch.cuda.current_stream(dev)
+
+        def three(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 3
+
+        print(json.dumps({"fwd_long_sequence_curve": run_curve(lib, _lib, dev, stream.cuda_stream, three,
+                                                               [args.curve_only])}), flush=True)
+        return
 
     if args.decode_only:
         dev = torch.device("cuda:0")
@@ -667,31 +726,8 @@ def main():
             out["decode"]["cpu_baseline"] = cpu_dec
 
     if not args.no_curve:
-        # the long-sequence sweep: B=1, H=16, d=128, chunk 64, bf16, S0 ~ 0.02 N(0,1); forward (no chunk
-        # states) at each T.
-        # Few heads and long sequences: the two-stage forward takes the two-level chain here.
-        curve = {}
-        for Tc in synth.WORKLOADS["fwd-long-B1-H16-d128"]["T"]:
-            ci = synth.workload_inputs("fwd-long-B1-H16-d128", T=Tc)
-            cd = {k: v.to(dev) for k, v in ci.items()}
-            oc = torch.empty(1, Tc, 16, D, device=dev)
-            Sf = torch.empty(1, 16, D, D, device=dev)
-            nwc = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, Tc, 16, D, D, C, _lib.GDN2_BF16)
-            wc = torch.empty(max(nwc, 1), dtype=torch.uint8, device=dev)
-
-            def cf():
-                st = lib.gdn2_fwd_chunked(P(cd["q"]), P(cd["k"]), P(cd["v"]), P(cd["log_alpha"]), P(cd["b"]),
-                                          P(cd["w"]), P(cd["S0"]), P(oc), P(Sf), None, P(wc), nwc, 1, Tc, 16, D,
-                                          D, C, _lib.GDN2_BF16, sh)
-                _lib.check(st, "gdn2_fwd_chunked")
-
-            ms = timed_flushed(cf, n=10, warm=2)
-            byt = fwd_bytes(C, D, save_states=False) * Tc * 16
-            gbs = byt / (ms / 1e3) / 1e9
-            curve[str(Tc)] = {"ms": round(ms, 3), "tokens_per_s": round(Tc / (ms / 1e3), 1),
-                              "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                              "segments": _segments_from_workspace(lib, _lib, Tc, D, C)}
-            del cd, ci
+        curve = run_curve(lib, _lib, dev, sh, lambda fn: timed_flushed(fn, n=10, warm=2),
+                          synth.WORKLOADS["fwd-long-B1-H16-d128"]["T"])
         out["fwd_long_sequence_curve"] = curve
         if cpu_long is not None:
             out["fwd_long_sequence_cpu_baseline"] = cpu_long
