@@ -377,10 +377,10 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   };
   // fp16 entry states (S16): the key phase's rows of S0 and dS (this wave's
   // key-channel block, 8 value columns per lane group and step) are fetched
-  // right after the column phase's gathers, so that they arrive during the
-  // column phase instead of opening the key phase with a wait (not with
-  // per-head scalar gates, whose reductions leave no registers for them)
-  constexpr bool kEarly = S16 && !GS;
+  // as the column phase starts, so that they arrive during it instead of
+  // opening the key phase with a wait (with per-head scalar gates too: B8 H16
+  // T4096 KDA training step 2.43 -> 2.34 ms)
+  constexpr bool kEarly = S16;
   constexpr int kNStepE = kEarly ? Cfg::DVM / 32 : 1;
   f16x8 eS[kNStepE], eD[kNStepE];
   auto fetch_rows = [&]() {
