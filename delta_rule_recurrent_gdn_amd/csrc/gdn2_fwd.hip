@@ -89,12 +89,7 @@ struct FwdCfg {
   static constexpr int oUT = oWm + C * LDK * OPB;                  // OpT [BV][LDC]  U^T
   static constexpr int oXs = oUT + BV * LDC * OPB;                 // float inversion scratch
   static constexpr int endW = oXs + KS::kXsBytes;
-  // the fp32 state handed from the fast to the slow chunk loop: below sST if it fits there, else
-  // from the gate constants on (extending the allocation where needed); either way over buffers
-  // written only after the slow loop's first barrier
-  static constexpr int oSt = DK * BV * 4 <= oST ? 0 : oCH;
-  static constexpr int endSt = oSt + DK * BV * 4;
-  static constexpr int kLdsBytes = endF > endW ? (endF > endSt ? endF : endSt) : (endW > endSt ? endW : endSt);
+  static constexpr int kLdsBytes = endF > endW ? endF : endW;
   static constexpr bool kFits = kLdsBytes <= 160 * 1024;
 
   static constexpr int NUT = NB * (BV / 16);                       // U / O tiles
@@ -276,20 +271,21 @@ __device__ __forceinline__ void fwd_wide_chunk(const FwdArgs& a, int64_t baseK, 
 // FL: some gate option (pre-activation or per-head scalar gates) is on; without
 // it every gate-option branch of the loads folds away.
 //
-// The chunk loop of one workgroup from chunk n0. SLOW = false: from chunk 0 and
-// S0, with no code for wide-decay chunks: at the first one it leaves the fp32
-// state in LDS (sSt, over per-chunk buffers) and returns the chunk's index
-// (NC when the sequence is done). SLOW = true: from chunk n0 and the state in
-// sSt, every chunk on, the wide ones through fwd_wide_chunk -- reached only
-// through the called function below, so the fast loop keeps its registers.
-template <int DK, int C, int BV, bool F32IN, bool FL, bool SLOW>
-__device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) {
+// The chunk loop of one workgroup, from S0. EXACT = false: no code for
+// wide-decay chunks; a sequence that has one is computed to the end regardless
+// (its results from that chunk on are wrong) and marked by kWideMark in the
+// first value column of its last output row. EXACT = true (the second kernel):
+// only marked sequences, every chunk, the wide ones through fwd_wide_chunk; it
+// rewrites all of the sequence's outputs, the marked word included. Two kernels
+// rather than one with a second loop exit or a call: either costs the fast
+// loop's register allocation more spills than the rare sequence costs.
+template <int DK, int C, int BV, bool F32IN, bool FL, bool EXACT>
+__device__ __forceinline__ void fwd_chunks(const FwdArgs& a, char* smem) {
   using Cfg = FwdCfg<DK, C, BV, F32IN>;
   using KS = typename Cfg::KS;
   using OpT = typename Cfg::OpT;
   constexpr int NW = Cfg::kWaves, NB = Cfg::NB;
   constexpr int LDC = Cfg::LDC, LDK = Cfg::LDK, LDCF = Cfg::LDCF;
-  float* sSt = reinterpret_cast<float*>(smem + Cfg::oSt);  // [DK][BV] fp32 state between the two loops
   OpT* sKhT = reinterpret_cast<OpT*>(smem + Cfg::oKhT);
   OpT* sQs = reinterpret_cast<OpT*>(smem + Cfg::oQs);
   OpT* sKbT = reinterpret_cast<OpT*>(smem + Cfg::oKbT);
@@ -313,7 +309,7 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
   const int nbh = a.B * a.H;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int bh = (slot / nv) * 8 + xcd, vt = slot % nv;
-  if (bh >= nbh) return 0;
+  if (bh >= nbh) return;
   const int bi = bh / a.H, h = bh - bi * a.H;
   const int j0 = vt * BV;
   const int Dv = a.Dv, T = a.T, H = a.H;
@@ -322,6 +318,12 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
   const int64_t baseK = ((int64_t)bi * T * H + h) * DK;
   const int64_t baseV = ((int64_t)bi * T * H + h) * Dv + j0;
   const int64_t stBase = (int64_t)bh * DK * Dv + j0;
+  // the mark: the first value column of this workgroup's tile in the sequence's last output row
+  const int64_t mark = baseV + (int64_t)(T - 1) * rowV;
+  if constexpr (EXACT) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(__float_as_uint(a.o[mark]));
+    if (m != kWideMark) return;
+  }
 
   KS ks;
   ks.init(tid);
@@ -357,10 +359,7 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
     accS[i] = zero4();
     if (t < Cfg::NST) {
       const int cb = t / (BV / 16), jb = t % (BV / 16);
-      if (SLOW) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) accS[i][e] = sSt[(16 * cb + 4 * lg + e) * BV + 16 * jb + lr];
-      } else if (a.S0) {
+      if (a.S0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           accS[i][e] = a.S0[stBase + (int64_t)(16 * cb + 4 * lg + e) * Dv + 16 * jb + lr];
@@ -368,10 +367,10 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
       store_tile_t(sST + 16 * jb * LDK + 16 * cb, LDK, accS[i]);
     }
   }
-  load_chunk(n0);
+  load_chunk(0);
 
-  int nstop = NC;
-  for (int n = n0; n < NC; ++n) {
+  bool any_wide = false;
+  for (int n = 0; n < NC; ++n) {
     const int t0 = n * C;
     const int Lr = min(C, T - t0);
 
@@ -408,11 +407,8 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
     // gates() also reports a wide-decay chunk: on some channel the cumulative decay from the chunk
     // middle leaves the range that the middle-referenced factors can carry (gdn2_wide.h)
     const bool wide = ks.gates(sTot, sG, sCh);
-    if (!SLOW && wide) {  // the rest of the sequence is the slow loop's
-      nstop = n;
-      break;
-    }
-    if (SLOW && wide) {
+    if constexpr (!EXACT) any_wide = any_wide || wide;
+    if (EXACT && wide) {
       fwd_wide_chunk<DK, C, BV, F32IN, FL>(a, baseK, t0, Lr, smem);
     } else {
       // ---- (2)+(3a) factors and the Gram products A, P ----
@@ -507,19 +503,6 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
     }
   }
 
-  if (!SLOW && nstop < NC) {  // hand the fp32 state over to the slow loop
-#pragma unroll
-    for (int i = 0; i < Cfg::SPW; ++i) {
-      const int t = wid + NW * i;
-      if (t < Cfg::NST) {
-        const int cb = t / (BV / 16), jb = t % (BV / 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sSt[(16 * cb + 4 * lg + e) * BV + 16 * jb + lr] = accS[i][e];
-      }
-    }
-    __syncthreads();
-    return nstop;
-  }
   if (a.S_final) {
 #pragma unroll
     for (int i = 0; i < Cfg::SPW; ++i) {
@@ -532,22 +515,25 @@ __device__ __forceinline__ int fwd_chunks(const FwdArgs& a, char* smem, int n0) 
       }
     }
   }
-  return NC;
-}
-
-// The slow loop as a called function (its registers do not add to the fast loop's). The arguments
-// are taken by value: a reference would make the kernel keep its own copy in private memory.
-template <int DK, int C, int BV, bool F32IN, bool FL>
-__device__ __attribute__((noinline)) void fwd_chunks_slow(FwdArgs a, char* smem, int n0) {
-  fwd_chunks<DK, C, BV, F32IN, FL, true>(a, smem, n0);
+  if constexpr (!EXACT) {
+    if (any_wide) {  // after every wave's stores of the last row
+      __syncthreads();
+      if (tid == 0) a.o[mark] = __uint_as_float(kWideMark);
+    }
+  }
 }
 
 template <int DK, int C, int BV, bool F32IN, bool FL>
 __global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_kernel(FwdArgs a) {
-  using Cfg = FwdCfg<DK, C, BV, F32IN>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::kLdsBytes];
-  const int n = fwd_chunks<DK, C, BV, F32IN, FL, false>(a, smem, 0);
-  if (n < (a.T + C - 1) / C) fwd_chunks_slow<DK, C, BV, F32IN, FL>(a, smem, n);
+  __shared__ __attribute__((aligned(16))) char smem[FwdCfg<DK, C, BV, F32IN>::kLdsBytes];
+  fwd_chunks<DK, C, BV, F32IN, FL, false>(a, smem);
+}
+
+// The sequences that the kernel above marked, recomputed exactly.
+template <int DK, int C, int BV, bool F32IN, bool FL>
+__global__ __launch_bounds__(kFwdThreads) void gdn2_fwd_exact_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[FwdCfg<DK, C, BV, F32IN>::kLdsBytes];
+  fwd_chunks<DK, C, BV, F32IN, FL, true>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -561,10 +547,19 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int nv = a.Dv / BV;
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * nv;
-    if (a.raw_gates || a.scalar_b || a.scalar_w || a.scalar_decay)
+    if (a.raw_gates || a.scalar_b || a.scalar_w || a.scalar_decay) {
       hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN, true>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
-    else
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gdn2_fwd_exact_kernel<DK, C, BV, F32IN, true>), dim3(grid), dim3(kFwdThreads), 0, stream,
+                         a);
+    } else {
       hipLaunchKernelGGL((gdn2_fwd_kernel<DK, C, BV, F32IN, false>), dim3(grid), dim3(kFwdThreads), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gdn2_fwd_exact_kernel<DK, C, BV, F32IN, false>), dim3(grid), dim3(kFwdThreads), 0, stream,
+                         a);
+    }
     return hipGetLastError();
   }
 }

@@ -39,6 +39,9 @@ constexpr float kWideSpan = 60.f;
 // at a time, in parallel
 constexpr int kWideGrid = 256;
 constexpr int kWideBatch = 64;
+// the single-pass forward's mark of a sequence that met a wide chunk: a quiet NaN with a payload that
+// no arithmetic produces (an input NaN carrying it only makes the sequence recompute, exactly)
+constexpr uint32_t kWideMark = 0x7fc0d1deu;
 
 // NaN stays NaN (an fmaxf would replace it)
 __device__ __forceinline__ float la_floor(float x) { return x < kLaFloor ? kLaFloor : x; }
