@@ -242,8 +242,8 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   const int bCs = scalar_b ? 0 : 1;
   const int64_t wBase = scalar_w ? baseS : baseV, wRow = scalar_w ? H : rowV;
   const int wCs = scalar_w ? 0 : 1;
-  // the column phase's gathers (this wave's 16 value columns: rows of S0 and dS in operand slots, dO,
-  // v, w) are issued here as well, ahead of the record units, so that one memory latency covers both
+  // the column phase's gathers of dO, v and w (this wave's 16 value columns) are issued here as well,
+  // ahead of the record units, so that one memory latency covers both
   using Fr = Frag<F32IN>;
   constexpr int KU = Fr::KU, UKd = Fr::units(DK), UCc = Fr::units(C), RC = C / 16;
   using RhsT = typename std::conditional<F32IN, f32x4, f16x8>::type;
@@ -253,14 +253,6 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   float s0r[UKd][NE], dsr[UKd][NE];
   InT dor[UCc][NE], vr[RC][4], wr[RC][4];
   if (16 * wid < Dv) {
-#pragma unroll
-    for (int u = 0; u < UKd; ++u)
-#pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        const int d = KU * u + Fr::kslot(lg, j);
-        s0r[u][j] = ld_sel(S0g, (int64_t)d * Dv + jc, jc, d < DK);
-        dsr[u][j] = ld_sel(dSg, (int64_t)d * Dv + jc, jc, d < DK);
-      }
 #pragma unroll
     for (int u = 0; u < UCc; ++u)
 #pragma unroll
@@ -396,6 +388,15 @@ __device__ __forceinline__ void grad_chunk(const BwdArgs& a, int item, char* sme
   };
   if (16 * wid >= Dv) fetch_rows();  // a wave with no value columns
   if (16 * wid < Dv) {
+    // S0 and dS in operand slots, then the key phase's rows of the same lines (read from L2)
+#pragma unroll
+    for (int u = 0; u < UKd; ++u)
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        const int d = KU * u + Fr::kslot(lg, j);
+        s0r[u][j] = ld_sel(S0g, (int64_t)d * Dv + jc, jc, d < DK);
+        dsr[u][j] = ld_sel(dSg, (int64_t)d * Dv + jc, jc, d < DK);
+      }
     fetch_rows();
     __builtin_amdgcn_sched_barrier(0);
     RhsT s0f[UKd], dsf[UKd], dof[UCc];
