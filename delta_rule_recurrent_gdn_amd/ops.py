@@ -109,6 +109,36 @@ def gdn2_fwd_chunked(q, k, v, log_alpha, b, w, S0=None, chunk=64, want_final_sta
     return o, S_final, states
 
 
+def gdn2_fwd_chunked_noalloc(q, k, v, log_alpha, b, w, o, S0=None, S_final=None, chunk_states=None, chunk=64):
+    """gdn2_fwd_chunked_noalloc: the two-stage forward with its workspace in the library's own device array
+    (GDN2_NOALLOC_SCRATCH_BYTES per GPU), for callers that cannot allocate. Every output is the caller's:
+    o [B, T, H, Dv] fp32, and S_final [B, H, Dk, Dv] / chunk_states [B, H, NC, Dk, Dv] fp32 when given. Sizes
+    whose forward workspace exceeds the array raise (GDN2_ERR_WORKSPACE). Calls that overlap on one GPU race.
+    Returns (o, S_final, chunk_states)."""
+    lib = _lib.load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check_inputs(("q", "k", "b"), (q, k, b), q.dtype, dev)
+    _check_inputs(("v", "w"), (v, w), q.dtype, dev)
+    _check_inputs(("log_alpha",), (log_alpha,), torch.float32, dev)
+    NC = (T + chunk - 1) // chunk
+    for n, t, shp in (("k", k, (B, T, H, Dk)), ("b", b, (B, T, H, Dk)), ("log_alpha", log_alpha, (B, T, H, Dk)),
+                      ("v", v, (B, T, H, Dv)), ("w", w, (B, T, H, Dv)), ("o", o, (B, T, H, Dv)),
+                      ("S_final", S_final, (B, H, Dk, Dv)), ("chunk_states", chunk_states, (B, H, NC, Dk, Dv))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
+    for n, t in (("o", o), ("S_final", S_final), ("chunk_states", chunk_states)):
+        if t is not None and (t.dtype != torch.float32 or t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous float32 tensor on {dev}")
+    S0 = _f32_state(S0, "S0", dev, (B, H, Dk, Dv))
+    st = lib.gdn2_fwd_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                      _ptr(o), _ptr(S_final), _ptr(chunk_states), B, T, H, Dk, Dv, chunk,
+                                      _dtype_code(q.dtype), _stream(dev))
+    _lib.check(st, "gdn2_fwd_chunked_noalloc")
+    return o, S_final, chunk_states
+
+
 def gdn2_decode_step(q, k, v, log_alpha, b, w, S, o=None, raw_gates=False, scalar_b=False, scalar_w=False,
                      scalar_decay=False):
     """One decode step; S ([B,H,Dk,Dv] fp32) is updated in place. Returns o [B,H,Dv] fp32.

@@ -81,3 +81,18 @@ def test_noalloc_rejects_sizes_beyond_the_array():
     st = lib.gdn2_fwd_chunked_noalloc(*([_p(x)] * 10), B, T, H, D, D, C, _lib.GDN2_BF16,
                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == _lib.GDN2_ERR_WORKSPACE
+
+
+def test_noalloc_python_binding():
+    """The binding with caller-owned outputs: same bits as gdn2_fwd_chunked with its own workspace."""
+    from delta_rule_recurrent_gdn_amd import gdn2_fwd_chunked, gdn2_fwd_chunked_noalloc
+
+    inp = synth.make_inputs(1, 3 * 64 + 9, 2, 64, 64, "bf16", seed=74, s0_std=0.3)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o = torch.empty(1, 3 * 64 + 9, 2, 64, device="cuda")
+    S = torch.empty(1, 2, 64, 64, device="cuda")
+    gdn2_fwd_chunked_noalloc(*x, o, S0=d["S0"], S_final=S, chunk=64)
+    o_ref, S_ref, _ = gdn2_fwd_chunked(*x, d["S0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
