@@ -442,19 +442,6 @@ def main():
                                   B, T, H, D, D, C, _lib.GDN2_BF16, sh)
         _lib.check(st, "gdn2_bwd_chunked")
 
-    def timed_ms(fn, n=10, warm=3):
-        """Average ms of fn over n calls after warm untimed ones (HIP events on the launch stream)."""
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
     def timed_pair(f, b, n, warm, fl=None):
         """Average ms of f, of b and of the whole step over n steps (HIP events on the launch stream).
         With fl, the buffer fl is read before every step (evict_caches), outside the step's events."""
@@ -508,14 +495,7 @@ def main():
     _, _, ms_step_nf = timed_pair(fwd, bwd, min(args.steps, 10), 1) if flush is not None else (0, 0, ms_step)
     s_fwd, s_bwd, s_step = timed_pair(fwd_sep, bwd_sep, min(args.steps, 10), 1, flush)
     # the single-pass forward (no workspace), timed on its own for comparison
-    fwd_sep(single_pass=True)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
-        fwd_sep(single_pass=True)
-    s1.record(stream)
-    torch.cuda.synchronize()
-    t_fwd_single = s0.elapsed_time(s1) / args.steps
+    t_fwd_single = timed_flushed(lambda: fwd_sep(single_pass=True), n=min(args.steps, 10))
     tokens = B * T
     value = tokens / (ms_step / 1e3)
 
@@ -626,7 +606,7 @@ def main():
 
         fe = {}
         for name, fn in (("fused_ms_per_step", raw_step), ("unfused_ms_per_step", unfused_step)):
-            fe[name] = round(timed_ms(fn), 4)
+            fe[name] = round(timed_flushed(fn), 4)
         fe["fused_tokens_per_s"] = round(tokens / (fe["fused_ms_per_step"] / 1e3), 1)
         fe["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with pre-activation gates b, w "
                           "(bf16) and a (fp32); unfused = torch sigmoid / softplus passes before and chain-rule "
@@ -651,7 +631,7 @@ def main():
         SB, SW, SD = _lib.GDN2_FLAG_SCALAR_B, _lib.GDN2_FLAG_SCALAR_W, _lib.GDN2_FLAG_SCALAR_DECAY
         for name, flags, la in (("kda_ms_per_step", SB | SW, d["log_alpha"]),
                                 ("gated_deltanet_ms_per_step", SB | SW | SD, adec)):
-            gg[name] = round(timed_ms(lambda: scalar_step(flags, la)), 4)
+            gg[name] = round(timed_flushed(lambda: scalar_step(flags, la)), 4)
         gg["channel_wise_ms_per_step"] = round(ms_step, 4)
         gg["workload"] = ("the B=8 H=16 T=4096 training step (training pair) with per-head scalar gates: KDA = "
                           "one beta [B,T,H] for both gates, Gated DeltaNet = also a scalar decay [B,T,H]; "
@@ -711,7 +691,7 @@ def main():
 
         vt = {}
         for name, fn in (("pair", varlen_pair_step), ("separate", varlen_step)):
-            vt[name] = timed_ms(fn)
+            vt[name] = timed_flushed(fn)
         vms = vt["pair"]
         out["varlen"] = {"workload": f"packed batch of {N} sequences (lengths uniform 256..8192, seed 5) totalling "
                                      f"{B * T} tokens, H=16 d=128 chunk 64 bf16: training step "
