@@ -412,11 +412,12 @@ def main():
     ws_br = torch.empty(need_br, dtype=torch.uint8, device=dev)
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     sh = stream.cuda_stream
+    launch = {"sh": sh}  # the stream the step's calls launch on (a capture stream while a graph is captured)
 
     def fwd(flags=0, x=d):
         st = lib.gdn2_fwd_chunked_train(P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["b"]), P(x["w"]),
                                         None, P(o), None, P(recs), need_r, P(ws_f), need_f, B, T, H, D, D, C,
-                                        _lib.GDN2_BF16, flags, sh)
+                                        _lib.GDN2_BF16, flags, launch["sh"])
         _lib.check(st, "gdn2_fwd_chunked_train")
 
     def bwd(flags=0, x=d, gb=None, gw=None, gla=None):
@@ -425,7 +426,7 @@ def main():
                                           P(grads["dk"]), P(grads["dv"]), P(grads["dlog_alpha"] if gla is None else gla),
                                           P(grads["db"] if gb is None else gb), P(grads["dw"] if gw is None else gw),
                                           P(dS0), P(ws_br), need_br,
-                                          B, T, H, D, D, C, _lib.GDN2_BF16, flags, sh)
+                                          B, T, H, D, D, C, _lib.GDN2_BF16, flags, launch["sh"])
         _lib.check(st, "gdn2_bwd_chunked_records")
 
     # the separate entry points (each call with its own record pass), for comparison
@@ -496,6 +497,19 @@ def main():
     s_fwd, s_bwd, s_step = timed_pair(fwd_sep, bwd_sep, min(args.steps, 10), 1, flush)
     # the single-pass forward (no workspace), timed on its own for comparison
     t_fwd_single = timed_flushed(lambda: fwd_sep(single_pass=True), n=min(args.steps, 10))
+    # the same training step captured once in a HIP graph and replayed (no allocation, synchronisation or
+    # memset inside it): the launch overhead of its kernels removed
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        launch["sh"] = torch.cuda.current_stream().cuda_stream
+        fwd()
+        bwd()
+    launch["sh"] = sh
+    torch.cuda.synchronize()
+    ms_graph = timed_flushed(graph.replay, n=min(args.steps, 10))
+    ms_graph_nf = timed_pair(graph.replay, lambda: None, min(args.steps, 10), 2)[2]
+    del graph
     tokens = B * T
     value = tokens / (ms_step / 1e3)
 
@@ -535,6 +549,7 @@ def main():
         "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4), "fwd_single_pass_ms": round(t_fwd_single, 4),
         "cache_flush": None if flush is None else f"{FLUSH_BYTES >> 20} MiB read before every timed step",
         "ms_per_step_back_to_back": round(ms_step_nf, 4),
+        "graph_ms_per_step": round(ms_graph, 4), "graph_ms_per_step_back_to_back": round(ms_graph_nf, 4),
         "separate_calls": {"fwd_ms": round(s_fwd, 4), "bwd_ms": round(s_bwd, 4), "ms_per_step": round(s_step, 4),
                            "note": "gdn2_fwd_chunked + gdn2_bwd_chunked, each with its own record pass"},
         "mfma_frac": round(mfma, 4),
