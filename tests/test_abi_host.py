@@ -251,3 +251,19 @@ def test_packed_training_pair_sizes_and_argument_errors():
         assert call(ws_bytes=need - 1) == _lib.GDN2_ERR_WORKSPACE
         assert call(rec=A + 16) == _lib.GDN2_ERR_ALIGN
         assert call(N=0) == _lib.GDN2_OK
+
+
+def test_noalloc_array_size_matches_header_and_refuses_oversize():
+    """GDN2_NOALLOC_SCRATCH_BYTES agrees between the header and the binding, and sizes whose forward workspace
+    exceeds it are refused on the host, before any device call (the pointers are never dereferenced)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+GDN2_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*\*\s*(\d+)u\s*\*\s*(\d+)u\)", text)
+    assert m, "the header defines the array size"
+    size = int(m.group(1)) * int(m.group(2)) * int(m.group(3))
+    assert size == _lib.GDN2_NOALLOC_SCRATCH_BYTES
+    lib = _lib.load()
+    B, T, H, D, C = 8, 4096, 16, 128, 64
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, _lib.GDN2_BF16) > size
+    fake = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never dereferenced
+    st = lib.gdn2_fwd_chunked_noalloc(*([fake] * 10), B, T, H, D, D, C, _lib.GDN2_BF16, None)
+    assert st == _lib.GDN2_ERR_WORKSPACE
