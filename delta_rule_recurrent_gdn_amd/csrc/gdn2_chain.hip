@@ -64,6 +64,26 @@ constexpr int kChainHelpers = 2;
 // vmcnt = 0, expcnt and lgkmcnt unconstrained)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Two-level chain: waves (of 16 value columns) per workgroup of the map and run passes. With four the
+// passes need twice the workgroups at one per CU, and the map pass a second round (B1 H16 T64K forward
+// 1.74 -> 1.85 ms).
+constexpr int kSegWaves = 8;
+
+// Segment slot and column group of a workgroup of the two-level chain's passes. The column groups of one
+// segment take workgroups 8 apart, so that they run on one XCD and read each record through its L2 once
+// (B1 H16 T64K forward 1.77 -> 1.74 ms); -1 past the last slot (the grid is rounded up to whole groups of
+// 8). Slots: dense, (batch*head, s) with s < nseg (map pass: nseg - 1); packed, (head, global segment).
+__device__ __forceinline__ int seg_block_item(const Varlen& vl, const SegArgs& sg, int nbh, int H, int ncg,
+                                              int& cg) {
+  const int nitems = vl.cu == nullptr ? nbh * (sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg) : H * vl.max_segs;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int item = (slot / ncg) * 8 + xcd;
+  cg = slot - (slot / ncg) * ncg;
+  return item < nitems ? item : -1;
+}
+// Workgroups of a two-level pass over `items` slots of ncg column groups each.
+inline unsigned seg_grid(int64_t items, int ncg) { return (unsigned)(((items + 7) / 8) * 8 * ncg); }
+
 // NHW helper waves: waves past the NWV column waves own no columns and only
 // copy the next record into LDS (used by the plain reverse chain; see
 // kChainHelpers).
@@ -96,8 +116,8 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
     // (batch*head, s), s < nseg (map pass: s < nseg - 1); packed sequences:
     // (head, global segment), a sequence's last segment skipped by the map pass.
     const int ncg = ((sg.mode == kSegMap ? Dv + DK : Dv) + Cfg::kCols - 1) / Cfg::kCols;
-    const int item = blockIdx.x / ncg;
-    cg = blockIdx.x - item * ncg;
+    const int item = seg_block_item(a.vl, sg, nbh, H, ncg, cg);
+    if (item < 0) return;
     int local;
     if (a.vl.cu == nullptr) {
       const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
@@ -468,8 +488,8 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_bwd_kernel(BwdArg
     // block -> (segment, column group) as in the forward's segmented chain, except that the map
     // pass covers every segment but the FIRST of each (batch row or sequence, head)
     const int ncg = ((sg.mode == kSegMap ? Dv + DK : Dv) + kCols - 1) / kCols;
-    const int item = blockIdx.x / ncg;
-    cg = blockIdx.x - item * ncg;
+    const int item = seg_block_item(a.vl, sg, nbh, H, ncg, cg);
+    if (item < 0) return;
     int local;
     if (a.vl.cu == nullptr) {
       const int nsb = sg.mode == kSegMap ? sg.nseg - 1 : sg.nseg;
@@ -935,7 +955,7 @@ size_t fwd_seg_bytes(int B, int H, int T, int Dk, int Dv, int chunk) {
 template <int DK, int C, bool F32IN>
 static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const float* ut, char* seg, int G,
                                    hipStream_t s) {
-  using Cfg = ChainCfg<DK, C, F32IN, 1, 8>;  // 8 waves of 16 columns
+  using Cfg = ChainCfg<DK, C, F32IN, 1, kSegWaves>;
   if constexpr (!Cfg::kFits) {
     return hipErrorInvalidConfiguration;
   } else {
@@ -954,8 +974,8 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     // (1) maps of every segment but the last of each (batch row or sequence, head)
     sg.mode = kSegMap;
     const int64_t map_items = packed ? slots : (int64_t)nbh * (G - 1);
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(map_items * ncg_map)),
-                       dim3(512), 0, s, a, rec, ut, sg);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, kSegWaves, true>), dim3(seg_grid(map_items, ncg_map)),
+                       dim3(Cfg::kThreads), 0, s, a, rec, ut, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments
@@ -965,8 +985,8 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     if (e != hipSuccess) return e;
     // (3) every segment from its true entry state
     sg.mode = kSegRun;
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(slots * ncg_run)),
-                       dim3(512), 0, s, a, rec, ut, sg);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, kSegWaves, true>), dim3(seg_grid(slots, ncg_run)),
+                       dim3(Cfg::kThreads), 0, s, a, rec, ut, sg);
     return hipGetLastError();
   }
 }
@@ -983,11 +1003,13 @@ static hipError_t launch_chain_c(const FwdArgs& a, const char* rec, const float*
     }
   }
   if (a.Dv == 16) return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);
-  // 64 columns per workgroup, over four waves (one per SIMD), while that keeps >= 256 workgroups (two
-  // waves of 32 columns: 0.89 -> 0.84 ms for the B8 H16 T4096 training forward); else 32 columns per
-  // one-wave workgroup, or 16 for few heads
+  // 64 columns per workgroup, over four waves (one per SIMD), from 64 workgroups up (two waves of 32
+  // columns: 0.89 -> 0.84 ms for the B8 H16 T4096 training forward); else 32 columns per one-wave
+  // workgroup, or 16 for few heads. The two record buffers hold a CU's LDS, so every shape runs one
+  // workgroup per CU: narrower workgroups past 256 of them take a second round of the whole walk (B7 H16
+  // T4096 training step 2.73 -> 2.03 ms, B3 1.54 -> 1.13 ms with four-wave workgroups from 64 up)
   const int tiles = a.Dv / 32;  // 32-column tiles per head
-  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_t<DK, C, F32IN, 1, 4>(a, rec, ut, s);
+  if (tiles >= 2 && nbh * (tiles / 2) >= 64) return launch_chain_t<DK, C, F32IN, 1, 4>(a, rec, ut, s);
   if (nbh * tiles >= 256) return launch_chain_t<DK, C, F32IN, 2, 1>(a, rec, ut, s);
   return launch_chain_t<DK, C, F32IN, 1, 1>(a, rec, ut, s);  // few heads: 16 columns per workgroup
 }
@@ -1038,7 +1060,7 @@ static hipError_t launch_chain_bwd_t(const BwdArgs& a, const char* rec, hipStrea
 template <int DK, int C, bool F32IN>
 static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* seg, int G, hipStream_t s) {
   using Rec = Record<DK, C, F32IN, 1>;
-  constexpr int kCols = 16 * 8;  // 8 waves of 16 columns
+  constexpr int kCols = 16 * kSegWaves;
   if constexpr (Rec::kChainBytes > 160 * 1024) {
     return hipErrorInvalidConfiguration;
   } else {
@@ -1055,8 +1077,8 @@ static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* 
     // (1) maps of every segment but the first of each (batch row or sequence, head)
     sg.mode = kSegMap;
     const int64_t map_items = packed ? slots : (int64_t)nbh * (G - 1);
-    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(map_items * ncg_map)),
-                       dim3(512), 0, s, a, rec, sg);
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, kSegWaves, true>), dim3(seg_grid(map_items, ncg_map)),
+                       dim3(kSegWaves * kWave), 0, s, a, rec, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) exit gradients of the earlier segments, composed backwards from dS_final
@@ -1066,8 +1088,8 @@ static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* 
     if (e != hipSuccess) return e;
     // (3) every segment from its true exit gradient
     sg.mode = kSegRun;
-    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, 8, true>), dim3((unsigned)(slots * ncg_run)),
-                       dim3(512), 0, s, a, rec, sg);
+    hipLaunchKernelGGL((gdn2_chain_bwd_kernel<DK, C, F32IN, 1, kSegWaves, true>), dim3(seg_grid(slots, ncg_run)),
+                       dim3(kSegWaves * kWave), 0, s, a, rec, sg);
     return hipGetLastError();
   }
 }
@@ -1085,7 +1107,7 @@ static hipError_t launch_chain_bwd_c(const BwdArgs& a, const char* rec, char* se
   // workgroup shapes as in the forward chain (four waves of 16 columns: 1.44 -> 1.39 ms for the B8 H16
   // T4096 backward), plus the helper waves
   const int tiles = a.Dv / 32;
-  if (tiles >= 2 && nbh * (tiles / 2) >= 256) return launch_chain_bwd_t<DK, C, F32IN, 1, 4>(a, rec, s);
+  if (tiles >= 2 && nbh * (tiles / 2) >= 64) return launch_chain_bwd_t<DK, C, F32IN, 1, 4>(a, rec, s);
   if (nbh * tiles >= 256) return launch_chain_bwd_t<DK, C, F32IN, 2, 1>(a, rec, s);
   return launch_chain_bwd_t<DK, C, F32IN, 1, 1>(a, rec, s);
 }

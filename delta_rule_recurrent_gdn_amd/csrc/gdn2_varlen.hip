@@ -95,17 +95,20 @@ __global__ __launch_bounds__(kPlanThreads) void gdn2_varlen_plan_kernel(const in
 
 int varlen_max_chunks(int N, int T, int C) { return T / C + N; }
 
-// Two-level chain inside packed sequences: used when the (sequence, head)
-// chains alone have too few 32-column wave tiles to fill the GPU and the
-// batch holds at least 32 chunks; L chunks per segment, sized so that the
-// run pass has about 128 workgroups at T / C chunks, at least 8 (as the dense
-// two-level chain: 3.09 -> 2.90 ms for the 7-document B8 H16 T4096-token
-// training step; 64 workgroups: 2.96 ms). The segment machinery (compose
-// kernel) needs Dv >= 32.
+// Two-level chain inside packed sequences: used, as for dense batches, only when
+// there are at most 32 (sequence, head) chains of 128 value columns (the plain
+// chain's four-wave workgroups cannot fill a quarter of the GPU) and the batch
+// holds at least 32 chunks; L chunks per segment, sized so that the run pass
+// has about 128 workgroups at T / C chunks, at least 8. Past 32 chains the
+// plain chain wins although it walks the longest sequence whole: the map pass
+// and the composition cost more than the walk saves unless one sequence is
+// several times the others (7-document B8 H16 T4096-token training step:
+// 3.22 -> 2.87 ms without segments; one 16K and four 4K documents: 3.25 ->
+// 3.70 ms). The segment machinery (compose kernel) needs Dv >= 32.
 int varlen_seg_len(int N, int T, int H, int Dk, int Dv, int C) {
   (void)Dk;
   const long nc = T / C;
-  if (Dv < 32 || nc < 32 || (long)N * H * (Dv / 32) >= 512) return 0;
+  if (Dv < 32 || nc < 32 || (long)N * H * ((Dv + 127) / 128) > 32) return 0;
   long L = (nc * H * ((Dv + 127) / 128) + 127) / 128;
   return (int)(L < 8 ? 8 : L);
 }

@@ -3,8 +3,8 @@
 The B = 8, H = 16, d = 128, chunk 64 launches (the training step's chain placement over 128 (batch, head)
 pairs, the XCD-aware workgroup order, four-wave chains) run here at a reduced sequence length with a ragged
 tail, and every (batch, head) pair is compared with the oracle: the two-stage and single-pass forwards, the
-training pair and the separate backward, all seven gradients. The decode batch (256 sequences x 16 heads)
-is compared on every sequence for a few steps.
+training pair and the separate backward, all seven gradients; so do B = 5, H = 13, whose chains fill only
+part of the GPU. The decode batch (256 sequences x 16 heads) is compared on every sequence for a few steps.
 """
 
 import numpy as np
@@ -72,6 +72,33 @@ def test_backward_every_pair(geometry_case, path):
     for n in GRADS:
         e, at = _per_pair_worst(f64(g[n]), g_ref[n], state=n == "dS0")
         print(f"{path}: {n} worst pair {e:.2e} at {at}")
+        assert np.isfinite(f64(g[n])).all() and e <= TOL_GRAD, (n, e, at)
+
+
+@pytest.mark.parametrize("path", ["training-pair", "separate"])
+def test_partly_filled_chains_every_pair(path):
+    """B = 5, H = 13 (65 (batch, head) pairs, 130 four-wave chain workgroups: fewer than the CUs, the last
+    group of 8 ragged): every pair's o, S_final and gradients against the oracle."""
+    T = 2 * 64 + 9
+    inp = synth.make_inputs(5, T, 13, 128, 128, "bf16", seed=44, grad=True)
+    args = [inp[n] for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    o_ref, S_ref = oracle.forward(*args)
+    g_ref = oracle.backward(*args, None, inp["dO"])
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    if path == "training-pair":
+        o, S, rec = gdn2_fwd_chunked_train(*x, None, chunk=64)
+        g = gdn2_bwd_chunked_records(*x, d["dO"], rec, chunk=64)
+    else:
+        o, S, _ = gdn2_fwd_chunked(*x, None, chunk=64)
+        g = gdn2_bwd_chunked(*x, d["dO"], chunk=64)
+    torch.cuda.synchronize()
+    eo, at_o = _per_pair_worst(f64(o), o_ref)
+    es, at_s = _per_pair_worst(f64(S), S_ref, state=True)
+    print(f"{path}: worst pair o {eo:.2e} at {at_o}, S {es:.2e} at {at_s}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for n in GRADS:
+        e, at = _per_pair_worst(f64(g[n]), g_ref[n], state=n == "dS0")
         assert np.isfinite(f64(g[n])).all() and e <= TOL_GRAD, (n, e, at)
 
 

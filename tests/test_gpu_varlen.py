@@ -7,8 +7,9 @@ import torch
 
 import oracle
 import synth
-from delta_rule_recurrent_gdn_amd import (gdn2_bwd_varlen, gdn2_decode_step_slots, gdn2_fwd_chunked,
-                                          gdn2_fwd_varlen, gdn2_varlen_max_chunks)
+from delta_rule_recurrent_gdn_amd import (gdn2_bwd_varlen, gdn2_bwd_varlen_records, gdn2_decode_step_slots,
+                                          gdn2_fwd_chunked, gdn2_fwd_varlen, gdn2_fwd_varlen_train,
+                                          gdn2_varlen_max_chunks)
 from tests.helpers import TOL_BF16, TOL_F32, TOL_GRAD, f64, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -226,6 +227,33 @@ def test_varlen_two_level_chain(dtype, Dk, Dv):
     gtol = TOL_F32 if dtype == "fp32" else TOL_GRAD
     for n_ in GRADS:
         assert rel_err(f64(g1[n_]), ref[n_]) <= gtol, n_
+
+
+def test_varlen_past_32_chains_plain_walk():
+    """The lengths of the two-level test with 8 heads (48 (sequence, head) chains, at least 32 chunks): no
+    segments, the plain four-wave chains walk every sequence whole; forward, chunk states and the training
+    pair's gradients against the oracle."""
+    from delta_rule_recurrent_gdn_amd import _lib
+    lengths, C, H, D = [1500, 37, 900, 3, 0, 600], 64, 8, 128
+    N, T = len(lengths), int(sum(lengths))
+    lib = _lib.load()
+    mc = gdn2_varlen_max_chunks(N, T, C)
+    per_chunk = lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, C, 1, D, D, C, _lib.GDN2_BF16)
+    ws = lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_FWD, N, T, H, D, D, C, _lib.GDN2_BF16)
+    assert ws < H * mc * per_chunk + H * (D * D + 2 * D * D) * 4  # no segment maps
+    inp, cu = _packed(lengths, H, D, D, "bf16", seed=150, grad=True)
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o, S, rec = gdn2_fwd_varlen_train(*x, cu.cuda(), d["S0"], chunk=C)
+    g = gdn2_bwd_varlen_records(*x, d["dO"], cu.cuda(), rec, chunk=C)
+    torch.cuda.synchronize()
+    args = [inp[n] for n in ("q", "k", "v", "log_alpha", "b", "w")]
+    o_ref, S_ref = oracle.forward_varlen(*args, cu, inp["S0"])
+    assert rel_err(f64(o), o_ref) <= TOL_BF16 and rel_err(f64(S), S_ref) <= TOL_BF16
+    ref = oracle.backward_varlen(*args, cu, inp["S0"], inp["dO"])
+    for n in GRADS:
+        e = rel_err(f64(g[n]), ref[n])
+        assert e <= TOL_GRAD, (n, e)
 
 
 def test_varlen_many_sequences_four_wave_chains():
