@@ -126,7 +126,9 @@ __device__ __forceinline__ void fwd_wide_chunk(const FwdArgs& a, int64_t baseK, 
   float* sPS = reinterpret_cast<float*>(smem + Cfg::oPS);
   float* sAf = reinterpret_cast<float*>(smem + Cfg::oAf);
   OpT* sPm = reinterpret_cast<OpT*>(smem + Cfg::oPm);
-  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
+  // the wave index in a scalar register: per-wave branches and offsets stay scalar (B8 H16 T4096 single-pass
+  // forward 1.34 -> 1.24 ms, training forward 0.86 -> 0.84 ms)
+  const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
   const int H = a.H;
   const int64_t rowK = (int64_t)H * DK, baseS = baseK / DK;
@@ -301,7 +303,9 @@ __device__ __forceinline__ void fwd_chunks(const FwdArgs& a, char* smem) {
   OpT* sUT = reinterpret_cast<OpT*>(smem + Cfg::oUT);
   float* sXs = reinterpret_cast<float*>(smem + Cfg::oXs);
 
-  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
+  // the wave index in a scalar register: per-wave branches and offsets stay scalar (B8 H16 T4096 single-pass
+  // forward 1.34 -> 1.24 ms, training forward 0.86 -> 0.84 ms)
+  const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid & (kWave - 1);
   const int lr = l & 15, lg = l >> 4;
 
   // block -> (batch*head, value tile); the value tiles of one head share an XCD

@@ -132,7 +132,9 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, char* rec_base, flo
   OpT* sT1 = reinterpret_cast<OpT*>(smem + Cfg::oT1);
   OpT* sWVT = reinterpret_cast<OpT*>(smem + Cfg::oWVT);
 
-  const int tid = threadIdx.x, wid = tid / kWave, l = tid & (kWave - 1);
+  // the wave index in a scalar register: per-wave branches and offsets stay scalar (B8 H16 T4096 single-pass
+  // forward 1.34 -> 1.24 ms, training forward 0.86 -> 0.84 ms)
+  const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid & (kWave - 1);
 
   const int Dv = a.Dv, T = a.T, H = a.H;
   const int NC = (T + C - 1) / C;
