@@ -815,17 +815,21 @@ static hipError_t launch_chain_t(const FwdArgs& a, const char* rec, const float*
 
 // Composition of the segment maps: S_in(s+1) = M_s S_in(s) + N_s, S_in(0) = S0
 // (or zero), in fp32. One workgroup (4 waves) per (batch*head, 32 value
-// columns). S_in(s) lives in LDS; each step copies M_s into LDS with coalesced
-// loads (the next one already in registers) and forms the product on fp32
-// matrix cores, N_s as the initial accumulator: wave w owns row tiles 2w and
-// 2w+1 (times DK / 128) of both 16-column tiles.
+// columns); the column groups of one head take workgroups 8 apart (one XCD, so
+// M_s comes through its L2 once). S_in(s) lives in LDS; each step copies M_s
+// into LDS with coalesced loads and forms the product on fp32 matrix cores,
+// N_s as the initial accumulator: wave w owns row tiles 2w and 2w+1 (times
+// DK / 128) of both 16-column tiles. M_{s+1} and N_{s+1} are loaded into
+// registers during step s, so a step waits on no load issued in it (B1 H16
+// T64K forward 1.94 -> 1.89 ms; N had been loaded after the next M, so each
+// step waited for both).
 template <int DK>
 // reverse (the backward's exit gradients): S_in(s-1) = M_s S_in(s) + N_s from
 // S_in(count-1) = start (dS_final), empty sequences copying start to empty_out (dS0).
 // gscale (reverse, 16-bit inputs): start is dS_final, taken times grad_scale() as the reverse chain
 // takes it; an empty sequence's dS0 is written without the scale.
 __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
-                                                              Varlen vl, int H, int Dv, bool reverse,
+                                                              Varlen vl, int nbh, int H, int Dv, bool reverse,
                                                               const float* gscale) {
   constexpr int LDM = DK + 4, LDS_ = 32 + 4;
   constexpr int NM4 = DK * DK / 4;              // float4 of one M
@@ -835,7 +839,9 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   __shared__ __attribute__((aligned(16))) float sM[DK * LDM];
   __shared__ __attribute__((aligned(16))) float sS[DK * LDS_];
   const int ncg = Dv / 32;
-  const int bh = blockIdx.x / ncg, j0 = (blockIdx.x - bh * ncg) * 32;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int bh = (slot / ncg) * 8 + xcd, j0 = (slot - (slot / ncg) * ncg) * 32;
+  if (bh >= nbh) return;  // the grid is rounded up to whole groups of 8
   // this (batch row or sequence, head)'s segments: slots base .. base + count - 1 of M, N, S_in
   int64_t base;
   int count;
@@ -854,6 +860,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     sS[d * LDS_ + c] = S0 ? gsc * S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
   }
   float4 mr[MV];
+  float nr[RPW][2][4];  // N of the same segment at the lane's accumulator positions
   // step i reads the map of segment src(i) and writes the entry of the next one in walking order
   auto src = [&](int i) { return reverse ? count - 1 - i : i; };
   auto load_m = [&](int s) {
@@ -861,6 +868,16 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
 #pragma unroll
     for (int i = 0; i < MV; ++i)
       if (tid + 256 * i < NM4) mr[i] = M[tid + 256 * i];
+    const float* N = sg.N + (base + src(s)) * DK * Dv + j0;
+#pragma unroll
+    for (int t = 0; t < RPW; ++t) {
+      const int R = wid + 4 * t;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          nr[t][c][i] = R < RT ? N[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] : 0.f;
+    }
   };
   if (count == 0) {  // an empty packed sequence has no segment to carry its state: S_final = S0
     __syncthreads();
@@ -878,19 +895,15 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
       const int e = tid + 256 * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
       if (e < NM4) *reinterpret_cast<float4*>(sM + row * LDM + c4) = mr[i];
     }
-    __syncthreads();  // M_s and S_in(s) are in LDS
-    if (s + 2 < count) load_m(s + 1);
-    const float* N = sg.N + sb * DK * Dv + j0;
     f32x4 acc[RPW][2];
 #pragma unroll
-    for (int t = 0; t < RPW; ++t) {
-      const int R = wid + 4 * t;
+    for (int t = 0; t < RPW; ++t)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[t][c][i] = R < RT ? N[(int64_t)(16 * R + 4 * lg + i) * Dv + 16 * c + lr] : 0.f;
-    }
+        for (int i = 0; i < 4; ++i) acc[t][c][i] = nr[t][c][i];
+    __syncthreads();  // M_s and S_in(s) are in LDS
+    if (s + 2 < count) load_m(s + 1);
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
       const int R = wid + 4 * t;
@@ -979,8 +992,8 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments
-    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.S0, a.S_final, sg,
-                       a.vl, a.H, a.Dv, false, static_cast<const float*>(nullptr));
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(256), 0, s, a.S0,
+                       a.S_final, sg, a.vl, nbh, a.H, a.Dv, false, static_cast<const float*>(nullptr));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true entry state
@@ -1082,8 +1095,8 @@ static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) exit gradients of the earlier segments, composed backwards from dS_final
-    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(nbh * (a.Dv / 32)), dim3(256), 0, s, a.dS_final, a.dS0,
-                       sg, a.vl, a.H, a.Dv, true, a.gscale);
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(256), 0, s, a.dS_final,
+                       a.dS0, sg, a.vl, nbh, a.H, a.Dv, true, a.gscale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (3) every segment from its true exit gradient
