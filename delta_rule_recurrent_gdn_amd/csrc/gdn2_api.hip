@@ -56,11 +56,28 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32);
 
+// The chunk that the backward and training-pair kernels tile a sequence with: the
+// caller's, except where their LDS does not hold it (fp32 inputs at Dk = 128 with
+// chunk 64), where they run 32-token chunks. The chunk size only tiles the
+// recurrence: every size computes the same result up to rounding order.
+int bwd_chunk(int Dk, int chunk, bool f32) {
+  const auto fits = [&](int c) { return gdn2::grad_supported(Dk, c, f32) && gdn2::prep_fwd_supported(Dk, c, f32); };
+  return (chunk == 64 && !fits(64) && fits(32)) ? 32 : chunk;
+}
+
+// The chunk of the single-pass forward (no workspace): likewise the caller's, or
+// 32 where its LDS does not hold chunk 64.
+int fwd_single_chunk(int Dk, int Dv, int chunk, bool f32) {
+  return (chunk == 64 && !gdn2::fwd_supported(Dk, Dv, 64, f32) && gdn2::fwd_supported(Dk, Dv, 32, f32)) ? 32 : chunk;
+}
+
 // Backward plan: the two-stage reverse pass (chunk-parallel records, then the
 // register-resident reverse chain), where the kernels cover the sizes (two_stage;
-// otherwise the backward calls return GDN2_ERR_UNSUPPORTED).
+// otherwise the backward calls return GDN2_ERR_UNSUPPORTED), at the kernels'
+// chunk (bwd_chunk).
 struct BwdPlan {
   bool two_stage;
+  int chunk;       // the kernels' chunk
   size_t part;     // one [B,H,NC,Dk,Dv] fp32 array, 256-byte aligned
   size_t records;  // records region (two-stage only): forward records for a
                    // state recompute, then the backward records
@@ -74,6 +91,8 @@ size_t gscale_bytes(int nst, bool f32) { return f32 ? 0 : al256((size_t)nst * gd
 
 BwdPlan bwd_plan(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   BwdPlan p{};
+  chunk = bwd_chunk(Dk, chunk, f32);
+  p.chunk = chunk;
   const size_t nc = (size_t)((T + chunk - 1) / chunk);
   p.part = (nc * state_bytes(B, H, Dk, Dv) + 255) & ~(size_t)255;
   p.two_stage = gdn2::grad_supported(Dk, chunk, f32) && gdn2::prep_fwd_supported(Dk, chunk, f32);
@@ -219,7 +238,12 @@ size_t gdn2_workspace_bytes(int op, int B, int T, int H, int Dk, int Dv, int chu
   }
   if (op == GDN2_OP_FWD) {
     if (!chunk_ok(chunk) || T == 0) return 0;
-    return fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+    // also enough for the training pair's forward, which runs at the backward's chunk
+    const bool f32 = dt == GDN2_F32;
+    const size_t own = fwd_workspace(B, T, H, Dk, Dv, chunk, f32);
+    const int kc = bwd_chunk(Dk, chunk, f32);
+    const size_t pair = kc != chunk && own ? fwd_workspace(B, T, H, Dk, Dv, kc, f32) : 0;
+    return own > pair ? own : pair;
   }
   if (op == GDN2_OP_BWD_RECORDS) {
     if (!chunk_ok(chunk) || T == 0) return 0;
@@ -233,7 +257,7 @@ size_t gdn2_records_bytes(int B, int T, int H, int Dk, int Dv, int chunk, int dt
   if (check_common(B, T, H, Dk, Dv, dt) != GDN2_OK || !chunk_ok(chunk) || T == 0) return 0;
   const bool f32 = dt == GDN2_F32;
   if (!bwd_plan(B, T, H, Dk, Dv, chunk, f32).two_stage) return 0;
-  return train_records(B, T, H, Dk, Dv, chunk, f32);
+  return train_records(B, T, H, Dk, Dv, bwd_chunk(Dk, chunk, f32), f32);
 }
 
 int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float* log_alpha, const void* b,
@@ -246,7 +270,8 @@ int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float
   if (!chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   // the two-stage path runs when a workspace is given and covers the sizes
   const bool two_stage = workspace != nullptr && gdn2::prep_fwd_supported(Dk, chunk, dt == GDN2_F32);
-  if (!two_stage && !gdn2::fwd_supported(Dk, Dv, chunk, dt == GDN2_F32)) return GDN2_ERR_UNSUPPORTED;
+  const int kc1 = two_stage ? chunk : fwd_single_chunk(Dk, Dv, chunk, dt == GDN2_F32);
+  if (!two_stage && !gdn2::fwd_supported(Dk, Dv, kc1, dt == GDN2_F32)) return GDN2_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {
@@ -259,7 +284,11 @@ int gdn2_fwd_chunked_ex(const void* q, const void* k, const void* v, const float
   if (st != GDN2_OK) return st;
   gdn2::FwdArgs a{q, k, v, log_alpha, b, w, S0, o, S_final, chunk_states, B, T, H, Dk, Dv, chunk, dt == GDN2_F32};
   set_gate_flags(a, flags);
-  if (!two_stage) return hip_status(gdn2::launch_fwd(a, s));
+  if (!two_stage) {
+    a.chunk = kc1;
+    a.state_every = chunk / kc1;
+    return hip_status(gdn2::launch_fwd(a, s));
+  }
   const size_t need = fwd_workspace(B, T, H, Dk, Dv, chunk, dt == GDN2_F32);
   if (workspace_bytes < need) return GDN2_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_ALIGN;
@@ -311,6 +340,12 @@ int gdn2_bwd_chunked_ex(const void* q, const void* k, const void* v, const float
   const bool f32 = dt == GDN2_F32;
   const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
   if (!plan.two_stage) return GDN2_ERR_UNSUPPORTED;
+  if (plan.chunk != chunk) {
+    // the kernels run finer chunks: the caller's chunk states lack their entry
+    // states, so they are recomputed
+    chunk = plan.chunk;
+    chunk_states = nullptr;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {
@@ -372,6 +407,7 @@ int gdn2_fwd_chunked_train(const void* q, const void* k, const void* v, const fl
   if ((flags & ~kKnownFlags) != 0 || !chunk_ok(chunk)) return GDN2_ERR_UNSUPPORTED;
   const bool f32 = dt == GDN2_F32;
   if (!bwd_plan(B, T, H, Dk, Dv, chunk, f32).two_stage) return GDN2_ERR_UNSUPPORTED;
+  chunk = bwd_chunk(Dk, chunk, f32);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {  // no chunks, no records: S_T = S0
@@ -411,6 +447,7 @@ int gdn2_bwd_chunked_records(const void* q, const void* k, const void* v, const 
   const bool f32 = dt == GDN2_F32;
   const BwdPlan plan = bwd_plan(B, T, H, Dk, Dv, chunk, f32);
   if (!plan.two_stage) return GDN2_ERR_UNSUPPORTED;
+  chunk = plan.chunk;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0 || H == 0) return GDN2_OK;
   if (T == 0) {  // S_T = S0, so dS0 = dS_final
@@ -464,9 +501,15 @@ size_t gdn2_varlen_workspace_bytes(int op, int N, int T, int H, int Dk, int Dv, 
   if (check_common(1, T, H, Dk, Dv, dt) != GDN2_OK || N < 0 || !chunk_ok(chunk)) return 0;
   if (op != GDN2_OP_FWD && op != GDN2_OP_BWD && op != GDN2_OP_BWD_RECORDS) return 0;
   const bool f32 = dt == GDN2_F32;
-  if (!gdn2::prep_fwd_supported(Dk, chunk, f32) || (op != GDN2_OP_FWD && !gdn2::grad_supported(Dk, chunk, f32)))
-    return 0;
-  return varlen_plan(op, N, T, H, Dk, Dv, chunk, f32).need;
+  if (!gdn2::prep_fwd_supported(Dk, chunk, f32)) return 0;
+  const int kc = bwd_chunk(Dk, chunk, f32);
+  if (op != GDN2_OP_FWD)
+    return gdn2::grad_supported(Dk, kc, f32) ? varlen_plan(op, N, T, H, Dk, Dv, kc, f32).need : 0;
+  // also enough for the training pair's forward, which runs at the backward's chunk
+  const size_t own = varlen_plan(op, N, T, H, Dk, Dv, chunk, f32).need;
+  const size_t pair = kc != chunk && gdn2::prep_fwd_supported(Dk, kc, f32)
+                          ? varlen_plan(op, N, T, H, Dk, Dv, kc, f32).need : 0;
+  return own > pair ? own : pair;
 }
 
 // The packed-batch training pair's records buffer: backward records over
@@ -483,7 +526,7 @@ static size_t varlen_train_records(int N, int T, int H, int Dk, int Dv, int chun
 
 size_t gdn2_varlen_records_bytes(int N, int T, int H, int Dk, int Dv, int chunk, int dt) {
   if (gdn2_varlen_workspace_bytes(GDN2_OP_BWD_RECORDS, N, T, H, Dk, Dv, chunk, dt) == 0) return 0;
-  return varlen_train_records(N, T, H, Dk, Dv, chunk, dt == GDN2_F32);
+  return varlen_train_records(N, T, H, Dk, Dv, bwd_chunk(Dk, chunk, dt == GDN2_F32), dt == GDN2_F32);
 }
 
 static int varlen_common(const int64_t* cu_seqlens, int N, int T, int H, int Dk, int Dv, int chunk, int dt,
@@ -539,6 +582,8 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
                     float* dlog_alpha, float* db, float* dw, float* dS0, void* workspace, size_t workspace_bytes,
                     int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags, void* stream) {
   const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  const int caller_chunk = chunk;
+  chunk = bwd_chunk(Dk, chunk, dt == GDN2_F32);
   int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
   if (st != GDN2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -562,7 +607,8 @@ int gdn2_bwd_varlen(const void* q, const void* k, const void* v, const float* lo
   if (st != GDN2_OK) return st;
   float* dS_chunks = reinterpret_cast<float*>(ws + p.tables);
   char* rec = ws + p.tables + 2 * p.part;
-  float* states = const_cast<float*>(chunk_states);
+  // finer kernel chunks than the caller's: its chunk states lack their entry states, so they are recomputed
+  float* states = caller_chunk == chunk ? const_cast<float*>(chunk_states) : nullptr;
   if (states == nullptr) {
     // the entry states from the two-stage forward, in the records region first
     states = reinterpret_cast<float*>(ws + p.tables + p.part);
@@ -595,6 +641,7 @@ int gdn2_fwd_varlen_train(const void* q, const void* k, const void* v, const flo
                           size_t workspace_bytes, int T, int H, int Dk, int Dv, int chunk, int dt, unsigned flags,
                           void* stream) {
   const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  chunk = bwd_chunk(Dk, chunk, dt == GDN2_F32);
   int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
   if (st != GDN2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -636,6 +683,7 @@ int gdn2_bwd_varlen_records(const void* q, const void* k, const void* v, const f
                             size_t workspace_bytes, int T, int H, int Dk, int Dv, int chunk, int dt,
                             unsigned flags, void* stream) {
   const int64_t* cu_seqlens = reinterpret_cast<const int64_t*>(cu_seqlens_);
+  chunk = bwd_chunk(Dk, chunk, dt == GDN2_F32);
   int st = varlen_common(cu_seqlens, N, T, H, Dk, Dv, chunk, dt, flags, GDN2_OP_BWD);
   if (st != GDN2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

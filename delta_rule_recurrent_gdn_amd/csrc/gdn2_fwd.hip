@@ -378,8 +378,10 @@ __device__ __forceinline__ void fwd_chunks(const FwdArgs& a, char* smem) {
     const int t0 = n * C;
     const int Lr = min(C, T - t0);
 
-    if (a.chunk_states) {
-      float* cs = a.chunk_states + ((int64_t)bh * NC + n) * DK * Dv + j0;
+    // entry states every state_every chunks (the caller's chunk when the kernel runs a finer one)
+    if (a.chunk_states && n % a.state_every == 0) {
+      const int ncs = (NC + a.state_every - 1) / a.state_every;
+      float* cs = a.chunk_states + ((int64_t)bh * ncs + n / a.state_every) * DK * Dv + j0;
 #pragma unroll
       for (int i = 0; i < Cfg::SPW; ++i) {
         const int t = wid + NW * i;

@@ -156,6 +156,8 @@ struct FwdArgs {
   Varlen vl;               // packed variable-length batch (B = 1), or dense
   // gates of one value per (token, head), [., T, H], broadcast over their channels
   bool scalar_b = false, scalar_w = false, scalar_decay = false;
+  int state_every = 1;     // single-pass forward: chunk_states holds the entry state of every
+                           // state_every-th chunk (the kernel's chunk is 1/state_every of the caller's)
 };
 
 // Segmented (two-level) forward chain: the pass and its buffers.

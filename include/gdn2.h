@@ -38,10 +38,14 @@
  *   tensors as passed. Nothing is clamped or range-checked; q is not scaled.
  * - Supported sizes: Dk, Dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
  *   B, H >= 1; T >= 0 (T = 0 writes S_final = S0 and nothing else). A ragged
- *   last chunk is handled exactly. One exception: the backward (and the
- *   training pair) with fp32 inputs at Dk = 128 and chunk 64 is not built
- *   (GDN2_ERR_UNSUPPORTED; gdn2_workspace_bytes and gdn2_records_bytes return
- *   0 for it); fp32 inputs run it at chunk 32.
+ *   last chunk is handled exactly. The chunk size tiles the recurrence and
+ *   does not change its result. With fp32 inputs at Dk = 128 and chunk 64
+ *   the backward, the training pair and the single-pass forward run 32-token
+ *   chunks inside (their LDS does not hold 64): the workspace and records
+ *   sizes are those of chunk 32 (gdn2_workspace_bytes(GDN2_OP_FWD, ...) is
+ *   large enough for both forwards), chunk_states keep the caller's chunk,
+ *   and the backward recomputes the chunk-32 entry states instead of reading
+ *   the caller's chunk_states.
  * - Numerics: fp32 inputs are computed with fp32 matrix-core products. bf16
  *   inputs use fp16 matrix-core operands for the value-side products and a
  *   two-term bf16 split for the decay-scaled key Gram matrices, always with

@@ -76,9 +76,18 @@ def test_workspace_bytes():
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == B * H * nc * (113 * 1024 + C * D * 4)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 48, D, C, 1) == 0   # unsupported size
-    # fp32 inputs at d_k = 128, chunk 64: the backward is not built, so no workspace size either
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 0) == 0
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD_RECORDS, B, T, H, D, D, C, 0) == 0
+    # fp32 inputs at d_k = 128, chunk 64: the backward kernels run 32-token chunks (their LDS does not hold
+    # 64), so the backward's sizes are those of chunk 32, and the forward workspace also holds the training
+    # pair's chunk-32 forward
+    for op in (_lib.GDN2_OP_BWD, _lib.GDN2_OP_BWD_RECORDS):
+        assert lib.gdn2_workspace_bytes(op, B, T, H, D, D, C, 0) == lib.gdn2_workspace_bytes(op, B, T, H, D, D, 32, 0) > 0
+    assert lib.gdn2_records_bytes(B, T, H, D, D, C, 0) == lib.gdn2_records_bytes(B, T, H, D, D, 32, 0) > 0
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) >= \
+        lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, 32, 0)
+    n = 3
+    assert lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, n, T, H, D, D, C, 0) == \
+        lib.gdn2_varlen_workspace_bytes(_lib.GDN2_OP_BWD, n, T, H, D, D, 32, 0) > 0
+    assert lib.gdn2_varlen_records_bytes(n, T, H, D, D, C, 0) == lib.gdn2_varlen_records_bytes(n, T, H, D, D, 32, 0) > 0
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, 100, H, D, D, 64, 1) == 2 * 2 * B * H * D * D * 4 + rec(2) + gsc
 
 
@@ -122,7 +131,6 @@ def fwd(**kw):
     (dict(C=128), _lib.GDN2_ERR_UNSUPPORTED),
     (dict(T=-1), _lib.GDN2_ERR_SHAPE),
     (dict(B=-2), _lib.GDN2_ERR_SHAPE),
-    (dict(dt=0, Dk=128, Dv=128, C=64), _lib.GDN2_ERR_UNSUPPORTED),   # fp32 inputs at d=128 need chunk <= 32
     (dict(ws=A, ws_bytes=1), _lib.GDN2_ERR_WORKSPACE),              # two-stage path: workspace too small
     (dict(ws=A + 16, ws_bytes=1 << 30), _lib.GDN2_ERR_ALIGN),       # workspace must be 256-byte aligned
     (dict(B=0), _lib.GDN2_OK),                                       # nothing to do, nothing launched
@@ -214,9 +222,9 @@ def test_training_pair_sizes_and_argument_errors():
     assert fwd(ws_bytes=fw - 1) == _lib.GDN2_ERR_WORKSPACE
     assert bwd(ws_bytes=bw - 1) == _lib.GDN2_ERR_WORKSPACE
     assert fwd(B=0) == _lib.GDN2_OK
-    # fp32 inputs at d = 128 need chunk <= 32 (the two-stage kernels do not cover chunk 64)
+    # fp32 inputs at d = 128, chunk 64 are accepted (run as 32-token chunks) and checked against those sizes
     assert lib.gdn2_fwd_chunked_train(A, A, A, A, A, A, None, A, None, A, rb, A, fw, 1, 64, 2, 128, 128, 64, 0, 0,
-                                      None) == _lib.GDN2_ERR_UNSUPPORTED
+                                      None) == _lib.GDN2_ERR_WORKSPACE
 
 
 def test_packed_training_pair_sizes_and_argument_errors():

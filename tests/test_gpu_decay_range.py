@@ -99,8 +99,6 @@ def test_forward_paths(Dk, Dv, C, dtype, kind):
     tol = TOL_F32 if dtype == "fp32" else TOL_BF16
     d = to_dev(inp)
     for single in (False, True):
-        if single and dtype == "fp32" and Dk == 128 and C == 64:
-            continue  # the single-pass kernel does not cover fp32 at this size (its own test checks the error)
         o, S, _ = gdn2_fwd_chunked(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], d["S0"], chunk=C,
                                    single_pass=single)
         torch.cuda.synchronize()
@@ -112,8 +110,6 @@ def test_forward_paths(Dk, Dv, C, dtype, kind):
 @pytest.mark.parametrize("Dk,Dv,C", CASES)
 def test_backward_and_training_pair(Dk, Dv, C, dtype, kind):
     """The separate backward and the training pair: all seven gradients, S0 and dS_final nonzero."""
-    if dtype == "fp32" and Dk == 128 and C == 64:
-        pytest.skip("fp32 backward is not built for d_k = 128 at chunk 64 (GDN2_ERR_UNSUPPORTED, tested elsewhere)")
     T = 2 * C + 5
     inp = make(1, T, 3, Dk, Dv, dtype, seed=7 * Dk + Dv + C, kind=kind)
     dS = torch.from_numpy(np.random.default_rng(C + Dk).standard_normal((1, 3, Dk, Dv)).astype(np.float32))
@@ -148,12 +144,12 @@ def test_pure_decay_and_no_decay(dtype):
         o, S, _ = gdn2_fwd_chunked(*x, d["S0"], chunk=C)
         torch.cuda.synchronize()
         check_fwd(o, S, ref, tol, f"two-stage {kind} b=w=0:{kind == 'mixed'} {dtype}")
-        if dtype == "bf16":  # the fp32 backward at d_k = 128, chunk 64 is not built
-            o2, S2, rec = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C)
-            g = gdn2_bwd_chunked_records(*x, d["dO"], rec, chunk=C)
-            torch.cuda.synchronize()
-            check_fwd(o2, S2, ref, tol, f"pair fwd {kind}")
-            check_grads(g, oracle_bwd(inp), TOL_GRAD, f"pair {kind} b=w=0:{kind == 'mixed'}")
+        o2, S2, rec = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C)
+        g = gdn2_bwd_chunked_records(*x, d["dO"], rec, chunk=C)
+        torch.cuda.synchronize()
+        check_fwd(o2, S2, ref, tol, f"pair fwd {kind} {dtype}")
+        check_grads(g, oracle_bwd(inp), TOL_F32 if dtype == "fp32" else TOL_GRAD,
+                    f"pair {kind} b=w=0:{kind == 'mixed'} {dtype}")
 
 
 def test_packed_batch_training_pair_strong_decay():

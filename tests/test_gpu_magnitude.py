@@ -41,13 +41,10 @@ def test_forward_value_scale(dtype, f):
     tol = TOL_F32 if dtype == "fp32" else TOL_BF16
     outs = {}
     for single in (False, True):
-        if single and dtype == "fp32":
-            continue  # not built for fp32 at d_k = 128, chunk 64
         o, S, _ = gdn2_fwd_chunked(*x, d["S0"], chunk=C, single_pass=single)
         outs["single" if single else "two-stage"] = (o, S)
-    if dtype == "bf16":  # the training pair is not built for fp32 at d_k = 128, chunk 64
-        o, S, _ = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C)
-        outs["training"] = (o, S)
+    o, S, _ = gdn2_fwd_chunked_train(*x, d["S0"], chunk=C)
+    outs["training"] = (o, S)
     torch.cuda.synchronize()
     for what, (o, S) in outs.items():
         e_o, e_s = rel_err(f64(o), o_ref), rel_err(f64(S), S_ref)
@@ -59,7 +56,7 @@ def test_forward_value_scale(dtype, f):
 @pytest.mark.parametrize("f", [2.0 ** 12, 2.0 ** -12, 1e-7, 1e-3])
 def test_backward_upstream_scale(dtype, f):
     """dO and dS_final times f (2^+-12, 1e-7, 1e-3): all seven gradients, separate backward and training pair."""
-    D, C = (64, 64) if dtype == "fp32" else (128, 64)  # the fp32 backward is not built for d_k = 128 at chunk 64
+    D, C = 128, 64
     T = 2 * C + 7
     base = synth.make_inputs(1, T, 3, D, D, dtype, seed=41, s0_std=0.3, grad=True)
     inp = dict(base)

@@ -48,8 +48,6 @@ MIXES = [
 @pytest.mark.parametrize("mix", range(len(MIXES)))
 def test_varlen_forward(dtype, Dk, Dv, mix):
     lengths, C = MIXES[mix]
-    if dtype == "fp32" and Dk == 128 and C == 64:
-        C = 32  # the chunk-parallel kernel's LDS holds fp32 operands of d = 128 at chunk <= 32
     H = 2
     inp, cu = _packed(lengths, H, Dk, Dv, dtype, seed=70 + Dk + mix)
     d = to_dev(inp)
