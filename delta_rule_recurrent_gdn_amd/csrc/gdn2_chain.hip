@@ -53,6 +53,17 @@ __device__ __forceinline__ void dma_units(const char* src, char* dst, int units,
   }
 }
 
+// The same, over units [0, units) less the ranges [s0, e0) and [s1, e1) (wave-uniform bounds).
+__device__ __forceinline__ void dma_units_skip(const char* src, char* dst, int units, int s0, int e0, int s1, int e1,
+                                               int wid, int nw) {
+  const int l = lane_id();
+  for (int t = wid; t < units; t += nw) {
+    if ((t >= s0 && t < e0) || (t >= s1 && t < e1)) continue;
+    __builtin_amdgcn_global_load_lds(src + (int64_t)t * 1024 + 16 * l,
+                                     (__attribute__((address_space(3))) void*)(dst + t * 1024), 16, 0, 0);
+  }
+}
+
 // Helper waves of the plain reverse chain (one workgroup per CU): they take the
 // record copies off the column waves, which also gather dO (1.41 -> 1.38 ms for
 // the B8 H16 T4096 backward; four helpers: 1.39 ms). The forward chain has none:
@@ -87,9 +98,11 @@ inline unsigned seg_grid(int64_t items, int ncg) { return (unsigned)(((items + 7
 // NHW helper waves: waves past the NWV column waves own no columns and only
 // copy the next record into LDS (used by the plain reverse chain; see
 // kChainHelpers).
-template <int DK, int C, bool F32IN, int NCT, int NWV, bool SEG, int NHW = 0>
+// MAP: the segmented map pass (sg.mode == kSegMap), compiled on its own: it writes no o.
+template <int DK, int C, bool F32IN, int NCT, int NWV, bool SEG, int NHW = 0, bool MAP = false>
 __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArgs a, const char* rec_base,
                                                                           const float* ut_base, SegArgs sg) {
+  static_assert(!MAP || (SEG && NHW == 0), "the map pass is a segmented pass without helper waves");
   using Cfg = ChainCfg<DK, C, F32IN, NCT, NWV>;
   using Rec = typename Cfg::Rec;
   using F = Frag<F32IN>;
@@ -203,9 +216,13 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
   // the value columns' outputs: every pass but the segmented map pass
   const bool outs = SEG ? (sg.mode == kSegRun && active) : active;
   const bool has_ut = active && !ident;
-  // record copies: by the helper waves when there are any, else by all waves
+  // record copies: by the helper waves when there are any, else by all waves. The segmented map pass
+  // (MAP) computes no o: it needs neither the decayed q nor the causal term, so it copies neither into
+  // LDS and skips their products (24 of the 57 units of a bf16 d = 128 record, a third of the products)
   auto dma = [&](const char* src, char* dst) {
-    if constexpr (NHW > 0) {
+    if constexpr (MAP) {
+      dma_units_skip(src, dst, Rec::kUnits, Rec::u1, Rec::u2, Rec::u3, Rec::uG, wid, NWV);
+    } else if constexpr (NHW > 0) {
       if (wid >= NWV) dma_units(src, dst, Rec::kUnits, wid - NWV, NHW);
     } else {
       dma_units(src, dst, Rec::kUnits, wid, NWV);
@@ -288,35 +305,64 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
     const float* gam = reinterpret_cast<const float*>(buf + Rec::uG * 1024);
 
     // ---- U = Ut - W S ; O = Qs S  (contraction over Dk) ----
-    if constexpr (F32IN) {
+    if constexpr (!MAP) {
+      if constexpr (F32IN) {
 #pragma unroll
-      for (int R = 0; R < RC; ++R)
+        for (int R = 0; R < RC; ++R)
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const uint4 aw = uW[(R * UK + u) * 64], aq = uQ[(R * UK + u) * 64];
+          for (int u = 0; u < UK; ++u) {
+            const uint4 aw = uW[(R * UK + u) * 64], aq = uQ[(R * UK + u) * 64];
 #pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            unit_mma(accU[R][c], aw, accS[u][c]);
-            unit_mma(accO[R][c], aq, accS[u][c]);
+            for (int c = 0; c < NCT; ++c) {
+              unit_mma(accU[R][c], aw, accS[u][c]);
+              unit_mma(accO[R][c], aq, accS[u][c]);
+            }
           }
-        }
-    } else {
-      f16x8 sb[UK][NCT];
+      } else {
+        f16x8 sb[UK][NCT];
 #pragma unroll
-      for (int u = 0; u < UK; ++u)
+        for (int u = 0; u < UK; ++u)
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) sb[u][c] = rhs_from_acc(accS[2 * u][c], 2 * u + 1 < RK ? accS[2 * u + 1][c] : zero4());
+          for (int c = 0; c < NCT; ++c)
+            sb[u][c] = rhs_from_acc(accS[2 * u][c], 2 * u + 1 < RK ? accS[2 * u + 1][c] : zero4());
 #pragma unroll
-      for (int R = 0; R < RC; ++R)
+        for (int R = 0; R < RC; ++R)
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const uint4 aw = uW[(R * UK + u) * 64], aq = uQ[(R * UK + u) * 64];
+          for (int u = 0; u < UK; ++u) {
+            const uint4 aw = uW[(R * UK + u) * 64], aq = uQ[(R * UK + u) * 64];
 #pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            unit_mma(accU[R][c], aw, sb[u][c]);
-            unit_mma(accO[R][c], aq, sb[u][c]);
+            for (int c = 0; c < NCT; ++c) {
+              unit_mma(accU[R][c], aw, sb[u][c]);
+              unit_mma(accO[R][c], aq, sb[u][c]);
+            }
           }
-        }
+      }
+    } else {  // map pass: U only
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int R = 0; R < RC; ++R)
+#pragma unroll
+          for (int u = 0; u < UK; ++u) {
+            const uint4 aw = uW[(R * UK + u) * 64];
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], aw, accS[u][c]);
+          }
+      } else {
+        f16x8 sb[UK][NCT];
+#pragma unroll
+        for (int u = 0; u < UK; ++u)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            sb[u][c] = rhs_from_acc(accS[2 * u][c], 2 * u + 1 < RK ? accS[2 * u + 1][c] : zero4());
+#pragma unroll
+        for (int R = 0; R < RC; ++R)
+#pragma unroll
+          for (int u = 0; u < UK; ++u) {
+            const uint4 aw = uW[(R * UK + u) * 64];
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) unit_mma(accU[R][c], aw, sb[u][c]);
+          }
+      }
     }
 
     // ---- O += P U (P lower triangular: row tile R needs contraction < 16(R+1)) ;
@@ -328,16 +374,18 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       gm[R][0] = g4.x; gm[R][1] = g4.y; gm[R][2] = g4.z; gm[R][3] = g4.w;
     }
     if constexpr (F32IN) {
+      if constexpr (!MAP) {
 #pragma unroll
-      for (int R = 0; R < RC; ++R)
+        for (int R = 0; R < RC; ++R)
 #pragma unroll
-        for (int u = 0; u < UC; ++u) {
-          if (KU * u < 16 * (R + 1)) {
-            const uint4 ap = uP[(R * UC + u) * 64];
+          for (int u = 0; u < UC; ++u) {
+            if (KU * u < 16 * (R + 1)) {
+              const uint4 ap = uP[(R * UC + u) * 64];
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) unit_mma(accO[R][c], ap, accU[u][c]);
+              for (int c = 0; c < NCT; ++c) unit_mma(accO[R][c], ap, accU[u][c]);
+            }
           }
-        }
+      }
 #pragma unroll
       for (int R = 0; R < RK; ++R)
 #pragma unroll
@@ -353,16 +401,18 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       for (int u = 0; u < UC; ++u)
 #pragma unroll
         for (int c = 0; c < NCT; ++c) ub[u][c] = rhs_from_acc(accU[2 * u][c], 2 * u + 1 < RC ? accU[2 * u + 1][c] : zero4());
+      if constexpr (!MAP) {
 #pragma unroll
-      for (int R = 0; R < RC; ++R)
+        for (int R = 0; R < RC; ++R)
 #pragma unroll
-        for (int u = 0; u < UC; ++u) {
-          if (KU * u < 16 * (R + 1)) {
-            const uint4 ap = uP[(R * UC + u) * 64];
+          for (int u = 0; u < UC; ++u) {
+            if (KU * u < 16 * (R + 1)) {
+              const uint4 ap = uP[(R * UC + u) * 64];
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) unit_mma(accO[R][c], ap, ub[u][c]);
+              for (int c = 0; c < NCT; ++c) unit_mma(accO[R][c], ap, ub[u][c]);
+            }
           }
-        }
+      }
 #pragma unroll
       for (int R = 0; R < RK; ++R) {
         uint4 ak[UC];
@@ -987,8 +1037,8 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     // (1) maps of every segment but the last of each (batch row or sequence, head)
     sg.mode = kSegMap;
     const int64_t map_items = packed ? slots : (int64_t)nbh * (G - 1);
-    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, kSegWaves, true>), dim3(seg_grid(map_items, ncg_map)),
-                       dim3(Cfg::kThreads), 0, s, a, rec, ut, sg);
+    hipLaunchKernelGGL((gdn2_chain_fwd_kernel<DK, C, F32IN, 1, kSegWaves, true, 0, true>),
+                       dim3(seg_grid(map_items, ncg_map)), dim3(Cfg::kThreads), 0, s, a, rec, ut, sg);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments

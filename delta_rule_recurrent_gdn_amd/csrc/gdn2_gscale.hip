@@ -27,7 +27,11 @@ constexpr int kScaleThreads = 256;
 constexpr int kScaleUnroll = 8;  // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(kScaleThreads) void gdn2_grad_scale_kernel(BwdArgs a, float* part) {
-  const int st = blockIdx.x / kGradScaleSplit, sp = blockIdx.x - st * kGradScaleSplit;
+  // heads fastest: the workgroups in flight read whole token rows (all heads' slices of a row) rather
+  // than one head's 2*Dv-byte slice of rows H*Dv*2 bytes apart
+  const int h = blockIdx.x % a.H, r = blockIdx.x / a.H;
+  const int sq = r / kGradScaleSplit, sp = r - sq * kGradScaleSplit;
+  const int st = sq * a.H + h;
   const SeqLoc sl = seq_loc(a.vl, a.T, a.H, a.Dk, a.Dv, a.chunk, st);
   const int t_lo = (int)((int64_t)sl.len * sp / kGradScaleSplit);
   const int t_hi = (int)((int64_t)sl.len * (sp + 1) / kGradScaleSplit);
