@@ -233,3 +233,38 @@ def test_packed_training_pair_scalar_gates():
         ref[n] = ref[n].sum(-1)
     for n in GRADS:
         assert rel_err(f64(g1[n]), ref[n]) <= 1e-4, n
+
+
+def test_fp32_d128_chunk64_runs_as_chunk32():
+    """fp32 inputs at d_k = 128, chunk 64: the training pair, the backward and the single-pass forward run
+    32-token chunks inside, so each equals its chunk-32 call bit for bit (the single-pass chunk-64 entry
+    states are every second chunk-32 one), and all match the oracle."""
+    inp = synth.make_inputs(1, 3 * 64 + 9, 2, 128, 128, "fp32", seed=140, s0_std=0.2, grad=True)
+    dS = torch.from_numpy(np.random.default_rng(141).standard_normal((1, 2, 128, 128)).astype(np.float32)).cuda()
+    d = to_dev(inp)
+    x = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    o1, S1, r1 = gdn2_fwd_chunked_train(*x, d["S0"], chunk=64)
+    g1 = gdn2_bwd_chunked_records(*x, d["dO"], r1, dS_final=dS, chunk=64)
+    o2, S2, r2 = gdn2_fwd_chunked_train(*x, d["S0"], chunk=32)
+    g2 = gdn2_bwd_chunked_records(*x, d["dO"], r2, dS_final=dS, chunk=32)
+    g3 = gdn2_bwd_chunked(*x, d["dO"], S0=d["S0"], dS_final=dS, chunk=64)
+    g4 = gdn2_bwd_chunked(*x, d["dO"], S0=d["S0"], dS_final=dS, chunk=32)
+    o5, S5, c5 = gdn2_fwd_chunked(*x, d["S0"], chunk=64, want_chunk_states=True, single_pass=True)
+    o6, S6, c6 = gdn2_fwd_chunked(*x, d["S0"], chunk=32, want_chunk_states=True, single_pass=True)
+    torch.cuda.synchronize()
+    assert r1.numel() == r2.numel()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o5, o6) and torch.equal(S5, S6)
+    assert c5.shape[2] == 4 and torch.equal(c5, c6[:, :, ::2])
+    for n in GRADS:
+        assert torch.equal(g1[n], g2[n]), n
+        assert torch.equal(g3[n], g4[n]), n
+    o_ref, S_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"])
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"], inp["S0"], inp["dO"],
+                          dS.cpu())
+    for got in (o1, o5):
+        assert rel_err(f64(got), o_ref) <= TOL_F32
+    assert rel_err(f64(S1), S_ref) <= TOL_F32
+    for g in (g1, g3):
+        for n in GRADS:
+            assert rel_err(f64(g[n]), ref[n]) <= TOL_F32, n

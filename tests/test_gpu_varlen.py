@@ -91,7 +91,7 @@ def test_varlen_equal_lengths_match_dense_bitwise():
 
 
 @pytest.mark.parametrize("dtype,Dk,Dv,mix", [("fp32", 32, 64, 0), ("fp32", 16, 16, 1), ("bf16", 128, 128, 0),
-                                             ("bf16", 64, 32, 2)])
+                                             ("bf16", 64, 32, 2), ("fp32", 128, 128, 0)])
 @pytest.mark.parametrize("use_states", [True, False], ids=["saved_states", "recomputed_states"])
 def test_varlen_backward(dtype, Dk, Dv, mix, use_states):
     lengths, C = MIXES[mix]
