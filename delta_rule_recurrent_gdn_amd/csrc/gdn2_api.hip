@@ -133,16 +133,19 @@ size_t bwd_records_workspace(const BwdPlan& p) { return p.part + p.seg + p.gsc; 
 // (256-byte aligned) the segment maps and entry states of the two-level chain
 // when it is used for the sizes; 0 when the chunk-parallel kernel does not
 // cover the sizes.
+// T (w v) of one chunk: fp32 for fp32 inputs, fp16 for 16-bit ones
+size_t ut_bytes(int chunk, int Dv, bool f32) { return (size_t)chunk * Dv * (f32 ? 4 : 2); }
+
 size_t fwd_seg_offset(int B, int T, int H, int Dv, int Dk, int chunk, bool f32) {
   const size_t nchunks = (size_t)B * H * ((T + chunk - 1) / chunk);
-  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + ut_bytes(chunk, Dv, f32));
   return (base + 255) & ~(size_t)255;
 }
 
 size_t fwd_workspace(int B, int T, int H, int Dk, int Dv, int chunk, bool f32) {
   if (!gdn2::prep_fwd_supported(Dk, chunk, f32)) return 0;
   const size_t nchunks = (size_t)B * H * ((T + chunk - 1) / chunk);
-  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * sizeof(float));
+  const size_t base = nchunks * (gdn2::fwd_record_bytes(Dk, chunk, f32) + ut_bytes(chunk, Dv, f32));
   const size_t sb = gdn2::fwd_seg_bytes(B, H, T, Dk, Dv, chunk);
   return sb ? fwd_seg_offset(B, T, H, Dv, Dk, chunk, f32) + sb : base;
 }
@@ -168,7 +171,7 @@ VarlenPlan varlen_plan(int op, int N, int T, int H, int Dk, int Dv, int chunk, b
   p.L = gdn2::varlen_seg_len(N, T, H, Dk, Dv, chunk);
   p.tables = al256(gdn2::varlen_table_bytes(N, T, chunk, p.L));
   // forward region: records, T (w v), then the two-level chain's segment maps
-  p.seg_off = al256((size_t)H * mc * (gdn2::fwd_record_bytes(Dk, chunk, f32) + (size_t)chunk * Dv * 4));
+  p.seg_off = al256((size_t)H * mc * (gdn2::fwd_record_bytes(Dk, chunk, f32) + ut_bytes(chunk, Dv, f32)));
   const size_t fwd_rec = p.seg_off + gdn2::varlen_seg_bytes(N, T, H, Dk, Dv, chunk);
   if (op == GDN2_OP_FWD) {
     p.records = al256(fwd_rec);

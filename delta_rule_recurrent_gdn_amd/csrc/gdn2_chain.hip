@@ -26,6 +26,8 @@
 // states and the final state. Same arithmetic per chunk; the sequential depth
 // drops from NC chunks to about 2L + NC/L.
 
+#include <type_traits>
+
 #include "gdn2_frag.h"
 #include "gdn2_internal.h"
 
@@ -171,7 +173,9 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
   const int64_t baseV = sl.baseV + j0;
   const int64_t stBase = sl.state * DK * Dv + j0;
   const char* recs = rec_base + sl.item0 * Rec::kBytes;
-  const float* uts = ut_base + sl.item0 * C * Dv;
+  // T (w v): fp32 tiles for fp32 inputs, fp16 for 16-bit ones, held packed until their step uses them
+  using UtReg = typename std::conditional<F32IN, f32x4, uint2>::type;
+  const char* uts = reinterpret_cast<const char*>(ut_base) + sl.item0 * C * Dv * (F32IN ? 4 : 2);
   const int nvt = Dv / 16, jb0 = j0 / 16;
 
   // state tiles: rows 16*RKt + 4*lg + i, column j0 + 16*c + lr
@@ -202,14 +206,18 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       }
     }
 
-  auto load_ut = [&](int nn, f32x4 (&dst)[RC][NCT]) {
-    const float* u = uts + (int64_t)nn * C * Dv;
+  auto load_ut = [&](int nn, UtReg (&dst)[RC][NCT]) {
 #pragma unroll
     for (int R = 0; R < RC; ++R)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(u + (int64_t)(R * nvt + jb0 + c) * 256 + 4 * l);
-        dst[R][c] = f32x4{v.x, v.y, v.z, v.w};
+        const int64_t e = (int64_t)nn * C * Dv + (int64_t)(R * nvt + jb0 + c) * 256 + 4 * l;
+        if constexpr (F32IN) {
+          const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(uts) + e);
+          dst[R][c] = f32x4{v.x, v.y, v.z, v.w};
+        } else {
+          dst[R][c] = *reinterpret_cast<const uint2*>(reinterpret_cast<const _Float16*>(uts) + e);
+        }
       }
   };
 
@@ -228,7 +236,17 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
       dma_units(src, dst, Rec::kUnits, wid, NWV);
     }
   };
-  f32x4 utA[RC][NCT], utB[RC][NCT];
+  UtReg utA[RC][NCT], utB[RC][NCT];
+  auto ut_f32 = [](const UtReg& x) -> f32x4 {
+    if constexpr (F32IN) {
+      return x;
+    } else {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 h = __builtin_bit_cast(h4, x);
+      return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+                   static_cast<float>(h[3])};
+    }
+  };
   if (n_begin < n_end) {  // an empty packed sequence has no chunk: S_final = S0
     dma(recs + (int64_t)n_begin * Rec::kBytes, smem);
     if (has_ut) load_ut(n_begin, utA);
@@ -259,7 +277,7 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
 
   // one chain step: record n in buf, the next record's copy into nbuf; T (w v) of chunk n in utc, the next
   // chunk's loaded into utx
-  auto step = [&](const int n, char* buf, char* nbuf, f32x4 (&utc)[RC][NCT], f32x4 (&utx)[RC][NCT])
+  auto step = [&](const int n, char* buf, char* nbuf, UtReg (&utc)[RC][NCT], UtReg (&utx)[RC][NCT])
                   __attribute__((always_inline)) {
     const int t0 = sl.tok0 + n * C, Lr = min(C, sl.len - n * C);
     wait_vm_all();
@@ -292,7 +310,7 @@ __global__ __launch_bounds__((NWV + NHW) * 64) void gdn2_chain_fwd_kernel(FwdArg
     for (int R = 0; R < RC; ++R)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        accU[R][c] = has_ut ? utc[R][c] : zero4();
+        accU[R][c] = has_ut ? ut_f32(utc[R][c]) : zero4();
         accO[R][c] = zero4();
       }
     if (has_ut && n + 1 < n_end) load_ut(n + 1, utx);

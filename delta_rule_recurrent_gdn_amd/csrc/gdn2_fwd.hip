@@ -456,6 +456,12 @@ __device__ __forceinline__ void fwd_chunks(const FwdArgs& a, char* smem) {
       if (t < Cfg::NUT) {
         const int R = t / (BV / 16), jb = t % (BV / 16);
         mma_nt_xf32<OpT>(accU[i], sAf + 16 * R * LDCF, LDCF, sWVT + 16 * jb * LDC, LDC, 16 * (R + 1));
+        // 16-bit inputs: T (w v) rounded to fp16, as the two-stage path stores it, so that both paths
+        // round the same operands (U itself becomes an fp16 operand in every use)
+        if constexpr (!F32IN) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accU[i][e] = static_cast<float>(static_cast<_Float16>(accU[i][e]));
+        }
       }
     }
     __syncthreads();

@@ -15,10 +15,11 @@
 // computes one (batch, head, chunk): all B*H*ceil(T/C) chunks run in parallel.
 //
 // Outputs (workspace): the record of units -W, Qs, Kb^T, P, gamma (see
-// gdn2_frag.h) and Ut as fp32 accumulator tiles: tile (R, jb) of 16 x 16 at
-// float offset 256 * (R * Dv/16 + jb), lane l's 4 values (rows 4(l/16)+i,
-// column l%16) contiguous, so the chain reads each tile with one 16-byte load
-// per lane.
+// gdn2_frag.h) and Ut as accumulator tiles: tile (R, jb) of 16 x 16 at
+// element offset 256 * (R * Dv/16 + jb), lane l's 4 values (rows 4(l/16)+i,
+// column l%16) contiguous, so the chain reads each tile with one load per lane;
+// fp32 for fp32 inputs, fp16 for 16-bit inputs (U = Ut - W S becomes an fp16
+// operand in each of its uses, so the stored Ut needs no more).
 //
 // Precision as in the single-pass forward: A and P from a two-term bf16 split
 // of their decay-scaled factors (referenced to the chunk middle so that the
@@ -146,7 +147,8 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, char* rec_base, flo
   const int64_t baseK = cl.baseK, baseV = cl.baseV;
   char* rec = rec_base + cl.item * Rec::kBytes;  // forward record (DIR 0, 2), backward record (DIR 1)
   char* recB = DIR == 1 ? rec : (DIR == 2 ? brec_base + cl.item * RecB::kBytes : nullptr);
-  float* ut = ut_base + cl.item * C * Dv;
+  // Ut: fp32 tiles for fp32 inputs, fp16 for 16-bit ones (each use of U = Ut - W S is an fp16 operand)
+  char* ut = reinterpret_cast<char*>(ut_base) + cl.item * C * Dv * (F32IN ? 4 : 2);
 
   // ---- loads: row r, channels sl*SW + 4*c4 .. +3 of every slice sl ----
   const int r = tid / TPR, c4 = tid - r * TPR;
@@ -705,7 +707,15 @@ __device__ __forceinline__ void prep_chunk(const FwdArgs& a, char* rec_base, flo
       f32x4 acc = zero4();
       mma_nt_xf32<OpT>(acc, sAf + 16 * R * LDCF, LDCF, sWVT + 16 * jb * LDC, LDC, 16 * (R + 1), 16 * jb,
                        Cfg::kWvSwz);
-      *reinterpret_cast<float4*>(ut + (int64_t)t * 256 + 4 * l) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if constexpr (F32IN) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(ut) + (int64_t)t * 256 + 4 * l) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 h = {static_cast<_Float16>(acc[0]), static_cast<_Float16>(acc[1]), static_cast<_Float16>(acc[2]),
+                      static_cast<_Float16>(acc[3])};
+        *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(ut) + (int64_t)t * 256 + 4 * l) = h;
+      }
     }
   }
 }

@@ -60,18 +60,18 @@ def test_workspace_bytes():
     B, T, H, D, C = 8, 4096, 16, 128, 64
     nc = T // C
     # backward: exit-state gradients and room for recomputed entry states (one [B,H,NC,D,D] fp32 array
-    # each), then a records region that holds the forward records (for a state recompute) and later the
-    # backward ones: 57 units of 1 KB per chunk plus T (w v)
-    # backward records: 57 units of 1 KB per chunk plus T (w v); for 16-bit inputs, at the end, the
-    # partial maxima of the upstream gradients: 8 floats per (batch, head), 256-byte aligned
-    rec = lambda n: B * H * n * (57 * 1024 + C * D * 4)  # noqa: E731
+    # each), then a records region that holds the forward records (for a state recompute: 57 units of
+    # 1 KB per chunk plus T (w v), fp16 for 16-bit inputs) and later the backward ones (81 units per
+    # chunk); for 16-bit inputs, at the end, the partial maxima of the upstream gradients: 8 floats per
+    # (batch, head), 256-byte aligned
+    rec = lambda n: B * H * n * max(81 * 1024, 57 * 1024 + C * D * 2)  # noqa: E731
     gsc = (B * H * 8 * 4 + 255) // 256 * 256
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, D, D, C, 1) == 2 * nc * B * H * D * D * 4 + rec(nc) + gsc
     # fp32 inputs: no upstream-gradient scaling
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_BWD, B, T, H, 64, 64, C, 0) > 0
     # two-stage forward: per chunk a record of 57 units of 1 KB (W, decayed q: 16 each; decayed k^T: 16;
-    # causal term: 8; exp(g_last): 1) plus T (w v) in fp32
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 4)
+    # causal term: 8; exp(g_last): 1) plus T (w v) in fp16 (fp32 for fp32 inputs)
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == B * H * nc * (57 * 1024 + C * D * 2)
     # fp32: units of 16 contraction indices, so twice the units (113), and T (w v) the same size
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 0) == B * H * nc * (113 * 1024 + C * D * 4)
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_DECODE, B, 1, H, D, D, C, 1) == 0
@@ -98,13 +98,13 @@ def test_workspace_bytes_two_level_forward():
     lib = _lib.load()
     B, T, H, D, C = 1, 65536, 16, 128, 64
     nc = T // C
-    base = B * H * nc * (57 * 1024 + C * D * 4)
+    base = B * H * nc * (57 * 1024 + C * D * 2)
     seg = B * H * 8 * (D * D + 2 * D * D) * 4
     assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, B, T, H, D, D, C, 1) == (base + 255) // 256 * 256 + seg
     # 128 heads fill the GPU with the plain chain: no segment buffers (the B=8 H=16 T=4096 training figure above)
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 8, 4096, 16, D, D, C, 1) == 8 * 16 * 64 * (57 * 1024 + C * D * 4)
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 8, 4096, 16, D, D, C, 1) == 8 * 16 * 64 * (57 * 1024 + C * D * 2)
     # fewer than 32 chunks: no segments
-    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, 31 * C, 2, D, D, C, 1) == 2 * 31 * (57 * 1024 + C * D * 4)
+    assert lib.gdn2_workspace_bytes(_lib.GDN2_OP_FWD, 1, 31 * C, 2, D, D, C, 1) == 2 * 31 * (57 * 1024 + C * D * 2)
 
 
 A = 4096  # a fake, 16-byte aligned address: never dereferenced because validation fails first

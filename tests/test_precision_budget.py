@@ -46,7 +46,7 @@ def split(x):
 POLICIES = {"bf16": (bf16, bf16), "fp16": (fp16, fp16), "kernel": (split, fp16)}  # (Gram factors, others)
 
 
-def chunk_fwd_rounded(S0, q, k, v, la, b, w, rg, rv):
+def chunk_fwd_rounded(S0, q, k, v, la, b, w, rg, rv, ut16=False):
     """One chunk of the WY forward with product operands rounded: rg for the Gram factors, rv otherwise."""
     L = q.shape[0]
     g = np.cumsum(la, axis=0)
@@ -63,13 +63,16 @@ def chunk_fwd_rounded(S0, q, k, v, la, b, w, rg, rv):
     Qh = q * np.exp(g)
     Kb = k * np.exp(gC - g)
     W = rv(T) @ rv(Kh)
-    U = rv(T) @ rv(w * v) - rv(W) @ rv(S0)
+    Ut = rv(T) @ rv(w * v)
+    if ut16:  # stored between the passes as fp16 (from its fp32 accumulator)
+        Ut = fp16(np.float32(Ut))
+    U = Ut - rv(W) @ rv(S0)
     O = rv(Qh) @ rv(S0) + rv(P) @ rv(U)
     S1 = np.exp(gC)[:, None] * S0 + rv(Kb).T @ rv(U)
     return O, S1
 
 
-def chunked_forward_rounded(inp, C, policy):
+def chunked_forward_rounded(inp, C, policy, ut16=False):
     rg, rv = POLICIES[policy]
     q, k, v, la, b, w = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v", "log_alpha", "b", "w"))
     B, T, H, _ = q.shape
@@ -80,7 +83,7 @@ def chunked_forward_rounded(inp, C, policy):
             for s in range(0, T, C):
                 e = min(s + C, T)
                 sl = (bi, slice(s, e), h)
-                o[sl], S = chunk_fwd_rounded(S, q[sl], k[sl], v[sl], la[sl], b[sl], w[sl], rg, rv)
+                o[sl], S = chunk_fwd_rounded(S, q[sl], k[sl], v[sl], la[sl], b[sl], w[sl], rg, rv, ut16)
     return o
 
 
@@ -130,6 +133,24 @@ def test_model_is_exact_without_rounding():
         del POLICIES["exact"]
     o_ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"])
     assert rel_err(o, o_ref) < 1e-9
+
+
+def test_stored_ut_in_fp16_costs_nothing():
+    """T (w v) stored as fp16 between the record pass and the chain (16-bit inputs): U = Ut - W S becomes an
+    fp16 operand in each of its uses, so one more rounding of Ut leaves the error against the oracle where
+    the kernel policy has it (within 10 %), at both decay levels."""
+    for strong in (False, True):
+        inp = _inputs(strong)
+        o_ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["b"], inp["w"])
+        e = {}
+        for ut16 in (False, True):
+            POLICIES["ut"] = (split, fp16)
+            try:
+                o = chunked_forward_rounded(inp, 64, "ut", ut16=ut16)
+            finally:
+                del POLICIES["ut"]
+            e[ut16] = rel_err(o, o_ref)
+        assert e[True] < 1.1 * e[False] and e[True] < TOL_BF16 / 2, (strong, e)
 
 
 @pytest.mark.parametrize("scale", [1e-7, 1e-3, 1.0, 1e3])
