@@ -1019,6 +1019,9 @@ int fwd_segments(int B, int H, int T, int Dk, int Dv, int chunk) {
   // less than the extra map and composition work of more (B1 H16 d128: T = 8K 0.36 -> 0.31 ms, 16K
   // 0.57 -> 0.52 ms; equal at 32K and 64K; one per CU at 64K was not faster)
   long g = 128 / (nbh * ((Dv + 127) / 128));
+  // twice as many where the segments stay at least 64 chunks long (one run-pass workgroup per CU: B1 H16
+  // d128 T = 64K 1.67 -> 1.62 ms; at 8K-32K the map and composition work of the shorter segments lost or tied)
+  if (g >= 4 && NC / (2 * g) >= 64) g *= 2;
   if (g > NC / 8) g = NC / 8;                // at least 8 chunks per segment
   if (g > 64) g = 64;
   if (g < 4) return 1;
