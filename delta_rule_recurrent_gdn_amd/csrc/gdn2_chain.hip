@@ -82,6 +82,10 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // 1.74 -> 1.85 ms).
 constexpr int kSegWaves = 8;
 
+// threads of the segment composition: eight waves, each one 16-row tile of the state's 32 columns
+// (its products are a chain of dependent fp32 matrix-core steps; two waves per SIMD overlap theirs)
+constexpr int kComposeThreads = 512;
+
 // Segment slot and column group of a workgroup of the two-level chain's passes. The column groups of one
 // segment take workgroups 8 apart, so that they run on one XCD and read each record through its L2 once
 // (B1 H16 T64K forward 1.77 -> 1.74 ms); -1 past the last slot (the grid is rounded up to whole groups of
@@ -896,14 +900,15 @@ template <int DK>
 // S_in(count-1) = start (dS_final), empty sequences copying start to empty_out (dS0).
 // gscale (reverse, 16-bit inputs): start is dS_final, taken times grad_scale() as the reverse chain
 // takes it; an empty sequence's dS0 is written without the scale.
-__global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
+__global__ __launch_bounds__(kComposeThreads) void gdn2_seg_compose_kernel(const float* S0, float* S_final, SegArgs sg,
                                                               Varlen vl, int nbh, int H, int Dv, bool reverse,
                                                               const float* gscale) {
   constexpr int LDM = DK + 4, LDS_ = 32 + 4;
   constexpr int NM4 = DK * DK / 4;              // float4 of one M
-  constexpr int MV = (NM4 + 255) / 256;         // per thread
+  constexpr int NT = kComposeThreads, NWC = NT / 64;
+  constexpr int MV = (NM4 + NT - 1) / NT;       // per thread
   constexpr int RT = DK / 16;                   // row tiles
-  constexpr int RPW = (RT + 3) / 4;             // row tiles per wave
+  constexpr int RPW = (RT + NWC - 1) / NWC;     // row tiles per wave
   __shared__ __attribute__((aligned(16))) float sM[DK * LDM];
   __shared__ __attribute__((aligned(16))) float sS[DK * LDS_];
   const int ncg = Dv / 32;
@@ -923,7 +928,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   }
   const int tid = threadIdx.x, wid = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const float gsc = grad_scale(gscale, bh);
-  for (int e = tid; e < DK * 32; e += 256) {
+  for (int e = tid; e < DK * 32; e += NT) {
     const int d = e >> 5, c = e & 31;
     sS[d * LDS_ + c] = S0 ? gsc * S0[((int64_t)bh * DK + d) * Dv + j0 + c] : 0.f;
   }
@@ -935,11 +940,11 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     const float4* M = reinterpret_cast<const float4*>(sg.M + (base + src(s)) * DK * DK);
 #pragma unroll
     for (int i = 0; i < MV; ++i)
-      if (tid + 256 * i < NM4) mr[i] = M[tid + 256 * i];
+      if (tid + NT * i < NM4) mr[i] = M[tid + NT * i];
     const float* N = sg.N + (base + src(s)) * DK * Dv + j0;
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
-      const int R = wid + 4 * t;
+      const int R = wid + NWC * t;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -949,7 +954,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
   };
   if (count == 0) {  // an empty packed sequence has no segment to carry its state: S_final = S0
     __syncthreads();
-    for (int e = tid; S_final && e < DK * 32; e += 256) {
+    for (int e = tid; S_final && e < DK * 32; e += NT) {
       const int d = e >> 5, c = e & 31;
       S_final[((int64_t)bh * DK + d) * Dv + j0 + c] = sS[d * LDS_ + c] / gsc;
     }
@@ -960,7 +965,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     const int64_t sb = base + src(s);
 #pragma unroll
     for (int i = 0; i < MV; ++i) {
-      const int e = tid + 256 * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
+      const int e = tid + NT * i, row = e / (DK / 4), c4 = 4 * (e % (DK / 4));
       if (e < NM4) *reinterpret_cast<float4*>(sM + row * LDM + c4) = mr[i];
     }
     f32x4 acc[RPW][2];
@@ -974,7 +979,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     if (s + 2 < count) load_m(s + 1);
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
-      const int R = wid + 4 * t;
+      const int R = wid + NWC * t;
       if (R < RT) {
         for (int k0 = 0; k0 < DK; k0 += 16) {
           const float4 a4 = *reinterpret_cast<const float4*>(sM + (16 * R + lr) * LDM + k0 + 4 * lg);
@@ -992,7 +997,7 @@ __global__ __launch_bounds__(256) void gdn2_seg_compose_kernel(const float* S0, 
     float* out = sg.S_in + (reverse ? sb - 1 : sb + 1) * DK * Dv + j0;
 #pragma unroll
     for (int t = 0; t < RPW; ++t) {
-      const int R = wid + 4 * t;
+      const int R = wid + NWC * t;
       if (R < RT) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -1063,7 +1068,7 @@ static hipError_t launch_chain_seg(const FwdArgs& a, const char* rec, const floa
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) entry states of the later segments
-    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(256), 0, s, a.S0,
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(kComposeThreads), 0, s, a.S0,
                        a.S_final, sg, a.vl, nbh, a.H, a.Dv, false, static_cast<const float*>(nullptr));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1166,7 +1171,7 @@ static hipError_t launch_chain_bwd_seg(const BwdArgs& a, const char* rec, char* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // (2) exit gradients of the earlier segments, composed backwards from dS_final
-    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(256), 0, s, a.dS_final,
+    hipLaunchKernelGGL((gdn2_seg_compose_kernel<DK>), dim3(seg_grid(nbh, a.Dv / 32)), dim3(kComposeThreads), 0, s, a.dS_final,
                        a.dS0, sg, a.vl, nbh, a.H, a.Dv, true, a.gscale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
