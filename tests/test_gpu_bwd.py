@@ -148,6 +148,7 @@ def test_bwd_gdn_special_case_matches_oracle():
     (1, 3, 40 * 64 + 7, 128, 128, 64, "bf16"),   # d = 128 heads: 5 segments
     (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16 identity columns after 64 value columns
     (1, 1, 36 * 32, 64, 128, 32, "fp32"),
+    (1, 4, 256 * 16 + 3, 32, 32, 16, "fp32"),   # 257 chunks: 29 segments of 9, a long composition
 ])
 @pytest.mark.parametrize("use_states", [True, False], ids=["saved_states", "recomputed_states"])
 def test_bwd_two_level_reverse_chain(B, H, T, Dk, Dv, C, dtype, use_states):

@@ -189,6 +189,7 @@ SEGMENTED = [
     (2, 1, 64 * 32, 16, 64, 32, "bf16"),         # Dk = 16: 16 identity columns after 64 value columns
     (1, 2, 48 * 32 + 31, 128, 32, 32, "bf16"),   # map pass of 160 columns: two column groups
     (1, 1, 36 * 32, 64, 128, 32, "fp32"),
+    (1, 4, 256 * 16 + 3, 32, 32, 16, "fp32"),   # 257 chunks: 29 segments of 9, a long composition
 ]
 
 
