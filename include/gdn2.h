@@ -62,9 +62,9 @@
  *   or sequence, head), by the power of two that brings their largest
  *   magnitude into [1, 2) (a pre-pass over dO), and every gradient back on its
  *   store, so the fp16 operand range does not limit the upstream gradients'
- *   scale; the forward's fp16 operands hold v, w*v, U and the state, whose
- *   products must stay within fp16's range (|v| and |S0| up to 2^12 are
- *   tested).
+ *   scale; the forward's fp16 operands hold v, w*v, T (w*v) (also stored as
+ *   fp16 between the two stages), U and the state, whose products must stay
+ *   within fp16's range (|v| and |S0| up to 2^12 are tested).
  * - Results are deterministic (no floating-point atomics): identical inputs
  *   give bitwise identical outputs.
  * - A nullable input means zeros; a nullable output means "not written".
